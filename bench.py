@@ -1,0 +1,183 @@
+"""Benchmark of the SSD chunked forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload layer27b]
+
+A step is one full forward pass (every kernel of the path) over one batch of
+seeded synthetic inputs already resident in HBM; the default workload is the
+Mamba-2 2.7B-shaped layer: batch 8, seqlen 2048, 80 heads, headdim 64, dstate
+128, 1 group, chunk 256, x/B/C/y in bf16, dt/A/D and the states in fp32.
+
+Prints one JSON line with the throughput (tokens/s), the HBM roofline of the
+dominant kernel (algorithmic bytes per launch over its average launch time,
+measured with HIP events on the stream the kernel runs on), and the fp64 CPU
+oracle timed on the host cores as a reported baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+METRIC = "SSD fwd tokens/s + HBM GB/s (% of peak), Mamba-2 2.7B layer, L=2048"
+KERNEL_SOURCES = ["ssd_common.hpp", "ssd_segsum.hpp", "ssd_chunk_bf16.hpp", "ssd_chunk_f32.hip",
+                  "ssd_aux.hip", "ssd_api.cpp", "ssd_chunk_bf16_q64.hip",
+                  "ssd_chunk_bf16_q128.hip", "ssd_chunk_bf16_q256.hip"]
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "ssd_chunked_scan_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of
+    this workload, if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"ssd_chunk_bf16_{workload}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(inp, repeats: int = 3):
+    """The fp64 oracle on the host cores over the whole workload (every batch
+    row and head); median of ``repeats`` runs."""
+    import oracle
+    threads = oracle.max_threads()
+    units = inp.wl.batch * inp.wl.nheads
+    times = []
+    for _ in range(repeats):
+        t = time.perf_counter()
+        oracle.ssd_forward(inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D, inp.seq_idx)
+        times.append(time.perf_counter() - t)
+    times.sort()
+    med = times[len(times) // 2]
+    return {"value": inp.wl.tokens / med, "unit": "tokens/s", "cores": min(threads, units),
+            "kind": "oracle",
+            "sample": f"whole workload ({inp.wl.batch}x{inp.wl.seqlen} tokens x {inp.wl.nheads} "
+                      f"heads), fp64 recurrence, median of {repeats} runs of {med:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="layer27b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the forward pass shards by head or by sequence without a collective for the "
+              "head split, but no multi-GPU path is built", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import ssd_chunked_scan_amd as ssd
+    import workloads
+
+    wl = workloads.WORKLOADS[args.workload]
+    inp = workloads.make_inputs(wl, seed=0)
+    dev = torch.device("cuda:0")
+    io = torch.bfloat16 if wl.io == "bf16" else torch.float32
+    t = lambda a, d=torch.float32: torch.from_numpy(a).to(dev).to(d).contiguous()
+    x, dt, A, B, C, D = t(inp.x, io), t(inp.dt), t(inp.A), t(inp.B, io), t(inp.C, io), t(inp.D)
+    seq = None if inp.seq_idx is None else torch.from_numpy(inp.seq_idx).to(dev)
+    y = torch.empty_like(x)
+    fs = torch.empty((wl.batch, wl.nheads, wl.headdim, wl.dstate), dtype=torch.float32, device=dev)
+    shape = ssd.Shape(wl.batch, wl.seqlen, wl.nheads, wl.headdim, wl.dstate, wl.ngroups)
+    io_code = 1 if wl.io == "bf16" else 0
+    ws_bytes = ssd.ssd_fwd_workspace_bytes(shape, wl.chunk_size, io_code)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    split_len = ssd.ssd_plan_split_len(shape, wl.chunk_size, io_code)
+
+    def step():
+        ssd.ssd_fwd(x, dt, A, B, C, D, seq, chunk_size=wl.chunk_size, y=y, final_states=fs,
+                    workspace=ws)
+
+    print(f"bench: {wl.name} {wl.batch}x{wl.seqlen} H{wl.nheads} P{wl.headdim} N{wl.dstate} "
+          f"G{wl.ngroups} Q{wl.chunk_size} {wl.io}; split {split_len} tokens; warmup "
+          f"{args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+
+    # Whole-job timing: K back-to-back steps between two synchronisations.
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    # Per-launch timing with HIP events on the stream the kernels run on.
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize(dev)
+    launch_ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    avg_launch_ms = sum(launch_ms) / len(launch_ms)
+    print(f"bench: wall {ms_per_step * 1e3:.1f} us/step; event avg {avg_launch_ms * 1e3:.1f} us "
+          f"(p10 {launch_ms[len(launch_ms) // 10] * 1e3:.1f}, "
+          f"p90 {launch_ms[(9 * len(launch_ms)) // 10] * 1e3:.1f})", file=sys.stderr, flush=True)
+
+    alg_bytes = wl.algorithmic_bytes()
+    achieved = alg_bytes / (avg_launch_ms * 1e-3) / 1e9
+    traffic = counter_traffic(wl.name)
+    out = {
+        "metric": METRIC,
+        "value": wl.tokens / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.io,
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: Mamba-2 2.7B-shaped SSD layer", "batch": wl.batch,
+                   "seqlen": wl.seqlen, "nheads": wl.nheads, "headdim": wl.headdim,
+                   "dstate": wl.dstate, "ngroups": wl.ngroups, "chunk_size": wl.chunk_size,
+                   "split_len": split_len, "parallelism": "single GPU"},
+        "hbm_gbs": alg_bytes / (ms_per_step * 1e-3) / 1e9,
+        "hbm_frac_of_peak": alg_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": alg_bytes,
+                     "avg_launch_us": avg_launch_ms * 1e3},
+    }
+    if not args.no_cpu_baseline:
+        print("bench: timing the fp64 CPU oracle", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,156 @@
+/*
+ * ssd.h - C ABI of the MI355X (gfx950) SSD chunked forward pass.
+ *
+ * The operation is the Mamba-2 structured-state-space-duality forward pass
+ * (page "State Space Duality and Mamba-2", sections "The Mathematical Bridge"
+ * and "The SSD Block Decomposition Algorithm"):
+ *
+ *     a_t = exp(dt_t * A_h)                       scalar decay per token/head
+ *     h_t = a_t * h_{t-1} + dt_t * x_t B_t^T      state, P x N per head
+ *     y_t = h_t C_t + D_h * x_t
+ *
+ * equivalently Y = ((C B^T) o L) (dt x) + D x with the 1-semiseparable decay
+ * mask L_ij = prod_{k=j+1..i} a_k (i >= j), evaluated blockwise: the sequence
+ * is cut into chunks of chunk_size tokens; each chunk's diagonal block is a
+ * masked quadratic product, and chunks are connected through the N x P state
+ * (chunk-state contraction, inter-chunk scan, state projection onto the next
+ * chunk's outputs).  Long rows are cut into sequence-parallel splits whose
+ * length is chosen independently of chunk_size (page "GPU Hierarchy Meets
+ * Structured Matrices", abstract: split-sequence algorithm); splits are joined
+ * by an affine scan of their boundary states (page "Parallel Scan and
+ * Hardware-Aware SSM Kernels", section "The scan").
+ *
+ * Document packing: where seq_idx changes between tokens t-1 and t the state
+ * is reset (a_t is masked to 0), so no information flows across a document
+ * boundary (page "Parallel Scan and Hardware-Aware SSM Kernels", section
+ * "When it breaks").
+ *
+ * Layouts: every tensor is dense and row-major, no strides.
+ *   x, y          [batch, seqlen, nheads, headdim]   io dtype
+ *   dt            [batch, seqlen, nheads]            fp32, > 0 (post-softplus)
+ *   A             [nheads]                           fp32, <= 0
+ *   B, C          [batch, seqlen, ngroups, dstate]   io dtype
+ *   D             [nheads]                           fp32 (nullable: no skip)
+ *   seq_idx       [batch, seqlen]                    int32 (nullable: 1 doc/row)
+ *   init_states,
+ *   final_states  [batch, nheads, headdim, dstate]   fp32 (nullable)
+ * Head h reads B/C group h / (nheads / ngroups) (grouped-query SSM, page
+ * "State Space Duality and Mamba-2", section "Architectural Scaling").
+ * init_states feeds only the first document of each row; final_states is the
+ * state after the row's last token.
+ *
+ * Ownership and threading: the caller allocates every device buffer,
+ * including the workspace; the library allocates no device memory and keeps
+ * no mutable global state except a per-device cache of the compute-unit
+ * count.  Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ * stream), reentrant, and make no implicit synchronisation.  Concurrent calls
+ * must not share a workspace.
+ *
+ * Errors: arguments are validated on the host before any HIP call; on failure
+ * the call returns a status, launches nothing and records a message readable
+ * with ssd_last_error() (thread-local).  A failed launch returns SSD_ERR_HIP.
+ * Device-side faults surface at the caller's next synchronisation.  NaN or
+ * Inf inputs propagate; the hot path does not check values.
+ *
+ * Supported set (anything else returns SSD_ERR_UNSUPPORTED):
+ *   chunk_size in {64, 128, 256}; headdim in {16, 32, 64, 128};
+ *   dstate in {16, 32, 64, 128}; nheads % ngroups == 0; seqlen >= 1;
+ *   batch >= 1; x, B, C, y 16-byte aligned; every fp32 buffer 4-byte aligned
+ *   and init/final states 16-byte aligned.
+ */
+#ifndef SSD_MI355X_H
+#define SSD_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SSD_OK = 0,
+    SSD_ERR_NULL = 1,         /* a required pointer is NULL               */
+    SSD_ERR_SHAPE = 2,        /* a size is < 1 or sizes are inconsistent  */
+    SSD_ERR_UNSUPPORTED = 3,  /* outside the supported set above          */
+    SSD_ERR_ALIGN = 4,        /* a pointer is not aligned as required     */
+    SSD_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than required  */
+    SSD_ERR_HIP = 6           /* a HIP runtime call or launch failed      */
+} ssd_status_t;
+
+typedef enum {
+    SSD_F32 = 0,   /* x, B, C, y in fp32; fp32 arithmetic throughout          */
+    SSD_BF16 = 1   /* x, B, C, y in bf16; bf16 MFMA with fp32 accumulation    */
+} ssd_dtype_t;
+
+typedef struct {
+    int64_t batch, seqlen, nheads, headdim, dstate, ngroups;
+} ssd_shape_t;
+
+/* Test/benchmark options.  Zero-initialise for the defaults. */
+typedef struct {
+    int64_t split_len;   /* tokens per sequence-parallel split: 0 = planner's
+                            choice, else a positive multiple of chunk_size   */
+    int64_t reserved[7]; /* must be zero                                      */
+} ssd_options_t;
+
+/* Bytes of device workspace ssd_fwd needs for this problem (16-byte aligned
+ * pointer required).  Returns 0 when no workspace is needed, and also for an
+ * invalid problem (ssd_fwd then reports the error). */
+size_t ssd_fwd_workspace_bytes(const ssd_shape_t *shape, int64_t chunk_size,
+                               ssd_dtype_t io);
+
+/* The forward pass.  x, dt, A, B, C, y are required; D, seq_idx, init_states
+ * and final_states may be NULL.  The workspace may be NULL when
+ * ssd_fwd_workspace_bytes() returns 0. */
+ssd_status_t ssd_fwd(const ssd_shape_t *shape, ssd_dtype_t io,
+                     const void *x, const float *dt, const float *A,
+                     const void *B, const void *C, const float *D,
+                     const int32_t *seq_idx, int64_t chunk_size,
+                     const float *init_states,
+                     void *y, float *final_states,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/* ssd_fwd with options (tests and benchmarks: forced split length). */
+size_t ssd_fwd_ex_workspace_bytes(const ssd_shape_t *shape, int64_t chunk_size,
+                                  ssd_dtype_t io, const ssd_options_t *opts);
+ssd_status_t ssd_fwd_ex(const ssd_shape_t *shape, ssd_dtype_t io,
+                        const void *x, const float *dt, const float *A,
+                        const void *B, const void *C, const float *D,
+                        const int32_t *seq_idx, int64_t chunk_size,
+                        const float *init_states,
+                        void *y, float *final_states,
+                        void *workspace, size_t workspace_bytes,
+                        const ssd_options_t *opts, void *stream);
+
+/* The split length (tokens) the planner would use; 0 for an invalid problem. */
+int64_t ssd_plan_split_len(const ssd_shape_t *shape, int64_t chunk_size,
+                           ssd_dtype_t io);
+
+/* Debug export of the decay mask exactly as the forward kernels build it
+ * (page "GPU Hierarchy Meets Structured Matrices", abstract: hierarchy-aware
+ * segsum; page "State Space Duality and Mamba-2", definition of L).  Writes
+ * fp32 L_out[batch][nheads][chunk_count][chunk_size][chunk_size] for chunks
+ * [chunk_begin, chunk_begin + chunk_count): L[i][j] = prod_{k=j+1..i} a_k for
+ * j <= i, 0 above the diagonal, 0 across a document boundary, 0 for tokens
+ * past the end of the row.  Only x-independent inputs are needed.  dstate,
+ * headdim and ngroups in `shape` are validated but unused. */
+ssd_status_t ssd_debug_chunk_mask(const ssd_shape_t *shape, const float *dt,
+                                  const float *A, const int32_t *seq_idx,
+                                  int64_t chunk_size, int64_t chunk_begin,
+                                  int64_t chunk_count, float *L_out,
+                                  void *stream);
+
+const char *ssd_status_str(ssd_status_t status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char *ssd_last_error(void);
+
+/* Library version string. */
+const char *ssd_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSD_MI355X_H */

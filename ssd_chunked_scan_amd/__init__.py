@@ -1,0 +1,214 @@
+"""MI355X (gfx950) SSD chunked forward pass: thin Python binding of libssd.so.
+
+Every step of the forward pass runs in the HIP kernels behind the C ABI in
+include/ssd.h; this module only marshals torch tensors (device memory and the
+current HIP stream) into that ABI.  There is no CPU or PyTorch fallback: if
+libssd.so is missing or fails to load, every call raises.
+
+    y, final_states = ssd_fwd(x, dt, A, B, C, D, seq_idx=None, chunk_size=256)
+
+Shapes (dense, contiguous): x [b, L, H, P]; dt [b, L, H] fp32; A [H] fp32;
+B, C [b, L, G, N]; D [H] fp32 or None; seq_idx [b, L] int32 or None;
+init_states [b, H, P, N] fp32 or None.  x, B, C share one dtype, bf16 or
+fp32; y has that dtype; final_states is fp32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+__all__ = [
+    "ssd_fwd", "ssd_fwd_workspace_bytes", "ssd_plan_split_len", "ssd_debug_chunk_mask",
+    "SsdError", "library_path", "load_library", "STATUS", "EXPORTS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libssd.so")
+
+SSD_F32, SSD_BF16 = 0, 1
+STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_UNSUPPORTED",
+          4: "SSD_ERR_ALIGN", 5: "SSD_ERR_WORKSPACE", 6: "SSD_ERR_HIP"}
+EXPORTS = ["ssd_fwd_workspace_bytes", "ssd_fwd", "ssd_fwd_ex_workspace_bytes", "ssd_fwd_ex",
+           "ssd_plan_split_len", "ssd_debug_chunk_mask", "ssd_status_str", "ssd_last_error",
+           "ssd_version"]
+
+
+class SsdError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64),
+                ("nheads", ctypes.c_int64), ("headdim", ctypes.c_int64),
+                ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64)]
+
+
+class Options(ctypes.Structure):
+    _fields_ = [("split_len", ctypes.c_int64), ("reserved", ctypes.c_int64 * 7)]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libssd.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with "
+                          "`python -m ssd_chunked_scan_amd._build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, sz, i64, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int64, ctypes.c_int
+    shp, opt = ctypes.POINTER(Shape), ctypes.POINTER(Options)
+    lib.ssd_fwd_workspace_bytes.argtypes = [shp, i64, i32]
+    lib.ssd_fwd_workspace_bytes.restype = sz
+    lib.ssd_fwd_ex_workspace_bytes.argtypes = [shp, i64, i32, opt]
+    lib.ssd_fwd_ex_workspace_bytes.restype = sz
+    lib.ssd_plan_split_len.argtypes = [shp, i64, i32]
+    lib.ssd_plan_split_len.restype = i64
+    fwd_args = [shp, i32, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz]
+    lib.ssd_fwd.argtypes = fwd_args + [vp]
+    lib.ssd_fwd.restype = i32
+    lib.ssd_fwd_ex.argtypes = fwd_args + [opt, vp]
+    lib.ssd_fwd_ex.restype = i32
+    lib.ssd_debug_chunk_mask.argtypes = [shp, vp, vp, vp, i64, i64, i64, vp, vp]
+    lib.ssd_debug_chunk_mask.restype = i32
+    lib.ssd_status_str.argtypes = [i32]
+    lib.ssd_status_str.restype = ctypes.c_char_p
+    lib.ssd_last_error.argtypes = []
+    lib.ssd_last_error.restype = ctypes.c_char_p
+    lib.ssd_version.argtypes = []
+    lib.ssd_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise SsdError(status, load_library().ssd_last_error().decode())
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _io_code(dtype) -> int:
+    import torch
+    if dtype == torch.bfloat16:
+        return SSD_BF16
+    if dtype == torch.float32:
+        return SSD_F32
+    raise TypeError(f"x/B/C dtype must be bfloat16 or float32, got {dtype}")
+
+
+def _need(t, name, shape, dtype, device):
+    if t.shape != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def make_shape(batch, seqlen, nheads, headdim, dstate, ngroups) -> Shape:
+    return Shape(batch, seqlen, nheads, headdim, dstate, ngroups)
+
+
+def ssd_fwd_workspace_bytes(shape: Shape, chunk_size: int, io: int, split_len: int = 0) -> int:
+    lib = load_library()
+    if split_len:
+        return int(lib.ssd_fwd_ex_workspace_bytes(ctypes.byref(shape), chunk_size, io,
+                                                  ctypes.byref(Options(split_len))))
+    return int(lib.ssd_fwd_workspace_bytes(ctypes.byref(shape), chunk_size, io))
+
+
+def ssd_plan_split_len(shape: Shape, chunk_size: int, io: int) -> int:
+    return int(load_library().ssd_plan_split_len(ctypes.byref(shape), chunk_size, io))
+
+
+def ssd_fwd(x, dt, A, B, C, D=None, seq_idx=None, chunk_size: int = 256, init_states=None,
+            return_final_states: bool = True, split_len: int = 0, y=None, final_states=None,
+            workspace=None, stream=None) -> Tuple[object, Optional[object]]:
+    """Run the forward pass on x.device.  Returns (y, final_states or None).
+    ``split_len`` forces the sequence-parallel split length (0 = planner).
+    Preallocated ``y`` / ``final_states`` / ``workspace`` (uint8) may be given."""
+    import torch
+    lib = load_library()
+    if x.dim() != 4 or B.dim() != 4:
+        raise ValueError("x must be [b, L, H, P] and B, C [b, L, G, N]")
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("ssd_fwd runs on the GPU only (x is on %s)" % dev)
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    io = _io_code(x.dtype)
+    _need(x, "x", (b, L, H, P), x.dtype, dev)
+    _need(dt, "dt", (b, L, H), torch.float32, dev)
+    _need(A, "A", (H,), torch.float32, dev)
+    _need(B, "B", (b, L, G, N), x.dtype, dev)
+    _need(C, "C", (b, L, G, N), x.dtype, dev)
+    if D is not None:
+        _need(D, "D", (H,), torch.float32, dev)
+    if seq_idx is not None:
+        _need(seq_idx, "seq_idx", (b, L), torch.int32, dev)
+    if init_states is not None:
+        _need(init_states, "init_states", (b, H, P, N), torch.float32, dev)
+    shape = Shape(b, L, H, P, N, G)
+    if y is None:
+        y = torch.empty_like(x)
+    else:
+        _need(y, "y", (b, L, H, P), x.dtype, dev)
+    if return_final_states and final_states is None:
+        final_states = torch.empty((b, H, P, N), dtype=torch.float32, device=dev)
+    elif final_states is not None:
+        _need(final_states, "final_states", (b, H, P, N), torch.float32, dev)
+    opts = Options(split_len)
+    with torch.cuda.device(dev):
+        ws_bytes = int(lib.ssd_fwd_ex_workspace_bytes(ctypes.byref(shape), chunk_size, io,
+                                                      ctypes.byref(opts)))
+        if ws_bytes and (workspace is None or workspace.numel() < ws_bytes):
+            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        if stream is None:
+            stream = torch.cuda.current_stream(dev).cuda_stream
+        st = lib.ssd_fwd_ex(ctypes.byref(shape), io, _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+                            _ptr(C), _ptr(D), _ptr(seq_idx), chunk_size, _ptr(init_states),
+                            _ptr(y), _ptr(final_states),
+                            _ptr(workspace) if ws_bytes else None, ws_bytes,
+                            ctypes.byref(opts), stream)
+    _check(st)
+    return y, (final_states if return_final_states else None)
+
+
+def ssd_debug_chunk_mask(dt, A, seq_idx=None, chunk_size: int = 256, chunk_begin: int = 0,
+                         chunk_count: Optional[int] = None):
+    """The decay mask of chunks [chunk_begin, chunk_begin + chunk_count) as the
+    forward kernels build it: fp32 [b, H, chunk_count, Q, Q]."""
+    import torch
+    lib = load_library()
+    b, L, H = dt.shape
+    dev = dt.device
+    _need(dt, "dt", (b, L, H), torch.float32, dev)
+    _need(A, "A", (H,), torch.float32, dev)
+    if seq_idx is not None:
+        _need(seq_idx, "seq_idx", (b, L), torch.int32, dev)
+    nchunks = (L + chunk_size - 1) // chunk_size
+    if chunk_count is None:
+        chunk_count = nchunks - chunk_begin
+    out = torch.empty((b, H, chunk_count, chunk_size, chunk_size), dtype=torch.float32, device=dev)
+    shape = Shape(b, L, H, 16, 16, 1)
+    with torch.cuda.device(dev):
+        st = lib.ssd_debug_chunk_mask(ctypes.byref(shape), _ptr(dt), _ptr(A), _ptr(seq_idx),
+                                      chunk_size, chunk_begin, chunk_count, _ptr(out),
+                                      torch.cuda.current_stream(dev).cuda_stream)
+    _check(st)
+    return out

@@ -1,0 +1,324 @@
+// Host side of the C ABI declared in include/ssd.h: argument validation,
+// the split planner and the kernel launches.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/ssd.h"
+#include "ssd_common.hpp"
+
+namespace ssd {
+bool launch_chunk_bf16_q64(int N, int PB, const ChunkArgs &a, hipStream_t stream);
+bool launch_chunk_bf16_q128(int N, int PB, const ChunkArgs &a, hipStream_t stream);
+bool launch_chunk_bf16_q256(int N, int PB, const ChunkArgs &a, hipStream_t stream);
+void launch_chunk_f32(int Q, const ChunkArgs &a, hipStream_t stream);
+void launch_split_scan(const float *init_states, float *ws_states, const float *ws_decay,
+                       int batch, int nheads, int nsplits, int pn, hipStream_t stream);
+void launch_mask(int Q, const MaskArgs &m, hipStream_t stream);
+}  // namespace ssd
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ssd_status_t fail(ssd_status_t st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool pow2_in(int64_t v, int64_t lo, int64_t hi) {
+    return v >= lo && v <= hi && (v & (v - 1)) == 0;
+}
+
+// Element counts above this are rejected so that every index fits the
+// kernels' 64-bit offsets and every per-row count fits 32 bits.
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+
+ssd_status_t check_shape(const ssd_shape_t *s, int64_t chunk) {
+    if (!s) return fail(SSD_ERR_NULL, "shape is NULL");
+    if (s->batch < 1 || s->seqlen < 1 || s->nheads < 1 || s->headdim < 1 || s->dstate < 1 ||
+        s->ngroups < 1)
+        return fail(SSD_ERR_SHAPE, "sizes must be >= 1 (batch %lld seqlen %lld nheads %lld "
+                    "headdim %lld dstate %lld ngroups %lld)", (long long)s->batch,
+                    (long long)s->seqlen, (long long)s->nheads, (long long)s->headdim,
+                    (long long)s->dstate, (long long)s->ngroups);
+    if (s->nheads % s->ngroups != 0)
+        return fail(SSD_ERR_SHAPE, "nheads (%lld) must be a multiple of ngroups (%lld)",
+                    (long long)s->nheads, (long long)s->ngroups);
+    if (s->batch > kMaxDim || s->seqlen > kMaxDim || s->nheads > 65536 ||
+        s->batch * s->seqlen > kMaxDim)
+        return fail(SSD_ERR_UNSUPPORTED, "problem too large");
+    if (chunk != 64 && chunk != 128 && chunk != 256)
+        return fail(SSD_ERR_UNSUPPORTED, "chunk_size %lld not in {64, 128, 256}", (long long)chunk);
+    if (!pow2_in(s->headdim, 16, 128))
+        return fail(SSD_ERR_UNSUPPORTED, "headdim %lld not in {16, 32, 64, 128}", (long long)s->headdim);
+    if (!pow2_in(s->dstate, 16, 128))
+        return fail(SSD_ERR_UNSUPPORTED, "dstate %lld not in {16, 32, 64, 128}", (long long)s->dstate);
+    return SSD_OK;
+}
+
+int g_cu_cache[64];
+std::atomic<int> g_cu_ready[64];
+
+// Compute units of the current device (cached; 256 when no device answers,
+// so that planning also works in host-only tests).
+int device_cus() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    if (g_cu_ready[dev].load(std::memory_order_acquire)) return g_cu_cache[dev];
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    g_cu_cache[dev] = cus;
+    g_cu_ready[dev].store(1, std::memory_order_release);
+    return cus;
+}
+
+struct Plan {
+    int nchunks, nsplits, split_chunks, npblocks, pblock;
+    size_t ws_bytes;
+};
+
+// Headdim block of the bf16 kernel: the whole head unless its LDS tiles do
+// not fit (chunk 256, dstate 128, headdim 128 -> two blocks of 64).
+int bf16_pblock(int64_t Q, int64_t N, int64_t P) {
+    if (Q == 256 && N == 128 && P == 128) return 64;
+    return (int)P;
+}
+
+// Host-only validation of the problem description (no HIP call).
+ssd_status_t check_problem(const ssd_shape_t *s, int64_t chunk, ssd_dtype_t io,
+                           const ssd_options_t *opts) {
+    if (io != SSD_F32 && io != SSD_BF16) return fail(SSD_ERR_UNSUPPORTED, "unknown io dtype %d", (int)io);
+    ssd_status_t st = check_shape(s, chunk);
+    if (st != SSD_OK) return st;
+    if (opts) {
+        for (int k = 0; k < 7; ++k)
+            if (opts->reserved[k] != 0) return fail(SSD_ERR_UNSUPPORTED, "reserved option fields must be zero");
+        if (opts->split_len < 0 || (opts->split_len > 0 && opts->split_len % chunk != 0))
+            return fail(SSD_ERR_UNSUPPORTED, "split_len %lld must be 0 or a positive multiple of chunk_size",
+                        (long long)opts->split_len);
+    }
+    return SSD_OK;
+}
+
+// Split plan and workspace size of a validated problem.
+ssd_status_t make_plan(const ssd_shape_t *s, int64_t chunk, ssd_dtype_t io,
+                       const ssd_options_t *opts, Plan *pl) {
+    ssd_status_t st = check_problem(s, chunk, io, opts);
+    if (st != SSD_OK) return st;
+    pl->nchunks = (int)((s->seqlen + chunk - 1) / chunk);
+    pl->pblock = (io == SSD_BF16) ? bf16_pblock(chunk, s->dstate, s->headdim) : (int)s->headdim;
+    pl->npblocks = (int)(s->headdim / pl->pblock);
+    int nsplits = 1;
+    if (opts && opts->split_len > 0) {
+        const int64_t sc = opts->split_len / chunk;
+        nsplits = (int)((pl->nchunks + sc - 1) / sc);
+    } else {
+        // Split-sequence planning: the split length is chosen from the amount
+        // of independent work, not from the chunk size.  Enough workgroups to
+        // cover the device twice; rows never split below one chunk per split.
+        const int64_t units = s->batch * s->nheads * pl->npblocks;
+        const int64_t cus = device_cus();
+        if (units < cus) {
+            const int64_t want = (2 * cus + units - 1) / units;
+            nsplits = (int)std::min<int64_t>(want, pl->nchunks);
+        }
+    }
+    pl->split_chunks = (pl->nchunks + nsplits - 1) / nsplits;
+    pl->nsplits = (pl->nchunks + pl->split_chunks - 1) / pl->split_chunks;
+    if (pl->nsplits > 1) {
+        const size_t states = (size_t)s->batch * s->nheads * pl->nsplits * s->headdim * s->dstate;
+        const size_t decay = (size_t)s->batch * s->nheads * pl->nsplits;
+        pl->ws_bytes = (states + ((decay + 3) / 4) * 4) * sizeof(float);
+    } else {
+        pl->ws_bytes = 0;
+    }
+    return SSD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *ssd_status_str(ssd_status_t status) {
+    switch (status) {
+    case SSD_OK: return "SSD_OK";
+    case SSD_ERR_NULL: return "SSD_ERR_NULL";
+    case SSD_ERR_SHAPE: return "SSD_ERR_SHAPE";
+    case SSD_ERR_UNSUPPORTED: return "SSD_ERR_UNSUPPORTED";
+    case SSD_ERR_ALIGN: return "SSD_ERR_ALIGN";
+    case SSD_ERR_WORKSPACE: return "SSD_ERR_WORKSPACE";
+    case SSD_ERR_HIP: return "SSD_ERR_HIP";
+    }
+    return "SSD_ERR_UNKNOWN";
+}
+
+const char *ssd_last_error(void) { return g_last_error.c_str(); }
+
+const char *ssd_version(void) { return "ssd-mi355x 0.1 (gfx950)"; }
+
+size_t ssd_fwd_ex_workspace_bytes(const ssd_shape_t *shape, int64_t chunk_size, ssd_dtype_t io,
+                                  const ssd_options_t *opts) {
+    Plan pl;
+    if (make_plan(shape, chunk_size, io, opts, &pl) != SSD_OK) return 0;
+    return pl.ws_bytes;
+}
+
+size_t ssd_fwd_workspace_bytes(const ssd_shape_t *shape, int64_t chunk_size, ssd_dtype_t io) {
+    return ssd_fwd_ex_workspace_bytes(shape, chunk_size, io, nullptr);
+}
+
+int64_t ssd_plan_split_len(const ssd_shape_t *shape, int64_t chunk_size, ssd_dtype_t io) {
+    Plan pl;
+    if (make_plan(shape, chunk_size, io, nullptr, &pl) != SSD_OK) return 0;
+    return (int64_t)pl.split_chunks * chunk_size;
+}
+
+ssd_status_t ssd_fwd_ex(const ssd_shape_t *shape, ssd_dtype_t io, const void *x, const float *dt,
+                        const float *A, const void *B, const void *C, const float *D,
+                        const int32_t *seq_idx, int64_t chunk_size, const float *init_states,
+                        void *y, float *final_states, void *workspace, size_t workspace_bytes,
+                        const ssd_options_t *opts, void *stream) {
+    g_last_error.clear();
+    ssd_status_t st = check_problem(shape, chunk_size, io, opts);
+    if (st != SSD_OK) return st;
+    if (!x || !dt || !A || !B || !C || !y)
+        return fail(SSD_ERR_NULL, "x, dt, A, B, C and y are required");
+    const size_t io_align = 16;
+    if (!aligned(x, io_align) || !aligned(B, io_align) || !aligned(C, io_align) || !aligned(y, io_align))
+        return fail(SSD_ERR_ALIGN, "x, B, C and y must be 16-byte aligned");
+    if (!aligned(dt, 4) || !aligned(A, 4) || (D && !aligned(D, 4)) || (seq_idx && !aligned(seq_idx, 4)))
+        return fail(SSD_ERR_ALIGN, "dt, A, D and seq_idx must be 4-byte aligned");
+    if ((init_states && !aligned(init_states, 16)) || (final_states && !aligned(final_states, 16)))
+        return fail(SSD_ERR_ALIGN, "init_states and final_states must be 16-byte aligned");
+    Plan pl;
+    st = make_plan(shape, chunk_size, io, opts, &pl);
+    if (st != SSD_OK) return st;
+    if (pl.ws_bytes > 0) {
+        if (!workspace || workspace_bytes < pl.ws_bytes)
+            return fail(SSD_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given%s", pl.ws_bytes,
+                        workspace_bytes, workspace ? "" : " (NULL)");
+        if (!aligned(workspace, 16)) return fail(SSD_ERR_ALIGN, "workspace must be 16-byte aligned");
+    }
+
+    ssd::ChunkArgs a;
+    memset(&a, 0, sizeof(a));
+    a.x = x;
+    a.dt = dt;
+    a.A = A;
+    a.B = B;
+    a.C = C;
+    a.D = D;
+    a.seq_idx = seq_idx;
+    a.init_states = init_states;
+    a.y = y;
+    a.final_states = final_states;
+    float *ws = (float *)workspace;
+    a.ws_states = pl.nsplits > 1 ? ws : nullptr;
+    a.ws_decay = pl.nsplits > 1
+                     ? ws + (size_t)shape->batch * shape->nheads * pl.nsplits * shape->headdim * shape->dstate
+                     : nullptr;
+    a.batch = (int)shape->batch;
+    a.seqlen = (int)shape->seqlen;
+    a.nheads = (int)shape->nheads;
+    a.headdim = (int)shape->headdim;
+    a.dstate = (int)shape->dstate;
+    a.ngroups = (int)shape->ngroups;
+    a.chunk = (int)chunk_size;
+    a.nchunks = pl.nchunks;
+    a.nsplits = pl.nsplits;
+    a.split_chunks = pl.split_chunks;
+    a.npblocks = pl.npblocks;
+    a.pblock = pl.pblock;
+    a.units = a.batch * a.nheads * a.nsplits * a.npblocks;
+    hipStream_t s = (hipStream_t)stream;
+
+    auto launch = [&](const ssd::ChunkArgs &args) -> bool {
+        if (io == SSD_F32) {
+            ssd::launch_chunk_f32(args.chunk, args, s);
+            return true;
+        }
+        switch (args.chunk) {
+        case 64: return ssd::launch_chunk_bf16_q64(args.dstate, args.pblock, args, s);
+        case 128: return ssd::launch_chunk_bf16_q128(args.dstate, args.pblock, args, s);
+        default: return ssd::launch_chunk_bf16_q256(args.dstate, args.pblock, args, s);
+        }
+    };
+
+    (void)hipGetLastError();
+    if (a.nsplits > 1) {
+        ssd::ChunkArgs loc = a;
+        loc.mode = ssd::kModeSplitLocal;
+        if (!launch(loc)) return fail(SSD_ERR_UNSUPPORTED, "no kernel for this shape");
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return fail(SSD_ERR_HIP, "split-local launch: %s", hipGetErrorString(e));
+        ssd::launch_split_scan(init_states, a.ws_states, a.ws_decay, a.batch, a.nheads, a.nsplits,
+                               a.headdim * a.dstate, s);
+        e = hipGetLastError();
+        if (e != hipSuccess) return fail(SSD_ERR_HIP, "split-scan launch: %s", hipGetErrorString(e));
+    }
+    a.mode = ssd::kModeFull;
+    if (!launch(a)) return fail(SSD_ERR_UNSUPPORTED, "no kernel for this shape");
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(SSD_ERR_HIP, "chunk launch: %s", hipGetErrorString(e));
+    return SSD_OK;
+}
+
+ssd_status_t ssd_fwd(const ssd_shape_t *shape, ssd_dtype_t io, const void *x, const float *dt,
+                     const float *A, const void *B, const void *C, const float *D,
+                     const int32_t *seq_idx, int64_t chunk_size, const float *init_states, void *y,
+                     float *final_states, void *workspace, size_t workspace_bytes, void *stream) {
+    return ssd_fwd_ex(shape, io, x, dt, A, B, C, D, seq_idx, chunk_size, init_states, y, final_states,
+                      workspace, workspace_bytes, nullptr, stream);
+}
+
+ssd_status_t ssd_debug_chunk_mask(const ssd_shape_t *shape, const float *dt, const float *A,
+                                  const int32_t *seq_idx, int64_t chunk_size, int64_t chunk_begin,
+                                  int64_t chunk_count, float *L_out, void *stream) {
+    g_last_error.clear();
+    ssd_status_t st = check_shape(shape, chunk_size);
+    if (st != SSD_OK) return st;
+    if (!dt || !A || !L_out) return fail(SSD_ERR_NULL, "dt, A and L_out are required");
+    if (!aligned(L_out, 16)) return fail(SSD_ERR_ALIGN, "L_out must be 16-byte aligned");
+    if (!aligned(dt, 4) || !aligned(A, 4) || (seq_idx && !aligned(seq_idx, 4)))
+        return fail(SSD_ERR_ALIGN, "dt, A and seq_idx must be 4-byte aligned");
+    const int64_t nchunks = (shape->seqlen + chunk_size - 1) / chunk_size;
+    if (chunk_begin < 0 || chunk_count < 1 || chunk_begin + chunk_count > nchunks || chunk_count > 65535)
+        return fail(SSD_ERR_SHAPE, "chunk range [%lld, %lld) outside [0, %lld)", (long long)chunk_begin,
+                    (long long)(chunk_begin + chunk_count), (long long)nchunks);
+    ssd::MaskArgs m;
+    m.dt = dt;
+    m.A = A;
+    m.seq_idx = seq_idx;
+    m.out = L_out;
+    m.batch = (int)shape->batch;
+    m.seqlen = (int)shape->seqlen;
+    m.nheads = (int)shape->nheads;
+    m.chunk_begin = (int)chunk_begin;
+    m.count = (int)chunk_count;
+    (void)hipGetLastError();
+    ssd::launch_mask((int)chunk_size, m, (hipStream_t)stream);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(SSD_ERR_HIP, "mask launch: %s", hipGetErrorString(e));
+    return SSD_OK;
+}
+
+}  // extern "C"

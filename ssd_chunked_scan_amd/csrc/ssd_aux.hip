@@ -1,0 +1,111 @@
+// Auxiliary kernels of the SSD forward pass:
+//  * the inter-split state scan that joins sequence-parallel splits, and
+//  * the debug export of the decay mask exactly as the chunk kernels build it.
+#include "ssd_common.hpp"
+#include "ssd_segsum.hpp"
+
+namespace ssd {
+
+// Entering state of every split.  Split s holds its local end state (from a
+// zero state) and its decay T_s; the affine composition of page "Parallel
+// Scan and Hardware-Aware SSM Kernels" ("The scan": applying (A1, b1) then
+// (A2, b2) gives (A2 A1, A2 b1 + b2)) walked sequentially over the splits of
+// one row gives E_0 = init, E_{s+1} = T_s E_s + local_s.  Each slot is
+// overwritten by the entering state of its split.  One thread per state
+// element; the split count is small, so the walk is short.
+__global__ __launch_bounds__(256) void ssd_split_scan_kernel(const float *init_states,
+                                                              float *ws_states,
+                                                              const float *ws_decay,
+                                                              int batch, int nheads, int nsplits,
+                                                              int pn) {
+    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t total = (int64_t)batch * nheads * pn;
+    if (e >= total) return;
+    const int64_t bh = e / pn, k = e % pn;
+    float E = init_states ? init_states[bh * pn + k] : 0.f;
+    for (int s = 0; s < nsplits; ++s) {
+        const int64_t idx = (bh * nsplits + s) * pn + k;
+        if (s + 1 < nsplits) {
+            const float loc = ws_states[idx];
+            const float T = ws_decay[bh * nsplits + s];
+            ws_states[idx] = E;
+            E = fmaf(T, E, loc);
+        } else {
+            ws_states[idx] = E;
+        }
+    }
+}
+
+void launch_split_scan(const float *init_states, float *ws_states, const float *ws_decay,
+                       int batch, int nheads, int nsplits, int pn, hipStream_t stream) {
+    const int64_t total = (int64_t)batch * nheads * pn;
+    const dim3 grid((unsigned)((total + 255) / 256)), block(256);
+    hipLaunchKernelGGL(ssd_split_scan_kernel, grid, block, 0, stream, init_states, ws_states,
+                       ws_decay, batch, nheads, nsplits, pn);
+}
+
+// One workgroup per (batch row * head, chunk).  Same segsum steps and the
+// same per-lane mask evaluation order as the bf16 chunk kernel: each wave
+// takes 16-row tiles, each lane one row i and columns 16 jt + 4 g + r, with
+// the F chain walked leftwards from the diagonal.
+template <int Q>
+__global__ __launch_bounds__(kThreads) void ssd_mask_kernel(MaskArgs m) {
+    constexpr int NB = Q / 16;
+    __shared__ __attribute__((aligned(16))) SegLds<Q> sg;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+    const int bh = blockIdx.x;
+    const int b = bh / m.nheads, h = bh % m.nheads;
+    const int ci = blockIdx.y;
+    const int c = m.chunk_begin + ci;
+    const int L = m.seqlen, H = m.nheads;
+    const int t0 = c * Q;
+    const int nvalid = max(0, min(Q, L - t0));
+    const float *dt_row = m.dt + (int64_t)b * L * H + h;
+    const int32_t *seq_row = m.seq_idx ? m.seq_idx + (int64_t)b * L : nullptr;
+
+    int flag_any = 0;
+    if (tid < Q) {
+        seg_load_token<Q>(sg, tid, t0, nvalid, dt_row, H, m.A[h], seq_row);
+        flag_any = sg.flag[tid];
+    }
+    flag_any = __syncthreads_or(flag_any);
+    if (tid == 0) sg.any_reset = flag_any;
+    if (tid < Q) seg_block_sums<Q>(sg, tid);
+    __syncthreads();
+    if (tid < Q) seg_chunk_products<Q>(sg, tid);
+    __syncthreads();
+
+    float *out = m.out + (((int64_t)b * H + h) * m.count + ci) * Q * Q;
+    for (int I = wave; I < NB; I += 4) {
+        const int i = I * 16 + l16;
+        const int rs_i = sg.rs[i];
+        float e[4];
+        const float sum0 = seg_diag_row(sg.d, I * 16, i, g, e);
+        float F = seg_chain_start(sum0, I * 16, rs_i);
+        for (int jt = NB - 1; jt >= 0; --jt) {
+            f32x4 v = {0.f, 0.f, 0.f, 0.f};
+            if (jt == I) {
+                for (int r = 0; r < 4; ++r) v[r] = seg_diag_value(e[r], i, jt * 16 + 4 * g + r, rs_i);
+            } else if (jt < I) {
+                if (jt < I - 1) F = seg_chain_step(F, sg.Tb[jt + 1]);
+                for (int r = 0; r < 4; ++r) v[r] = seg_offdiag(F, sg.W[jt * 16 + 4 * g + r]);
+            }
+            for (int r = 0; r < 4; ++r)
+                if (i >= nvalid || jt * 16 + 4 * g + r >= nvalid) v[r] = 0.f;
+            // element (i, j): row i, columns j = 16 jt + 4 g .. +3
+            *(f32x4 *)(out + (int64_t)i * Q + jt * 16 + 4 * g) = v;
+        }
+    }
+}
+
+void launch_mask(int Q, const MaskArgs &m, hipStream_t stream) {
+    const dim3 grid(m.batch * m.nheads, m.count), block(kThreads);
+    switch (Q) {
+    case 64: hipLaunchKernelGGL(ssd_mask_kernel<64>, grid, block, 0, stream, m); break;
+    case 128: hipLaunchKernelGGL(ssd_mask_kernel<128>, grid, block, 0, stream, m); break;
+    default: hipLaunchKernelGGL(ssd_mask_kernel<256>, grid, block, 0, stream, m); break;
+    }
+}
+
+}  // namespace ssd

@@ -1,0 +1,114 @@
+// Shared definitions of the gfx950 SSD forward kernels: argument block,
+// vector types, bf16 helpers and the workgroup -> work-unit map.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kThreads = 256;  // four wave64s per workgroup
+
+enum Mode : int {
+    kModeFull = 0,        // outputs y; carries the state; last split writes final_states
+    kModeSplitLocal = 1   // only the split's local end state and decay (zero entry state)
+};
+
+// Argument block shared by the chunk kernels (passed by value).
+struct ChunkArgs {
+    const void *x;
+    const float *dt;
+    const float *A;
+    const void *B;
+    const void *C;
+    const float *D;            // nullable
+    const int32_t *seq_idx;    // nullable
+    const float *init_states;  // nullable
+    void *y;
+    float *final_states;       // nullable
+    float *ws_states;          // [batch][nheads][nsplits][headdim][dstate]
+    float *ws_decay;           // [batch][nheads][nsplits]
+    int batch, seqlen, nheads, headdim, dstate, ngroups;
+    int chunk;                 // chunk_size Q
+    int nchunks;               // ceil(seqlen / Q)
+    int nsplits;               // sequence-parallel splits per row
+    int split_chunks;          // chunks per split
+    int npblocks;              // headdim blocks per head
+    int pblock;                // headdim columns per block
+    int mode;                  // Mode
+    int units;                 // batch * nheads * nsplits * npblocks
+};
+
+// Arguments of the decay-mask export kernel.
+struct MaskArgs {
+    const float *dt;
+    const float *A;
+    const int32_t *seq_idx;
+    float *out;          // [batch][nheads][count][Q][Q]
+    int batch, seqlen, nheads;
+    int chunk_begin, count;
+};
+
+struct Unit {
+    int b, h, s, pb;
+};
+
+// Workgroups are dealt to the 8 XCDs round-robin by block index.  Remap so
+// that each XCD receives a contiguous range of logical units; logical units
+// are ordered (batch, head, split, headdim block), so the heads of one batch
+// row that share its B/C rows run on one XCD and share its L2.
+__device__ inline Unit unit_of_block(const ChunkArgs &a) {
+    const int blk = blockIdx.x;
+    const int per = a.units / 8, rem = a.units % 8;
+    const int xcd = blk % 8, k = blk / 8;
+    const int logical = xcd * per + (xcd < rem ? xcd : rem) + k;
+    Unit u;
+    u.pb = logical % a.npblocks;
+    int r = logical / a.npblocks;
+    u.s = r % a.nsplits;
+    r /= a.nsplits;
+    u.h = r % a.nheads;
+    u.b = r / a.nheads;
+    return u;
+}
+
+__device__ inline float bf16_to_f32(bf16 v) { return (float)v; }
+
+__device__ inline bf16x4 f32x4_to_bf16x4(f32x4 v) {
+    bf16x4 r;
+    r[0] = (bf16)v[0];
+    r[1] = (bf16)v[1];
+    r[2] = (bf16)v[2];
+    r[3] = (bf16)v[3];
+    return r;
+}
+
+// 16-bit transpose read from LDS (gfx950 ds_read_b64_tr_b16).  Within each
+// group of 16 lanes, lane s supplies the address of 4 consecutive 16-bit
+// elements; lane i of the group receives element (i % 4) of the loads made by
+// lanes i/4, 4 + i/4, 8 + i/4 and 12 + i/4.  Callers point lane s at row
+// (r0 + s/4), column (c0 + 4 (s % 4)) of a row-major tile, so lane i gets
+// column c0 + i of rows r0 .. r0+3.
+__device__ inline i16x4 lds_read_tr16(const bf16 *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4 *)(p));
+}
+
+__device__ inline bf16x8 join_bf16x8(i16x4 lo, i16x4 hi) {
+    i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ inline f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+}  // namespace ssd

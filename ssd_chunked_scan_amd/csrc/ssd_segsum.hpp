@@ -1,0 +1,168 @@
+// Hierarchy-aware segsum: the per-chunk decay factors of the SSD forward
+// pass and the 1-semiseparable mask built from them.
+//
+// Page "GPU Hierarchy Meets Structured Matrices" (abstract) splits the
+// chunk's decay mask L (page "State Space Duality and Mamba-2", "The
+// Mathematical Bridge": L_ij = prod_{k=j+1..i} a_k for i >= j) into 1-SS
+// diagonal blocks and rank-one off-diagonal blocks.  Here the sub-blocks are
+// 16 tokens wide (the MFMA tile edge):
+//
+//   * log2-decays d_k = dt_k A_h log2(e) <= 0 are summed per sub-block with
+//     nested sequential sums (every partial sum is the previous one plus a
+//     term <= 0, so sums never increase and never cancel);
+//   * a diagonal sub-block entry is 2^(direct sum over (j, i]) taken
+//     leftwards from the diagonal;
+//   * an off-diagonal entry of sub-block (I, J), J < I, is F(i, J) * W_j:
+//     W_j = 2^(sum over (j, end of J]) is the sub-block suffix decay, and
+//     F(i, J) = L at column (end of J), carried leftwards across sub-blocks by
+//     F(i, J) = F(i, J+1) * Tb_{J+1}, Tb = whole-sub-block decay.  The chain
+//     starts at F(i, I-1) = 2^(the row's direct sum extended over the first
+//     token of block I).
+//
+// Every factor is 2^(sum of terms <= 0) in [0, 1] and every step multiplies
+// by a factor in [0, 1] or adds a term <= 0, so along each row the mask is in
+// [0, 1] and non-increasing away from the diagonal in fp32, for any input
+// (Tb_{J+1} <= W at the first column of J+1 because Tb extends that column's
+// nested suffix sum by one more non-positive term).
+//
+// Document boundaries (page "Parallel Scan and Hardware-Aware SSM Kernels",
+// "When it breaks": mask a_k to zero at a boundary) enter by selecting a
+// factor to exactly 0, never through -inf arithmetic.  The floating-point
+// operations below use explicit round-to-nearest intrinsics so that the
+// compiler cannot fuse them and every kernel that includes this header
+// produces bit-identical factors and mask values.
+#pragma once
+
+#include "ssd_common.hpp"
+
+namespace ssd {
+
+// Per-chunk segsum values in LDS.  Q = chunk size (multiple of 16, <= 256).
+template <int Q>
+struct SegLds {
+    static constexpr int NB = Q / 16;
+    float d[Q];      // log2-decay of token t (0 past the end of the row)
+    float dt[Q];     // dt of token t (0 past the end)
+    float W[Q];      // sub-block suffix decay over (t, end of t's sub-block]
+    float u[Q];      // decay from the previous chunk's state to token t: prod_{k<=t} a_k
+    float wcd[Q];    // decay from token t to the chunk end, times dt_t
+    int rs[Q];       // last reset position <= t in the chunk, -1 if none
+    int flag[Q];     // 1 if the state resets at token t (document boundary)
+    float Tb[NB];    // whole-sub-block decay (0 if a reset lies inside)
+    int blast[NB];   // last reset position inside sub-block, -1 if none
+    float T;         // whole-chunk decay (0 if a reset lies inside)
+    int any_reset;   // 1 if some token of the chunk resets the state
+};
+
+// Step 1, thread t < Q: token values.  t0 = chunk start, nvalid = tokens of
+// the chunk inside the row.  A reset happens at global token t > 0 where
+// seq_idx changes.
+template <int Q>
+__device__ inline void seg_load_token(SegLds<Q> &s, int t, int t0, int nvalid,
+                                      const float *dt_row, int dt_stride,
+                                      float A_h, const int32_t *seq_row) {
+    float dtv = 0.f, d = 0.f;
+    int flag = 0;
+    if (t < nvalid) {
+        dtv = dt_row[(int64_t)(t0 + t) * dt_stride];
+        d = __fmul_rn(__fmul_rn(dtv, A_h), kLog2e);
+        if (seq_row && (t0 + t) > 0)
+            flag = seq_row[t0 + t] != seq_row[t0 + t - 1];
+    }
+    s.d[t] = d;
+    s.dt[t] = dtv;
+    s.flag[t] = flag;
+}
+
+// Step 2, thread t < Q (after a barrier): nested sums inside t's sub-block.
+template <int Q>
+__device__ inline void seg_block_sums(SegLds<Q> &s, int t) {
+    const int B0 = t & ~15;
+    float pre = 0.f;
+    int lastin = -1;
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+        const int k = B0 + kk;
+        if (k <= t) {
+            pre = __fadd_rn(pre, s.d[k]);
+            if (s.flag[k]) lastin = k;
+        }
+    }
+    float suf = 0.f;
+    int fsuf = 0;
+#pragma unroll
+    for (int kk = 15; kk >= 1; --kk) {
+        const int k = B0 + kk;
+        if (k > t) {
+            suf = __fadd_rn(suf, s.d[k]);
+            fsuf |= s.flag[k];
+        }
+    }
+    // Decay of the prefix [B0, t]; stored in u[] and finished in step 3.
+    s.u[t] = (lastin >= 0) ? 0.f : __builtin_amdgcn_exp2f(pre);
+    s.W[t] = fsuf ? 0.f : __builtin_amdgcn_exp2f(suf);
+    s.rs[t] = lastin;
+    if (t == B0) {
+        const float tau = __fadd_rn(suf, s.d[B0]);
+        s.Tb[t >> 4] = (fsuf | s.flag[B0]) ? 0.f : __builtin_amdgcn_exp2f(tau);
+    }
+    if (t == B0 + 15) s.blast[t >> 4] = lastin;
+}
+
+// Step 3, thread t < Q (after a barrier): cross-sub-block products.
+template <int Q>
+__device__ inline void seg_chunk_products(SegLds<Q> &s, int t) {
+    constexpr int NB = Q / 16;
+    const int K = t >> 4;
+    float V = 1.f;
+    for (int k = 0; k < K; ++k) V = __fmul_rn(V, s.Tb[k]);
+    float Z = 1.f;
+    for (int k = NB - 1; k > K; --k) Z = __fmul_rn(Z, s.Tb[k]);
+    s.u[t] = __fmul_rn(s.u[t], V);
+    s.wcd[t] = __fmul_rn(__fmul_rn(s.W[t], Z), s.dt[t]);
+    if (s.any_reset) {
+        int rs = s.rs[t];
+        if (rs < 0)
+            for (int k = 0; k < K; ++k)
+                if (s.blast[k] >= 0) rs = s.blast[k];
+        s.rs[t] = rs;
+    }
+    if (t == 0) {
+        float T = 1.f;
+        for (int k = 0; k < NB; ++k) T = __fmul_rn(T, s.Tb[k]);
+        s.T = T;
+    }
+}
+
+// Diagonal sub-block of row i (sub-block start I0), in the MFMA accumulator
+// layout: the lane holds columns j = I0 + 4g + r, r = 0..3.  e[r] receives the
+// direct sum over (j, i] (meaningful for j <= i); the return value is the sum
+// over [I0, i], the start of the off-diagonal chain.
+__device__ inline float seg_diag_row(const float *d, int I0, int i, int g, float e[4]) {
+    float acc = 0.f;
+#pragma unroll
+    for (int kk = 15; kk >= 0; --kk) {
+        if ((kk >> 2) == g) e[kk & 3] = acc;
+        const float dk = d[I0 + kk];
+        acc = (I0 + kk <= i) ? __fadd_rn(acc, dk) : acc;
+    }
+    return acc;
+}
+
+// Mask value of a diagonal-sub-block entry (i, j) from its direct sum.
+__device__ inline float seg_diag_value(float e, int i, int j, int rs_i) {
+    return (j > i || rs_i > j) ? 0.f : __builtin_amdgcn_exp2f(e);
+}
+
+// Start of the off-diagonal chain for row i: F(i, I-1) = prod_{k=I0..i} a_k.
+__device__ inline float seg_chain_start(float sum_I0_i, int I0, int rs_i) {
+    return (rs_i >= I0) ? 0.f : __builtin_amdgcn_exp2f(sum_I0_i);
+}
+
+// F(i, J) from F(i, J+1) and the decay of sub-block J+1.
+__device__ inline float seg_chain_step(float F, float Tb_next) { return __fmul_rn(F, Tb_next); }
+
+// Off-diagonal mask entry L_ij = F(i, J) * W_j.
+__device__ inline float seg_offdiag(float F, float W) { return __fmul_rn(F, W); }
+
+}  // namespace ssd

@@ -1,0 +1,64 @@
+"""Helpers shared by the GPU tests: move seeded inputs to the device, run
+the HIP path through the C ABI, and compare with the fp64 oracle."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+import workloads
+
+
+def to_device(inp: workloads.Inputs, device="cuda"):
+    import torch
+    io = torch.bfloat16 if inp.wl.io == "bf16" else torch.float32
+    t = {
+        "x": torch.from_numpy(inp.x).to(device).to(io).contiguous(),
+        "dt": torch.from_numpy(inp.dt).to(device).contiguous(),
+        "A": torch.from_numpy(inp.A).to(device).contiguous(),
+        "B": torch.from_numpy(inp.B).to(device).to(io).contiguous(),
+        "C": torch.from_numpy(inp.C).to(device).to(io).contiguous(),
+        "D": torch.from_numpy(inp.D).to(device).contiguous(),
+        "seq_idx": None if inp.seq_idx is None else torch.from_numpy(inp.seq_idx).to(device).contiguous(),
+    }
+    return t
+
+
+def run_gpu(inp: workloads.Inputs, init_states=None, split_len=0, chunk_size=None, **kw):
+    import ssd_chunked_scan_amd as ssd
+    import torch
+    t = to_device(inp)
+    h0 = None if init_states is None else torch.from_numpy(np.asarray(init_states, np.float32)).cuda()
+    y, fs = ssd.ssd_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["seq_idx"],
+                        chunk_size=chunk_size or inp.wl.chunk_size, init_states=h0,
+                        split_len=split_len, **kw)
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy().astype(np.float64), fs.cpu().numpy().astype(np.float64)
+
+
+def oracle_slice(inp: workloads.Inputs, batches, heads, init_states=None):
+    """fp64 oracle on a subset of (batch rows, heads); B/C groups follow the
+    heads.  Returns y [nb, L, nh, P] and final_states [nb, nh, P, N]."""
+    H, G = inp.wl.nheads, inp.wl.ngroups
+    hpg = H // G
+    batches = list(batches)
+    heads = list(heads)
+    groups = [h // hpg for h in heads]
+    x = inp.x[batches][:, :, heads]
+    dt = inp.dt[batches][:, :, heads]
+    A = inp.A[heads]
+    D = inp.D[heads]
+    # one group per selected head keeps the head -> group map exact
+    B = inp.B[batches][:, :, groups]
+    C = inp.C[batches][:, :, groups]
+    si = None if inp.seq_idx is None else inp.seq_idx[batches]
+    h0 = None if init_states is None else np.asarray(init_states)[batches][:, heads]
+    return oracle.ssd_forward(x, dt, A, B, C, D, si, h0)
+
+
+def max_rel(a, ref):
+    a = np.asarray(a, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return float(np.abs(a - ref).max() / max(np.abs(ref).max(), 1e-30))
+
+
+TOL = {"bf16": 1e-2, "f32": 1e-4}

@@ -1,0 +1,143 @@
+"""The C-ABI library loads, exports every entry point include/ssd.h
+declares, and rejects every invalid argument on the host with the right
+status before any launch (CPU only: no kernel is ever started here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import ssd_chunked_scan_amd as ssd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "ssd.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssd_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ssd.load_library()
+    names = _declared()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in ssd.h but not exported"
+    assert sorted(ssd.EXPORTS) == names
+    assert lib.ssd_version().startswith(b"ssd-mi355x")
+
+
+def test_status_strings():
+    lib = ssd.load_library()
+    for code, name in ssd.STATUS.items():
+        assert lib.ssd_status_str(code).decode() == name
+
+
+FAKE = 0x100000  # aligned, never dereferenced: every call below fails validation
+
+
+def _fwd(shape, io=1, chunk=256, x=FAKE, dt=FAKE, A=FAKE, B=FAKE, C=FAKE, y=FAKE, fs=None,
+         h0=None, ws=None, ws_bytes=0, opts=None, seq=None, D=None):
+    lib = ssd.load_library()
+    o = None if opts is None else ctypes.byref(opts)
+    shp = None if shape is None else ctypes.byref(shape)
+    return lib.ssd_fwd_ex(shp, io, x, dt, A, B, C, D, seq, chunk, h0, y, fs, ws, ws_bytes, o, None)
+
+
+def good_shape():
+    return ssd.Shape(2, 1000, 8, 64, 128, 2)
+
+
+@pytest.mark.parametrize("mutate,status", [
+    (lambda s: setattr(s, "batch", 0), 2),
+    (lambda s: setattr(s, "seqlen", 0), 2),
+    (lambda s: setattr(s, "nheads", -1), 2),
+    (lambda s: setattr(s, "ngroups", 3), 2),      # 8 % 3 != 0
+    (lambda s: setattr(s, "headdim", 48), 3),
+    (lambda s: setattr(s, "headdim", 256), 3),
+    (lambda s: setattr(s, "dstate", 8), 3),
+    (lambda s: setattr(s, "dstate", 256), 3),
+])
+def test_shape_errors(mutate, status):
+    s = good_shape()
+    mutate(s)
+    assert _fwd(s) == status
+    assert ssd.load_library().ssd_last_error() != b""
+
+
+def test_argument_errors():
+    s = good_shape()
+    assert _fwd(None) == 1
+    assert _fwd(s, chunk=32) == 3
+    assert _fwd(s, chunk=512) == 3
+    assert _fwd(s, io=5) == 3
+    assert _fwd(s, x=None) == 1
+    assert _fwd(s, y=None) == 1
+    assert _fwd(s, C=None) == 1
+    assert _fwd(s, x=FAKE + 2) == 4
+    assert _fwd(s, B=FAKE + 8) == 4
+    assert _fwd(s, dt=FAKE + 2) == 4
+    assert _fwd(s, fs=FAKE + 4) == 4
+    assert _fwd(s, h0=FAKE + 8) == 4
+    o = ssd.Options(100)              # not a multiple of the chunk size
+    assert _fwd(s, opts=o) == 3
+    o = ssd.Options(256)
+    o.reserved[3] = 1
+    assert _fwd(s, opts=o) == 3
+    o = ssd.Options(256)              # 4 splits -> workspace required
+    assert _fwd(s, opts=o) == 5
+    assert b"workspace" in ssd.load_library().ssd_last_error()
+    need = ssd.ssd_fwd_workspace_bytes(s, 256, 1, split_len=256)
+    assert _fwd(s, opts=o, ws=FAKE, ws_bytes=need - 1) == 5
+    assert _fwd(s, opts=o, ws=FAKE + 4, ws_bytes=need) == 4
+
+
+def test_workspace_and_plan():
+    s = good_shape()
+    # forced split: 1000 tokens, chunk 256 -> 4 chunks; split 256 -> 4 splits
+    need = ssd.ssd_fwd_workspace_bytes(s, 256, 1, split_len=256)
+    assert need == (2 * 8 * 4 * 64 * 128 + 64) * 4
+    assert ssd.ssd_fwd_workspace_bytes(s, 256, 1, split_len=1024) == 0
+    # planner: plenty of (batch, head) pairs -> one split per row, no workspace
+    big = ssd.Shape(8, 2048, 80, 64, 128, 1)
+    assert ssd.ssd_plan_split_len(big, 256, 1) == 2048
+    assert ssd.ssd_fwd_workspace_bytes(big, 256, 1) == 0
+    # few long rows -> sequence-parallel splits, chosen independently of the chunk
+    long = ssd.Shape(1, 65536, 16, 64, 64, 1)
+    sl = ssd.ssd_plan_split_len(long, 256, 1)
+    assert sl % 256 == 0 and 256 <= sl < 65536
+    assert ssd.ssd_plan_split_len(long, 64, 1) == sl
+    assert ssd.ssd_fwd_workspace_bytes(long, 256, 1) > 0
+    assert ssd.ssd_fwd_workspace_bytes(ssd.Shape(0, 1, 1, 16, 16, 1), 256, 1) == 0
+
+
+def test_mask_errors():
+    lib = ssd.load_library()
+    s = ssd.Shape(1, 1000, 2, 16, 16, 1)
+    f = lib.ssd_debug_chunk_mask
+    assert f(ctypes.byref(s), FAKE, FAKE, None, 256, 0, 5, FAKE, None) == 2   # only 4 chunks
+    assert f(ctypes.byref(s), FAKE, FAKE, None, 256, -1, 1, FAKE, None) == 2
+    assert f(ctypes.byref(s), FAKE, FAKE, None, 256, 0, 0, FAKE, None) == 2
+    assert f(ctypes.byref(s), None, FAKE, None, 256, 0, 1, FAKE, None) == 1
+    assert f(ctypes.byref(s), FAKE, FAKE, None, 256, 0, 1, FAKE + 4, None) == 4
+    assert f(ctypes.byref(s), FAKE, FAKE, None, 100, 0, 1, FAKE, None) == 3
+
+
+def test_product_path_has_no_cpu_fallback(monkeypatch):
+    """Without libssd.so the binding raises instead of computing anything."""
+    monkeypatch.setattr(ssd, "_lib", None)
+    monkeypatch.setattr(ssd, "_LIB_PATH", os.path.join(ROOT, "no_such_libssd.so"))
+    with pytest.raises(ImportError):
+        ssd.load_library()
+
+
+def test_binding_does_not_import_oracle():
+    import ast
+    for fn in os.listdir(os.path.join(ROOT, "ssd_chunked_scan_amd")):
+        if fn.endswith(".py"):
+            tree = ast.parse(open(os.path.join(ROOT, "ssd_chunked_scan_amd", fn)).read())
+            for node in ast.walk(tree):
+                if isinstance(node, (ast.Import, ast.ImportFrom)):
+                    mods = [a.name for a in node.names] if isinstance(node, ast.Import) else [node.module or ""]
+                    assert not any(m.split(".")[0] == "oracle" for m in mods), fn

@@ -1,0 +1,113 @@
+"""Properties of the HIP path that hold at any size (needs an MI355X):
+chunk-size and split-length invariance, composition of two calls through the
+carried state, bitwise determinism, zero leakage across documents (bit for
+bit), batch-row independence and the trivial-input identities."""
+import numpy as np
+import pytest
+
+import workloads
+from ssd_testlib import TOL, max_rel, oracle_slice, run_gpu, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _wl(**kw):
+    base = dict(batch=2, seqlen=1100, nheads=4, headdim=64, dstate=64, ngroups=2,
+                chunk_size=128, io="bf16")
+    base.update(kw)
+    return workloads.custom_workload(**base)
+
+
+def test_chunk_size_invariance():
+    outs = {}
+    for Q in (64, 128, 256):
+        inp = workloads.make_inputs(_wl(chunk_size=Q), seed=11)
+        outs[Q] = run_gpu(inp)
+    for Q in (64, 128):
+        assert max_rel(outs[Q][0], outs[256][0]) <= TOL["bf16"]
+        assert max_rel(outs[Q][1], outs[256][1]) <= TOL["bf16"]
+
+
+def test_split_length_invariance():
+    inp = workloads.make_inputs(_wl(), seed=12)
+    y0, f0 = run_gpu(inp, split_len=0)
+    for sl in (128, 256, 640):
+        y, f = run_gpu(inp, split_len=sl)
+        assert max_rel(y, y0) <= TOL["bf16"] and max_rel(f, f0) <= TOL["bf16"]
+
+
+def test_two_calls_compose_through_state():
+    """[0, T/2) then [T/2, T) from the carried state equals one call (page
+    "Parallel Scan and Hardware-Aware SSM Kernels", "The scan": affine
+    composition)."""
+    import dataclasses
+    inp = workloads.make_inputs(_wl(seqlen=1024), seed=13)
+    y, f = run_gpu(inp)
+    half = 512
+    first = dataclasses.replace(inp, wl=dataclasses.replace(inp.wl, seqlen=half),
+                                x=inp.x[:, :half], dt=inp.dt[:, :half], B=inp.B[:, :half],
+                                C=inp.C[:, :half])
+    second = dataclasses.replace(inp, wl=dataclasses.replace(inp.wl, seqlen=half),
+                                 x=inp.x[:, half:], dt=inp.dt[:, half:], B=inp.B[:, half:],
+                                 C=inp.C[:, half:])
+    y1, f1 = run_gpu(first)
+    y2, f2 = run_gpu(second, init_states=f1.astype(np.float32))
+    assert max_rel(np.concatenate([y1, y2], axis=1), y) <= TOL["bf16"]
+    assert max_rel(f2, f) <= TOL["bf16"]
+
+
+def test_bitwise_determinism():
+    inp = workloads.make_inputs(_wl(), seed=14)
+    a = run_gpu(inp)
+    b = run_gpu(inp)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_zero_leakage_bitwise():
+    """Perturbing one document changes no bit of any other document's output
+    (page "Parallel Scan and Hardware-Aware SSM Kernels", "When it breaks")."""
+    wl = _wl(batch=1, seqlen=2000, packed=True, doc_range=(50, 600), doc_count=(3, 64))
+    inp = workloads.make_inputs(wl, seed=15)
+    y0, _ = run_gpu(inp)
+    lens = inp.doc_lens
+    starts = np.concatenate([[0], np.cumsum(lens)])
+    d = len(lens) // 2
+    s0, s1 = starts[d], starts[d + 1]
+    inp.x[:, s0:s1] = workloads.bf16_round(inp.x[:, s0:s1] * 3.0 + 1.0)
+    inp.B[:, s0:s1] = workloads.bf16_round(-inp.B[:, s0:s1])
+    y1, _ = run_gpu(inp)
+    other = np.ones(y0.shape[1], dtype=bool)
+    other[s0:s1] = False
+    assert np.array_equal(y0[:, other], y1[:, other])
+    assert not np.array_equal(y0[:, s0:s1], y1[:, s0:s1])
+
+
+def test_batch_rows_independent():
+    inp = workloads.make_inputs(_wl(batch=3), seed=16)
+    y, f = run_gpu(inp)
+    inp.x[1] = workloads.bf16_round(inp.x[1] * -2.0)
+    y2, f2 = run_gpu(inp)
+    assert np.array_equal(y[0], y2[0]) and np.array_equal(y[2], y2[2])
+    assert np.array_equal(f[0], f2[0]) and np.array_equal(f[2], f2[2])
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_zero_B_gives_skip_only(io):
+    inp = workloads.make_inputs(_wl(io=io), seed=17)
+    inp.B[:] = 0.0
+    y, f = run_gpu(inp)
+    ref = (inp.D[None, None, :, None] * inp.x).astype(np.float32)   # fp32 product
+    if io == "bf16":
+        ref = workloads.bf16_round(ref)
+    assert np.array_equal(y, ref.astype(np.float64))
+    assert np.all(f == 0)
+
+
+def test_reset_every_token():
+    """A document boundary at every token leaves only the diagonal of M."""
+    inp = workloads.make_inputs(_wl(batch=1, seqlen=300), seed=18)
+    inp = type(inp)(**{**inp.__dict__})
+    inp.seq_idx = np.arange(300, dtype=np.int32)[None, :]
+    y, f = run_gpu(inp)
+    yr, fr = oracle_slice(inp, [0], range(4))
+    assert max_rel(y, yr) <= TOL["bf16"] and max_rel(f, fr) <= TOL["bf16"]

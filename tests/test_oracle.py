@@ -154,3 +154,20 @@ def test_pins_catch_planted_mistake(name, mutant_dir):
 
     failed = [p.__name__ for p in pins.ALL_PINS if not p(fwd)[0]]
     assert failed, f"planted mistake {name} passed every pin"
+
+
+def test_mask_invariant_checker_accepts_oracle_and_rejects_violations():
+    """The invariant checker used on the GPU mask accepts the fp64 oracle's
+    mask and rejects planted violations."""
+    from mask_invariants import check_mask_invariants
+    x, dt, A, B, C, D = pins.small_inputs(seed=8, b=1, L=96, H=2, dt_lo=1e-3, dt_hi=1.0)
+    m = oracle.decay_mask(dt, A, chunk_size=32)
+    check_mask_invariants(m)
+    bad = m.copy()
+    bad[0, 0, 1, 20, 5] = min(1.0, bad[0, 0, 1, 20, 6] * 1.5 + 1e-3)   # increases leftwards
+    with pytest.raises(AssertionError):
+        check_mask_invariants(bad)
+    bad = m.copy()
+    bad[0, 1, 0, 3, 4] = 0.5                                            # above the diagonal
+    with pytest.raises(AssertionError):
+        check_mask_invariants(bad)
