@@ -148,6 +148,26 @@ def main():
 
     alg_bytes = wl.algorithmic_bytes()
     achieved = alg_bytes / (avg_launch_ms * 1e-3) / 1e9
+
+    # Measured device-to-device copy moving the same number of bytes (half
+    # read, half written): the attainable-bandwidth reference, and the plain
+    # copy kernel whose counters calibrate the HBM-traffic counters.
+    copy_src = torch.empty(alg_bytes // 2, dtype=torch.uint8, device=dev)
+    copy_dst = torch.empty_like(copy_src)
+    for _ in range(3):
+        copy_dst.copy_(copy_src)
+    cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(max(10, args.steps // 2))]
+    for e0, e1 in cev:
+        e0.record(stream)
+        copy_dst.copy_(copy_src)
+        e1.record(stream)
+    torch.cuda.synchronize(dev)
+    copy_ms = sum(e0.elapsed_time(e1) for e0, e1 in cev) / len(cev)
+    copy_gbs = alg_bytes / (copy_ms * 1e-3) / 1e9
+    del copy_src, copy_dst
+    print(f"bench: kernel {achieved:.0f} GB/s algorithmic; copy of the same bytes {copy_gbs:.0f} GB/s",
+          file=sys.stderr, flush=True)
     traffic = counter_traffic(wl.name)
     out = {
         "metric": METRIC,
@@ -172,6 +192,7 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": alg_bytes,
                      "avg_launch_us": avg_launch_ms * 1e3},
+        "copy_reference": {"gbs": copy_gbs, "bytes": alg_bytes, "frac_of_copy": achieved / copy_gbs},
     }
     if not args.no_cpu_baseline:
         print("bench: timing the fp64 CPU oracle", file=sys.stderr, flush=True)
