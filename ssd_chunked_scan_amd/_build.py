@@ -10,6 +10,7 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -56,14 +57,130 @@ def _compile(hipcc: str, src: str, verbose: bool) -> str:
     return obj
 
 
+_REG = re.compile(r"([vas])\[(\d+):(\d+)\]|\b([vas])(\d+)\b")
+
+# v_mfma_f32_16x16x32_bf16 on gfx950 with a VGPR destination: a VALU, memory
+# or MFMA A/B read of its result needs 8 wait states on the hardware (measured:
+# the first result registers are valid after 7, the last after 8).  Results
+# read as the accumulator of a following MFMA (same registers) need none, and
+# v_accvgpr_read of an AGPR destination is interlocked (measured: valid at 0).
+MFMA_READ_WAIT_STATES = 8
+
+
+def _regs(text: str):
+    out = set()
+    for m in _REG.finditer(text):
+        if m.group(1):
+            f, a, b = m.group(1), int(m.group(2)), int(m.group(3))
+        else:
+            f, a, b = m.group(4), int(m.group(5)), int(m.group(5))
+        if f in ("v", "a"):
+            out.update((f, r) for r in range(a, b + 1))
+    return out
+
+
+def _parse_functions(asm_text: str):
+    """Split assembly into functions: lists of (kind, text) with kind 'label'
+    or 'ins'."""
+    funcs, cur = [], None
+    for raw in asm_text.splitlines():
+        line = raw.split(";")[0].strip()
+        if not line:
+            continue
+        if line.endswith(":") and not line.startswith("."):
+            cur = []
+            funcs.append((line[:-1], cur))
+            continue
+        if cur is None:
+            continue
+        if line.endswith(":") and line.startswith(".LBB"):
+            cur.append(("label", line[:-1]))
+        elif not line.startswith("."):
+            cur.append(("ins", line))
+    return funcs
+
+
+def check_mfma_result_reads(asm_text: str, where: str) -> int:
+    """Follow every path (fall-through and branch targets) from each MFMA and
+    fail if an instruction reads its result registers, other than as the
+    accumulator of the next MFMA, within MFMA_READ_WAIT_STATES wait states."""
+    n = 0
+    for fname, items in _parse_functions(asm_text):
+        labels = {t: i for i, (k, t) in enumerate(items) if k == "label"}
+        for i, (kind, text) in enumerate(items):
+            if kind != "ins" or not text.startswith("v_mfma"):
+                continue
+            n += 1
+            ops = [o.strip() for o in text.split(None, 1)[1].split(",")]
+            dst = _regs(ops[0])
+            stack, seen = [(i + 1, 0)], set()
+            while stack:
+                j, ws = stack.pop()
+                while j < len(items) and ws < MFMA_READ_WAIT_STATES:
+                    if (j, ws) in seen:
+                        break
+                    seen.add((j, ws))
+                    k2, t2 = items[j]
+                    if k2 == "label":
+                        j += 1
+                        continue
+                    op = t2.split()[0]
+                    rest = t2.split(None, 1)[1] if " " in t2 else ""
+                    if op.startswith("s_nop"):
+                        ws += int(rest) + 1
+                        j += 1
+                        continue
+                    parts = [p.strip() for p in rest.split(",")] if rest else []
+                    if op.startswith("v_mfma"):
+                        srcab = _regs(",".join(parts[1:3]))
+                        if dst & srcab:
+                            raise RuntimeError(f"{where}: {fname}: MFMA result read as an A/B "
+                                               f"operand after {ws} wait states: {text} -> {t2}")
+                        if _regs(parts[0]) == dst:
+                            break          # same accumulator: result consumed in place
+                    elif op.startswith("v_accvgpr_read"):
+                        pass               # interlocked read of an AGPR result
+                    elif op.startswith(("v_", "ds_", "global_", "buffer_", "flat_", "scratch_")):
+                        srcs = _regs(",".join(parts[1:])) if op.startswith("v_") else _regs(rest)
+                        if op.startswith(("global_load", "buffer_load", "ds_read", "scratch_load",
+                                          "flat_load")):
+                            srcs = _regs(",".join(parts[1:]))
+                        if dst & srcs:
+                            raise RuntimeError(f"{where}: {fname}: MFMA result read after only {ws} "
+                                               f"wait states: {text} -> {t2}")
+                    if op in ("s_branch", "s_setpc_b64", "s_endpgm"):
+                        if op == "s_branch" and rest in labels:
+                            stack.append((labels[rest], ws + 1))
+                        break
+                    if op.startswith("s_cbranch") and rest in labels:
+                        stack.append((labels[rest], ws + 1))
+                    ws += 1
+                    j += 1
+    return n
+
+
+def _asm_check(hipcc: str, src: str) -> int:
+    cmd = [hipcc, *COMMON_FLAGS, "-S", "--cuda-device-only", src, "-o", "-"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed on {src}:\n{r.stderr}")
+    return check_mfma_result_reads(r.stdout, os.path.basename(src))
+
+
 def build(verbose: bool = True, jobs: int = 0) -> str:
     hipcc = _hipcc()
     os.makedirs(BUILD, exist_ok=True)
     srcs = sources()
-    jobs = jobs or min(len(srcs), max(1, (os.cpu_count() or 4)))
+    jobs = jobs or max(1, (os.cpu_count() or 4))
     t = time.time()
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(hipcc, s, verbose), srcs))
+        futs = [ex.submit(_compile, hipcc, s, verbose) for s in srcs]
+        chk = [ex.submit(_asm_check, hipcc, s) for s in srcs if s.endswith(".hip")]
+        objs = [f.result() for f in futs]
+        n_mfma = sum(f.result() for f in chk)
+    if verbose:
+        print(f"  checked {n_mfma} MFMA instructions: every read of a result is at least "
+              f"{MFMA_READ_WAIT_STATES} wait states away on every path", file=sys.stderr)
     tmp = LIB + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -9,7 +9,7 @@
 #include <cstring>
 #include <string>
 
-#include "../../include/ssd.h"
+#include "ssd.h"
 #include "ssd_common.hpp"
 
 namespace ssd {

@@ -5,12 +5,13 @@ namespace ssd {
 
 #define SSD_BF16_CASE(q, n, pb)                                                         \
     if (N == n && PB == pb) {                                                            \
-        hipLaunchKernelGGL((ssd_chunk_bf16_kernel<q, n, pb>), grid, block, 0, stream, a); \
+        hipLaunchKernelGGL((ssd_chunk_bf16_kernel<q, n, pb>), grid,                     \
+                           dim3(Bf16Cfg<q, n, pb>::THREADS), 0, stream, a);              \
         return true;                                                                    \
     }
 
 bool launch_chunk_bf16_q256(int N, int PB, const ChunkArgs &a, hipStream_t stream) {
-    const dim3 grid(a.units), block(kThreads);
+    const dim3 grid(a.units);
     SSD_BF16_CASE(256, 16, 16)
     SSD_BF16_CASE(256, 16, 32)
     SSD_BF16_CASE(256, 16, 64)

@@ -107,8 +107,32 @@ __device__ inline bf16x8 join_bf16x8(i16x4 lo, i16x4 hi) {
     return __builtin_bit_cast(bf16x8, v);
 }
 
+// D = A B + C on v_mfma_f32_16x16x32_bf16.
 __device__ inline f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// D = A B.
+__device__ inline f32x4 mfma_bf16_zero_acc(bf16x8 a, bf16x8 b) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+}
+
+// MFMA results are not interlocked: on gfx950 a read of a
+// v_mfma_f32_16x16x32_bf16 result needs 7 wait states (measured).  The
+// compiler inserts them on straight-line code but has been seen to miss a read
+// in the target block of a taken branch.  Values handed from MFMAs to vector
+// code pass through here: the asm takes them as operands, so it sits after
+// their MFMAs and before every read, on every path, and its s_nop supplies the
+// wait states.  The build re-checks every path in the generated assembly.
+__device__ inline void mfma_fence(f32x4 &a) { asm volatile("s_nop 7" : "+v"(a)); }
+__device__ inline void mfma_fence(f32x4 &a, f32x4 &b) { asm volatile("s_nop 7" : "+v"(a), "+v"(b)); }
+
+// The same for a whole array of accumulators (one wait for all of them).
+template <int K>
+__device__ inline void mfma_fence_all(f32x4 (&v)[K]) {
+    asm volatile("s_nop 7" : "+v"(v[0]));
+#pragma unroll
+    for (int k = 1; k < K; ++k) asm volatile("" : "+v"(v[k]));
 }
 
 }  // namespace ssd

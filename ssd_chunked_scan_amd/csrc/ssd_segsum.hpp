@@ -54,24 +54,38 @@ struct SegLds {
     int any_reset;   // 1 if some token of the chunk resets the state
 };
 
-// Step 1, thread t < Q: token values.  t0 = chunk start, nvalid = tokens of
-// the chunk inside the row.  A reset happens at global token t > 0 where
-// seq_idx changes.
+// Step 1a, thread t < Q: read token t's dt and reset flag from global memory
+// (dt = 0 and no reset past the end of the row).  t0 = chunk start, nvalid =
+// tokens of the chunk inside the row.  A reset happens at global token t > 0
+// where seq_idx changes.
+__device__ inline void seg_fetch_token(int t, int t0, int nvalid, const float *dt_row,
+                                       int dt_stride, const int32_t *seq_row, float &dtv,
+                                       int &flag) {
+    dtv = 0.f;
+    flag = 0;
+    if (t < nvalid) {
+        dtv = dt_row[(int64_t)(t0 + t) * dt_stride];
+        if (seq_row && (t0 + t) > 0) flag = seq_row[t0 + t] != seq_row[t0 + t - 1];
+    }
+}
+
+// Step 1b, thread t < Q: token values in LDS.
+template <int Q>
+__device__ inline void seg_store_token(SegLds<Q> &s, int t, float dtv, float A_h, int flag) {
+    s.d[t] = __fmul_rn(__fmul_rn(dtv, A_h), kLog2e);
+    s.dt[t] = dtv;
+    s.flag[t] = flag;
+}
+
+// Step 1 in one go (fetch + store), for kernels that do not prefetch.
 template <int Q>
 __device__ inline void seg_load_token(SegLds<Q> &s, int t, int t0, int nvalid,
                                       const float *dt_row, int dt_stride,
                                       float A_h, const int32_t *seq_row) {
-    float dtv = 0.f, d = 0.f;
-    int flag = 0;
-    if (t < nvalid) {
-        dtv = dt_row[(int64_t)(t0 + t) * dt_stride];
-        d = __fmul_rn(__fmul_rn(dtv, A_h), kLog2e);
-        if (seq_row && (t0 + t) > 0)
-            flag = seq_row[t0 + t] != seq_row[t0 + t - 1];
-    }
-    s.d[t] = d;
-    s.dt[t] = dtv;
-    s.flag[t] = flag;
+    float dtv;
+    int flag;
+    seg_fetch_token(t, t0, nvalid, dt_row, dt_stride, seq_row, dtv, flag);
+    seg_store_token<Q>(s, t, dtv, A_h, flag);
 }
 
 // Step 2, thread t < Q (after a barrier): nested sums inside t's sub-block.

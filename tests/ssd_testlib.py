@@ -23,19 +23,21 @@ def to_device(inp: workloads.Inputs, device="cuda"):
     return t
 
 
-def run_gpu(inp: workloads.Inputs, init_states=None, split_len=0, chunk_size=None, **kw):
+def run_gpu(inp: workloads.Inputs, init_states=None, split_len=0, chunk_size=None, skip=True,
+            **kw):
+    """Run the HIP path; skip=False drops the D x term (D = None)."""
     import ssd_chunked_scan_amd as ssd
     import torch
     t = to_device(inp)
     h0 = None if init_states is None else torch.from_numpy(np.asarray(init_states, np.float32)).cuda()
-    y, fs = ssd.ssd_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["seq_idx"],
+    y, fs = ssd.ssd_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"] if skip else None, t["seq_idx"],
                         chunk_size=chunk_size or inp.wl.chunk_size, init_states=h0,
                         split_len=split_len, **kw)
     torch.cuda.synchronize()
     return y.float().cpu().numpy().astype(np.float64), fs.cpu().numpy().astype(np.float64)
 
 
-def oracle_slice(inp: workloads.Inputs, batches, heads, init_states=None):
+def oracle_slice(inp: workloads.Inputs, batches, heads, init_states=None, skip=True):
     """fp64 oracle on a subset of (batch rows, heads); B/C groups follow the
     heads.  Returns y [nb, L, nh, P] and final_states [nb, nh, P, N]."""
     H, G = inp.wl.nheads, inp.wl.ngroups
@@ -46,7 +48,7 @@ def oracle_slice(inp: workloads.Inputs, batches, heads, init_states=None):
     x = inp.x[batches][:, :, heads]
     dt = inp.dt[batches][:, :, heads]
     A = inp.A[heads]
-    D = inp.D[heads]
+    D = inp.D[heads] if skip else None
     # one group per selected head keeps the head -> group map exact
     B = inp.B[batches][:, :, groups]
     C = inp.C[batches][:, :, groups]

@@ -1,0 +1,51 @@
+"""The build's path check over the generated gfx950 assembly: from every MFMA,
+every path (fall-through and branch targets) must keep reads of its result at
+least 8 wait states away, except the accumulator of the next MFMA on the same
+registers and interlocked v_accvgpr_read of an AGPR result (CPU only)."""
+import pytest
+
+from ssd_chunked_scan_amd import _build
+
+HDR = "k:\n"
+
+
+def _asm(*lines):
+    return HDR + "\n".join("\t" + l if not l.endswith(":") else l for l in lines) + "\n"
+
+
+def test_rejects_short_straight_line_read():
+    asm = _asm("v_mfma_f32_16x16x32_bf16 v[0:3], v[4:7], v[8:11], 0",
+               "s_nop 3",
+               "v_mul_f32_e32 v20, v1, v21")
+    with pytest.raises(RuntimeError):
+        _build.check_mfma_result_reads(asm, "t")
+
+
+def test_rejects_read_in_taken_branch_target():
+    # the fall-through path is long enough, the taken branch is not
+    asm = _asm("v_mfma_f32_16x16x32_bf16 v[62:65], v[194:197], v[34:37], 0",
+               "s_cbranch_vccnz .LBB0_2",
+               "s_nop 15",
+               "v_mul_f32_e32 v3, v63, v189",
+               ".LBB0_2:",
+               "v_mul_f32_e32 v3, v63, v189")
+    with pytest.raises(RuntimeError):
+        _build.check_mfma_result_reads(asm, "t")
+
+
+def test_accepts_safe_forms():
+    asm = _asm("v_mfma_f32_16x16x32_bf16 v[0:3], v[4:7], v[8:11], 0",
+               "v_mfma_f32_16x16x32_bf16 v[0:3], v[12:15], v[16:19], v[0:3]",   # chain
+               "s_nop 7",
+               "v_mul_f32_e32 v20, v1, v21",                                    # 8 wait states
+               "v_mfma_f32_16x16x32_bf16 a[0:3], v[4:7], v[8:11], 0",
+               "v_accvgpr_read_b32 v30, a0",                                    # interlocked
+               "s_endpgm")
+    assert _build.check_mfma_result_reads(asm, "t") == 3
+
+
+def test_rejects_result_used_as_a_operand_too_soon():
+    asm = _asm("v_mfma_f32_16x16x32_bf16 v[0:3], v[4:7], v[8:11], 0",
+               "v_mfma_f32_16x16x32_bf16 v[20:23], v[0:3], v[8:11], 0")
+    with pytest.raises(RuntimeError):
+        _build.check_mfma_result_reads(asm, "t")

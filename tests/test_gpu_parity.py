@@ -19,9 +19,9 @@ def _case(name, **kw):
     return workloads.custom_workload(name=name, **kw)
 
 
-def _check_full(inp, y, fs, tol, init_states=None):
+def _check_full(inp, y, fs, tol, init_states=None, skip=True):
     b, H = inp.wl.batch, inp.wl.nheads
-    yr, fsr = oracle_slice(inp, range(b), range(H), init_states)
+    yr, fsr = oracle_slice(inp, range(b), range(H), init_states, skip=skip)
     ey, ef = max_rel(y, yr), max_rel(fs, fsr)
     assert ey <= tol and ef <= tol, f"{inp.wl.name}: y err {ey:.3e}, final_states err {ef:.3e}"
     return ey, ef
@@ -49,13 +49,16 @@ SHAPES = [
 ]
 
 
+@pytest.mark.parametrize("skip", [True, False], ids=["with_skip", "no_skip"])
 @pytest.mark.parametrize("Q,N,P,G,H,L", SHAPES, ids=lambda v: str(v))
-def test_bf16_shapes(Q, N, P, G, H, L):
+def test_bf16_shapes(Q, N, P, G, H, L, skip):
+    """Without the D x skip (D = None) the error bound applies to the state-space
+    part alone, which the skip term would otherwise dominate."""
     wl = _case(f"bf16_{Q}_{N}_{P}", batch=2, seqlen=L, nheads=H, headdim=P, dstate=N, ngroups=G,
                chunk_size=Q, io="bf16")
     inp = workloads.make_inputs(wl, seed=1)
-    y, fs = run_gpu(inp)
-    _check_full(inp, y, fs, TOL["bf16"])
+    y, fs = run_gpu(inp, skip=skip)
+    _check_full(inp, y, fs, TOL["bf16"], skip=skip)
 
 
 @pytest.mark.parametrize("Q,N,P,G,H,L", [(64, 16, 16, 1, 2, 190), (128, 64, 32, 2, 4, 300),
@@ -101,10 +104,10 @@ def test_packed_documents_small(io):
 
 # ----------------------------------------------------------- full-size workloads
 
-def _sampled(inp, pairs, y, fs, tol, label):
+def _sampled(inp, pairs, y, fs, tol, label, skip=True):
     worst = 0.0
     for b, h in pairs:
-        yr, fsr = oracle_slice(inp, [b], [h])
+        yr, fsr = oracle_slice(inp, [b], [h], skip=skip)
         ey = max_rel(y[b:b + 1, :, h:h + 1], yr)
         ef = max_rel(fs[b:b + 1, h:h + 1], fsr)
         worst = max(worst, ey, ef)
@@ -112,27 +115,30 @@ def _sampled(inp, pairs, y, fs, tol, label):
     return worst
 
 
-def test_layer27b_full_size_sampled():
+@pytest.mark.parametrize("skip", [True, False], ids=["with_skip", "no_skip"])
+def test_layer27b_full_size_sampled(skip):
     inp = workloads.make_inputs(workloads.WORKLOADS["layer27b"], seed=0)
-    y, fs = run_gpu(inp)
+    y, fs = run_gpu(inp, skip=skip)
     assert np.isfinite(y).all() and np.isfinite(fs).all()
     pairs = [(0, 0), (3, 41), (7, 79), (5, 17)]
-    _sampled(inp, pairs, y, fs, TOL["bf16"], "layer27b")
+    _sampled(inp, pairs, y, fs, TOL["bf16"], "layer27b", skip=skip)
 
 
-def test_decay_stress_full_size_sampled():
+@pytest.mark.parametrize("skip", [True, False], ids=["with_skip", "no_skip"])
+def test_decay_stress_full_size_sampled(skip):
     inp = workloads.make_inputs(workloads.WORKLOADS["decay"], seed=0)
-    y, fs = run_gpu(inp)
+    y, fs = run_gpu(inp, skip=skip)
     assert np.isfinite(y).all() and np.isfinite(fs).all()
-    _sampled(inp, [(0, 0), (0, 9)], y, fs, TOL["bf16"], "decay")
+    _sampled(inp, [(0, 0), (0, 9)], y, fs, TOL["bf16"], "decay", skip=skip)
 
 
-def test_packed_full_size_sampled_and_per_document():
+@pytest.mark.parametrize("skip", [True, False], ids=["with_skip", "no_skip"])
+def test_packed_full_size_sampled_and_per_document(skip):
     import oracle
     inp = workloads.make_inputs(workloads.WORKLOADS["packed"], seed=0)
-    y, fs = run_gpu(inp)
+    y, fs = run_gpu(inp, skip=skip)
     assert np.isfinite(y).all()
-    _sampled(inp, [(0, 0), (0, 13), (0, 31)], y, fs, TOL["bf16"], "packed")
+    _sampled(inp, [(0, 0), (0, 13), (0, 31)], y, fs, TOL["bf16"], "packed", skip=skip)
     # independent per-document oracle runs from a zero state, head 5 (group 1)
     lens = inp.doc_lens
     starts = np.concatenate([[0], np.cumsum(lens)])
@@ -141,7 +147,7 @@ def test_packed_full_size_sampled_and_per_document():
         s0, s1 = starts[d], starts[d + 1]
         yd, fd = oracle.ssd_forward(inp.x[:, s0:s1, h:h + 1], inp.dt[:, s0:s1, h:h + 1],
                                     inp.A[h:h + 1], inp.B[:, s0:s1, g:g + 1],
-                                    inp.C[:, s0:s1, g:g + 1], inp.D[h:h + 1])
+                                    inp.C[:, s0:s1, g:g + 1], inp.D[h:h + 1] if skip else None)
         e = max_rel(y[:, s0:s1, h:h + 1], yd)
         assert e <= TOL["bf16"], f"document {d}: {e:.3e}"
         if d == len(lens) - 1:
@@ -151,6 +157,9 @@ def test_packed_full_size_sampled_and_per_document():
 @pytest.mark.parametrize("b,L", workloads.SWEEP_SHAPES)
 @pytest.mark.parametrize("Q", [128, 256])
 def test_sweep_sampled(b, L, Q):
+    """Sampled with the skip for one head and without it (D = None) for another."""
     inp = workloads.make_inputs(workloads.WORKLOADS[f"sweep_b{b}_L{L}_q{Q}"], seed=0)
     y, fs = run_gpu(inp)
     _sampled(inp, [(b - 1, 31), (0, 7)], y, fs, TOL["bf16"], f"sweep b{b} L{L} Q{Q}")
+    y, fs = run_gpu(inp, skip=False)
+    _sampled(inp, [(0, 3)], y, fs, TOL["bf16"], f"sweep b{b} L{L} Q{Q} no skip", skip=False)
