@@ -26,23 +26,22 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 METRIC = "SSD fwd tokens/s + HBM GB/s (% of peak), Mamba-2 2.7B layer, L=2048"
-KERNEL_SOURCES = ["ssd_common.hpp", "ssd_segsum.hpp", "ssd_chunk_bf16.hpp", "ssd_chunk_f32.hip",
-                  "ssd_aux.hip", "ssd_api.cpp", "ssd_chunk_bf16_q64.hip",
-                  "ssd_chunk_bf16_q128.hip", "ssd_chunk_bf16_q256.hip"]
-
-
 def kernel_source_digest() -> str:
+    """Digest of every kernel source (the counters are only valid for it)."""
+    csrc = os.path.join(ROOT, "ssd_chunked_scan_amd", "csrc")
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "ssd_chunked_scan_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp", ".cpp")):
+            h.update(f.encode())
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(fh.read())
     return h.hexdigest()[:16]
 
 
 def counter_traffic(workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary of
     this workload, if it was taken on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"ssd_chunk_bf16_{workload}_counters.txt")
+    path = os.path.join(ROOT, "profiles", f"ssd_scan_bf16_{workload}_counters.txt")
     if not os.path.exists(path):
         return None
     vals = {}

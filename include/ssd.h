@@ -96,7 +96,15 @@ typedef struct {
 
 /* Bytes of device workspace ssd_fwd needs for this problem (16-byte aligned
  * pointer required).  Returns 0 when no workspace is needed, and also for an
- * invalid problem (ssd_fwd then reports the error). */
+ * invalid problem (ssd_fwd then reports the error).  The workspace holds,
+ * each part rounded up to 256 bytes:
+ *   - with more than one sequence split: the splits' states and decays,
+ *     4 * batch * nheads * nsplits * (headdim * dstate + 1) bytes;
+ *   - bf16 io: the per-group C B^T blocks of every chunk (the lower triangle
+ *     of C_c B_c^T in 16 x 32-token blocks, 1 KiB each, (Q/32)(Q/32+1)
+ *     blocks per chunk) and B token-transposed, i.e.
+ *     batch * ngroups * nchunks * (1024 (Q/32)(Q/32+1) + 2 Q dstate) bytes.
+ * The contents are scratch: nothing survives the call. */
 size_t ssd_fwd_workspace_bytes(const ssd_shape_t *shape, int64_t chunk_size,
                                ssd_dtype_t io);
 

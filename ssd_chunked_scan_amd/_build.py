@@ -4,7 +4,9 @@
 
 Every source under csrc/ is compiled by hipcc for gfx950 only, in parallel,
 then linked into ssd_chunked_scan_amd/libssd.so.  Packed-fp32 instructions
-are disabled in device code (-packed-fp32-ops).
+are disabled in device code (-packed-fp32-ops), and so is floating-point
+contraction (-ffp-contract=off): the kernels write every FMA they want as
+fmaf, and the segsum relies on each term being rounded before it is added.
 """
 from __future__ import annotations
 
@@ -24,7 +26,7 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
 ARCH = "gfx950"
 COMMON_FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
     "-I", CSRC, "-I", INCLUDE,

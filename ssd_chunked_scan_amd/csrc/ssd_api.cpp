@@ -13,9 +13,11 @@
 #include "ssd_common.hpp"
 
 namespace ssd {
-bool launch_chunk_bf16_q64(int N, int PB, const ChunkArgs &a, hipStream_t stream);
-bool launch_chunk_bf16_q128(int N, int PB, const ChunkArgs &a, hipStream_t stream);
-bool launch_chunk_bf16_q256(int N, int PB, const ChunkArgs &a, hipStream_t stream);
+bool launch_scan_bf16_q64(int N, int PB, const ChunkArgs &a, hipStream_t stream);
+bool launch_scan_bf16_q128(int N, int PB, const ChunkArgs &a, hipStream_t stream);
+bool launch_scan_bf16_q256(int N, int PB, const ChunkArgs &a, hipStream_t stream);
+bool launch_cb(int Q, int N, const CbArgs &a, hipStream_t stream);
+size_t cb_s_elems(int Q);
 void launch_chunk_f32(int Q, const ChunkArgs &a, hipStream_t stream);
 void launch_split_scan(const float *init_states, float *ws_states, const float *ws_decay,
                        int batch, int nheads, int nsplits, int pn, hipStream_t stream);
@@ -93,13 +95,20 @@ int device_cus() {
 
 struct Plan {
     int nchunks, nsplits, split_chunks, npblocks, pblock;
+    size_t split_bytes;   // split states + decays (nsplits > 1)
+    size_t s_bytes;       // per-group C B^T blocks (bf16)
+    size_t bt_bytes;      // per-group token-transposed B (bf16)
     size_t ws_bytes;
 };
 
-// Headdim block of the bf16 kernel: the whole head unless its LDS tiles do
-// not fit (chunk 256, dstate 128, headdim 128 -> two blocks of 64).
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Headdim block of the bf16 head kernel: the whole head, except at chunk 256
+// with headdim 128, where the double-buffered X tile would not leave room
+// (LDS and registers) -> two blocks of 64.
 int bf16_pblock(int64_t Q, int64_t N, int64_t P) {
-    if (Q == 256 && N == 128 && P == 128) return 64;
+    (void)N;
+    if (Q == 256 && P == 128) return 64;
     return (int)P;
 }
 
@@ -144,13 +153,19 @@ ssd_status_t make_plan(const ssd_shape_t *s, int64_t chunk, ssd_dtype_t io,
     }
     pl->split_chunks = (pl->nchunks + nsplits - 1) / nsplits;
     pl->nsplits = (pl->nchunks + pl->split_chunks - 1) / pl->split_chunks;
+    pl->split_bytes = 0;
     if (pl->nsplits > 1) {
         const size_t states = (size_t)s->batch * s->nheads * pl->nsplits * s->headdim * s->dstate;
         const size_t decay = (size_t)s->batch * s->nheads * pl->nsplits;
-        pl->ws_bytes = (states + ((decay + 3) / 4) * 4) * sizeof(float);
-    } else {
-        pl->ws_bytes = 0;
+        pl->split_bytes = round_up((states + decay) * sizeof(float), 256);
     }
+    pl->s_bytes = pl->bt_bytes = 0;
+    if (io == SSD_BF16) {
+        const size_t bgc = (size_t)s->batch * s->ngroups * pl->nchunks;
+        pl->s_bytes = round_up(bgc * ssd::cb_s_elems((int)chunk) * 2, 256);
+        pl->bt_bytes = round_up(bgc * (size_t)chunk * s->dstate * 2, 256);
+    }
+    pl->ws_bytes = pl->split_bytes + pl->s_bytes + pl->bt_bytes;
     return SSD_OK;
 }
 
@@ -232,6 +247,9 @@ ssd_status_t ssd_fwd_ex(const ssd_shape_t *shape, ssd_dtype_t io, const void *x,
     a.y = y;
     a.final_states = final_states;
     float *ws = (float *)workspace;
+    char *wsb = (char *)workspace;
+    a.ws_S = pl.s_bytes ? wsb + pl.split_bytes : nullptr;
+    a.ws_BT = pl.bt_bytes ? wsb + pl.split_bytes + pl.s_bytes : nullptr;
     a.ws_states = pl.nsplits > 1 ? ws : nullptr;
     a.ws_decay = pl.nsplits > 1
                      ? ws + (size_t)shape->batch * shape->nheads * pl.nsplits * shape->headdim * shape->dstate
@@ -257,13 +275,27 @@ ssd_status_t ssd_fwd_ex(const ssd_shape_t *shape, ssd_dtype_t io, const void *x,
             return true;
         }
         switch (args.chunk) {
-        case 64: return ssd::launch_chunk_bf16_q64(args.dstate, args.pblock, args, s);
-        case 128: return ssd::launch_chunk_bf16_q128(args.dstate, args.pblock, args, s);
-        default: return ssd::launch_chunk_bf16_q256(args.dstate, args.pblock, args, s);
+        case 64: return ssd::launch_scan_bf16_q64(args.dstate, args.pblock, args, s);
+        case 128: return ssd::launch_scan_bf16_q128(args.dstate, args.pblock, args, s);
+        default: return ssd::launch_scan_bf16_q256(args.dstate, args.pblock, args, s);
         }
     };
 
     (void)hipGetLastError();
+    if (io == SSD_BF16) {
+        ssd::CbArgs cb;
+        cb.B = B;
+        cb.C = C;
+        cb.ws_S = wsb + pl.split_bytes;
+        cb.ws_BT = wsb + pl.split_bytes + pl.s_bytes;
+        cb.batch = a.batch;
+        cb.seqlen = a.seqlen;
+        cb.ngroups = a.ngroups;
+        cb.nchunks = a.nchunks;
+        if (!ssd::launch_cb(a.chunk, a.dstate, cb, s)) return fail(SSD_ERR_UNSUPPORTED, "no C B^T kernel for this shape");
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return fail(SSD_ERR_HIP, "C B^T launch: %s", hipGetErrorString(e));
+    }
     if (a.nsplits > 1) {
         ssd::ChunkArgs loc = a;
         loc.mode = ssd::kModeSplitLocal;

@@ -36,6 +36,8 @@ struct ChunkArgs {
     float *final_states;       // nullable
     float *ws_states;          // [batch][nheads][nsplits][headdim][dstate]
     float *ws_decay;           // [batch][nheads][nsplits]
+    const void *ws_S;          // per-group C B^T blocks (bf16 path)
+    const void *ws_BT;         // per-group token-transposed B (bf16 path)
     int batch, seqlen, nheads, headdim, dstate, ngroups;
     int chunk;                 // chunk_size Q
     int nchunks;               // ceil(seqlen / Q)
@@ -45,6 +47,28 @@ struct ChunkArgs {
     int pblock;                // headdim columns per block
     int mode;                  // Mode
     int units;                 // batch * nheads * nsplits * npblocks
+};
+
+// Arguments of the per-group operand kernel (bf16 path).
+struct CbArgs {
+    const void *B;
+    const void *C;
+    void *ws_S;    // [batch][ngroups][nchunks][CbShape<Q>::NBLK][64 lanes] x 16 bytes
+    void *ws_BT;   // [batch][ngroups][nchunks][Q/32][dstate][4] x 16 bytes
+    int batch, seqlen, ngroups, nchunks;
+};
+
+// Layout of the per-group C B^T blocks of one chunk: for each 16-token row
+// tile I, the blocks of its 32-token column pairs m = 0 .. I/2.
+template <int Q>
+struct CbShape {
+    static constexpr int TILES = Q / 16;
+    static constexpr int NP = Q / 32;   // 32-token pairs
+    // blocks of row tiles 0 .. I-1
+    static __host__ __device__ constexpr int off(int I) {
+        return (I & 1) ? ((I + 1) / 2) * ((I + 1) / 2) : (I / 2) * (I / 2 + 1);
+    }
+    static constexpr int NBLK = off(TILES);
 };
 
 // Arguments of the decay-mask export kernel.

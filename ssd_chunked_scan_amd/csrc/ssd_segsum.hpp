@@ -27,10 +27,11 @@
 //
 // Document boundaries (page "Parallel Scan and Hardware-Aware SSM Kernels",
 // "When it breaks": mask a_k to zero at a boundary) enter by selecting a
-// factor to exactly 0, never through -inf arithmetic.  The floating-point
-// operations below use explicit round-to-nearest intrinsics so that the
-// compiler cannot fuse them and every kernel that includes this header
-// produces bit-identical factors and mask values.
+// factor to exactly 0, never through -inf arithmetic.  The library is built
+// with floating-point contraction off (hipcc otherwise fuses a * b + c into
+// an FMA, even through __fmul_rn / __fadd_rn), so every term is rounded
+// before it is added and every kernel that includes this header produces
+// bit-identical factors and mask values.
 #pragma once
 
 #include "ssd_common.hpp"
@@ -146,6 +147,116 @@ __device__ inline void seg_chunk_products(SegLds<Q> &s, int t) {
         for (int k = 0; k < NB; ++k) T = __fmul_rn(T, s.Tb[k]);
         s.T = T;
     }
+}
+
+// ---------------------------------------------------------------------------
+// Wave form of steps 1-2 for the bf16 kernels: thread t < Q owns token t, and
+// a 16-lane DPP row of its wave is one sub-block.  The nested sums are built
+// by repeated row shifts (DPP row_shl:1 hands each lane the value of the next
+// lane of its row, 0 past the row end): after k rounds of e <- shl1(e) + d,
+// lane t holds the nested sum from the end of the sub-block down to t over up
+// to k + 1 terms, accumulated in exactly the order of the sequential loop of
+// seg_block_sums, so W and Tb are bit-identical to it.
+
+// Per-chunk segsum values of the bf16 kernels in LDS.
+template <int Q>
+struct SegBuf {
+    static constexpr int NB = Q / 16;
+    float d[Q];       // log2-decay of token t (0 past the end of the row)
+    float dt[Q];      // dt of token t (0 past the end)
+    float wd[Q];      // W_t * dt_t: decay to the end of t's sub-block, times dt
+    int last1[Q];     // 1 + last reset position <= t inside t's sub-block, 0 if none
+    float Tb[NB];     // whole-sub-block decay (0 if a reset lies inside)
+    int blast1[NB];   // 1 + last reset position inside the sub-block, 0 if none
+};
+
+template <int CTRL>
+__device__ inline int dpp_row(int v) {
+    // row_mask and bank_mask 0xf; lanes whose source lies outside the row read 0
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, true);
+}
+constexpr int kDppRowShl1 = 0x101;
+constexpr int kDppRowShr1 = 0x111;
+
+__device__ inline float dpp_row_shl1(float v) {
+    return __builtin_bit_cast(float, dpp_row<kDppRowShl1>(__builtin_bit_cast(int, v)));
+}
+
+// Steps 1-2 for token t (thread t < Q; whole waves only): dtv and flag are
+// the token's dt and reset flag (0 past the end of the row).  resets is
+// uniform: false when the call has no seq_idx.
+template <int Q>
+__device__ inline void seg_tokens(SegBuf<Q> &s, int t, float dtv, int flag, float A_h,
+                                  bool resets) {
+    const float d = __fmul_rn(__fmul_rn(dtv, A_h), kLog2e);
+    float e = d;
+#pragma unroll
+    for (int k = 0; k < 15; ++k) e = __fadd_rn(dpp_row_shl1(e), d);
+    // e = sum over [t, end of sub-block]; the suffix (t, end] is the next lane's e
+    const float suf = dpp_row_shl1(e);
+    int fsuf = 0, last1 = 0;
+    if (resets) {
+        // 1 + last reset position <= t in the sub-block: running max to the right
+        int v = flag ? t + 1 : 0;
+        v = max(v, dpp_row<kDppRowShr1>(v));
+        v = max(v, dpp_row<kDppRowShr1 + 1>(v));
+        v = max(v, dpp_row<kDppRowShr1 + 3>(v));
+        v = max(v, dpp_row<kDppRowShr1 + 7>(v));
+        last1 = v;
+        // any reset in (t, end of sub-block]: running OR to the left of the
+        // next lanes' flags
+        int f = dpp_row<kDppRowShl1>(flag);
+        f |= dpp_row<kDppRowShl1>(f);
+        f |= dpp_row<kDppRowShl1 + 1>(f);
+        f |= dpp_row<kDppRowShl1 + 3>(f);
+        f |= dpp_row<kDppRowShl1 + 7>(f);
+        fsuf = f;
+        s.last1[t] = last1;
+        if ((t & 15) == 15) s.blast1[t >> 4] = last1;
+    }
+    const float W = fsuf ? 0.f : __builtin_amdgcn_exp2f(suf);
+    s.d[t] = d;
+    s.dt[t] = dtv;
+    s.wd[t] = __fmul_rn(W, dtv);
+    if ((t & 15) == 0) s.Tb[t >> 4] = (fsuf | flag) ? 0.f : __builtin_amdgcn_exp2f(e);
+}
+
+// Step 3 in registers (every wave after a barrier): the cross-sub-block
+// products V_J = Tb_0 ... Tb_{J-1}, Z_J = Tb_{NB-1} ... Tb_{J+1} and the
+// chunk decay T, multiplied in the order of seg_chunk_products.
+template <int NB>
+struct SegProducts {
+    float Tb[NB], V[NB], Z[NB], T;
+};
+
+template <int Q>
+__device__ inline void seg_products(const SegBuf<Q> &s, SegProducts<Q / 16> &p) {
+    constexpr int NB = Q / 16;
+    // (uniform values; moving them to scalar registers with readfirstlane on
+    // the elements of one vector load was miscompiled: every element got the
+    // first one)
+#pragma unroll
+    for (int k = 0; k < NB; k += 4) {
+        const f32x4 v = *(const f32x4 *)&s.Tb[k];
+#pragma unroll
+        for (int r = 0; r < 4 && k + r < NB; ++r) p.Tb[k + r] = v[r];
+    }
+    p.V[0] = 1.f;
+#pragma unroll
+    for (int k = 1; k < NB; ++k) p.V[k] = __fmul_rn(p.V[k - 1], p.Tb[k - 1]);
+    p.T = __fmul_rn(p.V[NB - 1], p.Tb[NB - 1]);
+    p.Z[NB - 1] = 1.f;
+#pragma unroll
+    for (int k = NB - 2; k >= 0; --k) p.Z[k] = __fmul_rn(p.Z[k + 1], p.Tb[k + 1]);
+}
+
+// Last reset position <= i in the chunk (-1 if none); I = i / 16.
+template <int Q>
+__device__ inline int seg_last_reset(const SegBuf<Q> &s, int i, int I) {
+    int r = s.last1[i];
+    if (r == 0)
+        for (int k = 0; k < I; ++k) r = max(r, s.blast1[k]);
+    return r - 1;
 }
 
 // Diagonal sub-block of row i (sub-block start I0), in the MFMA accumulator

@@ -1,0 +1,80 @@
+// LDS tile helpers shared by the bf16 kernels: the swizzled row-major tile
+// layout, workgroup barriers and asynchronous direct-to-LDS row staging.
+#pragma once
+
+#include "ssd_common.hpp"
+
+namespace ssd {
+
+// Row tile k of wave w: the pair (w, TILES-1-w), or tile w alone.
+template <class Cfg>
+__device__ inline int row_tile(int w, int k) {
+    return (Cfg::IT == 2 && k == 1) ? (Cfg::TILES - 1 - w) : w;
+}
+
+// Swizzled LDS tiles: row r of a tile with CPR 16-byte chunks per row starts at
+// element r * CPR * 8 and holds logical chunk c at physical chunk c ^ swz(r).
+// With R = 16 / CPR rows per 256 bytes (one pass over the banks) and
+// q = r / R, swz = 2q mod CPR + (q / (CPR/2)) mod 2: 16 consecutive rows read
+// at one logical chunk (16-byte reads) land in 16 different bank groups, and
+// the 4 consecutive rows x 2 chunks of a transpose read do not collide.
+template <int CPR>
+__device__ inline int swz(int r) {
+    constexpr int R = 16 / CPR;
+    const int q = r / R;
+    return ((2 * q) % CPR + (q / (CPR / 2)) % 2) & (CPR - 1);
+}
+
+template <int CPR>
+__device__ inline int tile_off(int r, int c) {
+    return r * (CPR * 8) + ((c ^ swz<CPR>(r)) << 3);
+}
+
+// Element offset of column col (a multiple of 4) of row r in a swizzled tile.
+template <int CPR>
+__device__ inline int tile_off_col(int r, int col) {
+    return tile_off<CPR>(r, col >> 3) + (col & 7);
+}
+
+// Eight k-consecutive bf16 at p (16-byte aligned LDS or global), or zeros.
+__device__ inline bf16x8 load8(const bf16 *p, bool ok) {
+    if (!ok) return bf16x8{};
+    return *(const bf16x8 *)p;
+}
+
+// Workgroup barrier ordering LDS traffic only: waits for this wave's LDS
+// operations, not for its outstanding global loads (the prefetch).
+__device__ inline void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Barrier after which every direct-to-LDS load issued before it has landed.
+__device__ inline void vmem_lds_sync() {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Asynchronously copy rows [0, nvalid) of a Q-row tile (CPR 16-byte chunks
+// per row, row r at src + r * gstride elements) into a swizzled LDS tile; rows
+// [nvalid, Q) are zero-filled with ordinary LDS stores.  Every wave issues
+// whole 1 KB blocks: block k covers LDS slots [64 k, 64 k + 64), lane l fills
+// slot 64 k + l (row slot / CPR, physical chunk slot % CPR) from the global
+// chunk that the swizzle puts there.
+template <int Q, int W, int CPR>
+__device__ inline void stage_rows_async(bf16 *lds, const bf16 *src, int64_t gstride, int nvalid,
+                                        int wave, int lane, int tid) {
+    constexpr int nblk = Q * CPR / 64;
+    static_assert(Q * CPR % 64 == 0, "whole 1 KB blocks");
+    for (int k = wave; k < nblk; k += W) {
+        const int slot = k * 64 + lane;
+        const int r = slot / CPR, pc = slot % CPR;
+        const int c = pc ^ swz<CPR>(r);
+        if (r < nvalid)
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void *)(src + (int64_t)r * gstride + c * 8),
+                (__attribute__((address_space(3))) void *)(lds + k * 512), 16, 0, 0);
+    }
+    if (nvalid < Q) {
+        for (int v = tid; v < (Q - nvalid) * CPR; v += 64 * W)
+            *(bf16x8 *)&lds[(nvalid * CPR + v) * 8] = bf16x8{};
+    }
+}
+
+}  // namespace ssd

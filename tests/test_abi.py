@@ -93,22 +93,36 @@ def test_argument_errors():
     assert _fwd(s, opts=o, ws=FAKE + 4, ws_bytes=need) == 4
 
 
+def _ru(v):
+    return (v + 255) // 256 * 256
+
+
+def _bf16_group_bytes(b, G, nchunks, Q, N):
+    """Per-group C B^T blocks and token-transposed B, as documented in ssd.h."""
+    return _ru(b * G * nchunks * 1024 * (Q // 32) * (Q // 32 + 1)) + _ru(b * G * nchunks * 2 * Q * N)
+
+
 def test_workspace_and_plan():
     s = good_shape()
     # forced split: 1000 tokens, chunk 256 -> 4 chunks; split 256 -> 4 splits
     need = ssd.ssd_fwd_workspace_bytes(s, 256, 1, split_len=256)
-    assert need == (2 * 8 * 4 * 64 * 128 + 64) * 4
-    assert ssd.ssd_fwd_workspace_bytes(s, 256, 1, split_len=1024) == 0
-    # planner: plenty of (batch, head) pairs -> one split per row, no workspace
+    assert need == _ru((2 * 8 * 4 * (64 * 128 + 1)) * 4) + _bf16_group_bytes(2, 2, 4, 256, 128)
+    # fp32 io keeps no per-group operands
+    assert ssd.ssd_fwd_workspace_bytes(s, 256, 0, split_len=256) == _ru((2 * 8 * 4 * (64 * 128 + 1)) * 4)
+    assert ssd.ssd_fwd_workspace_bytes(s, 256, 0, split_len=1024) == 0
+    assert ssd.ssd_fwd_workspace_bytes(s, 256, 1, split_len=1024) == _bf16_group_bytes(2, 2, 4, 256, 128)
+    assert ssd.ssd_fwd_workspace_bytes(s, 64, 1, split_len=1024) == _bf16_group_bytes(2, 2, 16, 64, 128)
+    # planner: plenty of (batch, head) pairs -> one split per row
     big = ssd.Shape(8, 2048, 80, 64, 128, 1)
     assert ssd.ssd_plan_split_len(big, 256, 1) == 2048
-    assert ssd.ssd_fwd_workspace_bytes(big, 256, 1) == 0
+    assert ssd.ssd_fwd_workspace_bytes(big, 256, 1) == _bf16_group_bytes(8, 1, 8, 256, 128)
+    assert ssd.ssd_fwd_workspace_bytes(big, 256, 0) == 0
     # few long rows -> sequence-parallel splits, chosen independently of the chunk
     long = ssd.Shape(1, 65536, 16, 64, 64, 1)
     sl = ssd.ssd_plan_split_len(long, 256, 1)
     assert sl % 256 == 0 and 256 <= sl < 65536
     assert ssd.ssd_plan_split_len(long, 64, 1) == sl
-    assert ssd.ssd_fwd_workspace_bytes(long, 256, 1) > 0
+    assert ssd.ssd_fwd_workspace_bytes(long, 256, 0) > 0
     assert ssd.ssd_fwd_workspace_bytes(ssd.Shape(0, 1, 1, 16, 16, 1), 256, 1) == 0
 
 

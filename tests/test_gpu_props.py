@@ -93,13 +93,21 @@ def test_batch_rows_independent():
 
 @pytest.mark.parametrize("io", ["bf16", "f32"])
 def test_zero_B_gives_skip_only(io):
+    """B = 0 leaves only the skip term D x (and a zero state).  The fp32 path
+    forms D x in fp32; the bf16 path carries D on the diagonal of the bf16
+    intra-chunk matrix, so its skip is x times D rounded to bf16, exactly
+    (one product of two bf16 values is exact in fp32), then rounded to bf16."""
     inp = workloads.make_inputs(_wl(io=io), seed=17)
     inp.B[:] = 0.0
     y, f = run_gpu(inp)
-    ref = (inp.D[None, None, :, None] * inp.x).astype(np.float32)   # fp32 product
+    D = inp.D if io == "f32" else workloads.bf16_round(inp.D)
+    ref = (D[None, None, :, None] * inp.x).astype(np.float32)   # fp32 product
     if io == "bf16":
         ref = workloads.bf16_round(ref)
     assert np.array_equal(y, ref.astype(np.float64))
+    # and within the parity bound of the exact skip term
+    exact = inp.D[None, None, :, None].astype(np.float64) * inp.x
+    assert max_rel(y, exact) <= TOL[io]
     assert np.all(f == 0)
 
 
