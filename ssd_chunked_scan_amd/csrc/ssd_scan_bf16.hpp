@@ -39,9 +39,10 @@
 // direct loads (global_load_lds_dwordx4) issued at the start of chunk c into
 // the other half of a double buffer; the h tile (bf16, operand of the state
 // projection) and the segsum values are double-buffered too and written for
-// chunk c+1 at the end of chunk c.  C_{c+1} rows go to registers during chunk
-// c, the C B^T and B^T fragments two 32-token pairs ahead, and y of chunk c
-// is stored at the start of chunk c+1, so the wait before the barrier never
+// chunk c+1 at the end of chunk c.  The chunk's C rows go to registers at its
+// start (the segsum row factors are computed while they arrive), the C B^T
+// and B^T fragments one 32-token pair ahead of their use, and y of chunk c is
+// stored at the start of chunk c+1, so the wait before the barrier never
 // waits for fresh stores.
 #pragma once
 
@@ -71,7 +72,7 @@ struct ScanCfg {
     static constexpr int LDH = N + 8;                    // padded pitch of the h^T tile
     static constexpr int NBLK = CbShape<Q>::NBLK;
     static constexpr size_t kLdsBytes =
-        2 * (size_t)SX * 2 + 2 * (size_t)PB * LDH * 2 + 2 * sizeof(SegBuf<Q>);
+        2 * (size_t)SX * 2 + 2 * (size_t)PB * LDH * 2 + 2 * sizeof(SegBuf<Q>);   // X stage + work
     static_assert(Q % 64 == 0 && Q <= 256, "chunk size");
     static_assert(N % 16 == 0 && N <= 128, "dstate");
     static_assert(PB % 16 == 0 && PB <= 128, "headdim block");
@@ -89,7 +90,12 @@ __global__ __launch_bounds__(64 * ((Q == 256) ? 8 : 4)) void ssd_scan_bf16_kerne
     constexpr int CPRX = Cfg::CPRX, LDH = Cfg::LDH, NBLK = Cfg::NBLK;
     static_assert(THREADS == 64 * ((Q == 256) ? 8 : 4), "launch bounds");
 
-    __shared__ __attribute__((aligned(1024))) bf16 sXbuf[2 * Cfg::SX];
+    // X tiles: the asynchronous loads land in sXstage (written only by them)
+    // and are copied to sXwork (read only by the MFMA operand reads) after the
+    // chunk's barrier.  Two distinct LDS objects let the compiler see that
+    // reads of the current tile do not wait for the loads in flight.
+    __shared__ __attribute__((aligned(1024))) bf16 sXstage[Cfg::SX];
+    __shared__ __attribute__((aligned(1024))) bf16 sXwork[Cfg::SX];
     __shared__ __attribute__((aligned(16))) bf16 sHbuf[2 * PB * LDH];
     __shared__ __attribute__((aligned(16))) SegBuf<Q> segbuf[2];
 
@@ -107,27 +113,32 @@ __global__ __launch_bounds__(64 * ((Q == 256) ? 8 : 4)) void ssd_scan_bf16_kerne
     const bool resets = a.seq_idx != nullptr;
     const int c_begin = s * a.split_chunks;
     const int c_end = min(a.nchunks, c_begin + a.split_chunks);
+    if (c_begin >= c_end) return;
 
     const float A_h = a.A[h];
     const float D_h = a.D ? a.D[h] : 0.f;
     const float *dt_row = a.dt + (int64_t)b * L * H + h;
-    const int32_t *seq_row = resets ? a.seq_idx + (int64_t)b * L : nullptr;
+    // Without seq_idx the document-id loads read dt bits of the same row
+    // instead (any valid address; the values are not used).
+    const int32_t *seq_row = resets ? a.seq_idx + (int64_t)b * L : (const int32_t *)(a.dt + (int64_t)b * L * H);
     const int p_base = pb * PB;
     const bf16 *Csrc = (const bf16 *)a.C + ((int64_t)b * L * G + grp) * N;
     const bf16 *Xsrc = (const bf16 *)a.x + ((int64_t)b * L * H + h) * P + p_base;
     const int64_t bg = (int64_t)b * G + grp;
-    const bf16x8 *Sws = (const bf16x8 *)a.ws_S + bg * a.nchunks * NBLK * 64;
+    const bf16x8 *Sws = (const bf16x8 *)a.ws_S + bg * a.nchunks * NBLK * 64 + lane;
     const bf16x8 *BTws = (const bf16x8 *)a.ws_BT + bg * a.nchunks * NP * N * 4;
 
-    // Row tiles of this wave (uniform).
-    int Irow[IT];
+    // Row tiles of this wave: I0 = w < TILES/2 and, with two per wave,
+    // I1 = TILES-1-w >= TILES/2.  So for pairs m >= NP/2 only I1 can reach
+    // the pair, and for m < NP/2 the pair lies wholly left of I1's diagonal.
+    int Irow0[IT];
 #pragma unroll
-    for (int it = 0; it < IT; ++it) Irow[it] = row_tile<Cfg>(wave, it);
+    for (int it = 0; it < IT; ++it) Irow0[it] = row_tile<Cfg>(wave, it);
 
     // State tiles owned by this wave: n-tiles nt0.., headdim tiles pt0..
     const int st_first = wave * ST;
     const bool st_valid = st_first < NT * PT;
-    const int nt0 = st_first / PT, pt0 = st_first % PT;
+    const int nt0 = st_valid ? st_first / PT : 0, pt0 = st_valid ? st_first % PT : 0;
 
     f32x4 hs[ST];
     bool state_zero = true;   // uniform: the carried state is known to be 0
@@ -159,36 +170,58 @@ __global__ __launch_bounds__(64 * ((Q == 256) ? 8 : 4)) void ssd_scan_bf16_kerne
             *(bf16x4 *)&sH[(pt * 16 + l16) * LDH + nt * 16 + 4 * g] = f32x4_to_bf16x4(hs[k]);
         }
     };
+    // X rows of chunk c into sXstage (asynchronous)
     auto stage_x = [&](int c) {
         const int t0 = c * Q;
-        stage_rows_async<Q, W, CPRX>(sXbuf + (c & 1) * Cfg::SX, Xsrc + (int64_t)t0 * H * P,
-                                     (int64_t)H * P, min(Q, L - t0), wave, lane, tid);
+        stage_rows_async<Q, W, CPRX>(sXstage, Xsrc + (int64_t)t0 * H * P, (int64_t)H * P,
+                                     min(Q, L - t0), wave, lane);
     };
-    // C_c rows of this wave's row tiles (B operand of the state projection, k = n)
+    // sXstage -> sXwork, 16 bytes per thread and step (between two barriers)
+    auto copy_x = [&]() {
+#pragma unroll
+        for (int k = 0; k < (Cfg::SX + 8 * THREADS - 1) / (8 * THREADS); ++k) {
+            const int e = (k * THREADS + tid) * 8;
+            if (Cfg::SX % (8 * THREADS) == 0 || e < Cfg::SX)
+                *(bf16x8 *)&sXwork[e] = *(const bf16x8 *)&sXstage[e];
+        }
+    };
+    // C_c rows of this wave's row tiles (B operand of the state projection,
+    // k = n); rows past the end of the sequence read row L-1 (their outputs
+    // are not stored), columns past dstate are zeroed at use.
     bf16x8 cf[IT][KN];
-    auto load_c = [&](int c) {
-        const int t0 = c * Q;
-        const int nvalid = min(Q, L - t0);
+    auto load_c = [&](int c, const int (&Irow)[IT]) {
 #pragma unroll
         for (int it = 0; it < IT; ++it) {
-            const int i = Irow[it] * 16 + l16;
+            const int t = min(c * Q + Irow[it] * 16 + l16, L - 1);
 #pragma unroll
             for (int kk = 0; kk < KN; ++kk) {
-                const int col = kk * 32 + 8 * g;
-                cf[it][kk] = load8(Csrc + (int64_t)(t0 + i) * G * N + col, i < nvalid && col < N);
+                const int col = min(kk * 32 + 8 * g, N - 8);
+                cf[it][kk] = *(const bf16x8 *)(Csrc + (int64_t)t * G * N + col);
             }
         }
     };
+    // Raw token values of a chunk for thread tid % Q (selected at use).
     float p_dt = 0.f;
-    int p_flag = 0;
+    int p_cur = 0, p_prev = 0;
     auto fetch_token = [&](int c) {
-        const int t0 = c * Q;
-        if (tid < Q) seg_fetch_token(tid, t0, min(Q, L - t0), dt_row, H, seq_row, p_dt, p_flag);
+        const int tg = min(c * Q + tid % Q, L - 1);
+        p_dt = dt_row[(int64_t)tg * H];
+        p_cur = seq_row[tg];
+        p_prev = seq_row[max(tg - 1, 0)];
+    };
+    auto tokens = [&](int c, int buf) {
+        if (tid < Q) {
+            const int tg = c * Q + tid;
+            const bool valid = tg < L;
+            const float dtv = valid ? p_dt : 0.f;
+            const int flag = (resets && valid && tg > 0 && p_cur != p_prev) ? 1 : 0;
+            seg_tokens<Q>(segbuf[buf], tid, dtv, flag, A_h, resets);
+        }
     };
 
     // Output tile accumulators: acc[it][pt] = Y^T tile (rows p, columns i).
     f32x4 acc[IT][PT];
-    auto store_y = [&](int c) {
+    auto store_y = [&](int c, const int (&Irow)[IT]) {
         const int t0 = c * Q;
         const int nvalid = min(Q, L - t0);
 #pragma unroll
@@ -204,65 +237,114 @@ __global__ __launch_bounds__(64 * ((Q == 256) ? 8 : 4)) void ssd_scan_bf16_kerne
         }
     };
 
-    if (c_begin < c_end) {
-        write_h(c_begin & 1);
-        stage_x(c_begin);
-        fetch_token(c_begin);
-        if (tid < Q) seg_tokens<Q>(segbuf[c_begin & 1], tid, p_dt, p_flag, A_h, resets);
-        if (full) load_c(c_begin);
-        vmem_lds_sync();
-    }
+    // ---- prologue: state tile, X, token values and C rows of the first chunk
+    write_h(c_begin & 1);
+    stage_x(c_begin);
+    fetch_token(c_begin);
+    tokens(c_begin, c_begin & 1);
+    vmem_lds_sync();
+    copy_x();
+    lds_sync();
 
     for (int c = c_begin; c < c_end; ++c) {
+        // The row tiles pass through an empty asm once per chunk, so that
+        // the compiler recomputes the few scalar values derived from them
+        // here instead of keeping dozens of them live across the loop.
+        int Irow[IT];
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            Irow[it] = Irow0[it];
+            asm volatile("" : "+s"(Irow[it]));
+        }
         const int buf = c & 1;
-        const int t0 = c * Q;
-        const bf16 *sX = sXbuf + buf * Cfg::SX;
+        const bf16 *sX = sXwork;
         const bf16 *sH = sHbuf + buf * PB * LDH;
         const SegBuf<Q> &sg = segbuf[buf];
+        const int cn = min(c + 1, c_end - 1);   // next chunk (the last one repeats itself)
 
-        // ---- 1. y of the previous chunk; next chunk's X tile and token values
-        if (full && c > c_begin) store_y(c - 1);
-        if (c + 1 < c_end) {
-            stage_x(c + 1);
-            fetch_token(c + 1);
-        }
-
-        // ---- 2. cross-sub-block decay products; carry the state
-        SegProducts<NB> pr;
-        seg_products<Q>(sg, pr);
-        split_decay = __fmul_rn(split_decay, pr.T);
+        // ---- 1. loads, in this order: this chunk's C rows and the first
+        // column pair's fragments, the next chunk's X tile, y of the previous
+        // chunk and the next token values.  Vector-memory completions are
+        // counted in issue order, so waiting for the C rows or the first
+        // fragments does not wait for the X tile.
+        const bf16x8 *Sc = Sws + (int64_t)c * NBLK * 64;
+        const bf16x8 *BTc = BTws + (int64_t)c * NP * N * 4;
+        bf16x8 sfr[2][IT], bfr[2][NTW];
+        // Fragments of pair m, loaded unconditionally (a row tile that does not
+        // reach the pair loads its own diagonal block instead, unused).
+        auto load_pair = [&](int m) {
+            const int slot = m & 1;
 #pragma unroll
-        for (int k = 0; k < ST; ++k) hs[k] *= pr.T;
+            for (int it = 0; it < IT; ++it) {
+                const int I = Irow[it];
+                sfr[slot][it] = Sc[(CbShape<Q>::off(I) + min(m, I >> 1)) * 64];
+            }
+#pragma unroll
+            for (int q = 0; q < NTW; ++q)
+                bfr[slot][q] = BTc[((int64_t)m * N + min(nt0 + q, NT - 1) * 16 + l16) * 4 + g];
+        };
+        load_c(c, Irow);
+        load_pair(NP - 1);
+        stage_x(cn);
+        if (full && c > c_begin) store_y(c - 1, Irow);
+        fetch_token(cn);
+
+        // ---- 2. cross-sub-block decay products V_I (this wave's row tiles)
+        // and T; carry the state
+        float VI[IT], T;
+        {
+            float Tb[NB];
+#pragma unroll
+            for (int k = 0; k < NB; k += 4) {
+                const f32x4 v = *(const f32x4 *)&sg.Tb[k];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Tb[k + r] = v[r];
+            }
+            seg_prefix_products<NB, IT>(Tb, Irow, VI, T);
+        }
+        split_decay = __fmul_rn(split_decay, T);
+#pragma unroll
+        for (int k = 0; k < ST; ++k) hs[k] *= T;
 
         // ---- 3. per-row factors of this wave's row tiles
         //   u_i            decay from the previous chunk's state to token i
         //   Fc             the off-diagonal chain F(i, J), started at J = I-1
-        //   fdg, dadd      diagonal-sub-block factor L_ij dt_j and the skip D_h
-        float u[IT], Fc[IT], fdg[IT][4], dadd[IT][4];
+        //   fdg            diagonal-sub-block factor L_ij dt_j
+        float u[IT], Fc[IT], fdg[IT][4];
         if (full) {
 #pragma unroll
             for (int it = 0; it < IT; ++it) {
                 const int I = Irow[it], I0 = I * 16, i = I0 + l16;
                 const int rs = resets ? seg_last_reset<Q>(sg, i, I) : -1;
+                float dd[16];
+#pragma unroll
+                for (int k = 0; k < 16; k += 4) {
+                    const f32x4 v = *(const f32x4 *)&sg.d[I0 + k];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) dd[k + r] = v[r];
+                }
                 float ev[4];
-                const float sum0 = seg_diag_row(sg.d, I0, i, g, ev);
+                const float sum0 = seg_diag_row_regs(dd, I0, i, g, ev);
                 const float F0 = seg_chain_start(sum0, I0, rs);
-                float V = 1.f;
-                for (int k = 0; k < I; ++k) V = __fmul_rn(V, sg.Tb[k]);
-                u[it] = __fmul_rn(F0, V);
+                u[it] = __fmul_rn(F0, VI[it]);
                 Fc[it] = F0;
                 const f32x4 dtj = *(const f32x4 *)&sg.dt[I0 + 4 * g];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int j = I0 + 4 * g + r;
                     fdg[it][r] = __fmul_rn(seg_diag_value(ev[r], i, j, rs), dtj[r]);
-                    dadd[it][r] = (j == i) ? D_h : 0.f;
                 }
             }
         }
 
         // ---- 4. state projection Y^T = h^T C^T, then the row scale u
         if (full) {
+            if constexpr (N < 32) {
+                // k = n runs over 32 columns; zero the ones past dstate
+#pragma unroll
+                for (int it = 0; it < IT; ++it)
+                    if (8 * g >= N) cf[it][0] = bf16x8{};
+            }
             if (state_zero) {
 #pragma unroll
                 for (int it = 0; it < IT; ++it)
@@ -273,8 +355,11 @@ __global__ __launch_bounds__(64 * ((Q == 256) ? 8 : 4)) void ssd_scan_bf16_kerne
                 for (int pt = 0; pt < PT; ++pt) {
 #pragma unroll
                     for (int kk = 0; kk < KN; ++kk) {
-                        const int col = kk * 32 + 8 * g;
-                        const bf16x8 hfrag = load8(&sH[(pt * 16 + l16) * LDH + col], col < N);
+                        const int col = min(kk * 32 + 8 * g, N - 8);
+                        bf16x8 hfrag = *(const bf16x8 *)&sH[(pt * 16 + l16) * LDH + col];
+                        if constexpr (N < 32) {
+                            if (8 * g >= N) hfrag = bf16x8{};
+                        }
 #pragma unroll
                         for (int it = 0; it < IT; ++it)
                             acc[it][pt] = kk == 0 ? mfma_bf16_zero_acc(hfrag, cf[it][0])
@@ -288,34 +373,25 @@ __global__ __launch_bounds__(64 * ((Q == 256) ? 8 : 4)) void ssd_scan_bf16_kerne
 #pragma unroll
                     for (int pt = 0; pt < PT; ++pt) acc[it][pt] *= u[it];
             }
-            if (c + 1 < c_end) load_c(c + 1);
         }
         state_zero = false;
 
         // ---- 5. 32-token column pairs, last to first (the F chain runs leftwards)
-        const bf16x8 *Sc = Sws + (int64_t)c * NBLK * 64 + lane;
-        const bf16x8 *BTc = BTws + (int64_t)c * NP * N * 4;
-        bf16x8 sfr[3][IT], bfr[3][NTW];
-        auto load_pair = [&](int m) {
-            const int slot = m % 3;
-            if (full) {
-#pragma unroll
-                for (int it = 0; it < IT; ++it)
-                    if (2 * m <= Irow[it]) sfr[slot][it] = Sc[(CbShape<Q>::off(Irow[it]) + m) * 64];
-            }
-            if (st_valid) {
-#pragma unroll
-                for (int q = 0; q < NTW; ++q)
-                    bfr[slot][q] = BTc[((int64_t)m * N + (nt0 + q) * 16 + l16) * 4 + g];
-            }
-        };
-        load_pair(NP - 1);
-        if (NP >= 2) load_pair(NP - 2);
+        float Zrun = 1.f;   // decay from the end of sub-block 2m+1 to the chunk end
 #pragma unroll
         for (int m = NP - 1; m >= 0; --m) {
-            if (m >= 2) load_pair(m - 2);
-            const int slot = m % 3;
+            if (m >= 1) load_pair(m - 1);
+            const int slot = m & 1;
+            // consume the pair's fragments here on every path, so that their
+            // loads stay where they were issued
+#pragma unroll
+            for (int it = 0; it < IT; ++it) asm volatile("" ::"v"(sfr[slot][it]));
             const int jr0 = 32 * m + 4 * g;   // tokens of slots e = 0..3; +16 for e = 4..7
+            // whole-sub-block decays of the pair and the suffix products Z
+            // (Z_J = Z_{J+1} Tb_{J+1}, as in seg_chunk_products)
+            const float Tb_lo = sg.Tb[2 * m], Tb_hi = sg.Tb[2 * m + 1];
+            const float Z_hi = Zrun, Z_lo = __fmul_rn(Zrun, Tb_hi);
+            Zrun = __fmul_rn(Z_lo, Tb_lo);
             // X_c fragments: lane (p = 16 pt + l16) holds X[j][p] at the slot tokens.
             bf16x8 xa[PT];
 #pragma unroll
@@ -333,8 +409,8 @@ __global__ __launch_bounds__(64 * ((Q == 256) ? 8 : 4)) void ssd_scan_bf16_kerne
                 f32x4 flo, fhi;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    flo[r] = __fmul_rn(wlo[r], pr.Z[2 * m]);
-                    fhi[r] = __fmul_rn(whi[r], pr.Z[2 * m + 1]);
+                    flo[r] = __fmul_rn(wlo[r], Z_lo);
+                    fhi[r] = __fmul_rn(whi[r], Z_hi);
                 }
                 bf16x8 xs[PTW];
                 if constexpr (Cfg::kAllP) {
@@ -368,35 +444,39 @@ __global__ __launch_bounds__(64 * ((Q == 256) ? 8 : 4)) void ssd_scan_bf16_kerne
 #pragma unroll
                 for (int it = 0; it < IT; ++it) {
                     const int I = Irow[it];
-                    if (2 * m > I) continue;
+                    // statically known: with two row tiles per wave, tile 0
+                    // never reaches the upper half of the pairs and tile 1 lies
+                    // wholly right of the lower half
+                    if (IT == 2 && it == 0 && m >= NP / 2) continue;
+                    const bool whole = (IT == 2 && it == 1 && m < NP / 2) || m < (I >> 1);
+                    if (!whole && m > (I >> 1)) continue;
                     const bf16x8 sv = sfr[slot][it];
                     bf16x8 pf;
-                    if (m == (I >> 1)) {
-                        if (I & 1) {
-                            // slots 0..3: sub-block I-1 (chain start); 4..7: diagonal
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) {
-                                pf[r] = (bf16)((float)sv[r] * __fmul_rn(Fc[it], wlo[r]));
-                                pf[4 + r] = (bf16)fmaf((float)sv[4 + r], fdg[it][r], dadd[it][r]);
-                            }
-                            Fc[it] = __fmul_rn(Fc[it], pr.Tb[2 * m]);
-                        } else {
-                            // slots 0..3: diagonal; 4..7: above the diagonal
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) {
-                                pf[r] = (bf16)fmaf((float)sv[r], fdg[it][r], dadd[it][r]);
-                                pf[4 + r] = (bf16)0.f;
-                            }
-                        }
-                    } else {
+                    if (whole) {
                         // both sub-blocks left of the diagonal: Fc = F(i, 2m+1)
-                        const float Flo = __fmul_rn(Fc[it], pr.Tb[2 * m + 1]);
+                        const float Flo = __fmul_rn(Fc[it], Tb_hi);
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             pf[4 + r] = (bf16)((float)sv[4 + r] * __fmul_rn(Fc[it], whi[r]));
                             pf[r] = (bf16)((float)sv[r] * __fmul_rn(Flo, wlo[r]));
                         }
-                        Fc[it] = __fmul_rn(Flo, pr.Tb[2 * m]);
+                        Fc[it] = __fmul_rn(Flo, Tb_lo);
+                    } else if (I & 1) {
+                        // slots 0..3: sub-block I-1 (chain start); 4..7: diagonal
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            pf[r] = (bf16)((float)sv[r] * __fmul_rn(Fc[it], wlo[r]));
+                            pf[4 + r] = (bf16)fmaf((float)sv[4 + r], fdg[it][r],
+                                                   (4 * g + r == l16) ? D_h : 0.f);
+                        }
+                        Fc[it] = __fmul_rn(Fc[it], Tb_lo);
+                    } else {
+                        // slots 0..3: diagonal; 4..7: above the diagonal
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            pf[r] = (bf16)fmaf((float)sv[r], fdg[it][r], (4 * g + r == l16) ? D_h : 0.f);
+                            pf[4 + r] = (bf16)0.f;
+                        }
                     }
 #pragma unroll
                     for (int pt = 0; pt < PT; ++pt) acc[it][pt] = mfma_bf16(xa[pt], pf, acc[it][pt]);
@@ -404,15 +484,17 @@ __global__ __launch_bounds__(64 * ((Q == 256) ? 8 : 4)) void ssd_scan_bf16_kerne
             }
         }
 
-        // ---- 6. hand the next chunk its h tile and segsum values
-        if (c + 1 < c_end) {
-            mfma_fence_all(hs);
-            write_h((c + 1) & 1);
-            if (tid < Q) seg_tokens<Q>(segbuf[(c + 1) & 1], tid, p_dt, p_flag, A_h, resets);
-            vmem_lds_sync();   // X_{c+1} has landed; all reads of this chunk's buffers are done
-        }
+        // ---- 6. hand the next chunk its h tile and segsum values (also after
+        // the last chunk, harmlessly: an unconditional wait here lets the
+        // compiler see that nothing is in flight at the top of the loop)
+        mfma_fence_all(hs);
+        write_h(buf ^ 1);
+        tokens(c + 1, buf ^ 1);
+        vmem_lds_sync();   // X_{c+1} has landed; all reads of this chunk's buffers are done
+        copy_x();
+        lds_sync();
     }
-    if (full && c_begin < c_end) store_y(c_end - 1);
+    if (full) store_y(c_end - 1, Irow0);
 
     // ---- split end: final states (last split) or the split's local summary
     if (!st_valid) return;

@@ -222,32 +222,23 @@ __device__ inline void seg_tokens(SegBuf<Q> &s, int t, float dtv, int flag, floa
 }
 
 // Step 3 in registers (every wave after a barrier): the cross-sub-block
-// products V_J = Tb_0 ... Tb_{J-1}, Z_J = Tb_{NB-1} ... Tb_{J+1} and the
-// chunk decay T, multiplied in the order of seg_chunk_products.
-template <int NB>
-struct SegProducts {
-    float Tb[NB], V[NB], Z[NB], T;
-};
-
-template <int Q>
-__device__ inline void seg_products(const SegBuf<Q> &s, SegProducts<Q / 16> &p) {
-    constexpr int NB = Q / 16;
-    // (uniform values; moving them to scalar registers with readfirstlane on
-    // the elements of one vector load was miscompiled: every element got the
-    // first one)
+// prefix products V_I = Tb_0 ... Tb_{I-1} for the row tiles I = Irow[k] and
+// the chunk decay T, multiplied in the order of seg_chunk_products (the
+// suffix products are formed on the fly by the callers, also in that order).
+template <int NB, int K>
+__device__ inline void seg_prefix_products(const float (&Tb)[NB], const int (&Irow)[K],
+                                           float (&VI)[K], float &T) {
+    float V = 1.f;
 #pragma unroll
-    for (int k = 0; k < NB; k += 4) {
-        const f32x4 v = *(const f32x4 *)&s.Tb[k];
+    for (int k = 0; k < K; ++k) VI[k] = 1.f;
 #pragma unroll
-        for (int r = 0; r < 4 && k + r < NB; ++r) p.Tb[k + r] = v[r];
+    for (int j = 1; j <= NB; ++j) {
+        V = __fmul_rn(V, Tb[j - 1]);
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            if (j < NB && Irow[k] == j) VI[k] = V;
     }
-    p.V[0] = 1.f;
-#pragma unroll
-    for (int k = 1; k < NB; ++k) p.V[k] = __fmul_rn(p.V[k - 1], p.Tb[k - 1]);
-    p.T = __fmul_rn(p.V[NB - 1], p.Tb[NB - 1]);
-    p.Z[NB - 1] = 1.f;
-#pragma unroll
-    for (int k = NB - 2; k >= 0; --k) p.Z[k] = __fmul_rn(p.Z[k + 1], p.Tb[k + 1]);
+    T = V;
 }
 
 // Last reset position <= i in the chunk (-1 if none); I = i / 16.
@@ -270,6 +261,18 @@ __device__ inline float seg_diag_row(const float *d, int I0, int i, int g, float
         if ((kk >> 2) == g) e[kk & 3] = acc;
         const float dk = d[I0 + kk];
         acc = (I0 + kk <= i) ? __fadd_rn(acc, dk) : acc;
+    }
+    return acc;
+}
+
+// seg_diag_row with the sub-block's log2-decays already in registers
+// (dd[kk] = d[I0 + kk]); the same additions in the same order.
+__device__ inline float seg_diag_row_regs(const float (&dd)[16], int I0, int i, int g, float e[4]) {
+    float acc = 0.f;
+#pragma unroll
+    for (int kk = 15; kk >= 0; --kk) {
+        if ((kk >> 2) == g) e[kk & 3] = acc;
+        acc = (I0 + kk <= i) ? __fadd_rn(acc, dd[kk]) : acc;
     }
     return acc;
 }

@@ -42,38 +42,57 @@ __device__ inline bf16x8 load8(const bf16 *p, bool ok) {
     return *(const bf16x8 *)p;
 }
 
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// in 6:4, lgkmcnt in 11:8; an all-ones field does not wait).  The waits are
+// issued through the builtin rather than inline assembly so that the
+// compiler's own wait placement sees them and knows what has completed.
+constexpr int kWaitLgkm0 = 0xC07F;        // lgkmcnt(0)
+constexpr int kWaitVmemLgkm0 = 0x0070;    // vmcnt(0) lgkmcnt(0)
+
 // Workgroup barrier ordering LDS traffic only: waits for this wave's LDS
 // operations, not for its outstanding global loads (the prefetch).
-__device__ inline void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+__device__ inline void lds_sync() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
 // Barrier after which every direct-to-LDS load issued before it has landed.
 __device__ inline void vmem_lds_sync() {
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(kWaitVmemLgkm0);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// 16 zero bytes in global memory: the source of the padding rows of a tile.
+static __device__ __attribute__((aligned(16))) const bf16 kZeroChunk[8] = {};
+
 // Asynchronously copy rows [0, nvalid) of a Q-row tile (CPR 16-byte chunks
-// per row, row r at src + r * gstride elements) into a swizzled LDS tile; rows
-// [nvalid, Q) are zero-filled with ordinary LDS stores.  Every wave issues
-// whole 1 KB blocks: block k covers LDS slots [64 k, 64 k + 64), lane l fills
-// slot 64 k + l (row slot / CPR, physical chunk slot % CPR) from the global
-// chunk that the swizzle puts there.
+// per row, row r at src + r * gstride elements) into a swizzled LDS tile, and
+// zeros into rows [nvalid, Q).  Every wave issues whole 1 KB blocks: block k
+// covers LDS slots [64 k, 64 k + 64), lane l fills slot 64 k + l (row
+// slot / CPR, physical chunk slot % CPR) from the global chunk that the
+// swizzle puts there.  Straight-line code with a fixed number of loads per
+// wave, so that the compiler can count them when it places its waits.
 template <int Q, int W, int CPR>
 __device__ inline void stage_rows_async(bf16 *lds, const bf16 *src, int64_t gstride, int nvalid,
-                                        int wave, int lane, int tid) {
+                                        int wave, int lane) {
     constexpr int nblk = Q * CPR / 64;
+    constexpr int per = (nblk + W - 1) / W;
     static_assert(Q * CPR % 64 == 0, "whole 1 KB blocks");
-    for (int k = wave; k < nblk; k += W) {
+#pragma unroll
+    for (int kk = 0; kk < per; ++kk) {
+        const int k = wave + kk * W;
+        if (nblk % W != 0 && k >= nblk) break;
         const int slot = k * 64 + lane;
         const int r = slot / CPR, pc = slot % CPR;
         const int c = pc ^ swz<CPR>(r);
-        if (r < nvalid)
-            __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void *)(src + (int64_t)r * gstride + c * 8),
-                (__attribute__((address_space(3))) void *)(lds + k * 512), 16, 0, 0);
-    }
-    if (nvalid < Q) {
-        for (int v = tid; v < (Q - nvalid) * CPR; v += 64 * W)
-            *(bf16x8 *)&lds[(nvalid * CPR + v) * 8] = bf16x8{};
+        const bf16 *g = (r < nvalid) ? src + (int64_t)r * gstride + c * 8 : kZeroChunk;
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
+                                         (__attribute__((address_space(3))) void *)(lds + k * 512),
+                                         16, 0, 0);
     }
 }
 
