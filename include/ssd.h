@@ -91,8 +91,17 @@ typedef struct {
 typedef struct {
     int64_t split_len;   /* tokens per sequence-parallel split: 0 = planner's
                             choice, else a positive multiple of chunk_size   */
-    int64_t reserved[7]; /* must be zero                                      */
+    int64_t flags;       /* SSD_OPT_* bits                                    */
+    int64_t reserved[6]; /* must be zero                                      */
 } ssd_options_t;
+
+/* flags: the workspace already holds the per-group operands (C_c B_c^T blocks
+ * and token-transposed B) of exactly these B and C, shape and chunk size,
+ * written by an earlier bf16 call on the same stream with the same workspace;
+ * skip recomputing them.  Only the head kernels run.  Meaningful for bf16 io
+ * (ignored for fp32).  The caller guarantees that B and C are unchanged; the
+ * library cannot check it. */
+#define SSD_OPT_REUSE_GROUP_OPERANDS 1
 
 /* Bytes of device workspace ssd_fwd needs for this problem (16-byte aligned
  * pointer required).  Returns 0 when no workspace is needed, and also for an

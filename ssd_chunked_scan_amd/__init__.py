@@ -47,7 +47,11 @@ class Shape(ctypes.Structure):
 
 
 class Options(ctypes.Structure):
-    _fields_ = [("split_len", ctypes.c_int64), ("reserved", ctypes.c_int64 * 7)]
+    _fields_ = [("split_len", ctypes.c_int64), ("flags", ctypes.c_int64),
+                ("reserved", ctypes.c_int64 * 6)]
+
+
+SSD_OPT_REUSE_GROUP_OPERANDS = 1
 
 
 _lib = None
@@ -138,10 +142,13 @@ def ssd_plan_split_len(shape: Shape, chunk_size: int, io: int) -> int:
 
 def ssd_fwd(x, dt, A, B, C, D=None, seq_idx=None, chunk_size: int = 256, init_states=None,
             return_final_states: bool = True, split_len: int = 0, y=None, final_states=None,
-            workspace=None, stream=None) -> Tuple[object, Optional[object]]:
+            workspace=None, stream=None, reuse_group_operands: bool = False
+            ) -> Tuple[object, Optional[object]]:
     """Run the forward pass on x.device.  Returns (y, final_states or None).
     ``split_len`` forces the sequence-parallel split length (0 = planner).
-    Preallocated ``y`` / ``final_states`` / ``workspace`` (uint8) may be given."""
+    Preallocated ``y`` / ``final_states`` / ``workspace`` (uint8) may be given.
+    ``reuse_group_operands`` (bf16) skips the per-group C B^T / B^T kernel: the
+    given ``workspace`` must hold them from an earlier call with the same B, C."""
     import torch
     lib = load_library()
     if x.dim() != 4 or B.dim() != 4:
@@ -172,11 +179,16 @@ def ssd_fwd(x, dt, A, B, C, D=None, seq_idx=None, chunk_size: int = 256, init_st
         final_states = torch.empty((b, H, P, N), dtype=torch.float32, device=dev)
     elif final_states is not None:
         _need(final_states, "final_states", (b, H, P, N), torch.float32, dev)
-    opts = Options(split_len)
+    if reuse_group_operands and workspace is None:
+        raise ValueError("reuse_group_operands needs the workspace of the earlier call")
+    opts = Options(split_len, SSD_OPT_REUSE_GROUP_OPERANDS if reuse_group_operands else 0)
     with torch.cuda.device(dev):
         ws_bytes = int(lib.ssd_fwd_ex_workspace_bytes(ctypes.byref(shape), chunk_size, io,
                                                       ctypes.byref(opts)))
         if ws_bytes and (workspace is None or workspace.numel() < ws_bytes):
+            if reuse_group_operands:
+                raise ValueError(f"reuse_group_operands: the workspace holds {workspace.numel()} "
+                                 f"bytes, {ws_bytes} needed")
             workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         if stream is None:
             stream = torch.cuda.current_stream(dev).cuda_stream

@@ -119,8 +119,10 @@ ssd_status_t check_problem(const ssd_shape_t *s, int64_t chunk, ssd_dtype_t io,
     ssd_status_t st = check_shape(s, chunk);
     if (st != SSD_OK) return st;
     if (opts) {
-        for (int k = 0; k < 7; ++k)
+        for (int k = 0; k < 6; ++k)
             if (opts->reserved[k] != 0) return fail(SSD_ERR_UNSUPPORTED, "reserved option fields must be zero");
+        if (opts->flags & ~(int64_t)SSD_OPT_REUSE_GROUP_OPERANDS)
+            return fail(SSD_ERR_UNSUPPORTED, "unknown option flags 0x%llx", (long long)opts->flags);
         if (opts->split_len < 0 || (opts->split_len > 0 && opts->split_len % chunk != 0))
             return fail(SSD_ERR_UNSUPPORTED, "split_len %lld must be 0 or a positive multiple of chunk_size",
                         (long long)opts->split_len);
@@ -282,7 +284,8 @@ ssd_status_t ssd_fwd_ex(const ssd_shape_t *shape, ssd_dtype_t io, const void *x,
     };
 
     (void)hipGetLastError();
-    if (io == SSD_BF16) {
+    const bool reuse = opts && (opts->flags & SSD_OPT_REUSE_GROUP_OPERANDS);
+    if (io == SSD_BF16 && !reuse) {
         ssd::CbArgs cb;
         cb.B = B;
         cb.C = C;

@@ -3,9 +3,9 @@
 //
 // Page "State Space Duality and Mamba-2" ("The SSD Block Decomposition
 // Algorithm"): the diagonal block of chunk c is ((C_c B_c^T) o L) X_c, and
-// C_c B_c^T depends on the group only, not on the head; page "Structured
-// State Space Duality" puts B and C per group, shared by the heads in the
-// manner of grouped-query attention.  This kernel evaluates the lower
+// C_c B_c^T depends on the group only, not on the head; the same page
+// ("Multi-Head SSM Patterns") shares B and C across the heads of a group in
+// the manner of grouped-query attention.  This kernel evaluates the lower
 // triangle of C_c B_c^T once per group on MFMA (fp32 accumulation, rounded
 // to bf16 for the head kernels) and also writes B_c token-transposed, the
 // operand layout of the chunk-state contraction B_c^T diag(w dt) X_c.
@@ -25,18 +25,23 @@
 
 namespace ssd {
 
-// One wave per (batch row, group, chunk, k): row tiles k and TILES-1-k (equal
-// triangle work for every wave) and the B^T fragments of pair k.
+// One wave per work item of a (batch row, group, chunk): items 0 .. NBLK-1
+// are the C B^T blocks (I, m) in storage order, items NBLK .. NBLK+NP-1 the
+// B^T fragments of pair m.  Four items per workgroup.
 template <int Q, int N>
-__global__ __launch_bounds__(64) void ssd_cb_kernel(CbArgs a) {
+__global__ __launch_bounds__(256) void ssd_cb_kernel(CbArgs a) {
     using S = CbShape<Q>;
     constexpr int KN = (N >= 32) ? N / 32 : 1;
-    const int lane = threadIdx.x, l16 = lane & 15, g = lane >> 4;
-    const int k = blockIdx.x % S::NP;
-    const int bgc = blockIdx.x / S::NP;          // (b * G + grp) * nchunks + c
-    const int c = bgc % a.nchunks;
-    const int bg = bgc / a.nchunks;
-    const int grp = bg % a.ngroups, b = bg / a.ngroups;
+    constexpr int ITEMS = S::NBLK + S::NP;
+    const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
+    const int64_t item_all = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t nitems = (int64_t)a.batch * a.ngroups * a.nchunks * ITEMS;
+    if (item_all >= nitems) return;
+    const int item = (int)(item_all % ITEMS);
+    const int64_t bgc = item_all / ITEMS;        // (b * G + grp) * nchunks + c
+    const int c = (int)(bgc % a.nchunks);
+    const int64_t bg = bgc / a.nchunks;
+    const int grp = (int)(bg % a.ngroups), b = (int)(bg / a.ngroups);
     const int L = a.seqlen, G = a.ngroups;
     const int t0 = c * Q;
     const bf16 *Bsrc = (const bf16 *)a.B + ((int64_t)b * L * G + grp) * N;
@@ -46,45 +51,47 @@ __global__ __launch_bounds__(64) void ssd_cb_kernel(CbArgs a) {
         return *(const bf16x8 *)(src + (int64_t)t * G * N + col);
     };
 
-    bf16x8 *Sdst = (bf16x8 *)a.ws_S + (int64_t)bgc * S::NBLK * 64;
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        const int I = half ? (S::TILES - 1 - k) : k;
+    if (item < S::NBLK) {
+        // block (I, m): the row tile I with off(I) <= item < off(I + 1)
+        int I = 0;
+        while (I + 1 < S::TILES && S::off(I + 1) <= item) ++I;
+        const int m = item - S::off(I);
         bf16x8 cf[KN];
 #pragma unroll
         for (int kk = 0; kk < KN; ++kk) cf[kk] = row8(Csrc, t0 + 16 * I + l16, kk * 32 + 8 * g);
-        for (int m = 0; m <= I / 2; ++m) {
-            f32x4 d[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        f32x4 d[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int J = 2 * m + h;
-                if (J > I) continue;
+        for (int h = 0; h < 2; ++h) {
+            const int J = 2 * m + h;
+            if (J > I) continue;
+            bf16x8 bfr[KN];
 #pragma unroll
-                for (int kk = 0; kk < KN; ++kk)
-                    d[h] = mfma_bf16(row8(Bsrc, t0 + 16 * J + l16, kk * 32 + 8 * g), cf[kk], d[h]);
-            }
-            mfma_fence(d[0], d[1]);
-            bf16x8 o;
+            for (int kk = 0; kk < KN; ++kk) bfr[kk] = row8(Bsrc, t0 + 16 * J + l16, kk * 32 + 8 * g);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                o[r] = (bf16)d[0][r];
-                o[4 + r] = (bf16)d[1][r];
-            }
-            Sdst[(S::off(I) + m) * 64 + lane] = o;
+            for (int kk = 0; kk < KN; ++kk) d[h] = mfma_bf16(bfr[kk], cf[kk], d[h]);
         }
-    }
-
-    // B^T fragments of pair k
-    bf16x8 *BTdst = (bf16x8 *)a.ws_BT + ((int64_t)bgc * S::NP + k) * N * 4;
-    for (int o = lane; o < N * 4; o += 64) {
-        const int n = o >> 2, gg = o & 3;
-        bf16x8 v;
+        mfma_fence(d[0], d[1]);
+        bf16x8 o;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int t = t0 + 32 * k + 4 * gg + (e & 3) + 16 * (e >> 2);
-            v[e] = (t < L) ? Bsrc[(int64_t)t * G * N + n] : (bf16)0.f;
+        for (int r = 0; r < 4; ++r) {
+            o[r] = (bf16)d[0][r];
+            o[4 + r] = (bf16)d[1][r];
         }
-        BTdst[o] = v;
+        ((bf16x8 *)a.ws_S)[(bgc * S::NBLK + item) * 64 + lane] = o;
+    } else {
+        // B^T fragments of pair k
+        const int k = item - S::NBLK;
+        bf16x8 *BTdst = (bf16x8 *)a.ws_BT + (bgc * S::NP + k) * N * 4;
+        for (int o = lane; o < N * 4; o += 64) {
+            const int n = o >> 2, gg = o & 3;
+            bf16x8 v;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int t = t0 + 32 * k + 4 * gg + (e & 3) + 16 * (e >> 2);
+                v[e] = (t < L) ? Bsrc[(int64_t)t * G * N + n] : (bf16)0.f;
+            }
+            BTdst[o] = v;
+        }
     }
 }
 
@@ -98,12 +105,14 @@ size_t cb_s_elems(int Q) {
 
 #define SSD_CB_CASE(q, n)                                                                   \
     if (Q == q && N == n) {                                                                 \
-        hipLaunchKernelGGL((ssd_cb_kernel<q, n>), grid, dim3(64), 0, stream, a);            \
+        constexpr int items = CbShape<q>::NBLK + CbShape<q>::NP;                             \
+        const int64_t total = (int64_t)a.batch * a.ngroups * a.nchunks * items;              \
+        hipLaunchKernelGGL((ssd_cb_kernel<q, n>), dim3((unsigned)((total + 3) / 4)), dim3(256), \
+                           0, stream, a);                                                   \
         return true;                                                                        \
     }
 
 bool launch_cb(int Q, int N, const CbArgs &a, hipStream_t stream) {
-    const dim3 grid((unsigned)((int64_t)a.batch * a.ngroups * a.nchunks * (Q / 32)));
     SSD_CB_CASE(64, 16) SSD_CB_CASE(64, 32) SSD_CB_CASE(64, 64) SSD_CB_CASE(64, 128)
     SSD_CB_CASE(128, 16) SSD_CB_CASE(128, 32) SSD_CB_CASE(128, 64) SSD_CB_CASE(128, 128)
     SSD_CB_CASE(256, 16) SSD_CB_CASE(256, 32) SSD_CB_CASE(256, 64) SSD_CB_CASE(256, 128)

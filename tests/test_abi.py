@@ -85,6 +85,9 @@ def test_argument_errors():
     o = ssd.Options(256)
     o.reserved[3] = 1
     assert _fwd(s, opts=o) == 3
+    o = ssd.Options(0, 2)             # unknown flag bit
+    assert _fwd(s, opts=o) == 3
+    assert b"flags" in ssd.load_library().ssd_last_error()
     o = ssd.Options(256)              # 4 splits -> workspace required
     assert _fwd(s, opts=o) == 5
     assert b"workspace" in ssd.load_library().ssd_last_error()

@@ -119,3 +119,23 @@ def test_reset_every_token():
     y, f = run_gpu(inp)
     yr, fr = oracle_slice(inp, [0], range(4))
     assert max_rel(y, yr) <= TOL["bf16"] and max_rel(f, fr) <= TOL["bf16"]
+
+
+def test_reuse_group_operands_is_bitwise_identical():
+    """A call told that the workspace already holds the per-group operands
+    (C B^T blocks, token-transposed B) of these B and C gives exactly the
+    result of the full call that wrote them."""
+    import ssd_chunked_scan_amd as ssd
+    import torch
+    inp = workloads.make_inputs(_wl(), seed=19)
+    t = to_device(inp)
+    wl = inp.wl
+    shape = ssd.Shape(wl.batch, wl.seqlen, wl.nheads, wl.headdim, wl.dstate, wl.ngroups)
+    ws = torch.empty(ssd.ssd_fwd_workspace_bytes(shape, wl.chunk_size, 1), dtype=torch.uint8,
+                     device="cuda")
+    y0, f0 = ssd.ssd_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["seq_idx"],
+                         chunk_size=wl.chunk_size, workspace=ws)
+    y1, f1 = ssd.ssd_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["seq_idx"],
+                         chunk_size=wl.chunk_size, workspace=ws, reuse_group_operands=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1) and torch.equal(f0, f1)
