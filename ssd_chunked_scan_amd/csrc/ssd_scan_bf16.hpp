@@ -39,11 +39,11 @@
 // direct loads (global_load_lds_dwordx4) issued at the start of chunk c into
 // the other half of a double buffer; the h tile (bf16, operand of the state
 // projection) and the segsum values are double-buffered too and written for
-// chunk c+1 at the end of chunk c.  The chunk's C rows go to registers at its
-// start (the segsum row factors are computed while they arrive), the C B^T
-// and B^T fragments one 32-token pair ahead of their use, and y of chunk c is
-// stored at the start of chunk c+1, so the wait before the barrier never
-// waits for fresh stores.
+// chunk c+1 at the end of chunk c.  The C rows of chunk c+1 go to registers
+// last in chunk c and stay in flight across the barrier (its wait counts them
+// out), the C B^T and B^T fragments one 32-token pair ahead of their use, and
+// y of chunk c is stored at the start of chunk c+1, so the wait before the
+// barrier never waits for fresh stores.
 #pragma once
 
 #include "ssd_common.hpp"
@@ -242,7 +242,9 @@ __global__ __launch_bounds__(64 * ((Q == 256) ? 8 : 4)) void ssd_scan_bf16_kerne
     stage_x(c_begin);
     fetch_token(c_begin);
     tokens(c_begin, c_begin & 1);
-    vmem_lds_sync();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    load_c(c_begin, Irow0);
+    vmem_lds_sync_keep<IT * KN>();   // the C rows may still be in flight
     copy_x();
     lds_sync();
 
@@ -276,6 +278,7 @@ __global__ __launch_bounds__(64 * ((Q == 256) ? 8 : 4)) void ssd_scan_bf16_kerne
             const int slot = m & 1;
 #pragma unroll
             for (int it = 0; it < IT; ++it) {
+                if (IT == 2 && it == 0 && m >= NP / 2) continue;   // never reaches the pair
                 const int I = Irow[it];
                 sfr[slot][it] = Sc[(CbShape<Q>::off(I) + min(m, I >> 1)) * 64];
             }
@@ -283,7 +286,6 @@ __global__ __launch_bounds__(64 * ((Q == 256) ? 8 : 4)) void ssd_scan_bf16_kerne
             for (int q = 0; q < NTW; ++q)
                 bfr[slot][q] = BTc[((int64_t)m * N + min(nt0 + q, NT - 1) * 16 + l16) * 4 + g];
         };
-        load_c(c, Irow);
         load_pair(NP - 1);
         stage_x(cn);
         if (full && c > c_begin) store_y(c - 1, Irow);
@@ -385,7 +387,8 @@ __global__ __launch_bounds__(64 * ((Q == 256) ? 8 : 4)) void ssd_scan_bf16_kerne
             // consume the pair's fragments here on every path, so that their
             // loads stay where they were issued
 #pragma unroll
-            for (int it = 0; it < IT; ++it) asm volatile("" ::"v"(sfr[slot][it]));
+            for (int it = 0; it < IT; ++it)
+                if (!(IT == 2 && it == 0 && m >= NP / 2)) asm volatile("" ::"v"(sfr[slot][it]));
             const int jr0 = 32 * m + 4 * g;   // tokens of slots e = 0..3; +16 for e = 4..7
             // whole-sub-block decays of the pair and the suffix products Z
             // (Z_J = Z_{J+1} Tb_{J+1}, as in seg_chunk_products)
@@ -490,7 +493,12 @@ __global__ __launch_bounds__(64 * ((Q == 256) ? 8 : 4)) void ssd_scan_bf16_kerne
         mfma_fence_all(hs);
         write_h(buf ^ 1);
         tokens(c + 1, buf ^ 1);
-        vmem_lds_sync();   // X_{c+1} has landed; all reads of this chunk's buffers are done
+        // the next chunk's C rows go out last: the barrier lets them stay in
+        // flight, while X_{c+1} (issued earlier) has landed and every read of
+        // this chunk's buffers is done
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        load_c(cn, Irow);
+        vmem_lds_sync_keep<IT * KN>();
         copy_x();
         lds_sync();
     }

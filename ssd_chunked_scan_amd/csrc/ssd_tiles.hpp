@@ -49,6 +49,9 @@ __device__ inline bf16x8 load8(const bf16 *p, bool ok) {
 constexpr int kWaitLgkm0 = 0xC07F;        // lgkmcnt(0)
 constexpr int kWaitVmemLgkm0 = 0x0070;    // vmcnt(0) lgkmcnt(0)
 
+// vmcnt(vm) lgkmcnt(0), vm < 64
+constexpr int wait_vm_lgkm0(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4); }
+
 // Workgroup barrier ordering LDS traffic only: waits for this wave's LDS
 // operations, not for its outstanding global loads (the prefetch).
 __device__ inline void lds_sync() {
@@ -62,6 +65,19 @@ __device__ inline void lds_sync() {
 __device__ inline void vmem_lds_sync() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt(kWaitVmemLgkm0);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// The same, except that the KEEP most recently issued vector-memory
+// operations may still be in flight (completions are counted in issue order,
+// so everything older has landed).  The caller issues exactly KEEP operations
+// after the last one it needs, behind a compiler fence.
+template <int KEEP>
+__device__ inline void vmem_lds_sync_keep() {
+    static_assert(KEEP >= 0 && KEEP < 64, "vmcnt range");
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(KEEP));
     __builtin_amdgcn_s_barrier();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
