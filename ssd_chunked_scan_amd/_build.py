@@ -161,11 +161,54 @@ def check_mfma_result_reads(asm_text: str, where: str) -> int:
     return n
 
 
+_VMEM = ("global_load", "global_store", "buffer_load", "buffer_store", "scratch_load",
+         "scratch_store", "flat_load", "flat_store", "global_atomic", "buffer_atomic")
+_WAIT_VM = re.compile(r"s_waitcnt\s+vmcnt\((\d+)\)")
+
+
+def check_counted_barrier_waits(asm_text: str, where: str) -> int:
+    """A barrier whose wait leaves K > 0 vector-memory operations in flight is
+    only correct if the K most recent ones are not direct-to-LDS loads (whose
+    data the barrier publishes).  Walk back from every such wait over
+    straight-line code: K ordinary vector-memory operations must come before
+    any global_load_lds, label or branch."""
+    n = 0
+    for fname, items in _parse_functions(asm_text):
+        for i, (kind, text) in enumerate(items):
+            if kind != "ins":
+                continue
+            m = _WAIT_VM.search(text)
+            if not m or int(m.group(1)) == 0:
+                continue
+            nxt = next((t for k, t in items[i + 1:] if k == "ins"), "")
+            if not nxt.startswith("s_barrier"):
+                continue
+            need, j = int(m.group(1)), i - 1
+            n += 1
+            while need > 0:
+                if j < 0 or items[j][0] == "label":
+                    raise RuntimeError(f"{where}: {fname}: counted barrier wait '{text}' reaches "
+                                       f"a label before {m.group(1)} vector-memory operations")
+                t = items[j][1]
+                op = t.split()[0]
+                if op.startswith("global_load_lds") or op.startswith("buffer_load_lds"):
+                    raise RuntimeError(f"{where}: {fname}: counted barrier wait '{text}' would leave "
+                                       f"a direct-to-LDS load in flight: {t}")
+                if op.startswith(("s_branch", "s_cbranch", "s_setpc")):
+                    raise RuntimeError(f"{where}: {fname}: counted barrier wait '{text}' reaches "
+                                       f"a branch before {m.group(1)} vector-memory operations")
+                if op.startswith(_VMEM):
+                    need -= 1
+                j -= 1
+    return n
+
+
 def _asm_check(hipcc: str, src: str) -> int:
     cmd = [hipcc, *COMMON_FLAGS, "-S", "--cuda-device-only", src, "-o", "-"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc -S failed on {src}:\n{r.stderr}")
+    check_counted_barrier_waits(r.stdout, os.path.basename(src))
     return check_mfma_result_reads(r.stdout, os.path.basename(src))
 
 

@@ -49,3 +49,32 @@ def test_rejects_result_used_as_a_operand_too_soon():
                "v_mfma_f32_16x16x32_bf16 v[20:23], v[0:3], v[8:11], 0")
     with pytest.raises(RuntimeError):
         _build.check_mfma_result_reads(asm, "t")
+
+
+def test_counted_barrier_wait_accepts_newer_plain_loads():
+    asm = _asm("global_load_lds_dwordx4 v[0:1], off",
+               "global_load_dwordx4 v[2:5], v[6:7], off",
+               "global_load_dwordx4 v[8:11], v[6:7], off offset:64",
+               "s_waitcnt vmcnt(2) lgkmcnt(0)",
+               "s_barrier")
+    assert _build.check_counted_barrier_waits(asm, "t") == 1
+
+
+def test_counted_barrier_wait_rejects_lds_load_in_flight():
+    asm = _asm("global_load_dwordx4 v[2:5], v[6:7], off",
+               "global_load_lds_dwordx4 v[0:1], off",
+               "global_load_dwordx4 v[8:11], v[6:7], off offset:64",
+               "s_waitcnt vmcnt(2) lgkmcnt(0)",
+               "s_barrier")
+    with pytest.raises(RuntimeError):
+        _build.check_counted_barrier_waits(asm, "t")
+
+
+def test_counted_barrier_wait_rejects_label_in_window():
+    asm = _asm("global_load_dwordx4 v[2:5], v[6:7], off",
+               ".LBB0_3:",
+               "global_load_dwordx4 v[8:11], v[6:7], off offset:64",
+               "s_waitcnt vmcnt(2) lgkmcnt(0)",
+               "s_barrier")
+    with pytest.raises(RuntimeError):
+        _build.check_counted_barrier_waits(asm, "t")
