@@ -14,36 +14,60 @@
 //
 // C_c B_c^T is head-independent; ssd_cb.hip evaluates it once per group and
 // chunk (and B_c token-transposed), in the exact per-lane order in which it is
-// loaded here, so the heads only apply their own decay mask.  The skip term
-// D x is the diagonal D I added to the intra-chunk matrix: it rides on the
-// diagonal-block MFMA.
+// loaded here.  Neither is scaled here: the decays go onto X and onto the
+// accumulators.
+//
+// Decay factorisation (page "GPU Hierarchy Meets Structured Matrices": the
+// mask is 1-semiseparable, so an off-diagonal sub-block is rank one).  With
+// 16-token sub-blocks, Tb_K the decay over sub-block K, W_j the decay from
+// token j to the end of its sub-block and F_i the decay from the start of row
+// i's sub-block I through i, an entry of sub-block (I, J), J < I, is
+//
+//   L_ij dt_j = F_i * (Tb_{J+1} ... Tb_{I-1}) * W_j dt_j.
+//
+// The middle product does not depend on i or j.  Over 32-token column pairs
+// m (sub-blocks 2m, 2m+1; one MFMA K step) it is built by Horner's rule: with
+// X''_j = W_j dt_j x_j, times Tb_{J+1} when J is even (the first sub-block of
+// its pair),
+//
+//   acc <- acc * (Tb_{2m} Tb_{2m+1}) + (C B^T)_{I, pair m} X''_{pair m}
+//
+// run over the pairs left of row tile I's diagonal pair, starting from the
+// state projection, leaves every term with its middle product (and the
+// projection with Tb_0 ... Tb_{I-1}); one more factor Tb_{I-1} for odd I and
+// the row factor F_i finish it.  The chunk state takes the same recurrence
+// over all pairs, starting from h_{c-1}: the pair decays then multiply out to
+// the decay from each token to the chunk end.  Every factor is a product of
+// decays in [0, 1] (no division, no exp of a positive sum), so the recurrence
+// is as stable as the direct product.  Only the diagonal pair of each row
+// tile is masked element by element (with the unscaled X); D x rides on its
+// diagonal.
 //
 // Everything is computed transposed (rows = headdim p) so that each lane of
-// an output tile owns one token i and four consecutive p: the row scale u_i
+// an output tile owns one token i and four consecutive p: the row factor F_i
 // is one value per lane and y is written 8 bytes per lane.
 //
 // MFMA 16x16x32 bf16 operand layout (verified on gfx950): A (16 x 32):
 // lane l holds row l%16, k = 8(l/16)..+7; B (32 x 16): lane l holds column
 // l%16, the same k; D (16 x 16): lane l holds column l%16, rows 4(l/16)..+3.
 // Over tokens (k = j) both operands use the slot map
-// e -> j = j0 + 4g + (e%4) + 16(e/4), g = l/16: the X operand comes from
-// row-major LDS through 16-bit transpose reads, the masked C B^T blocks and
-// B^T come from the per-group buffers in that order.
+// e -> j = j0 + 4g + (e%4) + 16(e/4), g = l/16.
 //
 // Work split inside the workgroup: W waves (8 for Q = 256, else 4).  Output
 // rows (16-token tiles) are dealt in the pairs (w, Q/16-1-w) so every wave
 // gets the same number of lower-triangular tiles; state tiles (16 x 16 of
 // N x P) are split by n first.
 //
-// Pipelining, one barrier per chunk: X_{c+1} reaches LDS through asynchronous
-// direct loads (global_load_lds_dwordx4) issued at the start of chunk c into
-// the other half of a double buffer; the h tile (bf16, operand of the state
-// projection) and the segsum values are double-buffered too and written for
-// chunk c+1 at the end of chunk c.  The C rows of chunk c+1 go to registers
-// last in chunk c and stay in flight across the barrier (its wait counts them
-// out), the C B^T and B^T fragments one 32-token pair ahead of their use, and
-// y of chunk c is stored at the start of chunk c+1, so the wait before the
-// barrier never waits for fresh stores.
+// Per chunk, two barriers.  Between them X_c, which reached LDS through
+// asynchronous direct loads (global_load_lds_dwordx4) issued at the start of
+// chunk c-1, is turned into MFMA fragments once for all waves (unscaled and
+// X'', fragment-ordered so that each operand is one 16-byte LDS read per
+// lane), and the state h_{c-1} goes to LDS as bf16.  After the second barrier
+// the loads of X_{c+1} are issued and the chunk is computed from registers and
+// LDS; the C rows of chunk c+1 go out last and stay in flight across the first
+// barrier of the next hand-over (its wait counts them out), the C B^T and B^T
+// fragments one pair ahead of their use, and y of chunk c is stored at the
+// start of chunk c+1.
 #pragma once
 
 #include "ssd_common.hpp"
@@ -69,10 +93,11 @@ struct ScanCfg {
     static constexpr bool kAllP = (PTW == PT);           // a wave's state tiles span all of P
     static constexpr int CPRX = PB / 8;                  // 16-byte chunks per X_c row
     static constexpr int SX = Q * PB;                    // swizzled, unpadded X tile
+    static constexpr int NFRAG = NP * PT;                // X fragments (pair, headdim tile)
     static constexpr int LDH = N + 8;                    // padded pitch of the h^T tile
     static constexpr int NBLK = CbShape<Q>::NBLK;
     static constexpr size_t kLdsBytes =
-        2 * (size_t)SX * 2 + 2 * (size_t)PB * LDH * 2 + 2 * sizeof(SegBuf<Q>);   // X stage + work
+        3 * (size_t)SX * 2 + (size_t)PB * LDH * 2 + 2 * sizeof(SegBuf<Q>);   // stage, 2 fragment sets, h
     static_assert(Q % 64 == 0 && Q <= 256, "chunk size");
     static_assert(N % 16 == 0 && N <= 128, "dstate");
     static_assert(PB % 16 == 0 && PB <= 128, "headdim block");
@@ -86,17 +111,18 @@ __global__ __launch_bounds__(64 * ((Q == 256) ? 8 : 4)) void ssd_scan_bf16_kerne
     using Cfg = ScanCfg<Q, N, PB>;
     constexpr int W = Cfg::W, THREADS = Cfg::THREADS;
     constexpr int NT = Cfg::NT, PT = Cfg::PT, KN = Cfg::KN, IT = Cfg::IT, NP = Cfg::NP;
-    constexpr int NB = Cfg::NB, ST = Cfg::ST, NTW = Cfg::NTW, PTW = Cfg::PTW;
+    constexpr int ST = Cfg::ST, NTW = Cfg::NTW, PTW = Cfg::PTW, NFRAG = Cfg::NFRAG;
     constexpr int CPRX = Cfg::CPRX, LDH = Cfg::LDH, NBLK = Cfg::NBLK;
     static_assert(THREADS == 64 * ((Q == 256) ? 8 : 4), "launch bounds");
 
-    // X tiles: the asynchronous loads land in sXstage (written only by them)
-    // and are copied to sXwork (read only by the MFMA operand reads) after the
-    // chunk's barrier.  Two distinct LDS objects let the compiler see that
-    // reads of the current tile do not wait for the loads in flight.
+    // sXstage is written only by the asynchronous loads and read only between
+    // the two barriers of a hand-over; the fragment sets sXr (unscaled) and
+    // sXs (X'') are separate LDS objects, so that the compiler sees that their
+    // reads do not wait for the loads in flight.
     __shared__ __attribute__((aligned(1024))) bf16 sXstage[Cfg::SX];
-    __shared__ __attribute__((aligned(1024))) bf16 sXwork[Cfg::SX];
-    __shared__ __attribute__((aligned(16))) bf16 sHbuf[2 * PB * LDH];
+    __shared__ __attribute__((aligned(1024))) bf16x8 sXr[NFRAG * 64];
+    __shared__ __attribute__((aligned(1024))) bf16x8 sXs[NFRAG * 64];
+    __shared__ __attribute__((aligned(16))) bf16 sH[PB * LDH];
     __shared__ __attribute__((aligned(16))) SegBuf<Q> segbuf[2];
 
     const int tid = threadIdx.x;
@@ -161,9 +187,8 @@ __global__ __launch_bounds__(64 * ((Q == 256) ? 8 : 4)) void ssd_scan_bf16_kerne
     }
     float split_decay = 1.f;
 
-    auto write_h = [&](int buf) {
+    auto write_h = [&]() {
         if (!full || !st_valid) return;
-        bf16 *sH = sHbuf + buf * PB * LDH;
 #pragma unroll
         for (int k = 0; k < ST; ++k) {
             const int nt = nt0 + k / PTW, pt = pt0 + k % PTW;
@@ -176,13 +201,30 @@ __global__ __launch_bounds__(64 * ((Q == 256) ? 8 : 4)) void ssd_scan_bf16_kerne
         stage_rows_async<Q, W, CPRX>(sXstage, Xsrc + (int64_t)t0 * H * P, (int64_t)H * P,
                                      min(Q, L - t0), wave, lane);
     };
-    // sXstage -> sXwork, 16 bytes per thread and step (between two barriers)
-    auto copy_x = [&]() {
+    // sXstage -> fragments (between the two barriers of a hand-over): fragment
+    // (m, pt) holds, for lane (p = 16 pt + l16, g), X[j][p] at the slot tokens
+    // j = 32m + 4g + (e%4) + 16(e/4); sXs holds the same times the X'' factor.
+    auto make_fragments = [&](const SegBuf<Q> &sg) {
 #pragma unroll
-        for (int k = 0; k < (Cfg::SX + 8 * THREADS - 1) / (8 * THREADS); ++k) {
-            const int e = (k * THREADS + tid) * 8;
-            if (Cfg::SX % (8 * THREADS) == 0 || e < Cfg::SX)
-                *(bf16x8 *)&sXwork[e] = *(const bf16x8 *)&sXstage[e];
+        for (int k = 0; k < (NFRAG + W - 1) / W; ++k) {
+            const int fr = wave + k * W;
+            if (NFRAG % W != 0 && fr >= NFRAG) break;
+            const int m = fr / PT, pt = fr % PT;
+            const int jr = 32 * m + 4 * g;
+            const int rr = jr + (l16 >> 2), col = pt * 16 + 4 * (l16 & 3);
+            const bf16x8 xr = join_bf16x8(lds_read_tr16(&sXstage[tile_off_col<CPRX>(rr, col)]),
+                                          lds_read_tr16(&sXstage[tile_off_col<CPRX>(rr + 16, col)]));
+            const f32x4 wlo = *(const f32x4 *)&sg.wd[jr];
+            const f32x4 whi = *(const f32x4 *)&sg.wd[jr + 16];
+            const float tb_hi = sg.Tb[2 * m + 1];
+            bf16x8 xs;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                xs[r] = (bf16)((float)xr[r] * __fmul_rn(wlo[r], tb_hi));
+                xs[4 + r] = (bf16)((float)xr[4 + r] * whi[r]);
+            }
+            sXr[fr * 64 + lane] = xr;
+            sXs[fr * 64 + lane] = xs;
         }
     };
     // C_c rows of this wave's row tiles (B operand of the state projection,
@@ -237,15 +279,16 @@ __global__ __launch_bounds__(64 * ((Q == 256) ? 8 : 4)) void ssd_scan_bf16_kerne
         }
     };
 
-    // ---- prologue: state tile, X, token values and C rows of the first chunk
-    write_h(c_begin & 1);
+    // ---- prologue: token values, X fragments, state tile and C rows of the
+    // first chunk
     stage_x(c_begin);
     fetch_token(c_begin);
     tokens(c_begin, c_begin & 1);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     load_c(c_begin, Irow0);
     vmem_lds_sync_keep<IT * KN>();   // the C rows may still be in flight
-    copy_x();
+    if (!state_zero) write_h();
+    make_fragments(segbuf[c_begin & 1]);
     lds_sync();
 
     for (int c = c_begin; c < c_end; ++c) {
@@ -259,21 +302,20 @@ __global__ __launch_bounds__(64 * ((Q == 256) ? 8 : 4)) void ssd_scan_bf16_kerne
             asm volatile("" : "+s"(Irow[it]));
         }
         const int buf = c & 1;
-        const bf16 *sX = sXwork;
-        const bf16 *sH = sHbuf + buf * PB * LDH;
         const SegBuf<Q> &sg = segbuf[buf];
         const int cn = min(c + 1, c_end - 1);   // next chunk (the last one repeats itself)
 
-        // ---- 1. loads, in this order: this chunk's C rows and the first
-        // column pair's fragments, the next chunk's X tile, y of the previous
-        // chunk and the next token values.  Vector-memory completions are
-        // counted in issue order, so waiting for the C rows or the first
-        // fragments does not wait for the X tile.
+        // ---- 1. loads, in this order: the first column pair's fragments,
+        // the next chunk's X tile, y of the previous chunk and the next token
+        // values.  Vector-memory completions are counted in issue order, so
+        // waiting for the C rows or the first fragments does not wait for the
+        // X tile.
         const bf16x8 *Sc = Sws + (int64_t)c * NBLK * 64;
         const bf16x8 *BTc = BTws + (int64_t)c * NP * N * 4;
         bf16x8 sfr[2][IT], bfr[2][NTW];
-        // Fragments of pair m, loaded unconditionally (a row tile that does not
-        // reach the pair loads its own diagonal block instead, unused).
+        // Fragments of pair m, loaded unconditionally: a row tile whose
+        // diagonal pair lies left of m loads its diagonal pair again, so the
+        // last load of each row tile is its diagonal pair.
         auto load_pair = [&](int m) {
             const int slot = m & 1;
 #pragma unroll
@@ -286,60 +328,13 @@ __global__ __launch_bounds__(64 * ((Q == 256) ? 8 : 4)) void ssd_scan_bf16_kerne
             for (int q = 0; q < NTW; ++q)
                 bfr[slot][q] = BTc[((int64_t)m * N + min(nt0 + q, NT - 1) * 16 + l16) * 4 + g];
         };
-        load_pair(NP - 1);
+        load_pair(0);
         stage_x(cn);
         if (full && c > c_begin) store_y(c - 1, Irow);
         fetch_token(cn);
 
-        // ---- 2. cross-sub-block decay products V_I (this wave's row tiles)
-        // and T; carry the state
-        float VI[IT], T;
-        {
-            float Tb[NB];
-#pragma unroll
-            for (int k = 0; k < NB; k += 4) {
-                const f32x4 v = *(const f32x4 *)&sg.Tb[k];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) Tb[k + r] = v[r];
-            }
-            seg_prefix_products<NB, IT>(Tb, Irow, VI, T);
-        }
-        split_decay = __fmul_rn(split_decay, T);
-#pragma unroll
-        for (int k = 0; k < ST; ++k) hs[k] *= T;
-
-        // ---- 3. per-row factors of this wave's row tiles
-        //   u_i            decay from the previous chunk's state to token i
-        //   Fc             the off-diagonal chain F(i, J), started at J = I-1
-        //   fdg            diagonal-sub-block factor L_ij dt_j
-        float u[IT], Fc[IT], fdg[IT][4];
-        if (full) {
-#pragma unroll
-            for (int it = 0; it < IT; ++it) {
-                const int I = Irow[it], I0 = I * 16, i = I0 + l16;
-                const int rs = resets ? seg_last_reset<Q>(sg, i, I) : -1;
-                float dd[16];
-#pragma unroll
-                for (int k = 0; k < 16; k += 4) {
-                    const f32x4 v = *(const f32x4 *)&sg.d[I0 + k];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) dd[k + r] = v[r];
-                }
-                float ev[4];
-                const float sum0 = seg_diag_row_regs(dd, I0, i, g, ev);
-                const float F0 = seg_chain_start(sum0, I0, rs);
-                u[it] = __fmul_rn(F0, VI[it]);
-                Fc[it] = F0;
-                const f32x4 dtj = *(const f32x4 *)&sg.dt[I0 + 4 * g];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int j = I0 + 4 * g + r;
-                    fdg[it][r] = __fmul_rn(seg_diag_value(ev[r], i, j, rs), dtj[r]);
-                }
-            }
-        }
-
-        // ---- 4. state projection Y^T = h^T C^T, then the row scale u
+        // ---- 2. state projection Y^T = h^T C^T (the Horner steps below
+        // give it the decay from the chunk start to the row tile)
         if (full) {
             if constexpr (N < 32) {
                 // k = n runs over 32 columns; zero the ones past dstate
@@ -368,138 +363,139 @@ __global__ __launch_bounds__(64 * ((Q == 256) ? 8 : 4)) void ssd_scan_bf16_kerne
                                                   : mfma_bf16(hfrag, cf[it][kk], acc[it][pt]);
                     }
                 }
-#pragma unroll
-                for (int it = 0; it < IT; ++it) mfma_fence_all(acc[it]);
-#pragma unroll
-                for (int it = 0; it < IT; ++it)
-#pragma unroll
-                    for (int pt = 0; pt < PT; ++pt) acc[it][pt] *= u[it];
             }
         }
         state_zero = false;
 
-        // ---- 5. 32-token column pairs, last to first (the F chain runs leftwards)
-        float Zrun = 1.f;   // decay from the end of sub-block 2m+1 to the chunk end
+        // ---- 3. 32-token column pairs, first to last: Horner steps of the
+        // chunk state (every pair) and of the output row tiles (pairs left of
+        // their diagonal pair)
+        float Tchunk = 1.f;
 #pragma unroll
-        for (int m = NP - 1; m >= 0; --m) {
-            if (m >= 1) load_pair(m - 1);
+        for (int m = 0; m < NP; ++m) {
+            if (m + 1 < NP) load_pair(m + 1);
             const int slot = m & 1;
             // consume the pair's fragments here on every path, so that their
             // loads stay where they were issued
 #pragma unroll
             for (int it = 0; it < IT; ++it)
                 if (!(IT == 2 && it == 0 && m >= NP / 2)) asm volatile("" ::"v"(sfr[slot][it]));
-            const int jr0 = 32 * m + 4 * g;   // tokens of slots e = 0..3; +16 for e = 4..7
-            // whole-sub-block decays of the pair and the suffix products Z
-            // (Z_J = Z_{J+1} Tb_{J+1}, as in seg_chunk_products)
-            const float Tb_lo = sg.Tb[2 * m], Tb_hi = sg.Tb[2 * m + 1];
-            const float Z_hi = Zrun, Z_lo = __fmul_rn(Zrun, Tb_hi);
-            Zrun = __fmul_rn(Z_lo, Tb_lo);
-            // X_c fragments: lane (p = 16 pt + l16) holds X[j][p] at the slot tokens.
-            bf16x8 xa[PT];
+            const float tp = sg.Tp[m];
+            Tchunk = __fmul_rn(Tchunk, tp);
+            bf16x8 xf[PT];
 #pragma unroll
-            for (int pt = 0; pt < PT; ++pt) {
-                const int rr = jr0 + (l16 >> 2), col = pt * 16 + 4 * (l16 & 3);
-                xa[pt] = join_bf16x8(lds_read_tr16(&sX[tile_off_col<CPRX>(rr, col)]),
-                                     lds_read_tr16(&sX[tile_off_col<CPRX>(rr + 16, col)]));
-            }
-            const f32x4 wlo = *(const f32x4 *)&sg.wd[jr0];
-            const f32x4 whi = *(const f32x4 *)&sg.wd[jr0 + 16];
+            for (int pt = 0; pt < PT; ++pt) xf[pt] = sXs[(m * PT + pt) * 64 + lane];
 
-            // chunk state: h^T += (B_c^T diag(w dt)) X_c over these 32 tokens,
-            // w dt = (W dt) Z_J with Z_J the decay after sub-block J
+            // chunk state: h^T <- h^T * Tp_m + B_m^T X''_m
             if (st_valid) {
-                f32x4 flo, fhi;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    flo[r] = __fmul_rn(wlo[r], Z_lo);
-                    fhi[r] = __fmul_rn(whi[r], Z_hi);
-                }
                 bf16x8 xs[PTW];
                 if constexpr (Cfg::kAllP) {
 #pragma unroll
-                    for (int k = 0; k < PTW; ++k) xs[k] = xa[k];
+                    for (int k = 0; k < PTW; ++k) xs[k] = xf[k];
                 } else {
 #pragma unroll
-                    for (int k = 0; k < PTW; ++k) {
-                        const int rr = jr0 + (l16 >> 2), col = (pt0 + k) * 16 + 4 * (l16 & 3);
-                        xs[k] = join_bf16x8(lds_read_tr16(&sX[tile_off_col<CPRX>(rr, col)]),
-                                            lds_read_tr16(&sX[tile_off_col<CPRX>(rr + 16, col)]));
-                    }
+                    for (int k = 0; k < PTW; ++k) xs[k] = sXs[(m * PT + pt0 + k) * 64 + lane];
                 }
 #pragma unroll
                 for (int q = 0; q < NTW; ++q) {
-                    const bf16x8 bv = bfr[slot][q];
-                    bf16x8 bs;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        bs[r] = (bf16)((float)bv[r] * flo[r]);
-                        bs[4 + r] = (bf16)((float)bv[4 + r] * fhi[r]);
+                    for (int k = 0; k < PTW; ++k) {
+                        hs[q * PTW + k] *= tp;
+                        hs[q * PTW + k] = mfma_bf16(bfr[slot][q], xs[k], hs[q * PTW + k]);
                     }
-#pragma unroll
-                    for (int k = 0; k < PTW; ++k)
-                        hs[q * PTW + k] = mfma_bf16(bs, xs[k], hs[q * PTW + k]);
                 }
             }
 
-            // diagonal block: Y^T += X_c^T (masked C B^T)^T for row tiles I >= 2m
+            // output rows: Y^T <- Y^T * Tp_m + X''_m^T (C B^T)_{I,m}^T
             if (full) {
 #pragma unroll
                 for (int it = 0; it < IT; ++it) {
-                    const int I = Irow[it];
                     // statically known: with two row tiles per wave, tile 0
                     // never reaches the upper half of the pairs and tile 1 lies
                     // wholly right of the lower half
                     if (IT == 2 && it == 0 && m >= NP / 2) continue;
-                    const bool whole = (IT == 2 && it == 1 && m < NP / 2) || m < (I >> 1);
-                    if (!whole && m > (I >> 1)) continue;
-                    const bf16x8 sv = sfr[slot][it];
-                    bf16x8 pf;
-                    if (whole) {
-                        // both sub-blocks left of the diagonal: Fc = F(i, 2m+1)
-                        const float Flo = __fmul_rn(Fc[it], Tb_hi);
+                    const bool left = (IT == 2 && it == 1 && m < NP / 2) || m < (Irow[it] >> 1);
+                    if (!left) continue;
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            pf[4 + r] = (bf16)((float)sv[4 + r] * __fmul_rn(Fc[it], whi[r]));
-                            pf[r] = (bf16)((float)sv[r] * __fmul_rn(Flo, wlo[r]));
-                        }
-                        Fc[it] = __fmul_rn(Flo, Tb_lo);
-                    } else if (I & 1) {
-                        // slots 0..3: sub-block I-1 (chain start); 4..7: diagonal
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            pf[r] = (bf16)((float)sv[r] * __fmul_rn(Fc[it], wlo[r]));
-                            pf[4 + r] = (bf16)fmaf((float)sv[4 + r], fdg[it][r],
-                                                   (4 * g + r == l16) ? D_h : 0.f);
-                        }
-                        Fc[it] = __fmul_rn(Fc[it], Tb_lo);
-                    } else {
-                        // slots 0..3: diagonal; 4..7: above the diagonal
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            pf[r] = (bf16)fmaf((float)sv[r], fdg[it][r], (4 * g + r == l16) ? D_h : 0.f);
-                            pf[4 + r] = (bf16)0.f;
-                        }
+                    for (int pt = 0; pt < PT; ++pt) {
+                        acc[it][pt] *= tp;
+                        acc[it][pt] = mfma_bf16(xf[pt], sfr[slot][it], acc[it][pt]);
                     }
+                }
+            }
+        }
+        split_decay = __fmul_rn(split_decay, Tchunk);
+
+        // ---- 4. per row tile: the row factor, then the diagonal pair
+        //   F_i    decay from the start of row i's sub-block through i
+        //   fdg    diagonal-sub-block factor L_ij dt_j
+        if (full) {
 #pragma unroll
-                    for (int pt = 0; pt < PT; ++pt) acc[it][pt] = mfma_bf16(xa[pt], pf, acc[it][pt]);
+            for (int it = 0; it < IT; ++it) {
+                const int I = Irow[it], I0 = I * 16, i = I0 + l16;
+                const int md = I >> 1;
+                const int rs = resets ? seg_last_reset<Q>(sg, i, I) : -1;
+                float dd[16];
+#pragma unroll
+                for (int k = 0; k < 16; k += 4) {
+                    const f32x4 v = *(const f32x4 *)&sg.d[I0 + k];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) dd[k + r] = v[r];
+                }
+                float ev[4];
+                const float sum0 = seg_diag_row_regs(dd, I0, i, g, ev);
+                const float F0 = seg_chain_start(sum0, I0, rs);
+                const float Gi = (I & 1) ? __fmul_rn(F0, sg.Tb[max(I - 1, 0)]) : F0;
+                const f32x4 dtj = *(const f32x4 *)&sg.dt[I0 + 4 * g];
+                float fdg[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j = I0 + 4 * g + r;
+                    fdg[r] = __fmul_rn(seg_diag_value(ev[r], i, j, rs), dtj[r]);
+                }
+                // the diagonal pair's C B^T fragment is the row tile's last load
+                const int last = (IT == 2 && it == 0) ? NP / 2 - 1 : NP - 1;
+                const bf16x8 sv = sfr[last & 1][it];
+                bf16x8 pf;
+                if (I & 1) {
+                    // slots 0..3: sub-block I-1 (L_ij dt_j = F_i W_j dt_j); 4..7: diagonal
+                    const f32x4 wlo = *(const f32x4 *)&sg.wd[32 * md + 4 * g];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        pf[r] = (bf16)((float)sv[r] * __fmul_rn(F0, wlo[r]));
+                        pf[4 + r] = (bf16)fmaf((float)sv[4 + r], fdg[r], (4 * g + r == l16) ? D_h : 0.f);
+                    }
+                } else {
+                    // slots 0..3: diagonal; 4..7: above the diagonal
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        pf[r] = (bf16)fmaf((float)sv[r], fdg[r], (4 * g + r == l16) ? D_h : 0.f);
+                        pf[4 + r] = (bf16)0.f;
+                    }
+                }
+                mfma_fence_all(acc[it]);
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt) {
+                    const bf16x8 xr = sXr[(md * PT + pt) * 64 + lane];
+                    acc[it][pt] = mfma_bf16(xr, pf, acc[it][pt] * Gi);
                 }
             }
         }
 
-        // ---- 6. hand the next chunk its h tile and segsum values (also after
-        // the last chunk, harmlessly: an unconditional wait here lets the
-        // compiler see that nothing is in flight at the top of the loop)
-        mfma_fence_all(hs);
-        write_h(buf ^ 1);
+        // ---- 5. hand over to the next chunk: its token values, then (after
+        // the loads of X_{c+1} have landed and every wave is done with this
+        // chunk's fragments and h tile) its fragments and h_c
         tokens(c + 1, buf ^ 1);
         // the next chunk's C rows go out last: the barrier lets them stay in
-        // flight, while X_{c+1} (issued earlier) has landed and every read of
-        // this chunk's buffers is done
+        // flight
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         load_c(cn, Irow);
         vmem_lds_sync_keep<IT * KN>();
-        copy_x();
+        if (c + 1 < c_end) {
+            mfma_fence_all(hs);
+            write_h();
+            make_fragments(segbuf[buf ^ 1]);
+        }
         lds_sync();
     }
     if (full) store_y(c_end - 1, Irow0);

@@ -168,6 +168,7 @@ struct SegBuf {
     int last1[Q];     // 1 + last reset position <= t inside t's sub-block, 0 if none
     float Tb[NB];     // whole-sub-block decay (0 if a reset lies inside)
     int blast1[NB];   // 1 + last reset position inside the sub-block, 0 if none
+    float Tp[NB / 2]; // decay over 32-token pair m: Tb[2m] * Tb[2m+1]
 };
 
 template <int CTRL>
@@ -218,7 +219,13 @@ __device__ inline void seg_tokens(SegBuf<Q> &s, int t, float dtv, int flag, floa
     s.d[t] = d;
     s.dt[t] = dtv;
     s.wd[t] = __fmul_rn(W, dtv);
-    if ((t & 15) == 0) s.Tb[t >> 4] = (fsuf | flag) ? 0.f : __builtin_amdgcn_exp2f(e);
+    // meaningful on the first lane of each sub-block
+    const float tb = (fsuf | flag) ? 0.f : __builtin_amdgcn_exp2f(e);
+    if ((t & 15) == 0) s.Tb[t >> 4] = tb;
+    // the first lane of each 32-token pair takes the decay of the pair's
+    // second sub-block from 16 lanes up (same wave: waves own 64 tokens)
+    const float tb_hi = __shfl_down(tb, 16, 64);
+    if ((t & 31) == 0) s.Tp[t >> 5] = __fmul_rn(tb, tb_hi);
 }
 
 // Step 3 in registers (every wave after a barrier): the cross-sub-block
