@@ -106,10 +106,19 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // Headdim block of the bf16 head kernel: the whole head, except at chunk 256
 // with headdim 128, where the double-buffered X tile would not leave room
 // (LDS and registers) -> two blocks of 64.
+// LDS bytes of the bf16 head kernel for chunk Q, dstate N, headdim block PB:
+// X stage, two fragment sets and the y tile (Q x PB bf16 each), the padded
+// h^T tile and two buffers of segsum values.
+int64_t bf16_lds_bytes(int64_t Q, int64_t N, int64_t PB) {
+    const int64_t seg = 4 * (4 * Q + 2 * (Q / 16) + Q / 32);
+    return 4 * Q * PB * 2 + PB * (N + 8) * 2 + 2 * seg;
+}
+
+// Largest headdim block (P, P/2, ...) whose workgroup fits in 160 KiB of LDS.
 int bf16_pblock(int64_t Q, int64_t N, int64_t P) {
-    (void)N;
-    if (Q == 256 && P == 128) return 64;
-    return (int)P;
+    int64_t pb = P;
+    while (pb > 16 && bf16_lds_bytes(Q, N, pb) > 160 * 1024) pb /= 2;
+    return (int)pb;
 }
 
 // Host-only validation of the problem description (no HIP call).

@@ -58,17 +58,26 @@
 // gets the same number of lower-triangular tiles; state tiles (16 x 16 of
 // N x P) are split by n first.
 //
-// Per chunk, two barriers.  Between them X_c, which reached LDS through
-// asynchronous direct loads (global_load_lds_dwordx4) issued at the start of
-// chunk c-1, is turned into MFMA fragments once for all waves (unscaled and
-// X'', fragment-ordered so that each operand is one 16-byte LDS read per
-// lane), and the state h_{c-1} goes to LDS as bf16.  After the second barrier
-// the loads of X_{c+1} are issued and the chunk is computed from registers and
-// LDS; the C rows of chunk c+1 go out last and stay in flight across the first
-// barrier of the next hand-over (its wait counts them out), the C B^T and B^T
-// fragments one pair ahead of their use, and y of chunk c is stored at the
-// start of chunk c+1.
+// Wave roles.  Vector-memory loads and stores of one wave complete in issue
+// order, so a wave that has a slow HBM load or a scattered store in flight
+// cannot use any load it issued later.  All HBM traffic of the workgroup is
+// therefore issued by one extra producer wave, and the W compute waves only
+// load operands that the other heads of the row keep in L2 (C B^T, B^T and C
+// rows).  During chunk c the producer stores y_{c-1} (rows of 16-byte chunks
+// read from an LDS tile), issues the direct-to-LDS loads
+// (global_load_lds_dwordx4) of X_{c+1}, gathers dt of chunk c+1 and computes
+// its segsum values (page "GPU Hierarchy Meets Structured Matrices": the
+// sub-block sums) into the other half of a double buffer.
+//
+// Per chunk, two barriers.  Between them X_{c+1} is turned into MFMA
+// fragments once for all compute waves (unscaled and X'', fragment-ordered so
+// that each operand is one 16-byte LDS read per lane), h_c goes to LDS as
+// bf16, and the producer reads the y tile of chunk c.  The C rows of chunk c+1
+// go out last and stay in flight across the first barrier (its wait counts
+// them out), and the C B^T and B^T fragments one pair ahead of their use.
 #pragma once
+
+#include <type_traits>
 
 #include "ssd_common.hpp"
 #include "ssd_segsum.hpp"
@@ -76,10 +85,18 @@
 
 namespace ssd {
 
+#ifndef SSD_PRODUCER_INFLIGHT
+#define SSD_PRODUCER_INFLIGHT 32
+#endif
+#ifndef SSD_PAIR_PREFETCH
+#define SSD_PAIR_PREFETCH 1
+#endif
+
 template <int Q, int N, int PB>
 struct ScanCfg {
-    static constexpr int W = (Q == 256) ? 8 : 4;        // waves per workgroup
-    static constexpr int THREADS = 64 * W;
+    static constexpr int W = (Q == 256) ? 8 : 4;        // compute waves
+    static constexpr int NPROD = 2;                      // producer waves
+    static constexpr int THREADS = 64 * (W + NPROD);
     static constexpr int NT = N / 16;                    // state n-tiles
     static constexpr int PT = PB / 16;                   // headdim tiles
     static constexpr int KN = (N >= 32) ? N / 32 : 1;    // K=32 steps over n
@@ -95,9 +112,11 @@ struct ScanCfg {
     static constexpr int SX = Q * PB;                    // swizzled, unpadded X tile
     static constexpr int NFRAG = NP * PT;                // X fragments (pair, headdim tile)
     static constexpr int LDH = N + 8;                    // padded pitch of the h^T tile
+    static constexpr int NYB = Q * PB * 2 / 1024;        // 1 KB blocks of the y tile
     static constexpr int NBLK = CbShape<Q>::NBLK;
+    // X stage, two fragment sets, y tile, h tile, segsum values
     static constexpr size_t kLdsBytes =
-        3 * (size_t)SX * 2 + (size_t)PB * LDH * 2 + 2 * sizeof(SegBuf<Q>);   // stage, 2 fragment sets, h
+        4 * (size_t)SX * 2 + (size_t)PB * LDH * 2 + 2 * sizeof(SegBuf<Q>);
     static_assert(Q % 64 == 0 && Q <= 256, "chunk size");
     static_assert(N % 16 == 0 && N <= 128, "dstate");
     static_assert(PB % 16 == 0 && PB <= 128, "headdim block");
@@ -107,26 +126,30 @@ struct ScanCfg {
 };
 
 template <int Q, int N, int PB>
-__global__ __launch_bounds__(64 * ((Q == 256) ? 8 : 4)) void ssd_scan_bf16_kernel(ChunkArgs a) {
+__global__ __launch_bounds__(64 * (((Q == 256) ? 8 : 4) + 2)) void ssd_scan_bf16_kernel(ChunkArgs a) {
     using Cfg = ScanCfg<Q, N, PB>;
     constexpr int W = Cfg::W, THREADS = Cfg::THREADS;
     constexpr int NT = Cfg::NT, PT = Cfg::PT, KN = Cfg::KN, IT = Cfg::IT, NP = Cfg::NP;
     constexpr int ST = Cfg::ST, NTW = Cfg::NTW, PTW = Cfg::PTW, NFRAG = Cfg::NFRAG;
-    constexpr int CPRX = Cfg::CPRX, LDH = Cfg::LDH, NBLK = Cfg::NBLK;
-    static_assert(THREADS == 64 * ((Q == 256) ? 8 : 4), "launch bounds");
+    constexpr int CPRX = Cfg::CPRX, LDH = Cfg::LDH, NBLK = Cfg::NBLK, NYB = Cfg::NYB;
+    constexpr int CPRY = PB / 8;
+    constexpr int NPROD = Cfg::NPROD;
+    static_assert(THREADS == 64 * (((Q == 256) ? 8 : 4) + 2), "launch bounds");
 
-    // sXstage is written only by the asynchronous loads and read only between
-    // the two barriers of a hand-over; the fragment sets sXr (unscaled) and
-    // sXs (X'') are separate LDS objects, so that the compiler sees that their
-    // reads do not wait for the loads in flight.
+    // sXstage is written only by the producer's asynchronous loads and read
+    // only between the two barriers of a hand-over; the fragment sets sXr
+    // (unscaled) and sXs (X'') are separate LDS objects.  sY holds the y tile
+    // of one chunk (swizzled like the X stage, CPRY 16-byte chunks per row).
     __shared__ __attribute__((aligned(1024))) bf16 sXstage[Cfg::SX];
     __shared__ __attribute__((aligned(1024))) bf16x8 sXr[NFRAG * 64];
     __shared__ __attribute__((aligned(1024))) bf16x8 sXs[NFRAG * 64];
+    __shared__ __attribute__((aligned(1024))) bf16 sY[Cfg::SX];
     __shared__ __attribute__((aligned(16))) bf16 sH[PB * LDH];
     __shared__ __attribute__((aligned(16))) SegBuf<Q> segbuf[2];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool producer = wave >= W;
     const int lane = tid & 63, l16 = lane & 15, g = lane >> 4;
     const Unit un = unit_of_block(a);
     const int b = un.b, h = un.h, s = un.s, pb = un.pb;
@@ -149,11 +172,120 @@ __global__ __launch_bounds__(64 * ((Q == 256) ? 8 : 4)) void ssd_scan_bf16_kerne
     const int32_t *seq_row = resets ? a.seq_idx + (int64_t)b * L : (const int32_t *)(a.dt + (int64_t)b * L * H);
     const int p_base = pb * PB;
     const bf16 *Csrc = (const bf16 *)a.C + ((int64_t)b * L * G + grp) * N;
-    const bf16 *Xsrc = (const bf16 *)a.x + ((int64_t)b * L * H + h) * P + p_base;
     const int64_t bg = (int64_t)b * G + grp;
     const bf16x8 *Sws = (const bf16x8 *)a.ws_S + bg * a.nchunks * NBLK * 64 + lane;
     const bf16x8 *BTws = (const bf16x8 *)a.ws_BT + bg * a.nchunks * NP * N * 4;
 
+
+    // ================= producer waves =================
+    // Producer pw (wave W + pw) streams blocks [pw, pw+1) * NYB / NPROD of
+    // each tile and the segsum rounds k = pw mod NPROD (64 tokens each).
+    auto run_producer = [&](auto PW) __attribute__((always_inline)) {
+        constexpr int pw = decltype(PW)::value;
+        constexpr int KB0 = pw * NYB / NPROD, KB1 = (pw + 1) * NYB / NPROD;
+        const bf16 *Xsrc = (const bf16 *)a.x + ((int64_t)b * L * H + h) * P + p_base;
+        // token values of a chunk, lane k*64+l holds token k*64+l
+        float p_dt[Q / 64];
+        int p_cur[Q / 64], p_prev[Q / 64];
+        auto fetch_tokens = [&](int c) __attribute__((always_inline)) {
+#pragma unroll
+            for (int k = pw; k < Q / 64; k += NPROD) {
+                const int tg = min(c * Q + k * 64 + lane, L - 1);
+                p_dt[k] = dt_row[(int64_t)tg * H];
+                p_cur[k] = seq_row[tg];
+                p_prev[k] = seq_row[max(tg - 1, 0)];
+            }
+        };
+        auto segsum = [&](int c, SegBuf<Q> &sgb) __attribute__((always_inline)) {
+#pragma unroll
+            for (int k = pw; k < Q / 64; k += NPROD) {
+                const int t = k * 64 + lane, tg = c * Q + t;
+                const bool valid = tg < L;
+                const float dtv = valid ? p_dt[k] : 0.f;
+                const int flag = (resets && valid && tg > 0 && p_cur[k] != p_prev[k]) ? 1 : 0;
+                seg_tokens<Q>(sgb, t, dtv, flag, A_h, resets);
+            }
+        };
+        // HBM streams of the workgroup in 1 KB blocks (64 lanes x 16 bytes):
+        // block k of X_c goes straight to LDS (sXstage, swizzled, rows past
+        // the sequence end read zeros), block k of the y tile of chunk c goes
+        // from sY to global memory.  Lane l of block k is physical chunk
+        // 64k + l of the tile: row r = (64k + l) / CPR, logical chunk
+        // ((64k + l) % CPR) ^ swz(r).
+        // Per lane: row lane / CPR of each block and its byte offset, fixed
+        // for the whole kernel; per block: a uniform row base and the
+        // swizzled chunk (k is a compile-time constant after unrolling).
+        const uint32_t row_bytes = (uint32_t)H * P * 2;
+        const int xrow = lane / CPRX, xpc = lane % CPRX;
+        const int yrow = lane / CPRY, ypc = lane % CPRY;
+        const uint32_t xrow_off = (uint32_t)xrow * row_bytes, yrow_off = (uint32_t)yrow * row_bytes;
+        const char *xbase = (const char *)Xsrc;
+        char *ybase = (char *)a.y + ((((int64_t)b * L) * H + h) * P + p_base) * 2;
+        auto dma_x = [&](int c, int k) __attribute__((always_inline)) {
+            constexpr int RB = 64 / CPRX;   // rows per block
+            const int t0 = c * Q, r = k * RB + xrow;
+            const int cc = xpc ^ swz<CPRX>(r);
+            const char *src = xbase + (int64_t)(t0 + k * RB) * row_bytes + (xrow_off + cc * 16);
+            if (t0 + Q > L && t0 + r >= L) src = (const char *)kZeroChunk;
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                             (__attribute__((address_space(3))) void *)(sXstage + k * 512),
+                                             16, 0, 0);
+        };
+        auto store_y = [&](int c, int k) __attribute__((always_inline)) {
+            constexpr int RB = 64 / CPRY;
+            const int t0 = c * Q, r = k * RB + yrow;
+            const int cc = ypc ^ swz<CPRY>(r);
+            const bf16x8 v = *(const bf16x8 *)&sY[(k * 64 + lane) * 8];
+            char *dst = ybase + (int64_t)(t0 + k * RB) * row_bytes + (yrow_off + cc * 16);
+            if (t0 + Q <= L || t0 + r < L) *(bf16x8 *)dst = v;
+        };
+        // Both streams, interleaved, with at most kInFlight blocks
+        // outstanding: a steady trickle keeps HBM busy without filling the
+        // memory pipeline that the compute waves' L2 loads go through.
+        constexpr int kGroup = (KB1 - KB0) < 4 ? (KB1 - KB0) : 4, kInFlight = SSD_PRODUCER_INFLIGHT;
+        static_assert((KB1 - KB0) % kGroup == 0 && NYB % NPROD == 0, "whole groups");
+        auto stream = [&](int cx, int cy) __attribute__((always_inline)) {
+#pragma unroll
+            for (int k0 = KB0; k0 < KB1; k0 += kGroup) {
+#pragma unroll
+                for (int k = k0; k < k0 + kGroup; ++k) {
+                    if (cx >= 0) dma_x(cx, k);
+                    if (cy >= 0) store_y(cy, k);
+                }
+                if (k0 + kGroup < KB1) {
+                    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                    __builtin_amdgcn_s_waitcnt(wait_vm(kInFlight));
+                    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                }
+            }
+        };
+
+        // chunk c: the token values of chunk c+1 (a short gather), X_{c+1}
+        // and y_{c-1} (written to sY by the compute waves between the
+        // barriers of the previous hand-over), then the segsum of chunk c+1,
+        // whose token values arrived long before.
+        fetch_tokens(c_begin);
+        stream(c_begin, -1);
+        segsum(c_begin, segbuf[c_begin & 1]);
+        vmem_lds_sync();
+        lds_sync();
+        for (int c = c_begin; c < c_end; ++c) {
+            const bool more = c + 1 < c_end;
+            if (more) fetch_tokens(c + 1);
+            stream(more ? c + 1 : -1, (full && c > c_begin) ? c - 1 : -1);
+            if (more) segsum(c + 1, segbuf[(c + 1) & 1]);
+            vmem_lds_sync();   // X_{c+1} has landed, sY is read
+            lds_sync();        // the compute waves write y_c to sY in between
+        }
+        if (full) stream(-1, c_end - 1);
+    };
+    if (producer) {
+        if (wave == W) run_producer(std::integral_constant<int, 0>{});
+        else run_producer(std::integral_constant<int, 1>{});
+        return;
+    }
+
+    // ================= compute waves =================
     // Row tiles of this wave: I0 = w < TILES/2 and, with two per wave,
     // I1 = TILES-1-w >= TILES/2.  So for pairs m >= NP/2 only I1 can reach
     // the pair, and for m < NP/2 the pair lies wholly left of I1's diagonal.
@@ -187,7 +319,7 @@ __global__ __launch_bounds__(64 * ((Q == 256) ? 8 : 4)) void ssd_scan_bf16_kerne
     }
     float split_decay = 1.f;
 
-    auto write_h = [&]() {
+    auto write_h = [&]() __attribute__((always_inline)) {
         if (!full || !st_valid) return;
 #pragma unroll
         for (int k = 0; k < ST; ++k) {
@@ -195,16 +327,10 @@ __global__ __launch_bounds__(64 * ((Q == 256) ? 8 : 4)) void ssd_scan_bf16_kerne
             *(bf16x4 *)&sH[(pt * 16 + l16) * LDH + nt * 16 + 4 * g] = f32x4_to_bf16x4(hs[k]);
         }
     };
-    // X rows of chunk c into sXstage (asynchronous)
-    auto stage_x = [&](int c) {
-        const int t0 = c * Q;
-        stage_rows_async<Q, W, CPRX>(sXstage, Xsrc + (int64_t)t0 * H * P, (int64_t)H * P,
-                                     min(Q, L - t0), wave, lane);
-    };
     // sXstage -> fragments (between the two barriers of a hand-over): fragment
     // (m, pt) holds, for lane (p = 16 pt + l16, g), X[j][p] at the slot tokens
     // j = 32m + 4g + (e%4) + 16(e/4); sXs holds the same times the X'' factor.
-    auto make_fragments = [&](const SegBuf<Q> &sg) {
+    auto make_fragments = [&](const SegBuf<Q> &sg) __attribute__((always_inline)) {
 #pragma unroll
         for (int k = 0; k < (NFRAG + W - 1) / W; ++k) {
             const int fr = wave + k * W;
@@ -242,49 +368,23 @@ __global__ __launch_bounds__(64 * ((Q == 256) ? 8 : 4)) void ssd_scan_bf16_kerne
             }
         }
     };
-    // Raw token values of a chunk for thread tid % Q (selected at use).
-    float p_dt = 0.f;
-    int p_cur = 0, p_prev = 0;
-    auto fetch_token = [&](int c) {
-        const int tg = min(c * Q + tid % Q, L - 1);
-        p_dt = dt_row[(int64_t)tg * H];
-        p_cur = seq_row[tg];
-        p_prev = seq_row[max(tg - 1, 0)];
-    };
-    auto tokens = [&](int c, int buf) {
-        if (tid < Q) {
-            const int tg = c * Q + tid;
-            const bool valid = tg < L;
-            const float dtv = valid ? p_dt : 0.f;
-            const int flag = (resets && valid && tg > 0 && p_cur != p_prev) ? 1 : 0;
-            seg_tokens<Q>(segbuf[buf], tid, dtv, flag, A_h, resets);
-        }
-    };
-
     // Output tile accumulators: acc[it][pt] = Y^T tile (rows p, columns i).
     f32x4 acc[IT][PT];
-    auto store_y = [&](int c, const int (&Irow)[IT]) {
-        const int t0 = c * Q;
-        const int nvalid = min(Q, L - t0);
+    // y tile of this wave's row tiles into sY (bf16)
+    auto write_y = [&](const int (&Irow)[IT]) {
 #pragma unroll
         for (int it = 0; it < IT; ++it) mfma_fence_all(acc[it]);
 #pragma unroll
         for (int it = 0; it < IT; ++it) {
             const int i = Irow[it] * 16 + l16;
-            if (i >= nvalid) continue;
-            bf16 *yrow = (bf16 *)a.y + (((int64_t)b * L + t0 + i) * H + h) * P + p_base;
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt)
-                *(bf16x4 *)(yrow + pt * 16 + 4 * g) = f32x4_to_bf16x4(acc[it][pt]);
+                *(bf16x4 *)&sY[tile_off_col<CPRY>(i, pt * 16 + 4 * g)] = f32x4_to_bf16x4(acc[it][pt]);
         }
     };
 
-    // ---- prologue: token values, X fragments, state tile and C rows of the
-    // first chunk
-    stage_x(c_begin);
-    fetch_token(c_begin);
-    tokens(c_begin, c_begin & 1);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    // ---- prologue: X fragments, state tile and C rows of the first chunk
+    // (the producer loads X and computes the segsum values meanwhile)
     load_c(c_begin, Irow0);
     vmem_lds_sync_keep<IT * KN>();   // the C rows may still be in flight
     if (!state_zero) write_h();
@@ -305,19 +405,17 @@ __global__ __launch_bounds__(64 * ((Q == 256) ? 8 : 4)) void ssd_scan_bf16_kerne
         const SegBuf<Q> &sg = segbuf[buf];
         const int cn = min(c + 1, c_end - 1);   // next chunk (the last one repeats itself)
 
-        // ---- 1. loads, in this order: the first column pair's fragments,
-        // the next chunk's X tile, y of the previous chunk and the next token
-        // values.  Vector-memory completions are counted in issue order, so
-        // waiting for the C rows or the first fragments does not wait for the
-        // X tile.
+        // ---- 1. the first column pair's fragments
         const bf16x8 *Sc = Sws + (int64_t)c * NBLK * 64;
         const bf16x8 *BTc = BTws + (int64_t)c * NP * N * 4;
-        bf16x8 sfr[2][IT], bfr[2][NTW];
+        constexpr int PD = SSD_PAIR_PREFETCH;   // pairs loaded ahead of their use
+        constexpr int NS = PD + 1;               // fragment slots
+        bf16x8 sfr[NS][IT], bfr[NS][NTW];
         // Fragments of pair m, loaded unconditionally: a row tile whose
         // diagonal pair lies left of m loads its diagonal pair again, so the
         // last load of each row tile is its diagonal pair.
-        auto load_pair = [&](int m) {
-            const int slot = m & 1;
+        auto load_pair = [&](int m) __attribute__((always_inline)) {
+            const int slot = m % NS;
 #pragma unroll
             for (int it = 0; it < IT; ++it) {
                 if (IT == 2 && it == 0 && m >= NP / 2) continue;   // never reaches the pair
@@ -328,10 +426,8 @@ __global__ __launch_bounds__(64 * ((Q == 256) ? 8 : 4)) void ssd_scan_bf16_kerne
             for (int q = 0; q < NTW; ++q)
                 bfr[slot][q] = BTc[((int64_t)m * N + min(nt0 + q, NT - 1) * 16 + l16) * 4 + g];
         };
-        load_pair(0);
-        stage_x(cn);
-        if (full && c > c_begin) store_y(c - 1, Irow);
-        fetch_token(cn);
+#pragma unroll
+        for (int m = 0; m < PD && m < NP; ++m) load_pair(m);
 
         // ---- 2. state projection Y^T = h^T C^T (the Horner steps below
         // give it the decay from the chunk start to the row tile)
@@ -373,8 +469,8 @@ __global__ __launch_bounds__(64 * ((Q == 256) ? 8 : 4)) void ssd_scan_bf16_kerne
         float Tchunk = 1.f;
 #pragma unroll
         for (int m = 0; m < NP; ++m) {
-            if (m + 1 < NP) load_pair(m + 1);
-            const int slot = m & 1;
+            if (m + PD < NP) load_pair(m + PD);
+            const int slot = m % NS;
             // consume the pair's fragments here on every path, so that their
             // loads stay where they were issued
 #pragma unroll
@@ -455,7 +551,7 @@ __global__ __launch_bounds__(64 * ((Q == 256) ? 8 : 4)) void ssd_scan_bf16_kerne
                 }
                 // the diagonal pair's C B^T fragment is the row tile's last load
                 const int last = (IT == 2 && it == 0) ? NP / 2 - 1 : NP - 1;
-                const bf16x8 sv = sfr[last & 1][it];
+                const bf16x8 sv = sfr[last % NS][it];
                 bf16x8 pf;
                 if (I & 1) {
                     // slots 0..3: sub-block I-1 (L_ij dt_j = F_i W_j dt_j); 4..7: diagonal
@@ -482,15 +578,15 @@ __global__ __launch_bounds__(64 * ((Q == 256) ? 8 : 4)) void ssd_scan_bf16_kerne
             }
         }
 
-        // ---- 5. hand over to the next chunk: its token values, then (after
-        // the loads of X_{c+1} have landed and every wave is done with this
-        // chunk's fragments and h tile) its fragments and h_c
-        tokens(c + 1, buf ^ 1);
-        // the next chunk's C rows go out last: the barrier lets them stay in
-        // flight
+        // ---- 5. hand over to the next chunk: after the loads of X_{c+1}
+        // have landed, every wave is done with this chunk's fragments and h
+        // tile and the producer with y_{c-1}: y_c to the producer, the next
+        // fragments and h_c.  The next chunk's C rows go out last: the
+        // barrier lets them stay in flight.
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         load_c(cn, Irow);
         vmem_lds_sync_keep<IT * KN>();
+        if (full) write_y(Irow);
         if (c + 1 < c_end) {
             mfma_fence_all(hs);
             write_h();
@@ -498,7 +594,6 @@ __global__ __launch_bounds__(64 * ((Q == 256) ? 8 : 4)) void ssd_scan_bf16_kerne
         }
         lds_sync();
     }
-    if (full) store_y(c_end - 1, Irow0);
 
     // ---- split end: final states (last split) or the split's local summary
     if (!st_valid) return;

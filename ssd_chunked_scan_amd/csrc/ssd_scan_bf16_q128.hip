@@ -27,7 +27,6 @@ bool launch_scan_bf16_q128(int N, int PB, const ChunkArgs &a, hipStream_t stream
     SSD_SCAN_CASE(128, 128, 16)
     SSD_SCAN_CASE(128, 128, 32)
     SSD_SCAN_CASE(128, 128, 64)
-    SSD_SCAN_CASE(128, 128, 128)
     return false;
 }
 

@@ -51,6 +51,8 @@ constexpr int kWaitVmemLgkm0 = 0x0070;    // vmcnt(0) lgkmcnt(0)
 
 // vmcnt(vm) lgkmcnt(0), vm < 64
 constexpr int wait_vm_lgkm0(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4); }
+// vmcnt(vm) only, vm < 64
+constexpr int wait_vm(int vm) { return wait_vm_lgkm0(vm) | (15 << 8); }
 
 // Workgroup barrier ordering LDS traffic only: waits for this wave's LDS
 // operations, not for its outstanding global loads (the prefetch).
