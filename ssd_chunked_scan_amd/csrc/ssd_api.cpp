@@ -114,6 +114,20 @@ int64_t bf16_lds_bytes(int64_t Q, int64_t N, int64_t PB) {
     return 4 * Q * PB * 2 + PB * (N + 8) * 2 + 2 * seg;
 }
 
+// Units of the last, partial round of bf16 head-kernel workgroups, which run
+// as two workgroups each (one per half of the headdim block): with W
+// workgroups resident per device, U units take ceil(U / W) rounds and the last
+// one holds T = U - (rounds - 1) W; when 2T <= W, halving those T units fills
+// that round with workgroups of about half the work.
+int bf16_half_units(int64_t units, int64_t Q, int64_t N, int64_t PB) {
+    if (PB < 32) return 0;
+    const int64_t per_cu = std::max<int64_t>(1, (160 * 1024) / bf16_lds_bytes(Q, N, PB));
+    const int64_t slots = device_cus() * per_cu;
+    const int64_t rounds = (units + slots - 1) / slots;
+    const int64_t tail = units - (rounds - 1) * slots;
+    return (rounds >= 2 && 2 * tail <= slots) ? (int)tail : 0;
+}
+
 // Largest headdim block (P, P/2, ...) whose workgroup fits in 160 KiB of LDS.
 int bf16_pblock(int64_t Q, int64_t N, int64_t P) {
     int64_t pb = P;
@@ -278,6 +292,7 @@ ssd_status_t ssd_fwd_ex(const ssd_shape_t *shape, ssd_dtype_t io, const void *x,
     a.npblocks = pl.npblocks;
     a.pblock = pl.pblock;
     a.units = a.batch * a.nheads * a.nsplits * a.npblocks;
+    a.half_units = (io == SSD_BF16) ? bf16_half_units(a.units, chunk_size, a.dstate, a.pblock) : 0;
     hipStream_t s = (hipStream_t)stream;
 
     auto launch = [&](const ssd::ChunkArgs &args) -> bool {

@@ -47,6 +47,8 @@ struct ChunkArgs {
     int pblock;                // headdim columns per block
     int mode;                  // Mode
     int units;                 // batch * nheads * nsplits * npblocks
+    int half_units;            // the last half_units units run as two workgroups,
+                               // one per half of the headdim block (grid = units + half_units)
 };
 
 // Arguments of the per-group operand kernel (bf16 path).
@@ -83,18 +85,30 @@ struct MaskArgs {
 
 struct Unit {
     int b, h, s, pb;
+    int half;   // -1: the whole headdim block; 0 or 1: that half of it
 };
 
 // Workgroups are dealt to the 8 XCDs round-robin by block index.  Remap so
 // that each XCD receives a contiguous range of logical units; logical units
 // are ordered (batch, head, split, headdim block), so the heads of one batch
-// row that share its B/C rows run on one XCD and share its L2.
+// row that share its B/C rows run on one XCD and share its L2.  The last
+// half_units units come after all others, two blocks each (the blocks of the
+// last, partial round of workgroups: halving them fills that round).
 __device__ inline Unit unit_of_block(const ChunkArgs &a) {
     const int blk = blockIdx.x;
-    const int per = a.units / 8, rem = a.units % 8;
-    const int xcd = blk % 8, k = blk / 8;
-    const int logical = xcd * per + (xcd < rem ? xcd : rem) + k;
+    const int whole = a.units - a.half_units;
+    int logical, half = -1;
+    if (blk < whole) {
+        const int per = whole / 8, rem = whole % 8;
+        const int xcd = blk % 8, k = blk / 8;
+        logical = xcd * per + (xcd < rem ? xcd : rem) + k;
+    } else {
+        const int j = blk - whole;
+        logical = whole + (j >> 1);
+        half = j & 1;
+    }
     Unit u;
+    u.half = half;
     u.pb = logical % a.npblocks;
     int r = logical / a.npblocks;
     u.s = r % a.nsplits;

@@ -125,8 +125,14 @@ struct ScanCfg {
     static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 };
 
+// One workgroup's walk over its chunks.  PB is the number of headdim columns
+// the workgroup owns (a whole headdim block, or half of one); the LDS arrays
+// belong to the kernel and are at least as large as this PB needs.
 template <int Q, int N, int PB>
-__global__ __launch_bounds__(64 * (((Q == 256) ? 8 : 4) + 2)) void ssd_scan_bf16_kernel(ChunkArgs a) {
+__device__ __attribute__((always_inline)) inline void scan_body(
+        const ChunkArgs &a, const Unit un, const int p_base, bf16 *__restrict__ sXstage,
+        bf16x8 *__restrict__ sXr, bf16x8 *__restrict__ sXs, bf16 *__restrict__ sY,
+        bf16 *__restrict__ sH, SegBuf<Q> *__restrict__ segbuf) {
     using Cfg = ScanCfg<Q, N, PB>;
     constexpr int W = Cfg::W, THREADS = Cfg::THREADS;
     constexpr int NT = Cfg::NT, PT = Cfg::PT, KN = Cfg::KN, IT = Cfg::IT, NP = Cfg::NP;
@@ -136,22 +142,10 @@ __global__ __launch_bounds__(64 * (((Q == 256) ? 8 : 4) + 2)) void ssd_scan_bf16
     constexpr int NPROD = Cfg::NPROD;
     static_assert(THREADS == 64 * (((Q == 256) ? 8 : 4) + 2), "launch bounds");
 
-    // sXstage is written only by the producer's asynchronous loads and read
-    // only between the two barriers of a hand-over; the fragment sets sXr
-    // (unscaled) and sXs (X'') are separate LDS objects.  sY holds the y tile
-    // of one chunk (swizzled like the X stage, CPRY 16-byte chunks per row).
-    __shared__ __attribute__((aligned(1024))) bf16 sXstage[Cfg::SX];
-    __shared__ __attribute__((aligned(1024))) bf16x8 sXr[NFRAG * 64];
-    __shared__ __attribute__((aligned(1024))) bf16x8 sXs[NFRAG * 64];
-    __shared__ __attribute__((aligned(1024))) bf16 sY[Cfg::SX];
-    __shared__ __attribute__((aligned(16))) bf16 sH[PB * LDH];
-    __shared__ __attribute__((aligned(16))) SegBuf<Q> segbuf[2];
-
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool producer = wave >= W;
     const int lane = tid & 63, l16 = lane & 15, g = lane >> 4;
-    const Unit un = unit_of_block(a);
     const int b = un.b, h = un.h, s = un.s, pb = un.pb;
     // The last split's local summary is never used (its entering state comes
     // from the scan and its end state is the final state).
@@ -170,7 +164,6 @@ __global__ __launch_bounds__(64 * (((Q == 256) ? 8 : 4) + 2)) void ssd_scan_bf16
     // Without seq_idx the document-id loads read dt bits of the same row
     // instead (any valid address; the values are not used).
     const int32_t *seq_row = resets ? a.seq_idx + (int64_t)b * L : (const int32_t *)(a.dt + (int64_t)b * L * H);
-    const int p_base = pb * PB;
     const bf16 *Csrc = (const bf16 *)a.C + ((int64_t)b * L * G + grp) * N;
     const int64_t bg = (int64_t)b * G + grp;
     const bf16x8 *Sws = (const bf16x8 *)a.ws_S + bg * a.nchunks * NBLK * 64 + lane;
@@ -602,7 +595,7 @@ __global__ __launch_bounds__(64 * (((Q == 256) ? 8 : 4) + 2)) void ssd_scan_bf16
         if (s == a.nsplits - 1 && a.final_states) dst = a.final_states + ((int64_t)b * H + h) * P * N;
     } else {
         dst = a.ws_states + (((int64_t)b * H + h) * a.nsplits + s) * P * N;
-        if (tid == 0 && pb == 0) a.ws_decay[((int64_t)b * H + h) * a.nsplits + s] = split_decay;
+        if (tid == 0 && pb == 0 && un.half <= 0) a.ws_decay[((int64_t)b * H + h) * a.nsplits + s] = split_decay;
     }
     if (dst) {
         mfma_fence_all(hs);
@@ -613,6 +606,31 @@ __global__ __launch_bounds__(64 * (((Q == 256) ? 8 : 4) + 2)) void ssd_scan_bf16
             *(f32x4 *)(dst + (int64_t)p * N + n) = hs[k];
         }
     }
+}
+
+// The head kernel: one workgroup per unit, or per half unit for the units of
+// the last, partial round (see unit_of_block).  sXstage is written only by the
+// producer waves' asynchronous loads and read only between the two barriers of
+// a hand-over; the fragment sets sXr (unscaled) and sXs (X'') are separate LDS
+// objects, so that the compiler sees that their reads do not wait for the loads
+// in flight.  sY holds the y tile of one chunk (swizzled like the X stage).
+template <int Q, int N, int PB>
+__global__ __launch_bounds__(64 * (((Q == 256) ? 8 : 4) + 2)) void ssd_scan_bf16_kernel(ChunkArgs a) {
+    using Cfg = ScanCfg<Q, N, PB>;
+    __shared__ __attribute__((aligned(1024))) bf16 sXstage[Cfg::SX];
+    __shared__ __attribute__((aligned(1024))) bf16x8 sXr[Cfg::NFRAG * 64];
+    __shared__ __attribute__((aligned(1024))) bf16x8 sXs[Cfg::NFRAG * 64];
+    __shared__ __attribute__((aligned(1024))) bf16 sY[Cfg::SX];
+    __shared__ __attribute__((aligned(16))) bf16 sH[PB * Cfg::LDH];
+    __shared__ __attribute__((aligned(16))) SegBuf<Q> segbuf[2];
+    const Unit un = unit_of_block(a);
+    if constexpr (PB >= 32) {
+        if (un.half >= 0) {
+            scan_body<Q, N, PB / 2>(a, un, un.pb * PB + un.half * (PB / 2), sXstage, sXr, sXs, sY, sH, segbuf);
+            return;
+        }
+    }
+    scan_body<Q, N, PB>(a, un, un.pb * PB, sXstage, sXr, sXs, sY, sH, segbuf);
 }
 
 }  // namespace ssd

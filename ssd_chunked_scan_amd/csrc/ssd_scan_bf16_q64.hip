@@ -11,7 +11,7 @@ namespace ssd {
     }
 
 bool launch_scan_bf16_q64(int N, int PB, const ChunkArgs &a, hipStream_t stream) {
-    const dim3 grid(a.units);
+    const dim3 grid(a.units + a.half_units);
     SSD_SCAN_CASE(64, 16, 16)
     SSD_SCAN_CASE(64, 16, 32)
     SSD_SCAN_CASE(64, 16, 64)

@@ -125,6 +125,21 @@ def test_layer27b_full_size_sampled(skip):
 
 
 @pytest.mark.parametrize("skip", [True, False], ids=["with_skip", "no_skip"])
+def test_partial_last_round_half_blocks(skip):
+    """288 (batch row, head) units of one workgroup each on a 256-CU device: the
+    last 32 units (batch row 1, heads 112..143) run as two workgroups of half
+    the headdim block each.  Samples on both sides of that boundary, ragged
+    tail chunk, two groups."""
+    wl = _case("half_blocks", batch=2, seqlen=600, nheads=144, headdim=64, dstate=128, ngroups=2,
+               chunk_size=256, io="bf16")
+    inp = workloads.make_inputs(wl, seed=3)
+    y, fs = run_gpu(inp, skip=skip)
+    assert np.isfinite(y).all() and np.isfinite(fs).all()
+    _sampled(inp, [(0, 5), (1, 111), (1, 112), (1, 127), (1, 143)], y, fs, TOL["bf16"],
+             "half blocks", skip=skip)
+
+
+@pytest.mark.parametrize("skip", [True, False], ids=["with_skip", "no_skip"])
 def test_decay_stress_full_size_sampled(skip):
     inp = workloads.make_inputs(workloads.WORKLOADS["decay"], seed=0)
     y, fs = run_gpu(inp, skip=skip)
