@@ -111,8 +111,10 @@ typedef struct {
  *     4 * batch * nheads * nsplits * (headdim * dstate + 1) bytes;
  *   - bf16 io: the per-group C B^T blocks of every chunk (the lower triangle
  *     of C_c B_c^T in 16 x 32-token blocks, 1 KiB each, (Q/32)(Q/32+1)
- *     blocks per chunk) and B token-transposed, i.e.
- *     batch * ngroups * nchunks * (1024 (Q/32)(Q/32+1) + 2 Q dstate) bytes.
+ *     blocks per chunk), B token-transposed and C in operand order, i.e.
+ *     batch * ngroups * nchunks * (1024 (Q/32)(Q/32+1) + 2 Q dstate) bytes
+ *     + batch * ngroups * nchunks * 2 Q max(dstate, 32) bytes (C; dstate 16
+ *     is padded to 32 columns).
  * The contents are scratch: nothing survives the call. */
 size_t ssd_fwd_workspace_bytes(const ssd_shape_t *shape, int64_t chunk_size,
                                ssd_dtype_t io);

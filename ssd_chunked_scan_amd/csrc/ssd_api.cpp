@@ -98,6 +98,7 @@ struct Plan {
     size_t split_bytes;   // split states + decays (nsplits > 1)
     size_t s_bytes;       // per-group C B^T blocks (bf16)
     size_t bt_bytes;      // per-group token-transposed B (bf16)
+    size_t c_bytes;       // per-group C in operand order (bf16)
     size_t ws_bytes;
 };
 
@@ -184,13 +185,14 @@ ssd_status_t make_plan(const ssd_shape_t *s, int64_t chunk, ssd_dtype_t io,
         const size_t decay = (size_t)s->batch * s->nheads * pl->nsplits;
         pl->split_bytes = round_up((states + decay) * sizeof(float), 256);
     }
-    pl->s_bytes = pl->bt_bytes = 0;
+    pl->s_bytes = pl->bt_bytes = pl->c_bytes = 0;
     if (io == SSD_BF16) {
         const size_t bgc = (size_t)s->batch * s->ngroups * pl->nchunks;
         pl->s_bytes = round_up(bgc * ssd::cb_s_elems((int)chunk) * 2, 256);
         pl->bt_bytes = round_up(bgc * (size_t)chunk * s->dstate * 2, 256);
+        pl->c_bytes = round_up(bgc * (size_t)chunk * std::max<int64_t>(s->dstate, 32) * 2, 256);
     }
-    pl->ws_bytes = pl->split_bytes + pl->s_bytes + pl->bt_bytes;
+    pl->ws_bytes = pl->split_bytes + pl->s_bytes + pl->bt_bytes + pl->c_bytes;
     return SSD_OK;
 }
 
@@ -275,6 +277,7 @@ ssd_status_t ssd_fwd_ex(const ssd_shape_t *shape, ssd_dtype_t io, const void *x,
     char *wsb = (char *)workspace;
     a.ws_S = pl.s_bytes ? wsb + pl.split_bytes : nullptr;
     a.ws_BT = pl.bt_bytes ? wsb + pl.split_bytes + pl.s_bytes : nullptr;
+    a.ws_C = pl.c_bytes ? wsb + pl.split_bytes + pl.s_bytes + pl.bt_bytes : nullptr;
     a.ws_states = pl.nsplits > 1 ? ws : nullptr;
     a.ws_decay = pl.nsplits > 1
                      ? ws + (size_t)shape->batch * shape->nheads * pl.nsplits * shape->headdim * shape->dstate
@@ -315,6 +318,7 @@ ssd_status_t ssd_fwd_ex(const ssd_shape_t *shape, ssd_dtype_t io, const void *x,
         cb.C = C;
         cb.ws_S = wsb + pl.split_bytes;
         cb.ws_BT = wsb + pl.split_bytes + pl.s_bytes;
+        cb.ws_C = wsb + pl.split_bytes + pl.s_bytes + pl.bt_bytes;
         cb.batch = a.batch;
         cb.seqlen = a.seqlen;
         cb.ngroups = a.ngroups;

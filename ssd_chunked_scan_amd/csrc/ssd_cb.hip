@@ -19,6 +19,8 @@
 //     blocks are stored row tile by row tile, I ascending, m ascending.
 //   B^T fragment (m, n): 4 x 16 bytes, part g holds B_c[j][n] at the same
 //     8 tokens j(e, g).
+//   C fragment (I, kk): lane l holds C_c[16 I + l%16][32 kk + 8 (l/16) .. +7]
+//     (the B operand of the state projection), written by block (I, 0).
 //
 // Tokens past the end of the row read as zero.
 #include "ssd_common.hpp"
@@ -26,13 +28,19 @@
 namespace ssd {
 
 // One wave per work item of a (batch row, group, chunk): items 0 .. NBLK-1
-// are the C B^T blocks (I, m) in storage order, items NBLK .. NBLK+NP-1 the
-// B^T fragments of pair m.  Four items per workgroup.
+// are the C B^T blocks (I, m) in storage order, items NBLK .. NBLK+NP*N/16-1
+// the B^T fragments (pair m, 16-column n-tile).  Four items per workgroup.
+template <int Q, int N>
+struct CbItems {
+    static constexpr int NTILE = N / 16;
+    static constexpr int COUNT = CbShape<Q>::NBLK + CbShape<Q>::NP * NTILE;
+};
+
 template <int Q, int N>
 __global__ __launch_bounds__(256) void ssd_cb_kernel(CbArgs a) {
     using S = CbShape<Q>;
     constexpr int KN = (N >= 32) ? N / 32 : 1;
-    constexpr int ITEMS = S::NBLK + S::NP;
+    constexpr int ITEMS = CbItems<Q, N>::COUNT, NTILE = CbItems<Q, N>::NTILE;
     const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
     const int64_t item_all = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int64_t nitems = (int64_t)a.batch * a.ngroups * a.nchunks * ITEMS;
@@ -59,6 +67,11 @@ __global__ __launch_bounds__(256) void ssd_cb_kernel(CbArgs a) {
         bf16x8 cf[KN];
 #pragma unroll
         for (int kk = 0; kk < KN; ++kk) cf[kk] = row8(Csrc, t0 + 16 * I + l16, kk * 32 + 8 * g);
+        if (m == 0) {
+#pragma unroll
+            for (int kk = 0; kk < KN; ++kk)
+                ((bf16x8 *)a.ws_C)[((bgc * S::TILES + I) * KN + kk) * 64 + lane] = cf[kk];
+        }
         f32x4 d[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -79,19 +92,18 @@ __global__ __launch_bounds__(256) void ssd_cb_kernel(CbArgs a) {
         }
         ((bf16x8 *)a.ws_S)[(bgc * S::NBLK + item) * 64 + lane] = o;
     } else {
-        // B^T fragments of pair k
-        const int k = item - S::NBLK;
-        bf16x8 *BTdst = (bf16x8 *)a.ws_BT + (bgc * S::NP + k) * N * 4;
-        for (int o = lane; o < N * 4; o += 64) {
-            const int n = o >> 2, gg = o & 3;
-            bf16x8 v;
+        // B^T fragment (pair k, n-tile nt): lane (l16, g) gathers B[t][n] at
+        // n = 16 nt + l16 for its 8 slot tokens (16 lanes read 32 contiguous
+        // bytes of one token row per load), all loads in one round trip
+        const int k = (item - S::NBLK) / NTILE, nt = (item - S::NBLK) % NTILE;
+        const int n = 16 * nt + l16;
+        bf16x8 v;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int t = t0 + 32 * k + 4 * gg + (e & 3) + 16 * (e >> 2);
-                v[e] = (t < L) ? Bsrc[(int64_t)t * G * N + n] : (bf16)0.f;
-            }
-            BTdst[o] = v;
+        for (int e = 0; e < 8; ++e) {
+            const int t = t0 + 32 * k + 4 * g + (e & 3) + 16 * (e >> 2);
+            v[e] = (t < L) ? Bsrc[(int64_t)t * G * N + n] : (bf16)0.f;
         }
+        ((bf16x8 *)a.ws_BT)[((bgc * S::NP + k) * N + n) * 4 + g] = v;
     }
 }
 
@@ -105,7 +117,7 @@ size_t cb_s_elems(int Q) {
 
 #define SSD_CB_CASE(q, n)                                                                   \
     if (Q == q && N == n) {                                                                 \
-        constexpr int items = CbShape<q>::NBLK + CbShape<q>::NP;                             \
+        constexpr int items = CbItems<q, n>::COUNT;                                          \
         const int64_t total = (int64_t)a.batch * a.ngroups * a.nchunks * items;              \
         hipLaunchKernelGGL((ssd_cb_kernel<q, n>), dim3((unsigned)((total + 3) / 4)), dim3(256), \
                            0, stream, a);                                                   \

@@ -38,6 +38,7 @@ struct ChunkArgs {
     float *ws_decay;           // [batch][nheads][nsplits]
     const void *ws_S;          // per-group C B^T blocks (bf16 path)
     const void *ws_BT;         // per-group token-transposed B (bf16 path)
+    const void *ws_C;          // per-group C in operand order (bf16 path)
     int batch, seqlen, nheads, headdim, dstate, ngroups;
     int chunk;                 // chunk_size Q
     int nchunks;               // ceil(seqlen / Q)
@@ -57,6 +58,8 @@ struct CbArgs {
     const void *C;
     void *ws_S;    // [batch][ngroups][nchunks][CbShape<Q>::NBLK][64 lanes] x 16 bytes
     void *ws_BT;   // [batch][ngroups][nchunks][Q/32][dstate][4] x 16 bytes
+    void *ws_C;    // [batch][ngroups][nchunks][Q/16][KN][64 lanes] x 16 bytes,
+                   // KN = max(dstate, 32) / 32
     int batch, seqlen, ngroups, nchunks;
 };
 

@@ -164,10 +164,10 @@ __device__ __attribute__((always_inline)) inline void scan_body(
     // Without seq_idx the document-id loads read dt bits of the same row
     // instead (any valid address; the values are not used).
     const int32_t *seq_row = resets ? a.seq_idx + (int64_t)b * L : (const int32_t *)(a.dt + (int64_t)b * L * H);
-    const bf16 *Csrc = (const bf16 *)a.C + ((int64_t)b * L * G + grp) * N;
     const int64_t bg = (int64_t)b * G + grp;
     const bf16x8 *Sws = (const bf16x8 *)a.ws_S + bg * a.nchunks * NBLK * 64 + lane;
     const bf16x8 *BTws = (const bf16x8 *)a.ws_BT + bg * a.nchunks * NP * N * 4;
+    const bf16x8 *Cws = (const bf16x8 *)a.ws_C + bg * a.nchunks * Cfg::TILES * KN * 64 + lane;
 
 
     // ================= producer waves =================
@@ -350,24 +350,22 @@ __device__ __attribute__((always_inline)) inline void scan_body(
         }
     };
     // C_c rows of this wave's row tiles (B operand of the state projection,
-    // k = n); rows past the end of the sequence read row L-1 (their outputs
-    // are not stored), columns past dstate are zeroed at use.
+    // k = n), in operand order from the per-group kernel (one contiguous
+    // 1 KB load each; rows past the sequence end and columns past dstate are
+    // zero there).
     bf16x8 cf[IT][KN];
-    auto load_c = [&](int c, const int (&Irow)[IT]) {
+    auto load_c = [&](int c, const int (&Irow)[IT]) __attribute__((always_inline)) {
 #pragma unroll
         for (int it = 0; it < IT; ++it) {
-            const int t = min(c * Q + Irow[it] * 16 + l16, L - 1);
 #pragma unroll
-            for (int kk = 0; kk < KN; ++kk) {
-                const int col = min(kk * 32 + 8 * g, N - 8);
-                cf[it][kk] = *(const bf16x8 *)(Csrc + (int64_t)t * G * N + col);
-            }
+            for (int kk = 0; kk < KN; ++kk)
+                cf[it][kk] = Cws[(((int64_t)c * Cfg::TILES + Irow[it]) * KN + kk) * 64];
         }
     };
     // Output tile accumulators: acc[it][pt] = Y^T tile (rows p, columns i).
     f32x4 acc[IT][PT];
     // y tile of this wave's row tiles into sY (bf16)
-    auto write_y = [&](const int (&Irow)[IT]) {
+    auto write_y = [&](const int (&Irow)[IT]) __attribute__((always_inline)) {
 #pragma unroll
         for (int it = 0; it < IT; ++it) mfma_fence_all(acc[it]);
 #pragma unroll
@@ -428,12 +426,6 @@ __device__ __attribute__((always_inline)) inline void scan_body(
         // ---- 2. state projection Y^T = h^T C^T (the Horner steps below
         // give it the decay from the chunk start to the row tile)
         if (full) {
-            if constexpr (N < 32) {
-                // k = n runs over 32 columns; zero the ones past dstate
-#pragma unroll
-                for (int it = 0; it < IT; ++it)
-                    if (8 * g >= N) cf[it][0] = bf16x8{};
-            }
             if (state_zero) {
 #pragma unroll
                 for (int it = 0; it < IT; ++it)

@@ -101,8 +101,10 @@ def _ru(v):
 
 
 def _bf16_group_bytes(b, G, nchunks, Q, N):
-    """Per-group C B^T blocks and token-transposed B, as documented in ssd.h."""
-    return _ru(b * G * nchunks * 1024 * (Q // 32) * (Q // 32 + 1)) + _ru(b * G * nchunks * 2 * Q * N)
+    """Per-group C B^T blocks, token-transposed B and C in operand order, as
+    documented in ssd.h."""
+    return (_ru(b * G * nchunks * 1024 * (Q // 32) * (Q // 32 + 1)) + _ru(b * G * nchunks * 2 * Q * N)
+            + _ru(b * G * nchunks * 2 * Q * max(N, 32)))
 
 
 def test_workspace_and_plan():
