@@ -24,86 +24,124 @@
 //
 // Tokens past the end of the row read as zero.
 #include "ssd_common.hpp"
+#include "ssd_tiles.hpp"
 
 namespace ssd {
 
-// One wave per work item of a (batch row, group, chunk): items 0 .. NBLK-1
-// are the C B^T blocks (I, m) in storage order, items NBLK .. NBLK+NP*N/16-1
-// the B^T fragments (pair m, 16-column n-tile).  Four items per workgroup.
+// Work split: NQ = Q/64 workgroups per (batch row, group, chunk).  Workgroup
+// k owns the row tiles {k, 2NQ-1-k, 2NQ+k, 4NQ-1-k} (the same number of C B^T
+// blocks for every k) and the B^T fragments of pairs [k NP/NQ, (k+1) NP/NQ).
+// It stages the chunk's B rows and its own four C row tiles in LDS with
+// direct loads (each global byte read once per workgroup), then every
+// operand is an LDS read.
 template <int Q, int N>
-struct CbItems {
-    static constexpr int NTILE = N / 16;
-    static constexpr int COUNT = CbShape<Q>::NBLK + CbShape<Q>::NP * NTILE;
+struct CbCfg {
+    static constexpr int NQ = Q / 64;          // workgroups per chunk
+    static constexpr int TILES = Q / 16, NP = Q / 32;
+    static constexpr int KN = (N >= 32) ? N / 32 : 1;
+    static constexpr int CPR = N / 8;          // 16-byte chunks per B or C row
+    static constexpr int NT = N / 16;          // n-tiles
+    static constexpr int PPW = NP / NQ;        // B^T pairs per workgroup
 };
 
 template <int Q, int N>
 __global__ __launch_bounds__(256) void ssd_cb_kernel(CbArgs a) {
     using S = CbShape<Q>;
-    constexpr int KN = (N >= 32) ? N / 32 : 1;
-    constexpr int ITEMS = CbItems<Q, N>::COUNT, NTILE = CbItems<Q, N>::NTILE;
-    const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
-    const int64_t item_all = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int64_t nitems = (int64_t)a.batch * a.ngroups * a.nchunks * ITEMS;
-    if (item_all >= nitems) return;
-    const int item = (int)(item_all % ITEMS);
-    const int64_t bgc = item_all / ITEMS;        // (b * G + grp) * nchunks + c
+    using Cfg = CbCfg<Q, N>;
+    constexpr int NQ = Cfg::NQ, TILES = Cfg::TILES, KN = Cfg::KN, CPR = Cfg::CPR, NT = Cfg::NT;
+    constexpr int PPW = Cfg::PPW;
+    // B rows of the chunk and the workgroup's 4 C row tiles, swizzled rows of
+    // CPR 16-byte chunks
+    __shared__ __attribute__((aligned(1024))) bf16 sB[Q * N];
+    __shared__ __attribute__((aligned(1024))) bf16 sC[64 * N];
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+    const int k = (int)(blockIdx.x % NQ);
+    const int64_t bgc = blockIdx.x / NQ;         // (b * G + grp) * nchunks + c
     const int c = (int)(bgc % a.nchunks);
     const int64_t bg = bgc / a.nchunks;
     const int grp = (int)(bg % a.ngroups), b = (int)(bg / a.ngroups);
-    const int L = a.seqlen, G = a.ngroups;
-    const int t0 = c * Q;
-    const bf16 *Bsrc = (const bf16 *)a.B + ((int64_t)b * L * G + grp) * N;
-    const bf16 *Csrc = (const bf16 *)a.C + ((int64_t)b * L * G + grp) * N;
-    auto row8 = [&](const bf16 *src, int t, int col) -> bf16x8 {
-        if (t >= L || col >= N) return bf16x8{};
-        return *(const bf16x8 *)(src + (int64_t)t * G * N + col);
+    const int L = a.seqlen, G = a.ngroups, t0 = c * Q;
+    const int nvalid = min(Q, L - t0);
+    const bf16 *Bsrc = (const bf16 *)a.B + (((int64_t)b * L + t0) * G + grp) * N;
+    const bf16 *Csrc = (const bf16 *)a.C + (((int64_t)b * L + t0) * G + grp) * N;
+    auto tile_of = [&](int ti) __attribute__((always_inline)) {
+        return ti == 0 ? k : ti == 1 ? 2 * NQ - 1 - k : ti == 2 ? 2 * NQ + k : 4 * NQ - 1 - k;
     };
 
-    if (item < S::NBLK) {
-        // block (I, m): the row tile I with off(I) <= item < off(I + 1)
-        int I = 0;
-        while (I + 1 < S::TILES && S::off(I + 1) <= item) ++I;
-        const int m = item - S::off(I);
-        bf16x8 cf[KN];
-#pragma unroll
-        for (int kk = 0; kk < KN; ++kk) cf[kk] = row8(Csrc, t0 + 16 * I + l16, kk * 32 + 8 * g);
-        if (m == 0) {
-#pragma unroll
-            for (int kk = 0; kk < KN; ++kk)
-                ((bf16x8 *)a.ws_C)[((bgc * S::TILES + I) * KN + kk) * 64 + lane] = cf[kk];
+    // ---- staging: whole 1 KB blocks of 64 16-byte chunks, 4 waves
+    {
+        constexpr int nbB = Q * CPR / 64;
+        for (int blk = wave; blk < nbB; blk += 4) {
+            const int slot = blk * 64 + lane, r = slot / CPR, pc = slot % CPR;
+            const int cc = pc ^ swz<CPR>(r);
+            const bf16 *src = (r < nvalid) ? Bsrc + (int64_t)r * G * N + cc * 8 : kZeroChunk;
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                             (__attribute__((address_space(3))) void *)(sB + blk * 512), 16, 0, 0);
         }
-        f32x4 d[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int J = 2 * m + h;
-            if (J > I) continue;
-            bf16x8 bfr[KN];
-#pragma unroll
-            for (int kk = 0; kk < KN; ++kk) bfr[kk] = row8(Bsrc, t0 + 16 * J + l16, kk * 32 + 8 * g);
-#pragma unroll
-            for (int kk = 0; kk < KN; ++kk) d[h] = mfma_bf16(bfr[kk], cf[kk], d[h]);
+        constexpr int nbC = 64 * CPR / 64;
+        for (int blk = wave; blk < nbC; blk += 4) {
+            const int slot = blk * 64 + lane, r = slot / CPR, pc = slot % CPR;   // r: row of the 4 staged tiles
+            const int cc = pc ^ swz<CPR>(r);
+            const int t = tile_of(r >> 4) * 16 + (r & 15);
+            const bf16 *src = (t < nvalid) ? Csrc + (int64_t)t * G * N + cc * 8 : kZeroChunk;
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                             (__attribute__((address_space(3))) void *)(sC + blk * 512), 16, 0, 0);
         }
-        mfma_fence(d[0], d[1]);
-        bf16x8 o;
+        vmem_lds_sync();
+    }
+    // 8 k-consecutive bf16 of a staged row at column col (a multiple of 8),
+    // zero past dstate
+    auto row8 = [&](const bf16 *tile, int r, int col) __attribute__((always_inline)) -> bf16x8 {
+        if (col >= N) return bf16x8{};
+        return *(const bf16x8 *)&tile[tile_off<CPR>(r, col >> 3)];
+    };
+
+    // ---- C B^T blocks (I, m) of the 4 row tiles, dealt to the waves in turn
+    {
+        int q = 0;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            o[r] = (bf16)d[0][r];
-            o[4 + r] = (bf16)d[1][r];
-        }
-        ((bf16x8 *)a.ws_S)[(bgc * S::NBLK + item) * 64 + lane] = o;
-    } else {
-        // B^T fragment (pair k, n-tile nt): lane (l16, g) gathers B[t][n] at
-        // n = 16 nt + l16 for its 8 slot tokens (16 lanes read 32 contiguous
-        // bytes of one token row per load), all loads in one round trip
-        const int k = (item - S::NBLK) / NTILE, nt = (item - S::NBLK) % NTILE;
-        const int n = 16 * nt + l16;
-        bf16x8 v;
+        for (int ti = 0; ti < 4; ++ti) {
+            const int I = tile_of(ti);
+            for (int m = 0; m <= I / 2; ++m, ++q) {
+                if (q % 4 != wave) continue;
+                bf16x8 cf[KN];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int t = t0 + 32 * k + 4 * g + (e & 3) + 16 * (e >> 2);
-            v[e] = (t < L) ? Bsrc[(int64_t)t * G * N + n] : (bf16)0.f;
+                for (int kk = 0; kk < KN; ++kk) cf[kk] = row8(sC, ti * 16 + l16, kk * 32 + 8 * g);
+                f32x4 d[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int J = 2 * m + h;
+                    if (J > I) continue;
+#pragma unroll
+                    for (int kk = 0; kk < KN; ++kk)
+                        d[h] = mfma_bf16(row8(sB, J * 16 + l16, kk * 32 + 8 * g), cf[kk], d[h]);
+                }
+                mfma_fence(d[0], d[1]);
+                bf16x8 o;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    o[r] = (bf16)d[0][r];
+                    o[4 + r] = (bf16)d[1][r];
+                }
+                ((bf16x8 *)a.ws_S)[(bgc * S::NBLK + S::off(I) + m) * 64 + lane] = o;
+            }
         }
-        ((bf16x8 *)a.ws_BT)[((bgc * S::NP + k) * N + n) * 4 + g] = v;
+    }
+    // ---- C fragments (I, kk) of the 4 row tiles
+    for (int f = wave; f < 4 * KN; f += 4) {
+        const int ti = f / KN, kk = f % KN;
+        ((bf16x8 *)a.ws_C)[((bgc * TILES + tile_of(ti)) * KN + kk) * 64 + lane] =
+            row8(sC, ti * 16 + l16, kk * 32 + 8 * g);
+    }
+    // ---- B^T fragments (pair m, n-tile nt): lane (l16, g) holds B[j][n] at
+    // n = 16 nt + l16 for its 8 slot tokens j, by 16-bit transpose reads
+    for (int f = wave; f < PPW * NT; f += 4) {
+        const int m = k * PPW + f / NT, nt = f % NT;
+        const int rr = 32 * m + 4 * g + (l16 >> 2), col = nt * 16 + 4 * (l16 & 3);
+        const bf16x8 v = join_bf16x8(lds_read_tr16(&sB[tile_off_col<CPR>(rr, col)]),
+                                     lds_read_tr16(&sB[tile_off_col<CPR>(rr + 16, col)]));
+        ((bf16x8 *)a.ws_BT)[((bgc * S::NP + m) * N + nt * 16 + l16) * 4 + g] = v;
     }
 }
 
@@ -117,10 +155,8 @@ size_t cb_s_elems(int Q) {
 
 #define SSD_CB_CASE(q, n)                                                                   \
     if (Q == q && N == n) {                                                                 \
-        constexpr int items = CbItems<q, n>::COUNT;                                          \
-        const int64_t total = (int64_t)a.batch * a.ngroups * a.nchunks * items;              \
-        hipLaunchKernelGGL((ssd_cb_kernel<q, n>), dim3((unsigned)((total + 3) / 4)), dim3(256), \
-                           0, stream, a);                                                   \
+        const int64_t total = (int64_t)a.batch * a.ngroups * a.nchunks * CbCfg<q, n>::NQ;   \
+        hipLaunchKernelGGL((ssd_cb_kernel<q, n>), dim3((unsigned)total), dim3(256), 0, stream, a); \
         return true;                                                                        \
     }
 
