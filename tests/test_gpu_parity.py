@@ -139,6 +139,24 @@ def test_partial_last_round_half_blocks(skip):
              "half blocks", skip=skip)
 
 
+def test_half_blocks_with_forced_splits_and_init_state():
+    """The 288-unit shape in three sequence splits: 864 units, of which the last
+    96 (batch row 1, heads 112..143, every split) run as half-headdim
+    workgroups on a 256-CU device, through the split-local pass, the split
+    scan and the full pass, with an entering state."""
+    wl = _case("half_blocks_split", batch=2, seqlen=600, nheads=144, headdim=64, dstate=128,
+               ngroups=2, chunk_size=256, io="bf16")
+    inp = workloads.make_inputs(wl, seed=5)
+    h0 = np.random.default_rng(6).standard_normal((2, 144, 64, 128)).astype(np.float32) * 0.5
+    y, fs = run_gpu(inp, init_states=h0, split_len=256)
+    assert np.isfinite(y).all() and np.isfinite(fs).all()
+    for b, h in [(0, 0), (1, 111), (1, 112), (1, 143)]:
+        yr, fsr = oracle_slice(inp, [b], [h], init_states=h0)
+        ey = max_rel(y[b:b + 1, :, h:h + 1], yr)
+        ef = max_rel(fs[b:b + 1, h:h + 1], fsr)
+        assert ey <= TOL["bf16"] and ef <= TOL["bf16"], f"(b={b}, h={h}): y {ey:.3e} fs {ef:.3e}"
+
+
 @pytest.mark.parametrize("skip", [True, False], ids=["with_skip", "no_skip"])
 def test_decay_stress_full_size_sampled(skip):
     inp = workloads.make_inputs(workloads.WORKLOADS["decay"], seed=0)
