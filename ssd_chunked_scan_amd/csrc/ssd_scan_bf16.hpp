@@ -327,26 +327,33 @@ __device__ __attribute__((always_inline)) inline void scan_body(
     // (m, pt) holds, for lane (p = 16 pt + l16, g), X[j][p] at the slot tokens
     // j = 32m + 4g + (e%4) + 16(e/4); sXs holds the same times the X'' factor.
     auto make_fragments = [&](const SegBuf<Q> &sg) __attribute__((always_inline)) {
+        // wave w makes the fragments of pairs w, w + W, ...: the pair's X''
+        // factors are read and multiplied once for all its headdim tiles
 #pragma unroll
-        for (int k = 0; k < (NFRAG + W - 1) / W; ++k) {
-            const int fr = wave + k * W;
-            if (NFRAG % W != 0 && fr >= NFRAG) break;
-            const int m = fr / PT, pt = fr % PT;
+        for (int m0 = 0; m0 < NP; m0 += W) {
+            const int m = m0 + wave;
+            if (NP % W != 0 && m >= NP) break;
             const int jr = 32 * m + 4 * g;
-            const int rr = jr + (l16 >> 2), col = pt * 16 + 4 * (l16 & 3);
-            const bf16x8 xr = join_bf16x8(lds_read_tr16(&sXstage[tile_off_col<CPRX>(rr, col)]),
-                                          lds_read_tr16(&sXstage[tile_off_col<CPRX>(rr + 16, col)]));
             const f32x4 wlo = *(const f32x4 *)&sg.wd[jr];
             const f32x4 whi = *(const f32x4 *)&sg.wd[jr + 16];
             const float tb_hi = sg.Tb[2 * m + 1];
-            bf16x8 xs;
+            float flo[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                xs[r] = (bf16)((float)xr[r] * __fmul_rn(wlo[r], tb_hi));
-                xs[4 + r] = (bf16)((float)xr[4 + r] * whi[r]);
+            for (int r = 0; r < 4; ++r) flo[r] = __fmul_rn(wlo[r], tb_hi);
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) {
+                const int rr = jr + (l16 >> 2), col = pt * 16 + 4 * (l16 & 3);
+                const bf16x8 xr = join_bf16x8(lds_read_tr16(&sXstage[tile_off_col<CPRX>(rr, col)]),
+                                              lds_read_tr16(&sXstage[tile_off_col<CPRX>(rr + 16, col)]));
+                bf16x8 xs;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    xs[r] = (bf16)((float)xr[r] * flo[r]);
+                    xs[4 + r] = (bf16)((float)xr[4 + r] * whi[r]);
+                }
+                sXr[(m * PT + pt) * 64 + lane] = xr;
+                sXs[(m * PT + pt) * 64 + lane] = xs;
             }
-            sXr[fr * 64 + lane] = xr;
-            sXs[fr * 64 + lane] = xs;
         }
     };
     // C_c rows of this wave's row tiles (B operand of the state projection,
