@@ -76,6 +76,46 @@ def cpu_baseline(inp, repeats: int = 3):
                       f"heads), fp64 recurrence, median of {repeats} runs of {med:.2f} s"}
 
 
+def segsum_ablation(wl, inp, args):
+    """One JSON line: per-launch time of the mask evaluation over every
+    (batch row, head, chunk) of the workload for each segsum variant (HIP
+    events, sums-only export: no mask traffic), and the ratios to the
+    hierarchy-aware one (page "GPU Hierarchy Meets Structured Matrices",
+    abstract: direct segsum ~30% slower than the diff segsum; hierarchy-aware
+    1.35-1.40x faster than a naive direct one)."""
+    import torch
+    import ssd_chunked_scan_amd as ssd
+    dev = torch.device("cuda:0")
+    dt = torch.from_numpy(inp.dt).to(dev)
+    A = torch.from_numpy(inp.A).to(dev)
+    seq = None if inp.seq_idx is None else torch.from_numpy(inp.seq_idx).to(dev)
+    stream = torch.cuda.current_stream(dev)
+    res = {}
+    for v in ("hierarchy", "direct", "diff"):
+        run = lambda: ssd.ssd_debug_chunk_mask(dt, A, seq, chunk_size=wl.chunk_size, variant=v,
+                                               sums_only=True)
+        for _ in range(args.warmup):
+            run()
+        torch.cuda.synchronize(dev)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for e0, e1 in ev:
+            e0.record(stream)
+            run()
+            e1.record(stream)
+        torch.cuda.synchronize(dev)
+        t = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in ev)
+        res[v] = sum(t) / len(t)
+        print(f"bench: segsum {v}: {res[v]:.1f} us per launch (p10 {t[len(t) // 10]:.1f})",
+              file=sys.stderr, flush=True)
+    units = wl.batch * wl.nheads * ((wl.seqlen + wl.chunk_size - 1) // wl.chunk_size)
+    print(json.dumps({
+        "metric": "segsum evaluation time per launch (sums-only mask export)", "unit": "us",
+        "higher_is_better": False, "workload": wl.name, "chunk_units": units,
+        "us": res, "direct_over_hierarchy": res["direct"] / res["hierarchy"],
+        "diff_over_hierarchy": res["diff"] / res["hierarchy"]}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -83,6 +123,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="layer27b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--segsum-ablation", action="store_true",
+                    help="instead of the forward pass: time the three segsum evaluations of the "
+                         "decay mask (hierarchy-aware, dense direct, prefix difference) on the "
+                         "workload's dt and A, every chunk, mask evaluated but not written")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -98,6 +142,9 @@ def main():
 
     wl = workloads.WORKLOADS[args.workload]
     inp = workloads.make_inputs(wl, seed=0)
+    if args.segsum_ablation:
+        segsum_ablation(wl, inp, args)
+        return
     dev = torch.device("cuda:0")
     io = torch.bfloat16 if wl.io == "bf16" else torch.float32
     t = lambda a, d=torch.float32: torch.from_numpy(a).to(dev).to(d).contiguous()

@@ -160,6 +160,25 @@ ssd_status_t ssd_debug_chunk_mask(const ssd_shape_t *shape, const float *dt,
                                   int64_t chunk_count, float *L_out,
                                   void *stream);
 
+/* Segsum evaluations of the decay mask (page "GPU Hierarchy Meets Structured
+ * Matrices", abstract): the forward kernels use the hierarchy-aware one; the
+ * other two exist for the comparison the page makes. */
+#define SSD_SEGSUM_HIERARCHY 0 /* nested sub-block sums, rank-one off-diagonal factors */
+#define SSD_SEGSUM_DIRECT 1    /* each entry its own running sum (dense direct segsum) */
+#define SSD_SEGSUM_DIFF 2      /* difference of chunk prefix sums (diff segsum)      */
+
+/* ssd_debug_chunk_mask with a choice of segsum evaluation.  L_out (as above)
+ * and sums_out (fp32 [batch][nheads][chunk_count], the sum of each chunk's
+ * mask entries) may each be NULL, not both; with L_out NULL the mask is
+ * evaluated but not written (for timing the evaluation alone).  An unknown
+ * variant returns SSD_ERR_UNSUPPORTED. */
+ssd_status_t ssd_debug_chunk_mask_ex(const ssd_shape_t *shape, const float *dt,
+                                     const float *A, const int32_t *seq_idx,
+                                     int64_t chunk_size, int64_t chunk_begin,
+                                     int64_t chunk_count, int32_t variant,
+                                     float *L_out, float *sums_out,
+                                     void *stream);
+
 const char *ssd_status_str(ssd_status_t status);
 
 /* Detail of the last failure on the calling thread ("" if none). */

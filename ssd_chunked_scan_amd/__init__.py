@@ -30,8 +30,10 @@ SSD_F32, SSD_BF16 = 0, 1
 STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_UNSUPPORTED",
           4: "SSD_ERR_ALIGN", 5: "SSD_ERR_WORKSPACE", 6: "SSD_ERR_HIP"}
 EXPORTS = ["ssd_fwd_workspace_bytes", "ssd_fwd", "ssd_fwd_ex_workspace_bytes", "ssd_fwd_ex",
-           "ssd_plan_split_len", "ssd_debug_chunk_mask", "ssd_status_str", "ssd_last_error",
-           "ssd_version"]
+           "ssd_plan_split_len", "ssd_debug_chunk_mask", "ssd_debug_chunk_mask_ex",
+           "ssd_status_str", "ssd_last_error", "ssd_version"]
+# segsum evaluations of the mask export (ssd.h SSD_SEGSUM_*)
+SEGSUM = {"hierarchy": 0, "direct": 1, "diff": 2}
 
 
 class SsdError(RuntimeError):
@@ -85,6 +87,8 @@ def load_library():
     lib.ssd_fwd_ex.restype = i32
     lib.ssd_debug_chunk_mask.argtypes = [shp, vp, vp, vp, i64, i64, i64, vp, vp]
     lib.ssd_debug_chunk_mask.restype = i32
+    lib.ssd_debug_chunk_mask_ex.argtypes = [shp, vp, vp, vp, i64, i64, i64, i32, vp, vp, vp]
+    lib.ssd_debug_chunk_mask_ex.restype = i32
     lib.ssd_status_str.argtypes = [i32]
     lib.ssd_status_str.restype = ctypes.c_char_p
     lib.ssd_last_error.argtypes = []
@@ -202,11 +206,17 @@ def ssd_fwd(x, dt, A, B, C, D=None, seq_idx=None, chunk_size: int = 256, init_st
 
 
 def ssd_debug_chunk_mask(dt, A, seq_idx=None, chunk_size: int = 256, chunk_begin: int = 0,
-                         chunk_count: Optional[int] = None):
+                         chunk_count: Optional[int] = None, variant: str = "hierarchy",
+                         sums_only: bool = False):
     """The decay mask of chunks [chunk_begin, chunk_begin + chunk_count) as the
-    forward kernels build it: fp32 [b, H, chunk_count, Q, Q]."""
+    forward kernels build it (variant "hierarchy"), or by the dense direct or
+    the prefix-difference segsum: fp32 [b, H, chunk_count, Q, Q].  With
+    sums_only, only each chunk's sum of mask entries, fp32 [b, H, chunk_count]
+    (the mask is evaluated but not written)."""
     import torch
     lib = load_library()
+    if variant not in SEGSUM:
+        raise ValueError(f"variant must be one of {sorted(SEGSUM)}")
     b, L, H = dt.shape
     dev = dt.device
     _need(dt, "dt", (b, L, H), torch.float32, dev)
@@ -216,11 +226,13 @@ def ssd_debug_chunk_mask(dt, A, seq_idx=None, chunk_size: int = 256, chunk_begin
     nchunks = (L + chunk_size - 1) // chunk_size
     if chunk_count is None:
         chunk_count = nchunks - chunk_begin
-    out = torch.empty((b, H, chunk_count, chunk_size, chunk_size), dtype=torch.float32, device=dev)
+    out = None if sums_only else torch.empty((b, H, chunk_count, chunk_size, chunk_size),
+                                             dtype=torch.float32, device=dev)
+    sums = torch.empty((b, H, chunk_count), dtype=torch.float32, device=dev) if sums_only else None
     shape = Shape(b, L, H, 16, 16, 1)
     with torch.cuda.device(dev):
-        st = lib.ssd_debug_chunk_mask(ctypes.byref(shape), _ptr(dt), _ptr(A), _ptr(seq_idx),
-                                      chunk_size, chunk_begin, chunk_count, _ptr(out),
-                                      torch.cuda.current_stream(dev).cuda_stream)
+        st = lib.ssd_debug_chunk_mask_ex(ctypes.byref(shape), _ptr(dt), _ptr(A), _ptr(seq_idx),
+                                         chunk_size, chunk_begin, chunk_count, SEGSUM[variant],
+                                         _ptr(out), _ptr(sums), torch.cuda.current_stream(dev).cuda_stream)
     _check(st)
-    return out
+    return sums if sums_only else out

@@ -356,11 +356,27 @@ ssd_status_t ssd_fwd(const ssd_shape_t *shape, ssd_dtype_t io, const void *x, co
 ssd_status_t ssd_debug_chunk_mask(const ssd_shape_t *shape, const float *dt, const float *A,
                                   const int32_t *seq_idx, int64_t chunk_size, int64_t chunk_begin,
                                   int64_t chunk_count, float *L_out, void *stream) {
+    if (!L_out) {
+        g_last_error.clear();
+        return fail(SSD_ERR_NULL, "L_out is required");
+    }
+    return ssd_debug_chunk_mask_ex(shape, dt, A, seq_idx, chunk_size, chunk_begin, chunk_count,
+                                   SSD_SEGSUM_HIERARCHY, L_out, nullptr, stream);
+}
+
+ssd_status_t ssd_debug_chunk_mask_ex(const ssd_shape_t *shape, const float *dt, const float *A,
+                                     const int32_t *seq_idx, int64_t chunk_size, int64_t chunk_begin,
+                                     int64_t chunk_count, int32_t variant, float *L_out,
+                                     float *sums_out, void *stream) {
     g_last_error.clear();
     ssd_status_t st = check_shape(shape, chunk_size);
     if (st != SSD_OK) return st;
-    if (!dt || !A || !L_out) return fail(SSD_ERR_NULL, "dt, A and L_out are required");
-    if (!aligned(L_out, 16)) return fail(SSD_ERR_ALIGN, "L_out must be 16-byte aligned");
+    if (!dt || !A) return fail(SSD_ERR_NULL, "dt and A are required");
+    if (!L_out && !sums_out) return fail(SSD_ERR_NULL, "at least one of L_out and sums_out is required");
+    if (variant != SSD_SEGSUM_HIERARCHY && variant != SSD_SEGSUM_DIRECT && variant != SSD_SEGSUM_DIFF)
+        return fail(SSD_ERR_UNSUPPORTED, "unknown segsum variant %d", (int)variant);
+    if (L_out && !aligned(L_out, 16)) return fail(SSD_ERR_ALIGN, "L_out must be 16-byte aligned");
+    if (sums_out && !aligned(sums_out, 4)) return fail(SSD_ERR_ALIGN, "sums_out must be 4-byte aligned");
     if (!aligned(dt, 4) || !aligned(A, 4) || (seq_idx && !aligned(seq_idx, 4)))
         return fail(SSD_ERR_ALIGN, "dt, A and seq_idx must be 4-byte aligned");
     const int64_t nchunks = (shape->seqlen + chunk_size - 1) / chunk_size;
@@ -372,6 +388,8 @@ ssd_status_t ssd_debug_chunk_mask(const ssd_shape_t *shape, const float *dt, con
     m.A = A;
     m.seq_idx = seq_idx;
     m.out = L_out;
+    m.sums = sums_out;
+    m.variant = (int)variant;
     m.batch = (int)shape->batch;
     m.seqlen = (int)shape->seqlen;
     m.nheads = (int)shape->nheads;

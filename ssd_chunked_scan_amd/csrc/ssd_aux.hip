@@ -44,14 +44,29 @@ void launch_split_scan(const float *init_states, float *ws_states, const float *
                        ws_decay, batch, nheads, nsplits, pn);
 }
 
-// One workgroup per (batch row * head, chunk).  Same segsum steps and the
-// same per-lane mask evaluation order as the bf16 chunk kernel: each wave
-// takes 16-row tiles, each lane one row i and columns 16 jt + 4 g + r, with
-// the F chain walked leftwards from the diagonal.
-template <int Q>
+// One workgroup per (batch row * head, chunk).  VARIANT selects how the mask
+// entries L_ij = 2^(sum of d_k over (j, i]) are evaluated (page "GPU Hierarchy
+// Meets Structured Matrices", abstract, names the three):
+//   kSegsumHierarchy  the forward kernels' construction: nested sums inside
+//                     16-token sub-blocks, rank-one factors across them (same
+//                     steps and per-lane order as the bf16 chunk kernel: each
+//                     wave takes 16-row tiles, each lane one row i and columns
+//                     16 jt + 4 g + r, the F chain walked leftwards);
+//   kSegsumDirect     the dense "direct segsum": thread j owns column j and
+//                     keeps the running sum over (j, i] as i grows, one exp per
+//                     entry (Q^2/2 of them);
+//   kSegsumDiff       the "diff segsum": inclusive prefix sums cs over the
+//                     chunk by an associative scan, entry 2^(cs_i - cs_j)
+//                     (prefix subtraction).
+// Document boundaries zero an entry by select in all three.  With out ==
+// nullptr only the per-chunk sums are written (the evaluation without the
+// mask's HBM traffic, for timing).
+template <int Q, int VARIANT>
 __global__ __launch_bounds__(kThreads) void ssd_mask_kernel(MaskArgs m) {
     constexpr int NB = Q / 16;
     __shared__ __attribute__((aligned(16))) SegLds<Q> sg;
+    __shared__ float cs[Q];
+    __shared__ float block_sum;
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
     const int bh = blockIdx.x;
@@ -76,7 +91,48 @@ __global__ __launch_bounds__(kThreads) void ssd_mask_kernel(MaskArgs m) {
     if (tid < Q) seg_chunk_products<Q>(sg, tid);
     __syncthreads();
 
-    float *out = m.out + (((int64_t)b * H + h) * m.count + ci) * Q * Q;
+    if (tid == 0) block_sum = 0.f;
+    float *out = m.out ? m.out + (((int64_t)b * H + h) * m.count + ci) * Q * Q : nullptr;
+    float csum = 0.f;
+    if constexpr (VARIANT == kSegsumDirect || VARIANT == kSegsumDiff) {
+        if constexpr (VARIANT == kSegsumDiff) {
+            // inclusive prefix sums by an associative (Kogge-Stone) scan, as
+            // chunkwise kernels compute them: each token's sum is grouped
+            // differently, so the sums need not be monotone in fp32
+            if (tid < Q) cs[tid] = sg.d[tid];
+            __syncthreads();
+            for (int off = 1; off < Q; off *= 2) {
+                const float v = (tid < Q && tid >= off) ? cs[tid - off] : 0.f;
+                __syncthreads();
+                if (tid < Q && tid >= off) cs[tid] = __fadd_rn(cs[tid], v);
+                __syncthreads();
+            }
+        }
+        // thread j: column j, rows i = 0 .. Q-1 (a row is written by
+        // consecutive threads)
+        const int j = tid;
+        if (j < Q) {
+            float run = 0.f;
+            bool cut = false;
+            for (int i = 0; i < Q; ++i) {
+                float v = 0.f;
+                if (i >= j) {
+                    if (VARIANT == kSegsumDirect && i > j) {
+                        run = __fadd_rn(run, sg.d[i]);
+                        cut = cut || sg.flag[i];
+                        v = cut ? 0.f : __builtin_amdgcn_exp2f(run);
+                    } else if (VARIANT == kSegsumDirect) {
+                        v = 1.f;
+                    } else {
+                        v = (sg.rs[i] > j) ? 0.f : __builtin_amdgcn_exp2f(__fsub_rn(cs[i], cs[j]));
+                    }
+                }
+                if (i >= nvalid || j >= nvalid) v = 0.f;
+                csum += v;
+                if (out) out[(int64_t)i * Q + j] = v;
+            }
+        }
+    } else
     for (int I = wave; I < NB; I += 4) {
         const int i = I * 16 + l16;
         const int rs_i = sg.rs[i];
@@ -93,18 +149,34 @@ __global__ __launch_bounds__(kThreads) void ssd_mask_kernel(MaskArgs m) {
             }
             for (int r = 0; r < 4; ++r)
                 if (i >= nvalid || jt * 16 + 4 * g + r >= nvalid) v[r] = 0.f;
+            csum += (v[0] + v[1]) + (v[2] + v[3]);
             // element (i, j): row i, columns j = 16 jt + 4 g .. +3
-            *(f32x4 *)(out + (int64_t)i * Q + jt * 16 + 4 * g) = v;
+            if (out) *(f32x4 *)(out + (int64_t)i * Q + jt * 16 + 4 * g) = v;
         }
+    }
+    if (m.sums) {
+        __syncthreads();
+        atomicAdd(&block_sum, csum);
+        __syncthreads();
+        if (tid == 0) m.sums[((int64_t)b * H + h) * m.count + ci] = block_sum;
+    }
+}
+
+template <int Q>
+static void launch_mask_q(const MaskArgs &m, hipStream_t stream) {
+    const dim3 grid(m.batch * m.nheads, m.count), block(kThreads);
+    switch (m.variant) {
+    case kSegsumDirect: hipLaunchKernelGGL((ssd_mask_kernel<Q, kSegsumDirect>), grid, block, 0, stream, m); break;
+    case kSegsumDiff: hipLaunchKernelGGL((ssd_mask_kernel<Q, kSegsumDiff>), grid, block, 0, stream, m); break;
+    default: hipLaunchKernelGGL((ssd_mask_kernel<Q, kSegsumHierarchy>), grid, block, 0, stream, m); break;
     }
 }
 
 void launch_mask(int Q, const MaskArgs &m, hipStream_t stream) {
-    const dim3 grid(m.batch * m.nheads, m.count), block(kThreads);
     switch (Q) {
-    case 64: hipLaunchKernelGGL(ssd_mask_kernel<64>, grid, block, 0, stream, m); break;
-    case 128: hipLaunchKernelGGL(ssd_mask_kernel<128>, grid, block, 0, stream, m); break;
-    default: hipLaunchKernelGGL(ssd_mask_kernel<256>, grid, block, 0, stream, m); break;
+    case 64: launch_mask_q<64>(m, stream); break;
+    case 128: launch_mask_q<128>(m, stream); break;
+    default: launch_mask_q<256>(m, stream); break;
     }
 }
 

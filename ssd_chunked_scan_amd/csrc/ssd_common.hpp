@@ -77,11 +77,20 @@ struct CbShape {
 };
 
 // Arguments of the decay-mask export kernel.
+// Segsum evaluations of the mask export (the forward kernels use the first).
+enum SegsumVariant : int {
+    kSegsumHierarchy = 0,   // sub-block sums + rank-one off-diagonal factors
+    kSegsumDirect = 1,      // every entry its own running sum, column by column
+    kSegsumDiff = 2         // prefix sums over the chunk, entry = difference
+};
+
 struct MaskArgs {
     const float *dt;
     const float *A;
     const int32_t *seq_idx;
-    float *out;          // [batch][nheads][count][Q][Q]
+    float *out;          // [batch][nheads][count][Q][Q], nullable
+    float *sums;         // [batch][nheads][count]: sum of each chunk's mask, nullable
+    int variant;         // SegsumVariant
     int batch, seqlen, nheads;
     int chunk_begin, count;
 };

@@ -160,3 +160,20 @@ def test_binding_does_not_import_oracle():
                 if isinstance(node, (ast.Import, ast.ImportFrom)):
                     mods = [a.name for a in node.names] if isinstance(node, ast.Import) else [node.module or ""]
                     assert not any(m.split(".")[0] == "oracle" for m in mods), fn
+
+
+def test_mask_ex_host_validation():
+    """Argument errors of ssd_debug_chunk_mask_ex are reported before any HIP
+    call (fake but aligned device pointers; nothing is dereferenced)."""
+    lib = ssd.load_library()
+    s = ssd.Shape(1, 256, 2, 16, 16, 1)
+    p = ctypes.c_void_p(1 << 20)
+    # both outputs missing
+    st = lib.ssd_debug_chunk_mask_ex(ctypes.byref(s), p, p, None, 64, 0, 1, 0, None, None, None)
+    assert st == 1 and b"at least one" in lib.ssd_last_error()
+    # unknown variant
+    st = lib.ssd_debug_chunk_mask_ex(ctypes.byref(s), p, p, None, 64, 0, 1, 7, p, None, None)
+    assert st == 3 and b"variant" in lib.ssd_last_error()
+    # chunk range outside the sequence
+    st = lib.ssd_debug_chunk_mask_ex(ctypes.byref(s), p, p, None, 64, 3, 2, 1, None, p, None)
+    assert st == 2

@@ -1,0 +1,90 @@
+"""Segsum ablation (page "GPU Hierarchy Meets Structured Matrices", abstract):
+the same chunk decay mask by the hierarchy-aware segsum the forward kernels
+use, by the dense direct segsum and by the prefix-difference ("diff") segsum,
+through the C ABI's mask export, against the fp64 mask oracle.  The page's
+claims checked here: direct and hierarchy-aware are both accurate and the
+hierarchy-aware mask keeps the invariants (entries in [0, 1], non-increasing
+along a row away from the diagonal); the diff segsum loses accuracy to
+cancellation and breaks the invariants once the chunk's prefix sums are large
+next to the decays that follow."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from mask_invariants import check_mask_invariants
+
+pytestmark = pytest.mark.gpu
+
+VARIANTS = ("hierarchy", "direct", "diff")
+
+
+def _mask(dt, A, Q, variant, seq_idx=None, sums_only=False, begin=0, count=None):
+    import torch
+    import ssd_chunked_scan_amd as ssd
+    si = None if seq_idx is None else torch.from_numpy(seq_idx).cuda()
+    m = ssd.ssd_debug_chunk_mask(torch.from_numpy(dt).cuda(), torch.from_numpy(A).cuda(), si,
+                                 chunk_size=Q, chunk_begin=begin, chunk_count=count,
+                                 variant=variant, sums_only=sums_only)
+    torch.cuda.synchronize()
+    return m.cpu().numpy()
+
+
+@pytest.mark.parametrize("Q", [64, 256])
+def test_variants_match_oracle_with_resets_and_ragged_tail(Q):
+    wl = workloads.custom_workload(seqlen=3 * Q - 29, nheads=3, chunk_size=Q, packed=True,
+                                   doc_range=(1, 90), doc_count=(2, 400),
+                                   dt_range=(1e-3, 1.0), a_range=(0.5, 20.0))
+    inp = workloads.make_inputs(wl, seed=7)
+    ref = oracle.decay_mask(inp.dt, inp.A, inp.seq_idx, chunk_size=Q)
+    tol = {"hierarchy": 1e-5, "direct": 1e-5, "diff": 1e-3}
+    for v in VARIANTS:
+        m = _mask(inp.dt, inp.A, Q, v, inp.seq_idx)
+        assert m.shape == ref.shape
+        err = np.abs(m - ref).max()
+        assert err <= tol[v], f"{v}: {err:.3e}"
+        # exact zeros above the diagonal, across documents and past the row end
+        assert np.all(m[ref == 0] == 0.0), v
+    check_mask_invariants(_mask(inp.dt, inp.A, Q, "hierarchy", inp.seq_idx))
+
+
+def _strong_then_tiny(Q=256, heads=2):
+    """One chunk: strong decays on its first half (d = dt A log2 e ~ -58 per
+    token), decays of ~6e-5 on its second half.  The prefix sums reach ~-7400,
+    where an fp32 ulp (~5e-4) exceeds the later decays."""
+    dt = np.full((1, Q, heads), 1e-6, np.float32)
+    dt[:, :Q // 2] = 1.0
+    A = np.full(heads, -40.0, np.float32)
+    return dt, A
+
+
+def test_diff_segsum_breaks_invariants_hierarchy_keeps_them():
+    Q = 256
+    dt, A = _strong_then_tiny(Q)
+    ref = oracle.decay_mask(dt, A, chunk_size=Q)
+    mh = _mask(dt, A, Q, "hierarchy")
+    md = _mask(dt, A, Q, "direct")
+    mf = _mask(dt, A, Q, "diff")
+    eh, ed, ef = (np.abs(m - ref).max() for m in (mh, md, mf))
+    assert eh <= 1e-6 and ed <= 1e-6, (eh, ed)
+    check_mask_invariants(mh)
+    # the diff segsum: cancellation error far above the other two, entries
+    # above 1 and increases along rows (a monotonicity violation)
+    assert ef >= 1e-4 and ef >= 100 * max(eh, ed), (ef, eh, ed)
+    assert (mf > 1.0).any()
+    lower = np.tril(np.ones((Q, Q - 1), dtype=bool), -1)
+    rises = (mf[..., :, :-1] - mf[..., :, 1:])[..., lower] > 0     # L[i, j-1] > L[i, j]
+    assert rises.any()
+    with pytest.raises(AssertionError):
+        check_mask_invariants(mf)
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_sums_only_is_the_sum_of_the_mask(variant):
+    Q = 128
+    wl = workloads.custom_workload(seqlen=2 * Q + 40, nheads=3, chunk_size=Q)
+    inp = workloads.make_inputs(wl, seed=11)
+    m = _mask(inp.dt, inp.A, Q, variant).astype(np.float64)
+    sums = _mask(inp.dt, inp.A, Q, variant, sums_only=True)
+    assert sums.shape == m.shape[:3]
+    np.testing.assert_allclose(sums, m.sum(axis=(-1, -2)), rtol=1e-5)
