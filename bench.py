@@ -116,6 +116,48 @@ def segsum_ablation(wl, inp, args):
         "diff_over_hierarchy": res["diff"] / res["hierarchy"]}), flush=True)
 
 
+def decode_step_bench(wl, inp, args):
+    """One JSON line: the decode step (one token per (batch row, head)) at the
+    workload's sizes, timed with HIP events per launch; roofline against HBM:
+    algorithmic bytes = state read + written (fp32) + x, y, B, C, dt, A, D."""
+    import numpy as np
+    import torch
+    import ssd_chunked_scan_amd as ssd
+    dev = torch.device("cuda:0")
+    io = torch.bfloat16 if wl.io == "bf16" else torch.float32
+    esz = 2 if wl.io == "bf16" else 4
+    b, H, P, N, G = wl.batch, wl.nheads, wl.headdim, wl.dstate, wl.ngroups
+    t = lambda a, d=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(d)
+    x, dt, A = t(inp.x[:, 0], io), t(inp.dt[:, 0]), t(inp.A)
+    B, C, D = t(inp.B[:, 0], io), t(inp.C[:, 0], io), t(inp.D)
+    state = torch.zeros((b, H, P, N), dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    run = lambda: ssd.ssd_decode_step(x, dt, A, B, C, D, state, y=y)
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize(dev)
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        run()
+        e1.record(stream)
+    torch.cuda.synchronize(dev)
+    us = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in ev)
+    avg = sum(us) / len(us)
+    nbytes = 2 * b * H * P * N * 4 + 2 * b * H * P * esz + 2 * b * G * N * esz + b * H * 4 + 2 * H * 4
+    gbs = nbytes / (avg * 1e-6) / 1e9
+    print(f"bench: decode step {b}x{H} heads P{P} N{N}: {avg:.2f} us per launch "
+          f"(p10 {us[len(us) // 10]:.2f}), {gbs:.0f} GB/s", file=sys.stderr, flush=True)
+    print(json.dumps({
+        "metric": "decode step time per launch", "unit": "us", "value": avg, "higher_is_better": False,
+        "config": {"workload": wl.name + " decode step", "batch": b, "nheads": H, "headdim": P,
+                   "dstate": N, "ngroups": G, "io": wl.io},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": 8000.0, "unit": "GB/s",
+                     "frac": gbs / 8000.0, "bytes_per_launch": nbytes}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -123,6 +165,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="layer27b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode", action="store_true",
+                    help="instead of the forward pass: time the single-token decode step at the "
+                         "workload's batch, heads and state size (state read and written once)")
     ap.add_argument("--segsum-ablation", action="store_true",
                     help="instead of the forward pass: time the three segsum evaluations of the "
                          "decay mask (hierarchy-aware, dense direct, prefix difference) on the "
@@ -144,6 +189,9 @@ def main():
     inp = workloads.make_inputs(wl, seed=0)
     if args.segsum_ablation:
         segsum_ablation(wl, inp, args)
+        return
+    if args.decode:
+        decode_step_bench(wl, inp, args)
         return
     dev = torch.device("cuda:0")
     io = torch.bfloat16 if wl.io == "bf16" else torch.float32

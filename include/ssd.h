@@ -179,6 +179,21 @@ ssd_status_t ssd_debug_chunk_mask_ex(const ssd_shape_t *shape, const float *dt,
                                      float *L_out, float *sums_out,
                                      void *stream);
 
+/* One decode step (single token) of the recurrence of page "State Space
+ * Duality and Mamba-2" ("The Mathematical Bridge"), per (batch row, head h):
+ *   a = exp(dt A_h);  state <- a state + dt x B^T;  y = state C + D_h x,
+ * i.e. what ssd_fwd computes for one more token given its final_states.
+ * shape->seqlen must be 1.  x, y: [batch][nheads][headdim]; dt: [batch][nheads]
+ * fp32; B, C: [batch][ngroups][dstate]; A, D: [nheads] fp32 (D nullable);
+ * x, B, C, y in the io dtype (aligned to its size).  state:
+ * [batch][nheads][headdim][dstate] fp32, 16-byte aligned, updated in place
+ * (the caller zeroes it to start a new sequence).  headdim and dstate in
+ * {16, 32, 64, 128}; no workspace. */
+ssd_status_t ssd_decode_step(const ssd_shape_t *shape, ssd_dtype_t io,
+                             const void *x, const float *dt, const float *A,
+                             const void *B, const void *C, const float *D,
+                             float *state, void *y, void *stream);
+
 const char *ssd_status_str(ssd_status_t status);
 
 /* Detail of the last failure on the calling thread ("" if none). */

@@ -20,6 +20,7 @@ from typing import Optional, Tuple
 
 __all__ = [
     "ssd_fwd", "ssd_fwd_workspace_bytes", "ssd_plan_split_len", "ssd_debug_chunk_mask",
+    "ssd_decode_step",
     "SsdError", "library_path", "load_library", "STATUS", "EXPORTS",
 ]
 
@@ -31,7 +32,7 @@ STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_UNSUPP
           4: "SSD_ERR_ALIGN", 5: "SSD_ERR_WORKSPACE", 6: "SSD_ERR_HIP"}
 EXPORTS = ["ssd_fwd_workspace_bytes", "ssd_fwd", "ssd_fwd_ex_workspace_bytes", "ssd_fwd_ex",
            "ssd_plan_split_len", "ssd_debug_chunk_mask", "ssd_debug_chunk_mask_ex",
-           "ssd_status_str", "ssd_last_error", "ssd_version"]
+           "ssd_decode_step", "ssd_status_str", "ssd_last_error", "ssd_version"]
 # segsum evaluations of the mask export (ssd.h SSD_SEGSUM_*)
 SEGSUM = {"hierarchy": 0, "direct": 1, "diff": 2}
 
@@ -89,6 +90,8 @@ def load_library():
     lib.ssd_debug_chunk_mask.restype = i32
     lib.ssd_debug_chunk_mask_ex.argtypes = [shp, vp, vp, vp, i64, i64, i64, i32, vp, vp, vp]
     lib.ssd_debug_chunk_mask_ex.restype = i32
+    lib.ssd_decode_step.argtypes = [shp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.ssd_decode_step.restype = i32
     lib.ssd_status_str.argtypes = [i32]
     lib.ssd_status_str.restype = ctypes.c_char_p
     lib.ssd_last_error.argtypes = []
@@ -236,3 +239,38 @@ def ssd_debug_chunk_mask(dt, A, seq_idx=None, chunk_size: int = 256, chunk_begin
                                          _ptr(out), _ptr(sums), torch.cuda.current_stream(dev).cuda_stream)
     _check(st)
     return sums if sums_only else out
+
+
+def ssd_decode_step(x, dt, A, B, C, D, state, y=None, stream=None):
+    """One decode step: x [b, H, P], dt [b, H], B, C [b, G, N], A, D [H] (D may
+    be None), state [b, H, P, N] fp32 updated in place.  Returns y [b, H, P]."""
+    import torch
+    lib = load_library()
+    if x.dim() != 3 or B.dim() != 3:
+        raise ValueError("x must be [b, H, P] and B, C [b, G, N]")
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("ssd_decode_step runs on the GPU only (x is on %s)" % dev)
+    b, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    io = _io_code(x.dtype)
+    _need(x, "x", (b, H, P), x.dtype, dev)
+    _need(dt, "dt", (b, H), torch.float32, dev)
+    _need(A, "A", (H,), torch.float32, dev)
+    _need(B, "B", (b, G, N), x.dtype, dev)
+    _need(C, "C", (b, G, N), x.dtype, dev)
+    if D is not None:
+        _need(D, "D", (H,), torch.float32, dev)
+    _need(state, "state", (b, H, P, N), torch.float32, dev)
+    if y is None:
+        y = torch.empty_like(x)
+    else:
+        _need(y, "y", (b, H, P), x.dtype, dev)
+    shape = Shape(b, 1, H, P, N, G)
+    with torch.cuda.device(dev):
+        if stream is None:
+            stream = torch.cuda.current_stream(dev).cuda_stream
+        st = lib.ssd_decode_step(ctypes.byref(shape), io, _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+                                 _ptr(C), _ptr(D), _ptr(state), _ptr(y), stream)
+    _check(st)
+    return y

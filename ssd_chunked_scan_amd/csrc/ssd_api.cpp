@@ -22,6 +22,7 @@ void launch_chunk_f32(int Q, const ChunkArgs &a, hipStream_t stream);
 void launch_split_scan(const float *init_states, float *ws_states, const float *ws_decay,
                        int batch, int nheads, int nsplits, int pn, hipStream_t stream);
 void launch_mask(int Q, const MaskArgs &m, hipStream_t stream);
+bool launch_decode(bool bf16_io, int N, const DecodeArgs &a, hipStream_t stream);
 }  // namespace ssd
 
 namespace {
@@ -399,6 +400,45 @@ ssd_status_t ssd_debug_chunk_mask_ex(const ssd_shape_t *shape, const float *dt, 
     ssd::launch_mask((int)chunk_size, m, (hipStream_t)stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(SSD_ERR_HIP, "mask launch: %s", hipGetErrorString(e));
+    return SSD_OK;
+}
+
+ssd_status_t ssd_decode_step(const ssd_shape_t *shape, ssd_dtype_t io, const void *x,
+                             const float *dt, const float *A, const void *B, const void *C,
+                             const float *D, float *state, void *y, void *stream) {
+    g_last_error.clear();
+    if (io != SSD_F32 && io != SSD_BF16) return fail(SSD_ERR_UNSUPPORTED, "unknown io dtype %d", (int)io);
+    ssd_status_t st = check_shape(shape, 64);
+    if (st != SSD_OK) return st;
+    if (shape->seqlen != 1) return fail(SSD_ERR_SHAPE, "a decode step takes one token (seqlen %lld)",
+                                        (long long)shape->seqlen);
+    if (!x || !dt || !A || !B || !C || !state || !y)
+        return fail(SSD_ERR_NULL, "x, dt, A, B, C, state and y are required");
+    const size_t esz = io == SSD_BF16 ? 2 : 4;
+    if (!aligned(x, esz) || !aligned(B, esz) || !aligned(C, esz) || !aligned(y, esz))
+        return fail(SSD_ERR_ALIGN, "x, B, C and y must be aligned to their element size");
+    if (!aligned(dt, 4) || !aligned(A, 4) || (D && !aligned(D, 4)))
+        return fail(SSD_ERR_ALIGN, "dt, A and D must be 4-byte aligned");
+    if (!aligned(state, 16)) return fail(SSD_ERR_ALIGN, "state must be 16-byte aligned");
+    ssd::DecodeArgs a;
+    a.x = x;
+    a.dt = dt;
+    a.A = A;
+    a.B = B;
+    a.C = C;
+    a.D = D;
+    a.state = state;
+    a.y = y;
+    a.batch = (int)shape->batch;
+    a.nheads = (int)shape->nheads;
+    a.headdim = (int)shape->headdim;
+    a.dstate = (int)shape->dstate;
+    a.ngroups = (int)shape->ngroups;
+    (void)hipGetLastError();
+    if (!ssd::launch_decode(io == SSD_BF16, a.dstate, a, (hipStream_t)stream))
+        return fail(SSD_ERR_UNSUPPORTED, "no decode kernel for dstate %d", a.dstate);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(SSD_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
     return SSD_OK;
 }
 

@@ -95,6 +95,19 @@ struct MaskArgs {
     int chunk_begin, count;
 };
 
+// Arguments of the single-token decode step.
+struct DecodeArgs {
+    const void *x;       // [batch][nheads][headdim]  (io dtype)
+    const float *dt;     // [batch][nheads]
+    const float *A;      // [nheads]
+    const void *B;       // [batch][ngroups][dstate]  (io dtype)
+    const void *C;       // [batch][ngroups][dstate]  (io dtype)
+    const float *D;      // [nheads], nullable
+    float *state;        // [batch][nheads][headdim][dstate], in/out
+    void *y;             // [batch][nheads][headdim]  (io dtype)
+    int batch, nheads, headdim, dstate, ngroups;
+};
+
 struct Unit {
     int b, h, s, pb;
     int half;   // -1: the whole headdim block; 0 or 1: that half of it
