@@ -177,3 +177,25 @@ def test_mask_ex_host_validation():
     # chunk range outside the sequence
     st = lib.ssd_debug_chunk_mask_ex(ctypes.byref(s), p, p, None, 64, 3, 2, 1, None, p, None)
     assert st == 2
+
+
+def test_decode_step_host_validation():
+    """ssd_decode_step reports argument errors before any HIP call."""
+    lib = ssd.load_library()
+    p = ctypes.c_void_p(1 << 20)
+    one = ssd.Shape(2, 1, 4, 64, 128, 1)
+    # more than one token
+    st = lib.ssd_decode_step(ctypes.byref(ssd.Shape(2, 5, 4, 64, 128, 1)), 1, p, p, p, p, p, None, p, p, None)
+    assert st == 2 and b"one token" in lib.ssd_last_error()
+    # missing state
+    st = lib.ssd_decode_step(ctypes.byref(one), 1, p, p, p, p, p, None, None, p, None)
+    assert st == 1
+    # unknown io dtype
+    st = lib.ssd_decode_step(ctypes.byref(one), 9, p, p, p, p, p, None, p, p, None)
+    assert st == 3
+    # unsupported dstate
+    st = lib.ssd_decode_step(ctypes.byref(ssd.Shape(2, 1, 4, 64, 48, 1)), 1, p, p, p, p, p, None, p, p, None)
+    assert st == 3
+    # misaligned state
+    st = lib.ssd_decode_step(ctypes.byref(one), 1, p, p, p, p, p, None, ctypes.c_void_p((1 << 20) + 4), p, None)
+    assert st == 4
