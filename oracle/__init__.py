@@ -21,6 +21,21 @@ Contents
                      (page "State Space Duality and Mamba-2", section "The
                      Mathematical Bridge", definition of L), with entries
                      across a document boundary set to zero.
+  dt_prologue(...)   the step sizes from raw per-token values: plus a
+                     per-head bias, then optionally softplus, then optionally
+                     clamped to [lo, hi].
+  gate(...)          the element-wise output gate y * silu(z), silu(z) =
+                     z / (1 + e^-z).
+  ssd_forward_fused(...)  dt_prologue, then ssd_forward, then gate: the scan
+                     with the lightweight element-wise work around it that
+                     page "NVIDIA Accelerates Mamba-2 Forward Kernel with
+                     CUDA Tile" names as its neighbours ("What CUDA Tile Is
+                     and Why It Suits Writing Mamba-2 Kernels": element-wise
+                     gating; "From Python DSL to Production-Grade Kernels":
+                     the scan is followed by gating, fused into one kernel).
+                     The pages do not spell the gate or the dt map out; the
+                     readings taken are Mamba-2's own: dt = softplus(raw +
+                     bias) and out = (y + D x) * silu(z).
 """
 from __future__ import annotations
 
@@ -161,3 +176,62 @@ def decay_mask(dt, A, seq_idx=None, chunk_size: int = 64, chunk_begin: int = 0,
                 prod = prod * a[:, :, j + 1]
                 out[:, :, ci, i, j] = prod
     return out
+
+
+def softplus(v):
+    """softplus(v) = log(1 + e^v) in fp64, written as log1p(exp(v)) for
+    v <= 0 and as v + log1p(exp(-v)) for v > 0 (the same function; the
+    second form avoids overflowing e^v)."""
+    v = np.asarray(v, dtype=np.float64)
+    out = np.empty_like(v)
+    neg = v <= 0
+    out[neg] = np.log1p(np.exp(v[neg]))
+    pos = ~neg
+    out[pos] = v[pos] + np.log1p(np.exp(-v[pos]))
+    return out
+
+
+def dt_prologue(dt_raw, dt_bias=None, dt_softplus: bool = False, dt_limit=None):
+    """Step sizes dt [b, L, H] (fp64) from raw values dt_raw [b, L, H]:
+    dt = dt_raw + dt_bias[h] (if a bias is given), then softplus (if
+    dt_softplus), then clamped to [lo, hi] (if dt_limit = (lo, hi))."""
+    dt = np.asarray(dt_raw, dtype=np.float64).copy()
+    if dt_bias is not None:
+        dt = dt + np.asarray(dt_bias, dtype=np.float64)[None, None, :]
+    if dt_softplus:
+        dt = softplus(dt)
+    if dt_limit is not None:
+        lo, hi = float(dt_limit[0]), float(dt_limit[1])
+        dt = np.minimum(np.maximum(dt, lo), hi)
+    return dt
+
+
+def gate(y, z):
+    """Element-wise output gate y * silu(z) = y * z / (1 + e^-z), fp64.
+    For z < 0 the same value is formed as y * z e^z / (1 + e^z), which
+    cannot overflow."""
+    y = np.asarray(y, dtype=np.float64)
+    z = np.asarray(z, dtype=np.float64)
+    sig = np.empty_like(z)
+    pos = z >= 0
+    sig[pos] = 1.0 / (1.0 + np.exp(-z[pos]))
+    ez = np.exp(z[~pos])
+    sig[~pos] = ez / (1.0 + ez)
+    return y * z * sig
+
+
+def ssd_forward_fused(x, dt_raw, A, B, C, D=None, seq_idx=None, init_states=None,
+                      dt_bias=None, dt_softplus: bool = False, dt_limit=None, z=None,
+                      nthreads: int = 0, return_final: bool = True, lib=None):
+    """The forward pass with its element-wise neighbours, in order:
+    dt = dt_prologue(dt_raw, dt_bias, dt_softplus, dt_limit); the fp64
+    recurrence (ssd_forward) on that dt; then, if z [b, L, H, P] is given,
+    out = gate(y, z) with y including the skip D x.  final_states is the
+    recurrence's state (the gate touches only the output).  Returns
+    (out, final_states) like ssd_forward."""
+    dt = dt_prologue(dt_raw, dt_bias, dt_softplus, dt_limit)
+    y, fs = ssd_forward(x, dt, A, B, C, D, seq_idx, init_states, nthreads=nthreads,
+                        return_final=return_final, lib=lib)
+    if z is not None:
+        y = gate(y, z)
+    return y, fs
