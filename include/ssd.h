@@ -142,6 +142,46 @@ ssd_status_t ssd_fwd_ex(const ssd_shape_t *shape, ssd_dtype_t io,
                         void *workspace, size_t workspace_bytes,
                         const ssd_options_t *opts, void *stream);
 
+/* Fused prologue and epilogue of ssd_fwd_fused: the lightweight element-wise
+ * work on either side of the scan, done inside its kernels so that neither dt
+ * nor y makes an extra round trip through memory (page "NVIDIA Accelerates
+ * Mamba-2 Forward Kernel with CUDA Tile": the forward pass carries
+ * element-wise gating ("What CUDA Tile Is and Why It Suits Writing Mamba-2
+ * Kernels") and the gating that follows the scan is fused into its kernel
+ * ("From Python DSL to Production-Grade Kernels")).  The pages do not spell
+ * the two maps out; they are Mamba-2's:
+ *   dt_t  = clamp(softplus(dt_raw_t + dt_bias_h), dt_min, dt_max)
+ *   out_t = (y_t + D_h x_t) * silu(z_t),   silu(z) = z / (1 + e^-z)
+ * where each step applies only when enabled: dt_bias NULL = no bias,
+ * dt_softplus 0 = no softplus, dt_clamp 0 = no clamp, z NULL = no gate.
+ * Zero-initialise for none of them (then ssd_fwd_fused is ssd_fwd_ex).
+ * final_states is the state of the recurrence (the gate acts on the output
+ * only).  With io = SSD_BF16 the gate multiplies the bf16-rounded y, and
+ * the product is rounded to bf16 again. */
+typedef struct {
+    const float *dt_bias;   /* [nheads] fp32, 4-byte aligned, nullable          */
+    const void *z;          /* [batch, seqlen, nheads, headdim] io dtype,
+                               16-byte aligned, nullable                        */
+    int32_t dt_softplus;    /* nonzero: softplus after the bias                 */
+    int32_t dt_clamp;       /* nonzero: clamp to [dt_min, dt_max] (finite,
+                               dt_min <= dt_max, else SSD_ERR_UNSUPPORTED)      */
+    float dt_min, dt_max;
+    int64_t reserved[4];    /* must be zero                                     */
+} ssd_fused_t;
+
+/* ssd_fwd_ex with the fused prologue/epilogue above; dt holds the raw values
+ * (dt_raw) when any of bias, softplus or clamp is enabled, and the step sizes
+ * must come out > 0.  fused may be NULL.  Workspace as ssd_fwd_ex. */
+ssd_status_t ssd_fwd_fused(const ssd_shape_t *shape, ssd_dtype_t io,
+                           const void *x, const float *dt, const float *A,
+                           const void *B, const void *C, const float *D,
+                           const int32_t *seq_idx, int64_t chunk_size,
+                           const float *init_states,
+                           void *y, float *final_states,
+                           const ssd_fused_t *fused,
+                           void *workspace, size_t workspace_bytes,
+                           const ssd_options_t *opts, void *stream);
+
 /* The split length (tokens) the planner would use; 0 for an invalid problem. */
 int64_t ssd_plan_split_len(const ssd_shape_t *shape, int64_t chunk_size,
                            ssd_dtype_t io);

@@ -31,6 +31,7 @@ SSD_F32, SSD_BF16 = 0, 1
 STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_UNSUPPORTED",
           4: "SSD_ERR_ALIGN", 5: "SSD_ERR_WORKSPACE", 6: "SSD_ERR_HIP"}
 EXPORTS = ["ssd_fwd_workspace_bytes", "ssd_fwd", "ssd_fwd_ex_workspace_bytes", "ssd_fwd_ex",
+           "ssd_fwd_fused",
            "ssd_plan_split_len", "ssd_debug_chunk_mask", "ssd_debug_chunk_mask_ex",
            "ssd_decode_step", "ssd_status_str", "ssd_last_error", "ssd_version"]
 # segsum evaluations of the mask export (ssd.h SSD_SEGSUM_*)
@@ -55,6 +56,13 @@ class Options(ctypes.Structure):
 
 
 SSD_OPT_REUSE_GROUP_OPERANDS = 1
+
+
+class Fused(ctypes.Structure):
+    _fields_ = [("dt_bias", ctypes.c_void_p), ("z", ctypes.c_void_p),
+                ("dt_softplus", ctypes.c_int32), ("dt_clamp", ctypes.c_int32),
+                ("dt_min", ctypes.c_float), ("dt_max", ctypes.c_float),
+                ("reserved", ctypes.c_int64 * 4)]
 
 
 _lib = None
@@ -86,6 +94,8 @@ def load_library():
     lib.ssd_fwd.restype = i32
     lib.ssd_fwd_ex.argtypes = fwd_args + [opt, vp]
     lib.ssd_fwd_ex.restype = i32
+    lib.ssd_fwd_fused.argtypes = fwd_args[:13] + [ctypes.POINTER(Fused)] + fwd_args[13:] + [opt, vp]
+    lib.ssd_fwd_fused.restype = i32
     lib.ssd_debug_chunk_mask.argtypes = [shp, vp, vp, vp, i64, i64, i64, vp, vp]
     lib.ssd_debug_chunk_mask.restype = i32
     lib.ssd_debug_chunk_mask_ex.argtypes = [shp, vp, vp, vp, i64, i64, i64, i32, vp, vp, vp]
@@ -149,13 +159,18 @@ def ssd_plan_split_len(shape: Shape, chunk_size: int, io: int) -> int:
 
 def ssd_fwd(x, dt, A, B, C, D=None, seq_idx=None, chunk_size: int = 256, init_states=None,
             return_final_states: bool = True, split_len: int = 0, y=None, final_states=None,
-            workspace=None, stream=None, reuse_group_operands: bool = False
+            workspace=None, stream=None, reuse_group_operands: bool = False,
+            dt_bias=None, dt_softplus: bool = False, dt_limit=None, z=None
             ) -> Tuple[object, Optional[object]]:
     """Run the forward pass on x.device.  Returns (y, final_states or None).
     ``split_len`` forces the sequence-parallel split length (0 = planner).
     Preallocated ``y`` / ``final_states`` / ``workspace`` (uint8) may be given.
     ``reuse_group_operands`` (bf16) skips the per-group C B^T / B^T kernel: the
-    given ``workspace`` must hold them from an earlier call with the same B, C."""
+    given ``workspace`` must hold them from an earlier call with the same B, C.
+    Fused prologue/epilogue (ssd_fwd_fused): ``dt`` holds raw values mapped to
+    clamp(softplus(dt + dt_bias)) per enabled step (``dt_bias`` [H] fp32,
+    ``dt_softplus``, ``dt_limit`` = (lo, hi)); ``z`` [b, L, H, P] in x's dtype
+    gates the output, y * silu(z)."""
     import torch
     lib = load_library()
     if x.dim() != 4 or B.dim() != 4:
@@ -177,6 +192,14 @@ def ssd_fwd(x, dt, A, B, C, D=None, seq_idx=None, chunk_size: int = 256, init_st
         _need(seq_idx, "seq_idx", (b, L), torch.int32, dev)
     if init_states is not None:
         _need(init_states, "init_states", (b, H, P, N), torch.float32, dev)
+    if dt_bias is not None:
+        _need(dt_bias, "dt_bias", (H,), torch.float32, dev)
+    if z is not None:
+        _need(z, "z", (b, L, H, P), x.dtype, dev)
+    fused = Fused(_ptr(dt_bias), _ptr(z), 1 if dt_softplus else 0,
+                  0 if dt_limit is None else 1,
+                  0.0 if dt_limit is None else float(dt_limit[0]),
+                  0.0 if dt_limit is None else float(dt_limit[1]))
     shape = Shape(b, L, H, P, N, G)
     if y is None:
         y = torch.empty_like(x)
@@ -199,11 +222,11 @@ def ssd_fwd(x, dt, A, B, C, D=None, seq_idx=None, chunk_size: int = 256, init_st
             workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         if stream is None:
             stream = torch.cuda.current_stream(dev).cuda_stream
-        st = lib.ssd_fwd_ex(ctypes.byref(shape), io, _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
-                            _ptr(C), _ptr(D), _ptr(seq_idx), chunk_size, _ptr(init_states),
-                            _ptr(y), _ptr(final_states),
-                            _ptr(workspace) if ws_bytes else None, ws_bytes,
-                            ctypes.byref(opts), stream)
+        st = lib.ssd_fwd_fused(ctypes.byref(shape), io, _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+                               _ptr(C), _ptr(D), _ptr(seq_idx), chunk_size, _ptr(init_states),
+                               _ptr(y), _ptr(final_states), ctypes.byref(fused),
+                               _ptr(workspace) if ws_bytes else None, ws_bytes,
+                               ctypes.byref(opts), stream)
     _check(st)
     return y, (final_states if return_final_states else None)
 

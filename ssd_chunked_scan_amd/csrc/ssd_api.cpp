@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
@@ -235,14 +236,24 @@ int64_t ssd_plan_split_len(const ssd_shape_t *shape, int64_t chunk_size, ssd_dty
     return (int64_t)pl.split_chunks * chunk_size;
 }
 
-ssd_status_t ssd_fwd_ex(const ssd_shape_t *shape, ssd_dtype_t io, const void *x, const float *dt,
-                        const float *A, const void *B, const void *C, const float *D,
-                        const int32_t *seq_idx, int64_t chunk_size, const float *init_states,
-                        void *y, float *final_states, void *workspace, size_t workspace_bytes,
-                        const ssd_options_t *opts, void *stream) {
+ssd_status_t ssd_fwd_fused(const ssd_shape_t *shape, ssd_dtype_t io, const void *x, const float *dt,
+                           const float *A, const void *B, const void *C, const float *D,
+                           const int32_t *seq_idx, int64_t chunk_size, const float *init_states,
+                           void *y, float *final_states, const ssd_fused_t *fused,
+                           void *workspace, size_t workspace_bytes, const ssd_options_t *opts,
+                           void *stream) {
     g_last_error.clear();
     ssd_status_t st = check_problem(shape, chunk_size, io, opts);
     if (st != SSD_OK) return st;
+    if (fused) {
+        for (int k = 0; k < 4; ++k)
+            if (fused->reserved[k] != 0) return fail(SSD_ERR_UNSUPPORTED, "reserved fused fields must be zero");
+        if (fused->dt_clamp && !(std::isfinite(fused->dt_min) && std::isfinite(fused->dt_max) &&
+                                 fused->dt_min <= fused->dt_max))
+            return fail(SSD_ERR_UNSUPPORTED, "dt clamp needs finite dt_min <= dt_max");
+        if (fused->dt_bias && !aligned(fused->dt_bias, 4)) return fail(SSD_ERR_ALIGN, "dt_bias must be 4-byte aligned");
+        if (fused->z && !aligned(fused->z, 16)) return fail(SSD_ERR_ALIGN, "z must be 16-byte aligned");
+    }
     if (!x || !dt || !A || !B || !C || !y)
         return fail(SSD_ERR_NULL, "x, dt, A, B, C and y are required");
     const size_t io_align = 16;
@@ -297,6 +308,14 @@ ssd_status_t ssd_fwd_ex(const ssd_shape_t *shape, ssd_dtype_t io, const void *x,
     a.pblock = pl.pblock;
     a.units = a.batch * a.nheads * a.nsplits * a.npblocks;
     a.half_units = (io == SSD_BF16) ? bf16_half_units(a.units, chunk_size, a.dstate, a.pblock) : 0;
+    if (fused) {
+        a.dt_bias = fused->dt_bias;
+        a.z = fused->z;
+        a.dt_softplus = fused->dt_softplus != 0;
+        a.dt_clamp = fused->dt_clamp != 0;
+        a.dt_lo = fused->dt_min;
+        a.dt_hi = fused->dt_max;
+    }
     hipStream_t s = (hipStream_t)stream;
 
     auto launch = [&](const ssd::ChunkArgs &args) -> bool {
@@ -344,6 +363,15 @@ ssd_status_t ssd_fwd_ex(const ssd_shape_t *shape, ssd_dtype_t io, const void *x,
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(SSD_ERR_HIP, "chunk launch: %s", hipGetErrorString(e));
     return SSD_OK;
+}
+
+ssd_status_t ssd_fwd_ex(const ssd_shape_t *shape, ssd_dtype_t io, const void *x, const float *dt,
+                        const float *A, const void *B, const void *C, const float *D,
+                        const int32_t *seq_idx, int64_t chunk_size, const float *init_states,
+                        void *y, float *final_states, void *workspace, size_t workspace_bytes,
+                        const ssd_options_t *opts, void *stream) {
+    return ssd_fwd_fused(shape, io, x, dt, A, B, C, D, seq_idx, chunk_size, init_states, y,
+                         final_states, nullptr, workspace, workspace_bytes, opts, stream);
 }
 
 ssd_status_t ssd_fwd(const ssd_shape_t *shape, ssd_dtype_t io, const void *x, const float *dt,

@@ -81,7 +81,7 @@ __global__ __launch_bounds__(kThreads) void ssd_mask_kernel(MaskArgs m) {
 
     int flag_any = 0;
     if (tid < Q) {
-        seg_load_token<Q>(sg, tid, t0, nvalid, dt_row, H, m.A[h], seq_row);
+        seg_load_token<Q>(sg, tid, t0, nvalid, dt_row, H, m.A[h], seq_row, dt_map_identity());
         flag_any = sg.flag[tid];
     }
     flag_any = __syncthreads_or(flag_any);

@@ -9,6 +9,9 @@
 //     M[i][j] = (C_i . B_j) L_ij dt_j            masked diagonal block, in LDS
 //     y_i     = u_i h_{c-1} C_i + sum_j M[i][j] x_j + D x_i
 //   h_c = T_c h_{c-1} + sum_j (w_j dt_j) x_j B_j^T
+// With the fused prologue, dt is mapped from the raw values as it is loaded
+// (bias, softplus, clamp); with the fused gate, y_i is multiplied by
+// silu(z_i) as it is stored.
 // The mask L comes from the same segsum device functions as the bf16 kernel
 // (ssd_segsum.hpp), evaluated row by row.
 #include "ssd_common.hpp"
@@ -42,6 +45,8 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_chunk_f32_kernel(ChunkArgs a)
     const float A_h = a.A[h];
     const float D_h = a.D ? a.D[h] : 0.f;
     const float *dt_row = a.dt + (int64_t)b * L * H + h;
+    const DtMap dm = dt_map_of(a, h);
+    const float *zg = (const float *)a.z;
     const int32_t *seq_row = a.seq_idx ? a.seq_idx + (int64_t)b * L : nullptr;
     auto xrow = [&](int t) { return xg + (((int64_t)b * L + t) * H + h) * P; };
     auto brow = [&](int t) { return Bg + (((int64_t)b * L + t) * G + grp) * N; };
@@ -60,7 +65,7 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_chunk_f32_kernel(ChunkArgs a)
         const int nvalid = min(Q, L - t0);
         int flag_any = 0;
         if (tid < Q) {
-            seg_load_token<Q>(sg, tid, t0, nvalid, dt_row, H, A_h, seq_row);
+            seg_load_token<Q>(sg, tid, t0, nvalid, dt_row, H, A_h, seq_row, dm);
             flag_any = sg.flag[tid];
         }
         flag_any = __syncthreads_or(flag_any);
@@ -118,7 +123,11 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_chunk_f32_kernel(ChunkArgs a)
                     float acc = proj * sg.u[i];
                     for (int j = 0; j <= i; ++j) acc = fmaf(sM[ii * Q + j], xrow(t0 + j)[p], acc);
                     const float xi = xrow(t0 + i)[p];
-                    ((float *)a.y)[(((int64_t)b * L + t0 + i) * H + h) * P + p] = acc + D_h * xi;
+                    const int64_t o = (((int64_t)b * L + t0 + i) * H + h) * P + p;
+                    float out = acc + D_h * xi;
+                    // output gate (element-wise, after the skip term)
+                    if (zg) out = out * silu_f32(zg[o]);
+                    ((float *)a.y)[o] = out;
                 }
                 __syncthreads();
             }

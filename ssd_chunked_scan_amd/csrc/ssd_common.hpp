@@ -50,7 +50,49 @@ struct ChunkArgs {
     int units;                 // batch * nheads * nsplits * npblocks
     int half_units;            // the last half_units units run as two workgroups,
                                // one per half of the headdim block (grid = units + half_units)
+    // Fused prologue and epilogue (off when zero / null).
+    const float *dt_bias;      // [nheads], nullable: dt <- dt + dt_bias[h]
+    const void *z;             // [batch][seqlen][nheads][headdim] io dtype, nullable: y <- y silu(z)
+    int dt_softplus;           // nonzero: dt <- softplus(dt)
+    int dt_clamp;              // nonzero: dt <- min(max(dt, dt_lo), dt_hi)
+    float dt_lo, dt_hi;
 };
+
+// Map from a raw per-token value to the step size dt of one head: plus the
+// head's bias, then softplus, then the clamp, each step only when enabled.
+// With no bias, no softplus and no clamp it returns the value unchanged.
+struct DtMap {
+    float bias;
+    int softplus, clamp;
+    float lo, hi;
+};
+
+__device__ inline DtMap dt_map_of(const ChunkArgs &a, int h) {
+    DtMap m;
+    m.bias = a.dt_bias ? a.dt_bias[h] : 0.f;
+    m.softplus = a.dt_softplus;
+    m.clamp = a.dt_clamp;
+    m.lo = a.dt_lo;
+    m.hi = a.dt_hi;
+    return m;
+}
+
+__device__ inline DtMap dt_map_identity() { return DtMap{0.f, 0, 0, 0.f, 0.f}; }
+
+// softplus(v) = log(1 + e^v); above v = 20 it equals v to within e^-20 / v
+// (below fp32 resolution), which also keeps e^v finite.
+__device__ inline float softplus_f32(float v) { return v > 20.f ? v : log1pf(expf(v)); }
+
+__device__ inline float dt_apply(const DtMap &m, float raw) {
+    float v = m.bias != 0.f ? __fadd_rn(raw, m.bias) : raw;
+    if (m.softplus) v = softplus_f32(v);
+    if (m.clamp) v = fminf(fmaxf(v, m.lo), m.hi);
+    return v;
+}
+
+// silu(z) = z / (1 + e^-z); for very negative z the reciprocal goes to 0
+// and so does the product.
+__device__ inline float silu_f32(float z) { return z * __builtin_amdgcn_rcpf(1.f + __expf(-z)); }
 
 // Arguments of the per-group operand kernel (bf16 path).
 struct CbArgs {

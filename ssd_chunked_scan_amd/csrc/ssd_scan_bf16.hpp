@@ -177,6 +177,8 @@ __device__ __attribute__((always_inline)) inline void scan_body(
         constexpr int pw = decltype(PW)::value;
         constexpr int KB0 = pw * NYB / NPROD, KB1 = (pw + 1) * NYB / NPROD;
         const bf16 *Xsrc = (const bf16 *)a.x + ((int64_t)b * L * H + h) * P + p_base;
+        // raw dt -> step size (fused prologue: bias, softplus, clamp)
+        const DtMap dm = dt_map_of(a, h);
         // token values of a chunk, lane k*64+l holds token k*64+l
         float p_dt[Q / 64];
         int p_cur[Q / 64], p_prev[Q / 64];
@@ -194,7 +196,7 @@ __device__ __attribute__((always_inline)) inline void scan_body(
             for (int k = pw; k < Q / 64; k += NPROD) {
                 const int t = k * 64 + lane, tg = c * Q + t;
                 const bool valid = tg < L;
-                const float dtv = valid ? p_dt[k] : 0.f;
+                const float dtv = valid ? dt_apply(dm, p_dt[k]) : 0.f;
                 const int flag = (resets && valid && tg > 0 && p_cur[k] != p_prev[k]) ? 1 : 0;
                 seg_tokens<Q>(sgb, t, dtv, flag, A_h, resets);
             }
@@ -224,11 +226,34 @@ __device__ __attribute__((always_inline)) inline void scan_body(
                                              (__attribute__((address_space(3))) void *)(sXstage + k * 512),
                                              16, 0, 0);
         };
+        // Fused output gate: z of chunk c is loaded (16 bytes per lane and
+        // block, unconditionally: rows past the sequence end read zeros)
+        // while chunk c is computed, and multiplies y_c, as silu(z), when
+        // y_c is stored during chunk c+1.  The gate acts on the bf16 y tile.
+        const bool gated = a.z != nullptr;
+        const char *zbase = gated ? (const char *)a.z + ((((int64_t)b * L) * H + h) * P + p_base) * 2
+                                  : (const char *)kZeroChunk;
+        bf16x8 zr[KB1 - KB0];
+        auto load_z = [&](int c, int k) __attribute__((always_inline)) {
+            constexpr int RB = 64 / CPRY;
+            const int t0 = c * Q, r = k * RB + yrow;
+            const int cc = ypc ^ swz<CPRY>(r);
+            const char *src = zbase + (int64_t)(t0 + k * RB) * row_bytes + (yrow_off + cc * 16);
+            if (t0 + Q > L && t0 + r >= L) src = (const char *)kZeroChunk;
+            zr[k - KB0] = *(const bf16x8 *)src;
+        };
         auto store_y = [&](int c, int k) __attribute__((always_inline)) {
             constexpr int RB = 64 / CPRY;
             const int t0 = c * Q, r = k * RB + yrow;
             const int cc = ypc ^ swz<CPRY>(r);
-            const bf16x8 v = *(const bf16x8 *)&sY[(k * 64 + lane) * 8];
+            bf16x8 v = *(const bf16x8 *)&sY[(k * 64 + lane) * 8];
+            if (gated) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float zf = (float)zr[k - KB0][e];
+                    v[e] = (bf16)((float)v[e] * silu_f32(zf));
+                }
+            }
             char *dst = ybase + (int64_t)(t0 + k * RB) * row_bytes + (yrow_off + cc * 16);
             // non-temporal: y is not read again here, and plain stores of it
             // cost the L2-resident per-group operands (measured 207 -> 171 us
@@ -240,13 +265,16 @@ __device__ __attribute__((always_inline)) inline void scan_body(
         // memory pipeline that the compute waves' L2 loads go through.
         constexpr int kGroup = (KB1 - KB0) < 4 ? (KB1 - KB0) : 4, kInFlight = SSD_PRODUCER_INFLIGHT;
         static_assert((KB1 - KB0) % kGroup == 0 && NYB % NPROD == 0, "whole groups");
-        auto stream = [&](int cx, int cy) __attribute__((always_inline)) {
+        // cz >= 0: also load z of chunk cz (after block k of y_cy has taken
+        // the z of chunk cy from the same registers).
+        auto stream = [&](int cx, int cy, int cz) __attribute__((always_inline)) {
 #pragma unroll
             for (int k0 = KB0; k0 < KB1; k0 += kGroup) {
 #pragma unroll
                 for (int k = k0; k < k0 + kGroup; ++k) {
                     if (cx >= 0) dma_x(cx, k);
                     if (cy >= 0) store_y(cy, k);
+                    if (cz >= 0) load_z(cz, k);
                 }
                 if (k0 + kGroup < KB1) {
                     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -261,19 +289,19 @@ __device__ __attribute__((always_inline)) inline void scan_body(
         // barriers of the previous hand-over), then the segsum of chunk c+1,
         // whose token values arrived long before.
         fetch_tokens(c_begin);
-        stream(c_begin, -1);
+        stream(c_begin, -1, -1);
         segsum(c_begin, segbuf[c_begin & 1]);
         vmem_lds_sync();
         lds_sync();
         for (int c = c_begin; c < c_end; ++c) {
             const bool more = c + 1 < c_end;
             if (more) fetch_tokens(c + 1);
-            stream(more ? c + 1 : -1, (full && c > c_begin) ? c - 1 : -1);
+            stream(more ? c + 1 : -1, (full && c > c_begin) ? c - 1 : -1, (full && gated) ? c : -1);
             if (more) segsum(c + 1, segbuf[(c + 1) & 1]);
-            vmem_lds_sync();   // X_{c+1} has landed, sY is read
+            vmem_lds_sync();   // X_{c+1} and z_c have landed, sY is read
             lds_sync();        // the compute waves write y_c to sY in between
         }
-        if (full) stream(-1, c_end - 1);
+        if (full) stream(-1, c_end - 1, -1);
     };
     if (producer) {
         if (wave == W) run_producer(std::integral_constant<int, 0>{});

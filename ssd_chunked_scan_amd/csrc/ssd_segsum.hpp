@@ -82,10 +82,11 @@ __device__ inline void seg_store_token(SegLds<Q> &s, int t, float dtv, float A_h
 template <int Q>
 __device__ inline void seg_load_token(SegLds<Q> &s, int t, int t0, int nvalid,
                                       const float *dt_row, int dt_stride,
-                                      float A_h, const int32_t *seq_row) {
+                                      float A_h, const int32_t *seq_row, const DtMap &dm) {
     float dtv;
     int flag;
     seg_fetch_token(t, t0, nvalid, dt_row, dt_stride, seq_row, dtv, flag);
+    if (t < nvalid) dtv = dt_apply(dm, dtv);
     seg_store_token<Q>(s, t, dtv, A_h, flag);
 }
 

@@ -199,3 +199,27 @@ def test_decode_step_host_validation():
     # misaligned state
     st = lib.ssd_decode_step(ctypes.byref(one), 1, p, p, p, p, p, None, ctypes.c_void_p((1 << 20) + 4), p, None)
     assert st == 4
+
+
+def _fused_call(fused, ws=FAKE, ws_bytes=1 << 40):
+    lib = ssd.load_library()
+    s = good_shape()
+    f = None if fused is None else ctypes.byref(fused)
+    return lib.ssd_fwd_fused(ctypes.byref(s), 1, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 256,
+                             None, FAKE, None, f, ws, ws_bytes, None, None)
+
+
+def test_fused_argument_errors():
+    """ssd_fwd_fused validates its prologue/epilogue block on the host."""
+    F = ssd.Fused
+    bad = F()
+    bad.reserved[2] = 1
+    assert _fused_call(bad) == 3
+    assert _fused_call(F(None, None, 0, 1, 0.5, 0.1)) == 3            # dt_min > dt_max
+    assert _fused_call(F(None, None, 0, 1, 0.0, float("inf"))) == 3   # unbounded clamp
+    assert _fused_call(F(None, None, 0, 1, float("nan"), 1.0)) == 3
+    assert _fused_call(F(FAKE + 2, None, 1, 0, 0.0, 0.0)) == 4        # dt_bias misaligned
+    assert _fused_call(F(None, FAKE + 8, 1, 0, 0.0, 0.0)) == 4        # z misaligned
+    # a valid block reaches the workspace check (the last host check)
+    assert _fused_call(F(FAKE, FAKE, 1, 1, 0.001, 0.1), ws=None, ws_bytes=0) == 5
+    assert _fused_call(None, ws=None, ws_bytes=0) == 5

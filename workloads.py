@@ -192,3 +192,29 @@ def make_inputs(wl: Workload, seed: int = 0, batch: Optional[int] = None,
     if wl.io == "bf16":
         x, Bm, Cm = bf16_round(x), bf16_round(Bm), bf16_round(Cm)
     return Inputs(wl, x, dt, A, Bm, Cm, D, seq_idx, lens)
+
+
+@dataclasses.dataclass
+class FusedInputs:
+    """Extra inputs of the fused prologue/epilogue: raw per-token step-size
+    values (before bias and softplus), a per-head bias and the gate input z
+    (z already rounded to the storage dtype)."""
+    dt_raw: np.ndarray     # [b, L, H] fp32
+    dt_bias: np.ndarray    # [H] fp32
+    z: np.ndarray          # [b, L, H, P] fp32 values
+
+
+def make_fused_inputs(inp: Inputs, seed: int = 0) -> FusedInputs:
+    """Draw the fused-path inputs for ``inp`` from a stream of their own (the
+    arrays of make_inputs are unchanged): dt_raw ~ N(0, 0.5^2), dt_bias ~
+    U(-7, -2) per head (so that softplus(dt_raw + dt_bias) lies mostly in
+    [1e-3, 0.2], the range of the workloads' step sizes), z ~ N(0, 1)."""
+    wl = inp.wl
+    b, L, H, P = inp.x.shape
+    rng = np.random.default_rng([seed, 1])
+    dt_raw = (0.5 * rng.standard_normal((b, L, H))).astype(np.float32)
+    dt_bias = rng.uniform(-7.0, -2.0, size=(H,)).astype(np.float32)
+    z = rng.standard_normal((b, L, H, P)).astype(np.float32)
+    if wl.io == "bf16":
+        z = bf16_round(z)
+    return FusedInputs(dt_raw, dt_bias, z)
