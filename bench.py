@@ -172,6 +172,9 @@ def main():
                     help="instead of the forward pass: time the three segsum evaluations of the "
                          "decay mask (hierarchy-aware, dense direct, prefix difference) on the "
                          "workload's dt and A, every chunk, mask evaluated but not written")
+    ap.add_argument("--fused", action="store_true",
+                    help="time the forward pass with the fused prologue (raw dt + bias, softplus) "
+                         "and the silu(z) output gate; z counts as algorithmic bytes")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -206,9 +209,21 @@ def main():
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     split_len = ssd.ssd_plan_split_len(shape, wl.chunk_size, io_code)
 
-    def step():
-        ssd.ssd_fwd(x, dt, A, B, C, D, seq, chunk_size=wl.chunk_size, y=y, final_states=fs,
-                    workspace=ws)
+    # Fused prologue/epilogue variant: raw dt through bias + softplus, and the
+    # silu(z) output gate (z read once more: its bytes count as algorithmic).
+    fused_kw = {}
+    extra_bytes = 0
+    if args.fused:
+        fz = workloads.make_fused_inputs(inp, seed=0)
+        dt = t(fz.dt_raw)
+        fused_kw = dict(dt_bias=t(fz.dt_bias), dt_softplus=True, z=t(fz.z, io))
+        extra_bytes = fz.z.size * (2 if wl.io == "bf16" else 4) + fz.dt_bias.size * 4
+
+    # Arguments are checked and marshalled once; each step is one call into
+    # the C ABI (host work per step: one ctypes call and the library's own
+    # validation), so the timed loop measures the device, not Python.
+    step, _, _ = ssd.prepare_fwd(x, dt, A, B, C, D, seq, chunk_size=wl.chunk_size, y=y,
+                                 final_states=fs, workspace=ws, **fused_kw)
 
     print(f"bench: {wl.name} {wl.batch}x{wl.seqlen} H{wl.nheads} P{wl.headdim} N{wl.dstate} "
           f"G{wl.ngroups} Q{wl.chunk_size} {wl.io}; split {split_len} tokens; warmup "
@@ -245,9 +260,9 @@ def main():
     avg_step_ms = sum(step_ms) / len(step_ms)
     head_only = wl.io == "bf16" and split_len >= wl.seqlen
 
-    def head_step():
-        ssd.ssd_fwd(x, dt, A, B, C, D, seq, chunk_size=wl.chunk_size, y=y, final_states=fs,
-                    workspace=ws, reuse_group_operands=True)
+    head_step, _, _ = ssd.prepare_fwd(x, dt, A, B, C, D, seq, chunk_size=wl.chunk_size, y=y,
+                                      final_states=fs, workspace=ws, reuse_group_operands=True,
+                                      **fused_kw)
 
     launch_ms = event_times(head_step) if head_only else step_ms
     avg_launch_ms = sum(launch_ms) / len(launch_ms)
@@ -256,7 +271,7 @@ def main():
           f"(p10 {launch_ms[len(launch_ms) // 10] * 1e3:.1f}, "
           f"p90 {launch_ms[(9 * len(launch_ms)) // 10] * 1e3:.1f})", file=sys.stderr, flush=True)
 
-    alg_bytes = wl.algorithmic_bytes()
+    alg_bytes = wl.algorithmic_bytes() + extra_bytes
     achieved = alg_bytes / (avg_launch_ms * 1e-3) / 1e9
 
     # Measured device-to-device copy moving the same number of bytes (half
@@ -278,7 +293,7 @@ def main():
     del copy_src, copy_dst
     print(f"bench: kernel {achieved:.0f} GB/s algorithmic; copy of the same bytes {copy_gbs:.0f} GB/s",
           file=sys.stderr, flush=True)
-    traffic = counter_traffic(wl.name)
+    traffic = None if args.fused else counter_traffic(wl.name)
     out = {
         "metric": METRIC,
         "value": wl.tokens / (ms_per_step * 1e-3),
@@ -292,7 +307,9 @@ def main():
         "vs_baseline": None,
         "dtype": wl.io,
         "data": "synthetic",
-        "config": {"workload": f"{wl.name}: Mamba-2 2.7B-shaped SSD layer", "batch": wl.batch,
+        "config": {"workload": f"{wl.name}: Mamba-2 2.7B-shaped SSD layer"
+                               + (", fused dt softplus(dt + bias) and silu(z) gate" if args.fused else ""),
+                   "batch": wl.batch,
                    "seqlen": wl.seqlen, "nheads": wl.nheads, "headdim": wl.headdim,
                    "dstate": wl.dstate, "ngroups": wl.ngroups, "chunk_size": wl.chunk_size,
                    "split_len": split_len, "parallelism": "single GPU"},
@@ -306,7 +323,7 @@ def main():
                      "forward_avg_us": avg_step_ms * 1e3},
         "copy_reference": {"gbs": copy_gbs, "bytes": alg_bytes, "frac_of_copy": achieved / copy_gbs},
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.fused:
         print("bench: timing the fp64 CPU oracle", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(out), flush=True)

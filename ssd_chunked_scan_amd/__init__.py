@@ -19,7 +19,7 @@ import os
 from typing import Optional, Tuple
 
 __all__ = [
-    "ssd_fwd", "ssd_fwd_workspace_bytes", "ssd_plan_split_len", "ssd_debug_chunk_mask",
+    "ssd_fwd", "prepare_fwd", "ssd_fwd_workspace_bytes", "ssd_plan_split_len", "ssd_debug_chunk_mask",
     "ssd_decode_step",
     "SsdError", "library_path", "load_library", "STATUS", "EXPORTS",
 ]
@@ -163,6 +163,33 @@ def ssd_fwd(x, dt, A, B, C, D=None, seq_idx=None, chunk_size: int = 256, init_st
             dt_bias=None, dt_softplus: bool = False, dt_limit=None, z=None
             ) -> Tuple[object, Optional[object]]:
     """Run the forward pass on x.device.  Returns (y, final_states or None).
+    Arguments as for prepare_fwd, which this calls once."""
+    call, y, final_states = _marshal_fwd(
+        x, dt, A, B, C, D, seq_idx, chunk_size, init_states, return_final_states, split_len, y,
+        final_states, workspace, stream, reuse_group_operands, dt_bias, dt_softplus, dt_limit, z)
+    call()
+    return y, (final_states if return_final_states else None)
+
+
+def prepare_fwd(x, dt, A, B, C, D=None, seq_idx=None, chunk_size: int = 256, init_states=None,
+                return_final_states: bool = True, split_len: int = 0, y=None,
+                final_states=None, workspace=None, stream=None,
+                reuse_group_operands: bool = False, dt_bias=None, dt_softplus: bool = False,
+                dt_limit=None, z=None):
+    """Check and marshal the arguments of ssd_fwd once and return
+    (launch, y, final_states): each launch() call runs the forward pass again
+    on the same buffers and stream, with no per-call Python checks (for
+    loops over fixed buffers, e.g. timing).  The caller keeps the tensors
+    alive and unchanged in shape while it uses launch()."""
+    return _marshal_fwd(x, dt, A, B, C, D, seq_idx, chunk_size, init_states, return_final_states,
+                        split_len, y, final_states, workspace, stream, reuse_group_operands,
+                        dt_bias, dt_softplus, dt_limit, z)
+
+
+def _marshal_fwd(x, dt, A, B, C, D, seq_idx, chunk_size, init_states, return_final_states,
+                 split_len, y, final_states, workspace, stream, reuse_group_operands, dt_bias,
+                 dt_softplus, dt_limit, z):
+    """Argument checks and marshalling of ssd_fwd / prepare_fwd.
     ``split_len`` forces the sequence-parallel split length (0 = planner).
     Preallocated ``y`` / ``final_states`` / ``workspace`` (uint8) may be given.
     ``reuse_group_operands`` (bf16) skips the per-group C B^T / B^T kernel: the
@@ -222,13 +249,18 @@ def ssd_fwd(x, dt, A, B, C, D=None, seq_idx=None, chunk_size: int = 256, init_st
             workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         if stream is None:
             stream = torch.cuda.current_stream(dev).cuda_stream
-        st = lib.ssd_fwd_fused(ctypes.byref(shape), io, _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
-                               _ptr(C), _ptr(D), _ptr(seq_idx), chunk_size, _ptr(init_states),
-                               _ptr(y), _ptr(final_states), ctypes.byref(fused),
-                               _ptr(workspace) if ws_bytes else None, ws_bytes,
-                               ctypes.byref(opts), stream)
-    _check(st)
-    return y, (final_states if return_final_states else None)
+    args = (ctypes.byref(shape), io, _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+            _ptr(seq_idx), chunk_size, _ptr(init_states), _ptr(y), _ptr(final_states),
+            ctypes.byref(fused), _ptr(workspace) if ws_bytes else None, ws_bytes,
+            ctypes.byref(opts), stream)
+    keep = (shape, fused, opts, workspace)   # the byref targets live as long as the closure
+    fn = lib.ssd_fwd_fused
+
+    def launch():
+        _check(fn(*args))
+        return keep
+
+    return launch, y, final_states
 
 
 def ssd_debug_chunk_mask(dt, A, seq_idx=None, chunk_size: int = 256, chunk_begin: int = 0,

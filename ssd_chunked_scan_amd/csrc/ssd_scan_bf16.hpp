@@ -61,13 +61,16 @@
 // Wave roles.  Vector-memory loads and stores of one wave complete in issue
 // order, so a wave that has a slow HBM load or a scattered store in flight
 // cannot use any load it issued later.  All HBM traffic of the workgroup is
-// therefore issued by one extra producer wave, and the W compute waves only
-// load operands that the other heads of the row keep in L2 (C B^T, B^T and C
-// rows).  During chunk c the producer stores y_{c-1} (rows of 16-byte chunks
-// read from an LDS tile), issues the direct-to-LDS loads
-// (global_load_lds_dwordx4) of X_{c+1}, gathers dt of chunk c+1 and computes
-// its segsum values (page "GPU Hierarchy Meets Structured Matrices": the
-// sub-block sums) into the other half of a double buffer.
+// therefore issued by extra producer waves (4 at Q = 256, else 2), and the
+// W compute waves only load operands that the other heads of the row keep in
+// L2 (C B^T, B^T and C rows).  During chunk c the producers store y_{c-1}
+// (rows of 16-byte chunks read from an LDS tile; times silu(z_{c-1}) when the
+// output gate is fused), issue the direct-to-LDS loads
+// (global_load_lds_dwordx4) of X_{c+1}, gather dt of chunk c+1 (through the
+// fused dt map) and compute its segsum values (page "GPU Hierarchy Meets
+// Structured Matrices": the sub-block sums) into the other half of a double
+// buffer.  Four producers rather than two at Q = 256: the same time without
+// the gate (145 us at the 2.7B layer either way), 249 -> 217 us with it.
 //
 // Per chunk, two barriers.  Between them X_{c+1} is turned into MFMA
 // fragments once for all compute waves (unscaled and X'', fragment-ordered so
@@ -91,11 +94,14 @@ namespace ssd {
 #ifndef SSD_PAIR_PREFETCH
 #define SSD_PAIR_PREFETCH 1
 #endif
+#ifndef SSD_NPROD_Q256
+#define SSD_NPROD_Q256 4
+#endif
 
 template <int Q, int N, int PB>
 struct ScanCfg {
     static constexpr int W = (Q == 256) ? 8 : 4;        // compute waves
-    static constexpr int NPROD = 2;                      // producer waves
+    static constexpr int NPROD = (Q == 256) ? SSD_NPROD_Q256 : 2;   // producer waves
     static constexpr int THREADS = 64 * (W + NPROD);
     static constexpr int NT = N / 16;                    // state n-tiles
     static constexpr int PT = PB / 16;                   // headdim tiles
@@ -118,6 +124,7 @@ struct ScanCfg {
     static constexpr size_t kLdsBytes =
         4 * (size_t)SX * 2 + (size_t)PB * LDH * 2 + 2 * sizeof(SegBuf<Q>);
     static_assert(Q % 64 == 0 && Q <= 256, "chunk size");
+    static_assert(NPROD == 2 || NPROD == 4, "producer waves");
     static_assert(N % 16 == 0 && N <= 128, "dstate");
     static_assert(PB % 16 == 0 && PB <= 128, "headdim block");
     static_assert(ST % NTW == 0, "state tile split");
@@ -140,7 +147,7 @@ __device__ __attribute__((always_inline)) inline void scan_body(
     constexpr int CPRX = Cfg::CPRX, LDH = Cfg::LDH, NBLK = Cfg::NBLK, NYB = Cfg::NYB;
     constexpr int CPRY = PB / 8;
     constexpr int NPROD = Cfg::NPROD;
-    static_assert(THREADS == 64 * (((Q == 256) ? 8 : 4) + 2), "launch bounds");
+    static_assert(THREADS == 64 * (((Q == 256) ? 8 + SSD_NPROD_Q256 : 4 + 2)), "launch bounds");
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -305,7 +312,9 @@ __device__ __attribute__((always_inline)) inline void scan_body(
     };
     if (producer) {
         if (wave == W) run_producer(std::integral_constant<int, 0>{});
-        else run_producer(std::integral_constant<int, 1>{});
+        else if (NPROD == 2 || wave == W + 1) run_producer(std::integral_constant<int, 1>{});
+        else if (wave == W + 2) run_producer(std::integral_constant<int, (NPROD > 2) ? 2 : 0>{});
+        else run_producer(std::integral_constant<int, (NPROD > 3) ? 3 : 0>{});
         return;
     }
 
@@ -645,7 +654,7 @@ __device__ __attribute__((always_inline)) inline void scan_body(
 // objects, so that the compiler sees that their reads do not wait for the loads
 // in flight.  sY holds the y tile of one chunk (swizzled like the X stage).
 template <int Q, int N, int PB>
-__global__ __launch_bounds__(64 * (((Q == 256) ? 8 : 4) + 2)) void ssd_scan_bf16_kernel(ChunkArgs a) {
+__global__ __launch_bounds__(64 * (((Q == 256) ? 8 + SSD_NPROD_Q256 : 4 + 2))) void ssd_scan_bf16_kernel(ChunkArgs a) {
     using Cfg = ScanCfg<Q, N, PB>;
     __shared__ __attribute__((aligned(1024))) bf16 sXstage[Cfg::SX];
     __shared__ __attribute__((aligned(1024))) bf16x8 sXr[Cfg::NFRAG * 64];
