@@ -234,6 +234,17 @@ ssd_status_t ssd_decode_step(const ssd_shape_t *shape, ssd_dtype_t io,
                              const void *B, const void *C, const float *D,
                              float *state, void *y, void *stream);
 
+/* ssd_decode_step with the fused dt map and output gate of ssd_fused_t (the
+ * same maps as ssd_fwd_fused): dt holds the raw value when bias, softplus or
+ * clamp is enabled; fused->z, if set, is [batch][nheads][headdim] in the io
+ * dtype, aligned to its element size, and y becomes (state C + D_h x) *
+ * silu(z).  fused may be NULL (then this is ssd_decode_step). */
+ssd_status_t ssd_decode_step_fused(const ssd_shape_t *shape, ssd_dtype_t io,
+                                   const void *x, const float *dt, const float *A,
+                                   const void *B, const void *C, const float *D,
+                                   float *state, void *y, const ssd_fused_t *fused,
+                                   void *stream);
+
 const char *ssd_status_str(ssd_status_t status);
 
 /* Detail of the last failure on the calling thread ("" if none). */

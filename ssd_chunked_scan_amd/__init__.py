@@ -33,7 +33,8 @@ STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_UNSUPP
 EXPORTS = ["ssd_fwd_workspace_bytes", "ssd_fwd", "ssd_fwd_ex_workspace_bytes", "ssd_fwd_ex",
            "ssd_fwd_fused",
            "ssd_plan_split_len", "ssd_debug_chunk_mask", "ssd_debug_chunk_mask_ex",
-           "ssd_decode_step", "ssd_status_str", "ssd_last_error", "ssd_version"]
+           "ssd_decode_step", "ssd_decode_step_fused", "ssd_status_str", "ssd_last_error",
+           "ssd_version"]
 # segsum evaluations of the mask export (ssd.h SSD_SEGSUM_*)
 SEGSUM = {"hierarchy": 0, "direct": 1, "diff": 2}
 
@@ -102,6 +103,9 @@ def load_library():
     lib.ssd_debug_chunk_mask_ex.restype = i32
     lib.ssd_decode_step.argtypes = [shp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.ssd_decode_step.restype = i32
+    lib.ssd_decode_step_fused.argtypes = [shp, i32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                          ctypes.POINTER(Fused), vp]
+    lib.ssd_decode_step_fused.restype = i32
     lib.ssd_status_str.argtypes = [i32]
     lib.ssd_status_str.restype = ctypes.c_char_p
     lib.ssd_last_error.argtypes = []
@@ -296,9 +300,11 @@ def ssd_debug_chunk_mask(dt, A, seq_idx=None, chunk_size: int = 256, chunk_begin
     return sums if sums_only else out
 
 
-def ssd_decode_step(x, dt, A, B, C, D, state, y=None, stream=None):
+def ssd_decode_step(x, dt, A, B, C, D, state, y=None, stream=None, dt_bias=None,
+                    dt_softplus: bool = False, dt_limit=None, z=None):
     """One decode step: x [b, H, P], dt [b, H], B, C [b, G, N], A, D [H] (D may
-    be None), state [b, H, P, N] fp32 updated in place.  Returns y [b, H, P]."""
+    be None), state [b, H, P, N] fp32 updated in place.  Returns y [b, H, P].
+    Fused dt map and output gate as in ssd_fwd (z [b, H, P] in x's dtype)."""
     import torch
     lib = load_library()
     if x.dim() != 3 or B.dim() != 3:
@@ -317,6 +323,14 @@ def ssd_decode_step(x, dt, A, B, C, D, state, y=None, stream=None):
     if D is not None:
         _need(D, "D", (H,), torch.float32, dev)
     _need(state, "state", (b, H, P, N), torch.float32, dev)
+    if dt_bias is not None:
+        _need(dt_bias, "dt_bias", (H,), torch.float32, dev)
+    if z is not None:
+        _need(z, "z", (b, H, P), x.dtype, dev)
+    fused = Fused(_ptr(dt_bias), _ptr(z), 1 if dt_softplus else 0,
+                  0 if dt_limit is None else 1,
+                  0.0 if dt_limit is None else float(dt_limit[0]),
+                  0.0 if dt_limit is None else float(dt_limit[1]))
     if y is None:
         y = torch.empty_like(x)
     else:
@@ -325,7 +339,8 @@ def ssd_decode_step(x, dt, A, B, C, D, state, y=None, stream=None):
     with torch.cuda.device(dev):
         if stream is None:
             stream = torch.cuda.current_stream(dev).cuda_stream
-        st = lib.ssd_decode_step(ctypes.byref(shape), io, _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
-                                 _ptr(C), _ptr(D), _ptr(state), _ptr(y), stream)
+        st = lib.ssd_decode_step_fused(ctypes.byref(shape), io, _ptr(x), _ptr(dt), _ptr(A),
+                                       _ptr(B), _ptr(C), _ptr(D), _ptr(state), _ptr(y),
+                                       ctypes.byref(fused), stream)
     _check(st)
     return y

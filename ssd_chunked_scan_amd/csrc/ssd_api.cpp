@@ -156,6 +156,21 @@ ssd_status_t check_problem(const ssd_shape_t *s, int64_t chunk, ssd_dtype_t io,
     return SSD_OK;
 }
 
+// Host-only validation of the fused prologue/epilogue block (NULL = none);
+// z_align: required alignment of z in bytes.
+ssd_status_t check_fused(const ssd_fused_t *fused, size_t z_align) {
+    if (!fused) return SSD_OK;
+    for (int k = 0; k < 4; ++k)
+        if (fused->reserved[k] != 0) return fail(SSD_ERR_UNSUPPORTED, "reserved fused fields must be zero");
+    if (fused->dt_clamp && !(std::isfinite(fused->dt_min) && std::isfinite(fused->dt_max) &&
+                             fused->dt_min <= fused->dt_max))
+        return fail(SSD_ERR_UNSUPPORTED, "dt clamp needs finite dt_min <= dt_max");
+    if (fused->dt_bias && !aligned(fused->dt_bias, 4)) return fail(SSD_ERR_ALIGN, "dt_bias must be 4-byte aligned");
+    if (fused->z && !aligned(fused->z, z_align))
+        return fail(SSD_ERR_ALIGN, "z must be %zu-byte aligned", z_align);
+    return SSD_OK;
+}
+
 // Split plan and workspace size of a validated problem.
 ssd_status_t make_plan(const ssd_shape_t *s, int64_t chunk, ssd_dtype_t io,
                        const ssd_options_t *opts, Plan *pl) {
@@ -245,15 +260,8 @@ ssd_status_t ssd_fwd_fused(const ssd_shape_t *shape, ssd_dtype_t io, const void 
     g_last_error.clear();
     ssd_status_t st = check_problem(shape, chunk_size, io, opts);
     if (st != SSD_OK) return st;
-    if (fused) {
-        for (int k = 0; k < 4; ++k)
-            if (fused->reserved[k] != 0) return fail(SSD_ERR_UNSUPPORTED, "reserved fused fields must be zero");
-        if (fused->dt_clamp && !(std::isfinite(fused->dt_min) && std::isfinite(fused->dt_max) &&
-                                 fused->dt_min <= fused->dt_max))
-            return fail(SSD_ERR_UNSUPPORTED, "dt clamp needs finite dt_min <= dt_max");
-        if (fused->dt_bias && !aligned(fused->dt_bias, 4)) return fail(SSD_ERR_ALIGN, "dt_bias must be 4-byte aligned");
-        if (fused->z && !aligned(fused->z, 16)) return fail(SSD_ERR_ALIGN, "z must be 16-byte aligned");
-    }
+    st = check_fused(fused, 16);
+    if (st != SSD_OK) return st;
     if (!x || !dt || !A || !B || !C || !y)
         return fail(SSD_ERR_NULL, "x, dt, A, B, C and y are required");
     const size_t io_align = 16;
@@ -434,6 +442,13 @@ ssd_status_t ssd_debug_chunk_mask_ex(const ssd_shape_t *shape, const float *dt, 
 ssd_status_t ssd_decode_step(const ssd_shape_t *shape, ssd_dtype_t io, const void *x,
                              const float *dt, const float *A, const void *B, const void *C,
                              const float *D, float *state, void *y, void *stream) {
+    return ssd_decode_step_fused(shape, io, x, dt, A, B, C, D, state, y, nullptr, stream);
+}
+
+ssd_status_t ssd_decode_step_fused(const ssd_shape_t *shape, ssd_dtype_t io, const void *x,
+                                   const float *dt, const float *A, const void *B, const void *C,
+                                   const float *D, float *state, void *y, const ssd_fused_t *fused,
+                                   void *stream) {
     g_last_error.clear();
     if (io != SSD_F32 && io != SSD_BF16) return fail(SSD_ERR_UNSUPPORTED, "unknown io dtype %d", (int)io);
     ssd_status_t st = check_shape(shape, 64);
@@ -448,7 +463,18 @@ ssd_status_t ssd_decode_step(const ssd_shape_t *shape, ssd_dtype_t io, const voi
     if (!aligned(dt, 4) || !aligned(A, 4) || (D && !aligned(D, 4)))
         return fail(SSD_ERR_ALIGN, "dt, A and D must be 4-byte aligned");
     if (!aligned(state, 16)) return fail(SSD_ERR_ALIGN, "state must be 16-byte aligned");
+    st = check_fused(fused, esz);
+    if (st != SSD_OK) return st;
     ssd::DecodeArgs a;
+    memset(&a, 0, sizeof(a));
+    if (fused) {
+        a.dt_bias = fused->dt_bias;
+        a.z = fused->z;
+        a.dt_softplus = fused->dt_softplus != 0;
+        a.dt_clamp = fused->dt_clamp != 0;
+        a.dt_lo = fused->dt_min;
+        a.dt_hi = fused->dt_max;
+    }
     a.x = x;
     a.dt = dt;
     a.A = A;

@@ -67,7 +67,8 @@ struct DtMap {
     float lo, hi;
 };
 
-__device__ inline DtMap dt_map_of(const ChunkArgs &a, int h) {
+template <typename Args>
+__device__ inline DtMap dt_map_of(const Args &a, int h) {
     DtMap m;
     m.bias = a.dt_bias ? a.dt_bias[h] : 0.f;
     m.softplus = a.dt_softplus;
@@ -148,6 +149,11 @@ struct DecodeArgs {
     float *state;        // [batch][nheads][headdim][dstate], in/out
     void *y;             // [batch][nheads][headdim]  (io dtype)
     int batch, nheads, headdim, dstate, ngroups;
+    // fused dt map and output gate, as in ChunkArgs (z: [batch][nheads][headdim])
+    const float *dt_bias;
+    const void *z;
+    int dt_softplus, dt_clamp;
+    float dt_lo, dt_hi;
 };
 
 struct Unit {

@@ -3,7 +3,8 @@
 //
 //   a = exp(dt A_h)          h <- a h + dt x B^T          y = h C + D_h x
 //
-// with the N x P state carried in fp32 between calls (the final_states of the
+// (dt through the fused map and y through the silu(z) gate when they are
+// enabled, as in the forward pass) with the N x P state carried in fp32 between calls (the final_states of the
 // forward pass are its input).  The step is memory-bound: the state is read
 // and written once (2 * 4 P N bytes per head), everything else is a few
 // hundred bytes.  One workgroup per (batch row, head); the state is walked as
@@ -37,7 +38,8 @@ __global__ __launch_bounds__(256) void ssd_decode_kernel(DecodeArgs a) {
     const int P = a.headdim;
     const int tid = threadIdx.x, n4 = tid % LPR, r0 = tid / LPR;
 
-    const float dt = a.dt[bh];
+    const float dt = dt_apply(dt_map_of(a, h), a.dt[bh]);
+    const IO *zrow = (const IO *)a.z + (int64_t)bh * P;   // used only when a.z is set
     // the same per-token decay as the forward kernels: 2^(dt A log2 e)
     const float decay = __builtin_amdgcn_exp2f(__fmul_rn(__fmul_rn(dt, a.A[h]), kLog2e));
     const float Dh = a.D ? a.D[h] : 0.f;
@@ -65,7 +67,11 @@ __global__ __launch_bounds__(256) void ssd_decode_kernel(DecodeArgs a) {
         // row sum over the LPR lanes of this row (aligned groups of LPR lanes)
 #pragma unroll
         for (int off = LPR / 2; off >= 1; off >>= 1) part += __shfl_xor(part, off, LPR);
-        if (n4 == 0) io_store((IO *)a.y, (int64_t)bh * P + p, fmaf(Dh, xp, part));
+        if (n4 == 0) {
+            float out = fmaf(Dh, xp, part);
+            if (a.z) out *= silu_f32(io_load(zrow, p));   // fused output gate
+            io_store((IO *)a.y, (int64_t)bh * P + p, out);
+        }
     }
 }
 

@@ -73,3 +73,35 @@ def test_decode_continues_the_forward_pass(io):
     yr, fr = oracle.ssd_forward(inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D)
     ey, es = max_rel(y, yr[:, L - 1]), max_rel(st, fr)
     assert ey <= TOL[io] and es <= TOL[io], f"y {ey:.3e} state {es:.3e}"
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_decode_fused_continues_the_fused_forward(io):
+    """The fused forward (raw dt through bias + softplus, silu(z) gate) over
+    299 tokens, then one fused decode step with token 299, equals the
+    oracle's fused forward over all 300 tokens at the last output and the
+    final state."""
+    import torch
+    import ssd_chunked_scan_amd as ssd
+    L = 300
+    wl = workloads.custom_workload(name="decode_fused", batch=2, seqlen=L, nheads=4, headdim=64,
+                                   dstate=64, ngroups=2, chunk_size=128, io=io)
+    inp = workloads.make_inputs(wl, seed=25)
+    fz = workloads.make_fused_inputs(inp, seed=25)
+    t = lambda a, conv=False: _dev(np.ascontiguousarray(a), io if conv else "f32")
+    bias = t(fz.dt_bias)
+    _, fs = ssd.ssd_fwd(t(inp.x[:, :L - 1], True), t(fz.dt_raw[:, :L - 1]), t(inp.A),
+                        t(inp.B[:, :L - 1], True), t(inp.C[:, :L - 1], True), t(inp.D),
+                        chunk_size=128, dt_bias=bias, dt_softplus=True, dt_limit=(1e-3, 0.1),
+                        z=t(fz.z[:, :L - 1], True))
+    y = ssd.ssd_decode_step(t(inp.x[:, L - 1], True), t(fz.dt_raw[:, L - 1]), t(inp.A),
+                            t(inp.B[:, L - 1], True), t(inp.C[:, L - 1], True), t(inp.D), fs,
+                            dt_bias=bias, dt_softplus=True, dt_limit=(1e-3, 0.1),
+                            z=t(fz.z[:, L - 1], True))
+    torch.cuda.synchronize()
+    yr, fr = oracle.ssd_forward_fused(inp.x, fz.dt_raw, inp.A, inp.B, inp.C, inp.D,
+                                      dt_bias=fz.dt_bias, dt_softplus=True, dt_limit=(1e-3, 0.1),
+                                      z=fz.z)
+    ey = max_rel(y.float().cpu().numpy(), yr[:, L - 1])
+    es = max_rel(fs.cpu().numpy(), fr)
+    assert ey <= TOL[io] and es <= TOL[io], f"y {ey:.3e} state {es:.3e}"
