@@ -307,7 +307,8 @@ def main():
         "vs_baseline": None,
         "dtype": wl.io,
         "data": "synthetic",
-        "config": {"workload": f"{wl.name}: Mamba-2 2.7B-shaped SSD layer"
+        "config": {"workload": f"{wl.name}: " + ("Mamba-2 2.7B-shaped SSD layer" if wl.name == "layer27b"
+                                                 else "SSD forward, synthetic inputs")
                                + (", fused dt softplus(dt + bias) and silu(z) gate" if args.fused else ""),
                    "batch": wl.batch,
                    "seqlen": wl.seqlen, "nheads": wl.nheads, "headdim": wl.headdim,
