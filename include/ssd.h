@@ -92,7 +92,11 @@ typedef struct {
     int64_t split_len;   /* tokens per sequence-parallel split: 0 = planner's
                             choice, else a positive multiple of chunk_size   */
     int64_t flags;       /* SSD_OPT_* bits                                    */
-    int64_t reserved[6]; /* must be zero                                      */
+    int64_t headdim_block; /* headdim columns per workgroup: 0 = planner's
+                            choice, else a power of two >= 16 dividing
+                            headdim whose tiles fit the LDS (bf16 io only;
+                            fp32 io takes 0 or headdim)                     */
+    int64_t reserved[5]; /* must be zero                                      */
 } ssd_options_t;
 
 /* flags: the workspace already holds the per-group operands (C_c B_c^T blocks
@@ -185,6 +189,12 @@ ssd_status_t ssd_fwd_fused(const ssd_shape_t *shape, ssd_dtype_t io,
 /* The split length (tokens) the planner would use; 0 for an invalid problem. */
 int64_t ssd_plan_split_len(const ssd_shape_t *shape, int64_t chunk_size,
                            ssd_dtype_t io);
+
+/* The headdim columns per workgroup the planner would use (the whole head
+ * unless the tiles do not fit the LDS, or halved when that alone gives every
+ * CU a workgroup); 0 for an invalid problem. */
+int64_t ssd_plan_headdim_block(const ssd_shape_t *shape, int64_t chunk_size,
+                               ssd_dtype_t io);
 
 /* Debug export of the decay mask exactly as the forward kernels build it
  * (page "GPU Hierarchy Meets Structured Matrices", abstract: hierarchy-aware

@@ -32,7 +32,8 @@ STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_UNSUPP
           4: "SSD_ERR_ALIGN", 5: "SSD_ERR_WORKSPACE", 6: "SSD_ERR_HIP"}
 EXPORTS = ["ssd_fwd_workspace_bytes", "ssd_fwd", "ssd_fwd_ex_workspace_bytes", "ssd_fwd_ex",
            "ssd_fwd_fused",
-           "ssd_plan_split_len", "ssd_debug_chunk_mask", "ssd_debug_chunk_mask_ex",
+           "ssd_plan_split_len", "ssd_plan_headdim_block", "ssd_debug_chunk_mask",
+           "ssd_debug_chunk_mask_ex",
            "ssd_decode_step", "ssd_decode_step_fused", "ssd_status_str", "ssd_last_error",
            "ssd_version"]
 # segsum evaluations of the mask export (ssd.h SSD_SEGSUM_*)
@@ -53,7 +54,7 @@ class Shape(ctypes.Structure):
 
 class Options(ctypes.Structure):
     _fields_ = [("split_len", ctypes.c_int64), ("flags", ctypes.c_int64),
-                ("reserved", ctypes.c_int64 * 6)]
+                ("headdim_block", ctypes.c_int64), ("reserved", ctypes.c_int64 * 5)]
 
 
 SSD_OPT_REUSE_GROUP_OPERANDS = 1
@@ -90,6 +91,8 @@ def load_library():
     lib.ssd_fwd_ex_workspace_bytes.restype = sz
     lib.ssd_plan_split_len.argtypes = [shp, i64, i32]
     lib.ssd_plan_split_len.restype = i64
+    lib.ssd_plan_headdim_block.argtypes = [shp, i64, i32]
+    lib.ssd_plan_headdim_block.restype = i64
     fwd_args = [shp, i32, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz]
     lib.ssd_fwd.argtypes = fwd_args + [vp]
     lib.ssd_fwd.restype = i32
@@ -161,16 +164,21 @@ def ssd_plan_split_len(shape: Shape, chunk_size: int, io: int) -> int:
     return int(load_library().ssd_plan_split_len(ctypes.byref(shape), chunk_size, io))
 
 
+def ssd_plan_headdim_block(shape: Shape, chunk_size: int, io: int) -> int:
+    return int(load_library().ssd_plan_headdim_block(ctypes.byref(shape), chunk_size, io))
+
+
 def ssd_fwd(x, dt, A, B, C, D=None, seq_idx=None, chunk_size: int = 256, init_states=None,
             return_final_states: bool = True, split_len: int = 0, y=None, final_states=None,
             workspace=None, stream=None, reuse_group_operands: bool = False,
-            dt_bias=None, dt_softplus: bool = False, dt_limit=None, z=None
-            ) -> Tuple[object, Optional[object]]:
+            dt_bias=None, dt_softplus: bool = False, dt_limit=None, z=None,
+            headdim_block: int = 0) -> Tuple[object, Optional[object]]:
     """Run the forward pass on x.device.  Returns (y, final_states or None).
     Arguments as for prepare_fwd, which this calls once."""
     call, y, final_states = _marshal_fwd(
         x, dt, A, B, C, D, seq_idx, chunk_size, init_states, return_final_states, split_len, y,
-        final_states, workspace, stream, reuse_group_operands, dt_bias, dt_softplus, dt_limit, z)
+        final_states, workspace, stream, reuse_group_operands, dt_bias, dt_softplus, dt_limit, z,
+        headdim_block)
     call()
     return y, (final_states if return_final_states else None)
 
@@ -179,7 +187,7 @@ def prepare_fwd(x, dt, A, B, C, D=None, seq_idx=None, chunk_size: int = 256, ini
                 return_final_states: bool = True, split_len: int = 0, y=None,
                 final_states=None, workspace=None, stream=None,
                 reuse_group_operands: bool = False, dt_bias=None, dt_softplus: bool = False,
-                dt_limit=None, z=None):
+                dt_limit=None, z=None, headdim_block: int = 0):
     """Check and marshal the arguments of ssd_fwd once and return
     (launch, y, final_states): each launch() call runs the forward pass again
     on the same buffers and stream, with no per-call Python checks (for
@@ -187,14 +195,15 @@ def prepare_fwd(x, dt, A, B, C, D=None, seq_idx=None, chunk_size: int = 256, ini
     alive and unchanged in shape while it uses launch()."""
     return _marshal_fwd(x, dt, A, B, C, D, seq_idx, chunk_size, init_states, return_final_states,
                         split_len, y, final_states, workspace, stream, reuse_group_operands,
-                        dt_bias, dt_softplus, dt_limit, z)
+                        dt_bias, dt_softplus, dt_limit, z, headdim_block)
 
 
 def _marshal_fwd(x, dt, A, B, C, D, seq_idx, chunk_size, init_states, return_final_states,
                  split_len, y, final_states, workspace, stream, reuse_group_operands, dt_bias,
-                 dt_softplus, dt_limit, z):
+                 dt_softplus, dt_limit, z, headdim_block=0):
     """Argument checks and marshalling of ssd_fwd / prepare_fwd.
-    ``split_len`` forces the sequence-parallel split length (0 = planner).
+    ``split_len`` forces the sequence-parallel split length (0 = planner);
+    ``headdim_block`` the headdim columns per workgroup (0 = planner).
     Preallocated ``y`` / ``final_states`` / ``workspace`` (uint8) may be given.
     ``reuse_group_operands`` (bf16) skips the per-group C B^T / B^T kernel: the
     given ``workspace`` must hold them from an earlier call with the same B, C.
@@ -242,7 +251,8 @@ def _marshal_fwd(x, dt, A, B, C, D, seq_idx, chunk_size, init_states, return_fin
         _need(final_states, "final_states", (b, H, P, N), torch.float32, dev)
     if reuse_group_operands and workspace is None:
         raise ValueError("reuse_group_operands needs the workspace of the earlier call")
-    opts = Options(split_len, SSD_OPT_REUSE_GROUP_OPERANDS if reuse_group_operands else 0)
+    opts = Options(split_len, SSD_OPT_REUSE_GROUP_OPERANDS if reuse_group_operands else 0,
+                   headdim_block)
     with torch.cuda.device(dev):
         ws_bytes = int(lib.ssd_fwd_ex_workspace_bytes(ctypes.byref(shape), chunk_size, io,
                                                       ctypes.byref(opts)))

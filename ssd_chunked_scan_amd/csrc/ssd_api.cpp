@@ -145,8 +145,17 @@ ssd_status_t check_problem(const ssd_shape_t *s, int64_t chunk, ssd_dtype_t io,
     ssd_status_t st = check_shape(s, chunk);
     if (st != SSD_OK) return st;
     if (opts) {
-        for (int k = 0; k < 6; ++k)
+        for (int k = 0; k < 5; ++k)
             if (opts->reserved[k] != 0) return fail(SSD_ERR_UNSUPPORTED, "reserved option fields must be zero");
+        const int64_t hb = opts->headdim_block;
+        if (hb != 0) {
+            const bool pow2 = hb >= 16 && (hb & (hb - 1)) == 0;
+            if (io == SSD_F32 ? hb != s->headdim
+                              : (!pow2 || hb > s->headdim || s->headdim % hb != 0 ||
+                                 bf16_lds_bytes(chunk, s->dstate, hb) > 160 * 1024))
+                return fail(SSD_ERR_UNSUPPORTED, "headdim_block %lld is not usable for headdim %lld",
+                            (long long)hb, (long long)s->headdim);
+        }
         if (opts->flags & ~(int64_t)SSD_OPT_REUSE_GROUP_OPERANDS)
             return fail(SSD_ERR_UNSUPPORTED, "unknown option flags 0x%llx", (long long)opts->flags);
         if (opts->split_len < 0 || (opts->split_len > 0 && opts->split_len % chunk != 0))
@@ -178,19 +187,36 @@ ssd_status_t make_plan(const ssd_shape_t *s, int64_t chunk, ssd_dtype_t io,
     if (st != SSD_OK) return st;
     pl->nchunks = (int)((s->seqlen + chunk - 1) / chunk);
     pl->pblock = (io == SSD_BF16) ? bf16_pblock(chunk, s->dstate, s->headdim) : (int)s->headdim;
+    if (opts && opts->headdim_block > 0) pl->pblock = (int)opts->headdim_block;
     pl->npblocks = (int)(s->headdim / pl->pblock);
     int nsplits = 1;
+    const int64_t cus = device_cus();
+    const bool forced_pb = opts && opts->headdim_block > 0;
+    if (io == SSD_BF16 && !forced_pb && !(opts && opts->split_len > 0)) {
+        // Too few (batch row, head) units for one workgroup per CU: halve the
+        // headdim block first when that alone reaches a full round (no state
+        // recomputation; measured on the 32-head sweep at 4 x 8192 tokens:
+        // 166 us against 195 us for two sequence splits).
+        const int64_t units = s->batch * s->nheads * pl->npblocks;
+        if (units < cus && 2 * units >= cus && pl->pblock >= 64) {
+            pl->pblock /= 2;
+            pl->npblocks *= 2;
+        }
+    }
     if (opts && opts->split_len > 0) {
         const int64_t sc = opts->split_len / chunk;
         nsplits = (int)((pl->nchunks + sc - 1) / sc);
     } else {
         // Split-sequence planning: the split length is chosen from the amount
-        // of independent work, not from the chunk size.  Enough workgroups to
-        // cover the device twice; rows never split below one chunk per split.
+        // of independent work, not from the chunk size.  Enough splits for
+        // one round of workgroups over the CUs (a second round costs more in
+        // per-workgroup start-up and in the split-local pass than it gains:
+        // measured 4096-token splits 189-200 us against 2048-token splits
+        // 213-270 us at 2 x 16384 x 32 heads and 1 x 65536 x 16 heads); rows
+        // never split below one chunk per split.
         const int64_t units = s->batch * s->nheads * pl->npblocks;
-        const int64_t cus = device_cus();
         if (units < cus) {
-            const int64_t want = (2 * cus + units - 1) / units;
+            const int64_t want = (cus + units - 1) / units;
             nsplits = (int)std::min<int64_t>(want, pl->nchunks);
         }
     }
@@ -249,6 +275,12 @@ int64_t ssd_plan_split_len(const ssd_shape_t *shape, int64_t chunk_size, ssd_dty
     Plan pl;
     if (make_plan(shape, chunk_size, io, nullptr, &pl) != SSD_OK) return 0;
     return (int64_t)pl.split_chunks * chunk_size;
+}
+
+int64_t ssd_plan_headdim_block(const ssd_shape_t *shape, int64_t chunk_size, ssd_dtype_t io) {
+    Plan pl;
+    if (make_plan(shape, chunk_size, io, nullptr, &pl) != SSD_OK) return 0;
+    return pl.pblock;
 }
 
 ssd_status_t ssd_fwd_fused(const ssd_shape_t *shape, ssd_dtype_t io, const void *x, const float *dt,

@@ -223,3 +223,25 @@ def test_fused_argument_errors():
     # a valid block reaches the workspace check (the last host check)
     assert _fused_call(F(FAKE, FAKE, 1, 1, 0.001, 0.1), ws=None, ws_bytes=0) == 5
     assert _fused_call(None, ws=None, ws_bytes=0) == 5
+
+
+def test_headdim_block_option_errors():
+    """headdim_block: 0 or a power of two >= 16 dividing headdim whose tiles
+    fit the LDS (bf16); fp32 takes only 0 or headdim."""
+    s = good_shape()                                   # headdim 64, dstate 128
+    for hb, io, chunk in [(48, 1, 256), (8, 1, 256), (128, 1, 256), (-16, 1, 256),
+                          (32, 0, 256), (16, 0, 64)]:
+        o = ssd.Options(0, 0, hb)
+        assert _fwd(s, io=io, chunk=chunk, opts=o) == 3, (hb, io)
+    # accepted values reach the workspace check
+    for hb, io in [(16, 1), (32, 1), (64, 1), (64, 0)]:
+        assert _fwd(s, io=io, opts=ssd.Options(0, 0, hb)) == 5, (hb, io)
+
+
+def test_plan_queries():
+    lib = ssd.load_library()
+    s = ssd.Shape(8, 2048, 80, 64, 128, 1)
+    assert ssd.ssd_plan_headdim_block(s, 256, 1) == 64
+    assert ssd.ssd_plan_split_len(s, 256, 1) == 2048
+    assert ssd.ssd_plan_headdim_block(s, 256, 0) == 64
+    assert lib.ssd_plan_headdim_block(None, 256, 1) == 0

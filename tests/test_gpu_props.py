@@ -139,3 +139,25 @@ def test_reuse_group_operands_is_bitwise_identical():
                          chunk_size=wl.chunk_size, workspace=ws, reuse_group_operands=True)
     torch.cuda.synchronize()
     assert torch.equal(y0, y1) and torch.equal(f0, f1)
+
+
+@pytest.mark.parametrize("Q", [128, 256])
+def test_headdim_block_invariance(Q):
+    """Every headdim block size (whole head, halves, quarters) gives the same
+    outputs and final state bit for bit: each output element and state
+    element goes through the same sequence of operations whichever
+    workgroup owns its column; and against the oracle, with and without
+    sequence splits."""
+    wl = _wl(headdim=128, seqlen=1000, chunk_size=Q)
+    inp = workloads.make_inputs(wl, seed=19)
+    whole = -(-1000 // Q) * Q     # one split per row (the planner would split this row)
+    y0, f0 = run_gpu(inp, headdim_block=16, split_len=whole)
+    for hb in (32, 64, 128):
+        if Q == 256 and hb == 128:
+            continue   # the 256 x 128 tiles do not fit the LDS (SSD_ERR_UNSUPPORTED)
+        y, f = run_gpu(inp, headdim_block=hb, split_len=whole)
+        assert np.array_equal(y, y0) and np.array_equal(f, f0), f"headdim_block {hb}"
+        ys, fs = run_gpu(inp, headdim_block=hb, split_len=2 * Q)
+        assert max_rel(ys, y0) <= TOL["bf16"] and max_rel(fs, f0) <= TOL["bf16"]
+    yr, fr = oracle_slice(inp, range(2), range(4))
+    assert max_rel(y0, yr) <= TOL["bf16"] and max_rel(f0, fr) <= TOL["bf16"]
