@@ -256,6 +256,36 @@ def main():
         torch.cuda.synchronize(dev)
         return sorted(e0.elapsed_time(e1) for e0, e1 in ev)
 
+    # The same step captured in a HIP graph and replayed (no host launch work
+    # between kernels); every replay's outputs are checked against the eager
+    # step's before the graph is timed.
+    gstream = torch.cuda.Stream(dev)
+    with torch.cuda.stream(gstream):
+        gstep, gy, gfs = ssd.prepare_fwd(x, dt, A, B, C, D, seq, chunk_size=wl.chunk_size,
+                                         workspace=torch.empty_like(ws),
+                                         stream=gstream.cuda_stream, **fused_kw)
+        gstep()
+    torch.cuda.synchronize(dev)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=gstream):
+        gstep()
+    step()
+    torch.cuda.synchronize(dev)
+    for _ in range(3):
+        gy.zero_()
+        torch.cuda.synchronize(dev)
+        graph.replay()
+        torch.cuda.synchronize(dev)
+        if not (torch.equal(gy, y) and torch.equal(gfs, fs)):
+            raise RuntimeError("bench: graph replay differs from the eager step")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize(dev)
+    graph_ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    print(f"bench: graph replay {graph_ms_per_step * 1e3:.1f} us/step (eager {ms_per_step * 1e3:.1f})",
+          file=sys.stderr, flush=True)
+
     step_ms = event_times(step)
     avg_step_ms = sum(step_ms) / len(step_ms)
     head_only = wl.io == "bf16" and split_len >= wl.seqlen
@@ -302,6 +332,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "graph_ms_per_step": graph_ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
