@@ -86,6 +86,9 @@ def _parse_functions(asm_text: str):
     or 'ins'."""
     funcs, cur = [], None
     for raw in asm_text.splitlines():
+        if "ssd lookahead wait" in raw and cur is not None:
+            cur.append(("mark", "ssd lookahead wait"))   # see vmem_lds_sync_lookahead
+            continue
         line = raw.split(";")[0].strip()
         if not line:
             continue
@@ -123,7 +126,7 @@ def check_mfma_result_reads(asm_text: str, where: str) -> int:
                         break
                     seen.add((j, ws))
                     k2, t2 = items[j]
-                    if k2 == "label":
+                    if k2 in ("label", "mark"):
                         j += 1
                         continue
                     op = t2.split()[0]
@@ -185,6 +188,36 @@ def check_counted_barrier_waits(asm_text: str, where: str) -> int:
                 continue
             need, j = int(m.group(1)), i - 1
             n += 1
+            # the marker of vmem_lds_sync_lookahead: before the wait, with no
+            # label or vector-memory operation in between
+            marked, q = False, i - 1
+            while q >= 0 and items[q][0] != "label":
+                if items[q][0] == "mark":
+                    marked = True
+                    break
+                if items[q][1].startswith(_VMEM):
+                    break
+                q -= 1
+            if marked:
+                # run-ahead tile loads: the K newest vector-memory operations
+                # must be exactly direct-to-LDS loads on straight-line code
+                # (the tile the barrier publishes was issued before them)
+                while need > 0:
+                    if j < 0 or items[j][0] == "label":
+                        raise RuntimeError(f"{where}: {fname}: lookahead wait '{text}' reaches a "
+                                           f"label before {m.group(1)} direct-to-LDS loads")
+                    t = items[j][1]
+                    op = t.split()[0] if t.split() else ""
+                    if op.startswith(("s_branch", "s_cbranch", "s_setpc")):
+                        raise RuntimeError(f"{where}: {fname}: lookahead wait '{text}' reaches a "
+                                           f"branch before {m.group(1)} direct-to-LDS loads")
+                    if op.startswith(("global_load_lds", "buffer_load_lds")):
+                        need -= 1
+                    elif op.startswith(_VMEM):
+                        raise RuntimeError(f"{where}: {fname}: lookahead wait '{text}' would leave "
+                                           f"an ordinary vector-memory operation in flight: {t}")
+                    j -= 1
+                continue
             while need > 0:
                 if j < 0 or items[j][0] == "label":
                     raise RuntimeError(f"{where}: {fname}: counted barrier wait '{text}' reaches "

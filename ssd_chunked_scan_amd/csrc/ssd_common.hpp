@@ -246,4 +246,15 @@ __device__ inline void mfma_fence_all(f32x4 (&v)[K]) {
     for (int k = 1; k < K; ++k) asm volatile("" : "+v"(v[k]));
 }
 
+// The same for a two-dimensional array of accumulators.
+template <int K1, int K2>
+__device__ inline void mfma_fence_all(f32x4 (&v)[K1][K2]) {
+    asm volatile("s_nop 7" : "+v"(v[0][0]));
+#pragma unroll
+    for (int i = 0; i < K1; ++i)
+#pragma unroll
+        for (int k = 0; k < K2; ++k)
+            if (i + k > 0) asm volatile("" : "+v"(v[i][k]));
+}
+
 }  // namespace ssd

@@ -135,7 +135,7 @@ struct ScanCfg {
 // One workgroup's walk over its chunks.  PB is the number of headdim columns
 // the workgroup owns (a whole headdim block, or half of one); the LDS arrays
 // belong to the kernel and are at least as large as this PB needs.
-template <int Q, int N, int PB>
+template <int Q, int N, int PB, bool LOCAL>
 __device__ __attribute__((always_inline)) inline void scan_body(
         const ChunkArgs &a, const Unit un, const int p_base, bf16 *__restrict__ sXstage,
         bf16x8 *__restrict__ sXr, bf16x8 *__restrict__ sXs, bf16 *__restrict__ sY,
@@ -159,7 +159,7 @@ __device__ __attribute__((always_inline)) inline void scan_body(
     if (a.mode == kModeSplitLocal && s == a.nsplits - 1) return;
     const int L = a.seqlen, H = a.nheads, G = a.ngroups, P = a.headdim;
     const int grp = h / (H / G);
-    const bool full = a.mode == kModeFull;
+    constexpr bool full = !LOCAL;   // LOCAL: split-local pass (end state and decay only)
     const bool resets = a.seq_idx != nullptr;
     const int c_begin = s * a.split_chunks;
     const int c_end = min(a.nchunks, c_begin + a.split_chunks);
@@ -223,15 +223,53 @@ __device__ __attribute__((always_inline)) inline void scan_body(
         const uint32_t xrow_off = (uint32_t)xrow * row_bytes, yrow_off = (uint32_t)yrow * row_bytes;
         const char *xbase = (const char *)Xsrc;
         char *ybase = (char *)a.y + ((((int64_t)b * L) * H + h) * P + p_base) * 2;
+        auto dma_to = [&](const char *src, bf16 *dst) __attribute__((always_inline)) {
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                             (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+        };
         auto dma_x = [&](int c, int k) __attribute__((always_inline)) {
             constexpr int RB = 64 / CPRX;   // rows per block
             const int t0 = c * Q, r = k * RB + xrow;
             const int cc = xpc ^ swz<CPRX>(r);
             const char *src = xbase + (int64_t)(t0 + k * RB) * row_bytes + (xrow_off + cc * 16);
             if (t0 + Q > L && t0 + r >= L) src = (const char *)kZeroChunk;
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
-                                             (__attribute__((address_space(3))) void *)(sXstage + k * 512),
-                                             16, 0, 0);
+            dma_to(src, sXstage + k * 512);
+        };
+        // Split-local pass: X_c goes to staging buffer c mod 3 (sXstage, or
+        // the unscaled fragment set and the y tile, which that pass does not
+        // use).  The buffer is a compile-time choice, so that every
+        // asynchronous load names its LDS object and offset (the compiler
+        // then sees that the loads of one tile do not overlap).
+        auto stream_local = [&](int cx, auto BUF) __attribute__((always_inline)) {
+            constexpr int bsel = decltype(BUF)::value;
+            bf16 *base = bsel == 0 ? sXstage : (bsel == 1 ? (bf16 *)sXr : sY);
+            constexpr int RB = 64 / CPRX;
+            const int t0 = cx * Q;
+#pragma unroll
+            for (int k = KB0; k < KB1; ++k) {
+                const int r = k * RB + xrow;
+                const int cc = xpc ^ swz<CPRX>(r);
+                const char *src = xbase + (int64_t)(t0 + k * RB) * row_bytes + (xrow_off + cc * 16);
+                if (t0 + Q > L && t0 + r >= L) src = (const char *)kZeroChunk;
+                dma_to(src, base + k * 512);
+            }
+        };
+        // X_cx into its buffer; with WAIT, then the barrier that leaves
+        // exactly those loads in flight (the marker differs per buffer so
+        // that the three copies stay separate straight-line code).
+        auto prefetch_local = [&](int cx, bool wait) __attribute__((always_inline)) {
+            constexpr int KB = KB1 - KB0;
+            const int sel = cx % 3;
+            if (sel == 0) {
+                stream_local(cx, std::integral_constant<int, 0>{});
+                if (wait) vmem_lds_sync_lookahead<KB, 0>();
+            } else if (sel == 1) {
+                stream_local(cx, std::integral_constant<int, 1>{});
+                if (wait) vmem_lds_sync_lookahead<KB, 1>();
+            } else {
+                stream_local(cx, std::integral_constant<int, 2>{});
+                if (wait) vmem_lds_sync_lookahead<KB, 2>();
+            }
         };
         // Fused output gate: z of chunk c is loaded (16 bytes per lane and
         // block, unconditionally: rows past the sequence end read zeros)
@@ -295,6 +333,29 @@ __device__ __attribute__((always_inline)) inline void scan_body(
         // and y_{c-1} (written to sY by the compute waves between the
         // barriers of the previous hand-over), then the segsum of chunk c+1,
         // whose token values arrived long before.
+        if constexpr (LOCAL) {
+            // Split-local pass: X runs two chunks ahead (three staging
+            // buffers), because this pass has too little work per chunk to
+            // cover an HBM round trip.  At the first barrier of chunk c only
+            // X_{c+1} must have landed: the loads of X_{c+2}, issued last,
+            // may still be in flight (completions count in issue order).
+            fetch_tokens(c_begin);
+            prefetch_local(c_begin, false);
+            segsum(c_begin, segbuf[c_begin & 1]);
+            if (c_begin + 1 < c_end) prefetch_local(c_begin + 1, true);   // X_{c_begin} has landed
+            else vmem_lds_sync();
+            lds_sync();
+            for (int c = c_begin; c < c_end; ++c) {
+                if (c + 1 < c_end) {
+                    fetch_tokens(c + 1);
+                    segsum(c + 1, segbuf[(c + 1) & 1]);
+                }
+                if (c + 2 < c_end) prefetch_local(c + 2, true);   // X_{c+1} has landed
+                else vmem_lds_sync();
+                lds_sync();
+            }
+            return;
+        }
         fetch_tokens(c_begin);
         stream(c_begin, -1, -1);
         segsum(c_begin, segbuf[c_begin & 1]);
@@ -363,7 +424,13 @@ __device__ __attribute__((always_inline)) inline void scan_body(
     // sXstage -> fragments (between the two barriers of a hand-over): fragment
     // (m, pt) holds, for lane (p = 16 pt + l16, g), X[j][p] at the slot tokens
     // j = 32m + 4g + (e%4) + 16(e/4); sXs holds the same times the X'' factor.
-    auto make_fragments = [&](const SegBuf<Q> &sg) __attribute__((always_inline)) {
+    auto make_fragments = [&](const SegBuf<Q> &sg, int cx) __attribute__((always_inline)) {
+        // X_cx's staging buffer (always sXstage in the full pass)
+        const bf16 *xs_src = sXstage;
+        if constexpr (LOCAL) {
+            const int sel = cx % 3;
+            xs_src = sel == 0 ? sXstage : (sel == 1 ? (const bf16 *)sXr : (const bf16 *)sY);
+        }
         // wave w makes the fragments of pairs w, w + W, ...: the pair's X''
         // factors are read and multiplied once for all its headdim tiles
 #pragma unroll
@@ -380,15 +447,15 @@ __device__ __attribute__((always_inline)) inline void scan_body(
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt) {
                 const int rr = jr + (l16 >> 2), col = pt * 16 + 4 * (l16 & 3);
-                const bf16x8 xr = join_bf16x8(lds_read_tr16(&sXstage[tile_off_col<CPRX>(rr, col)]),
-                                              lds_read_tr16(&sXstage[tile_off_col<CPRX>(rr + 16, col)]));
+                const bf16x8 xr = join_bf16x8(lds_read_tr16(&xs_src[tile_off_col<CPRX>(rr, col)]),
+                                              lds_read_tr16(&xs_src[tile_off_col<CPRX>(rr + 16, col)]));
                 bf16x8 xs;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     xs[r] = (bf16)((float)xr[r] * flo[r]);
                     xs[4 + r] = (bf16)((float)xr[4 + r] * whi[r]);
                 }
-                sXr[(m * PT + pt) * 64 + lane] = xr;
+                if constexpr (!LOCAL) sXr[(m * PT + pt) * 64 + lane] = xr;   // a staging buffer when LOCAL
                 sXs[(m * PT + pt) * 64 + lane] = xs;
             }
         }
@@ -423,10 +490,14 @@ __device__ __attribute__((always_inline)) inline void scan_body(
 
     // ---- prologue: X fragments, state tile and C rows of the first chunk
     // (the producer loads X and computes the segsum values meanwhile)
-    load_c(c_begin, Irow0);
-    vmem_lds_sync_keep<IT * KN>();   // the C rows may still be in flight
+    if constexpr (LOCAL) {
+        vmem_lds_sync();                 // no C rows: the split-local pass has no outputs
+    } else {
+        load_c(c_begin, Irow0);
+        vmem_lds_sync_keep<IT * KN>();   // the C rows may still be in flight
+    }
     if (!state_zero) write_h();
-    make_fragments(segbuf[c_begin & 1]);
+    make_fragments(segbuf[c_begin & 1], c_begin);
     lds_sync();
 
     for (int c = c_begin; c < c_end; ++c) {
@@ -524,6 +595,9 @@ __device__ __attribute__((always_inline)) inline void scan_body(
 #pragma unroll
                     for (int k = 0; k < PTW; ++k) xs[k] = sXs[(m * PT + pt0 + k) * 64 + lane];
                 }
+                // without the output steps in between, the previous pair's
+                // state MFMAs are only a few instructions back
+                if constexpr (LOCAL) mfma_fence_all(hs);
 #pragma unroll
                 for (int q = 0; q < NTW; ++q) {
 #pragma unroll
@@ -536,6 +610,9 @@ __device__ __attribute__((always_inline)) inline void scan_body(
 
             // output rows: Y^T <- Y^T * Tp_m + X''_m^T (C B^T)_{I,m}^T
             if (full) {
+                // the previous pair's output MFMAs may be only a branch away
+                // (ROCm 7.2 has been seen to miss the wait on that path)
+                if (m > 0) mfma_fence_all(acc);
 #pragma unroll
                 for (int it = 0; it < IT; ++it) {
                     // statically known: with two row tiles per wave, tile 0
@@ -616,13 +693,17 @@ __device__ __attribute__((always_inline)) inline void scan_body(
         // fragments and h_c.  The next chunk's C rows go out last: the
         // barrier lets them stay in flight.
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        load_c(cn, Irow);
-        vmem_lds_sync_keep<IT * KN>();
+        if constexpr (LOCAL) {
+            vmem_lds_sync();
+        } else {
+            load_c(cn, Irow);
+            vmem_lds_sync_keep<IT * KN>();
+        }
         if (full) write_y(Irow);
         if (c + 1 < c_end) {
             mfma_fence_all(hs);
             write_h();
-            make_fragments(segbuf[buf ^ 1]);
+            make_fragments(segbuf[buf ^ 1], c + 1);
         }
         lds_sync();
     }
@@ -663,13 +744,23 @@ __global__ __launch_bounds__(64 * (((Q == 256) ? 8 + SSD_NPROD_Q256 : 4 + 2))) v
     __shared__ __attribute__((aligned(16))) bf16 sH[PB * Cfg::LDH];
     __shared__ __attribute__((aligned(16))) SegBuf<Q> segbuf[2];
     const Unit un = unit_of_block(a);
+    if (a.mode == kModeSplitLocal) {
+        if constexpr (PB >= 32) {
+            if (un.half >= 0) {
+                scan_body<Q, N, PB / 2, true>(a, un, un.pb * PB + un.half * (PB / 2), sXstage, sXr, sXs, sY, sH, segbuf);
+                return;
+            }
+        }
+        scan_body<Q, N, PB, true>(a, un, un.pb * PB, sXstage, sXr, sXs, sY, sH, segbuf);
+        return;
+    }
     if constexpr (PB >= 32) {
         if (un.half >= 0) {
-            scan_body<Q, N, PB / 2>(a, un, un.pb * PB + un.half * (PB / 2), sXstage, sXr, sXs, sY, sH, segbuf);
+            scan_body<Q, N, PB / 2, false>(a, un, un.pb * PB + un.half * (PB / 2), sXstage, sXr, sXs, sY, sH, segbuf);
             return;
         }
     }
-    scan_body<Q, N, PB>(a, un, un.pb * PB, sXstage, sXr, sXs, sY, sH, segbuf);
+    scan_body<Q, N, PB, false>(a, un, un.pb * PB, sXstage, sXr, sXs, sY, sH, segbuf);
 }
 
 }  // namespace ssd

@@ -84,6 +84,21 @@ __device__ inline void vmem_lds_sync_keep() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Barrier after which every direct-to-LDS load has landed except the KEEP
+// most recently issued ones, which are themselves direct-to-LDS loads of a
+// later tile that no wave reads before a later barrier (loads run ahead by
+// one more tile).  The marker lets the build check verify that exactly the
+// KEEP newest vector-memory operations before the wait are those loads.
+template <int KEEP, int TAG>
+__device__ inline void vmem_lds_sync_lookahead() {
+    static_assert(KEEP > 0 && KEEP < 64, "vmcnt range");
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    asm volatile("; ssd lookahead wait %0" ::"i"(TAG) : "memory");
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(KEEP));
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // 16 zero bytes in global memory: the source of the padding rows of a tile.
 static __device__ __attribute__((aligned(16))) const bf16 kZeroChunk[8] = {};
 
