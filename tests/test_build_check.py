@@ -1,4 +1,4 @@
-"""The build's path check over the generated gfx950 assembly: from every MFMA,
+"""The build's path checks over the generated gfx950 assembly.  From every MFMA,
 every path (fall-through and branch targets) must keep reads of its result at
 least 8 wait states away, except the accumulator of the next MFMA on the same
 registers and interlocked v_accvgpr_read of an AGPR result (CPU only)."""
@@ -78,3 +78,48 @@ def test_counted_barrier_wait_rejects_label_in_window():
                "s_barrier")
     with pytest.raises(RuntimeError):
         _build.check_counted_barrier_waits(asm, "t")
+
+
+# look-ahead waits (vmem_lds_sync_lookahead): the marker comment precedes the
+# wait, and exactly the K newest vector-memory operations must be
+# direct-to-LDS loads on straight-line code
+
+def test_lookahead_wait_accepts_newest_lds_loads():
+    asm = _asm("global_load_dwordx4 v[2:5], v[6:7], off",
+               "global_load_lds_dwordx4 v[0:1], off",
+               "s_mov_b32 m0, s6",
+               "global_load_lds_dwordx4 v[8:9], off",
+               "; ssd lookahead wait 1",
+               "s_waitcnt vmcnt(2) lgkmcnt(0)",
+               "s_barrier")
+    assert _build.check_counted_barrier_waits(asm, "t") == 1
+
+
+def test_lookahead_wait_rejects_plain_load_in_flight():
+    asm = _asm("global_load_lds_dwordx4 v[0:1], off",
+               "global_load_dwordx4 v[2:5], v[6:7], off",
+               "; ssd lookahead wait 0",
+               "s_waitcnt vmcnt(2) lgkmcnt(0)",
+               "s_barrier")
+    with pytest.raises(RuntimeError):
+        _build.check_counted_barrier_waits(asm, "t")
+
+
+def test_lookahead_wait_rejects_branch_in_window():
+    asm = _asm("global_load_lds_dwordx4 v[0:1], off",
+               "s_cbranch_scc1 .LBB0_4",
+               "global_load_lds_dwordx4 v[8:9], off",
+               "; ssd lookahead wait 2",
+               "s_waitcnt vmcnt(2) lgkmcnt(0)",
+               "s_barrier")
+    with pytest.raises(RuntimeError):
+        _build.check_counted_barrier_waits(asm, "t")
+
+
+def test_marker_does_not_count_as_a_wait_state():
+    asm = _asm("v_mfma_f32_16x16x32_bf16 v[0:3], v[4:7], v[8:11], 0",
+               "s_nop 6",
+               "; ssd lookahead wait 0",
+               "v_mul_f32_e32 v20, v1, v21")
+    with pytest.raises(RuntimeError):
+        _build.check_mfma_result_reads(asm, "t")
