@@ -54,6 +54,8 @@ SHAPES = [
     ("bf16", 128, 64, 128, 4, 8, 517),
     ("bf16", 256, 128, 64, 1, 4, 1000),
     ("bf16", 256, 32, 16, 1, 2, 300),
+    ("bf16", 256, 128, 128, 2, 4, 600),     # two headdim blocks per head (tiles of 256 x 64)
+    ("bf16", 64, 16, 32, 1, 2, 1),          # a single token
     ("f32", 64, 16, 16, 1, 2, 190),
     ("f32", 256, 128, 128, 1, 2, 300),
 ]
