@@ -23,15 +23,29 @@ __global__ __launch_bounds__(256) void ssd_split_scan_kernel(const float *init_s
     if (e >= total) return;
     const int64_t bh = e / pn, k = e % pn;
     float E = init_states ? init_states[bh * pn + k] : 0.f;
-    for (int s = 0; s < nsplits; ++s) {
-        const int64_t idx = (bh * nsplits + s) * pn + k;
-        if (s + 1 < nsplits) {
-            const float loc = ws_states[idx];
-            const float T = ws_decay[bh * nsplits + s];
-            ws_states[idx] = E;
-            E = fmaf(T, E, loc);
-        } else {
-            ws_states[idx] = E;
+    // Groups of splits: all loads of a group are issued before its stores
+    // (a store to ws_states could otherwise alias the next load, and each
+    // split would wait a full memory round trip).
+    constexpr int GRP = 8;
+    for (int s0 = 0; s0 < nsplits; s0 += GRP) {
+        float loc[GRP], T[GRP];
+#pragma unroll
+        for (int u = 0; u < GRP; ++u) {
+            const int s = s0 + u;
+            loc[u] = 0.f;
+            T[u] = 0.f;
+            if (s + 1 < nsplits) {
+                loc[u] = ws_states[(bh * nsplits + s) * pn + k];
+                T[u] = ws_decay[bh * nsplits + s];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < GRP; ++u) {
+            const int s = s0 + u;
+            if (s < nsplits) {
+                ws_states[(bh * nsplits + s) * pn + k] = E;
+                if (s + 1 < nsplits) E = fmaf(T[u], E, loc[u]);
+            }
         }
     }
 }
