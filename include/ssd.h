@@ -107,6 +107,13 @@ typedef struct {
  * library cannot check it. */
 #define SSD_OPT_REUSE_GROUP_OPERANDS 1
 
+/* flags (tests and benchmarks, fp32 io only; SSD_ERR_UNSUPPORTED with bf16):
+ * evaluate the intra-chunk decay mask by the dense direct segsum or by the
+ * diff segsum instead of the hierarchy-aware one (page "GPU Hierarchy Meets
+ * Structured Matrices", abstract, compares the three).  At most one. */
+#define SSD_OPT_SEGSUM_DIRECT 2
+#define SSD_OPT_SEGSUM_DIFF 4
+
 /* Bytes of device workspace ssd_fwd needs for this problem (16-byte aligned
  * pointer required).  Returns 0 when no workspace is needed, and also for an
  * invalid problem (ssd_fwd then reports the error).  The workspace holds,

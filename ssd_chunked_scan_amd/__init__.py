@@ -58,6 +58,7 @@ class Options(ctypes.Structure):
 
 
 SSD_OPT_REUSE_GROUP_OPERANDS = 1
+SSD_OPT_SEGSUM = {"hierarchy": 0, "direct": 2, "diff": 4}   # forward mask evaluation (fp32 io)
 
 
 class Fused(ctypes.Structure):
@@ -172,13 +173,13 @@ def ssd_fwd(x, dt, A, B, C, D=None, seq_idx=None, chunk_size: int = 256, init_st
             return_final_states: bool = True, split_len: int = 0, y=None, final_states=None,
             workspace=None, stream=None, reuse_group_operands: bool = False,
             dt_bias=None, dt_softplus: bool = False, dt_limit=None, z=None,
-            headdim_block: int = 0) -> Tuple[object, Optional[object]]:
+            headdim_block: int = 0, segsum: str = "hierarchy") -> Tuple[object, Optional[object]]:
     """Run the forward pass on x.device.  Returns (y, final_states or None).
     Arguments as for prepare_fwd, which this calls once."""
     call, y, final_states = _marshal_fwd(
         x, dt, A, B, C, D, seq_idx, chunk_size, init_states, return_final_states, split_len, y,
         final_states, workspace, stream, reuse_group_operands, dt_bias, dt_softplus, dt_limit, z,
-        headdim_block)
+        headdim_block, segsum)
     call()
     return y, (final_states if return_final_states else None)
 
@@ -187,7 +188,7 @@ def prepare_fwd(x, dt, A, B, C, D=None, seq_idx=None, chunk_size: int = 256, ini
                 return_final_states: bool = True, split_len: int = 0, y=None,
                 final_states=None, workspace=None, stream=None,
                 reuse_group_operands: bool = False, dt_bias=None, dt_softplus: bool = False,
-                dt_limit=None, z=None, headdim_block: int = 0):
+                dt_limit=None, z=None, headdim_block: int = 0, segsum: str = "hierarchy"):
     """Check and marshal the arguments of ssd_fwd once and return
     (launch, y, final_states): each launch() call runs the forward pass again
     on the same buffers and stream, with no per-call Python checks (for
@@ -195,15 +196,17 @@ def prepare_fwd(x, dt, A, B, C, D=None, seq_idx=None, chunk_size: int = 256, ini
     alive and unchanged in shape while it uses launch()."""
     return _marshal_fwd(x, dt, A, B, C, D, seq_idx, chunk_size, init_states, return_final_states,
                         split_len, y, final_states, workspace, stream, reuse_group_operands,
-                        dt_bias, dt_softplus, dt_limit, z, headdim_block)
+                        dt_bias, dt_softplus, dt_limit, z, headdim_block, segsum)
 
 
 def _marshal_fwd(x, dt, A, B, C, D, seq_idx, chunk_size, init_states, return_final_states,
                  split_len, y, final_states, workspace, stream, reuse_group_operands, dt_bias,
-                 dt_softplus, dt_limit, z, headdim_block=0):
+                 dt_softplus, dt_limit, z, headdim_block=0, segsum="hierarchy"):
     """Argument checks and marshalling of ssd_fwd / prepare_fwd.
     ``split_len`` forces the sequence-parallel split length (0 = planner);
-    ``headdim_block`` the headdim columns per workgroup (0 = planner).
+    ``headdim_block`` the headdim columns per workgroup (0 = planner);
+    ``segsum`` ("hierarchy", "direct" or "diff"; fp32 io only) how the
+    intra-chunk decay mask is evaluated (an ablation for tests and benchmarks).
     Preallocated ``y`` / ``final_states`` / ``workspace`` (uint8) may be given.
     ``reuse_group_operands`` (bf16) skips the per-group C B^T / B^T kernel: the
     given ``workspace`` must hold them from an earlier call with the same B, C.
@@ -251,8 +254,8 @@ def _marshal_fwd(x, dt, A, B, C, D, seq_idx, chunk_size, init_states, return_fin
         _need(final_states, "final_states", (b, H, P, N), torch.float32, dev)
     if reuse_group_operands and workspace is None:
         raise ValueError("reuse_group_operands needs the workspace of the earlier call")
-    opts = Options(split_len, SSD_OPT_REUSE_GROUP_OPERANDS if reuse_group_operands else 0,
-                   headdim_block)
+    flags = (SSD_OPT_REUSE_GROUP_OPERANDS if reuse_group_operands else 0) | SSD_OPT_SEGSUM[segsum]
+    opts = Options(split_len, flags, headdim_block)
     with torch.cuda.device(dev):
         ws_bytes = int(lib.ssd_fwd_ex_workspace_bytes(ctypes.byref(shape), chunk_size, io,
                                                       ctypes.byref(opts)))

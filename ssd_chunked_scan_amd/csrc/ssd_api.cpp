@@ -156,8 +156,12 @@ ssd_status_t check_problem(const ssd_shape_t *s, int64_t chunk, ssd_dtype_t io,
                 return fail(SSD_ERR_UNSUPPORTED, "headdim_block %lld is not usable for headdim %lld",
                             (long long)hb, (long long)s->headdim);
         }
-        if (opts->flags & ~(int64_t)SSD_OPT_REUSE_GROUP_OPERANDS)
+        const int64_t known = SSD_OPT_REUSE_GROUP_OPERANDS | SSD_OPT_SEGSUM_DIRECT | SSD_OPT_SEGSUM_DIFF;
+        if (opts->flags & ~known)
             return fail(SSD_ERR_UNSUPPORTED, "unknown option flags 0x%llx", (long long)opts->flags);
+        const int64_t seg = opts->flags & (SSD_OPT_SEGSUM_DIRECT | SSD_OPT_SEGSUM_DIFF);
+        if (seg == (SSD_OPT_SEGSUM_DIRECT | SSD_OPT_SEGSUM_DIFF) || (seg && io != SSD_F32))
+            return fail(SSD_ERR_UNSUPPORTED, "segsum variants: one at a time, fp32 io only");
         if (opts->split_len < 0 || (opts->split_len > 0 && opts->split_len % chunk != 0))
             return fail(SSD_ERR_UNSUPPORTED, "split_len %lld must be 0 or a positive multiple of chunk_size",
                         (long long)opts->split_len);
@@ -348,6 +352,8 @@ ssd_status_t ssd_fwd_fused(const ssd_shape_t *shape, ssd_dtype_t io, const void 
     a.pblock = pl.pblock;
     a.units = a.batch * a.nheads * a.nsplits * a.npblocks;
     a.half_units = (io == SSD_BF16) ? bf16_half_units(a.units, chunk_size, a.dstate, a.pblock) : 0;
+    if (opts && (opts->flags & SSD_OPT_SEGSUM_DIRECT)) a.segsum_variant = ssd::kSegsumDirect;
+    if (opts && (opts->flags & SSD_OPT_SEGSUM_DIFF)) a.segsum_variant = ssd::kSegsumDiff;
     if (fused) {
         a.dt_bias = fused->dt_bias;
         a.z = fused->z;

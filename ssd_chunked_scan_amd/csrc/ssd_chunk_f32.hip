@@ -19,11 +19,18 @@
 
 namespace ssd {
 
-template <int Q>
+// VARIANT selects how the intra-chunk mask entries are evaluated (tests and
+// benchmarks of page "GPU Hierarchy Meets Structured Matrices", abstract):
+// the hierarchy-aware segsum of the other kernels, the dense direct segsum
+// (each entry its own sum over (j, i]) or the diff segsum (2^(cs_i - cs_j)
+// from prefix sums cs of an associative scan).  Only the mask L varies; the
+// state decays u, w and T come from the same sub-block products in all three.
+template <int Q, int VARIANT>
 __global__ __launch_bounds__(kThreads, 1) void ssd_chunk_f32_kernel(ChunkArgs a) {
     constexpr int NB = Q / 16;
     constexpr int kMaxPN = 128 * 128;
     __shared__ __attribute__((aligned(16))) SegLds<Q> sg;
+    __shared__ float cs[Q];             // prefix sums (diff segsum only)
     __shared__ float sH[kMaxPN];        // state, [P][N]
     __shared__ float sM[16 * Q];        // masked strip of the diagonal block
     __shared__ float sRowF[16 * NB];    // F(i, J) of the strip's rows
@@ -74,11 +81,22 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_chunk_f32_kernel(ChunkArgs a)
         __syncthreads();
         if (tid < Q) seg_chunk_products<Q>(sg, tid);
         __syncthreads();
+        if constexpr (VARIANT == kSegsumDiff) {
+            // inclusive prefix sums of the log2-decays by a Kogge-Stone scan
+            if (tid < Q) cs[tid] = sg.d[tid];
+            __syncthreads();
+            for (int off = 1; off < Q; off *= 2) {
+                const float v = (tid < Q && tid >= off) ? cs[tid - off] : 0.f;
+                __syncthreads();
+                if (tid < Q && tid >= off) cs[tid] = __fadd_rn(cs[tid], v);
+                __syncthreads();
+            }
+        }
 
         if (full) {
             for (int I = 0; I < NB; ++I) {
                 const int I0 = I * 16;
-                if (tid < 16) {
+                if (VARIANT == kSegsumHierarchy && tid < 16) {
                     const int i = I0 + tid;
                     const int rs_i = sg.rs[i];
                     float e[4];
@@ -101,9 +119,18 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_chunk_f32_kernel(ChunkArgs a)
                     const int i = I0 + ii;
                     float v = 0.f;
                     if (i < nvalid && j <= i) {
-                        const int J = j >> 4;
-                        const float Lij = (J == I) ? sRowD[ii * 16 + (j & 15)]
-                                                   : seg_offdiag(sRowF[ii * NB + J], sg.W[j]);
+                        float Lij;
+                        if constexpr (VARIANT == kSegsumDirect) {
+                            float run = 0.f;
+                            for (int k = j + 1; k <= i; ++k) run = __fadd_rn(run, sg.d[k]);
+                            Lij = (sg.rs[i] > j) ? 0.f : __builtin_amdgcn_exp2f(run);
+                        } else if constexpr (VARIANT == kSegsumDiff) {
+                            Lij = (sg.rs[i] > j) ? 0.f : __builtin_amdgcn_exp2f(__fsub_rn(cs[i], cs[j]));
+                        } else {
+                            const int J = j >> 4;
+                            Lij = (J == I) ? sRowD[ii * 16 + (j & 15)]
+                                           : seg_offdiag(sRowF[ii * NB + J], sg.W[j]);
+                        }
                         const float *ci = crow(t0 + i), *bj = brow(t0 + j);
                         float dot = 0.f;
                         for (int n = 0; n < N; ++n) dot = fmaf(ci[n], bj[n], dot);
@@ -155,12 +182,21 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_chunk_f32_kernel(ChunkArgs a)
         for (int e = tid; e < PN; e += kThreads) dst[e] = sH[e];
 }
 
-void launch_chunk_f32(int Q, const ChunkArgs &a, hipStream_t stream) {
+template <int VARIANT>
+static void launch_chunk_f32_v(int Q, const ChunkArgs &a, hipStream_t stream) {
     const dim3 grid(a.units), block(kThreads);
     switch (Q) {
-    case 64: hipLaunchKernelGGL(ssd_chunk_f32_kernel<64>, grid, block, 0, stream, a); break;
-    case 128: hipLaunchKernelGGL(ssd_chunk_f32_kernel<128>, grid, block, 0, stream, a); break;
-    default: hipLaunchKernelGGL(ssd_chunk_f32_kernel<256>, grid, block, 0, stream, a); break;
+    case 64: hipLaunchKernelGGL((ssd_chunk_f32_kernel<64, VARIANT>), grid, block, 0, stream, a); break;
+    case 128: hipLaunchKernelGGL((ssd_chunk_f32_kernel<128, VARIANT>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((ssd_chunk_f32_kernel<256, VARIANT>), grid, block, 0, stream, a); break;
+    }
+}
+
+void launch_chunk_f32(int Q, const ChunkArgs &a, hipStream_t stream) {
+    switch (a.segsum_variant) {
+    case kSegsumDirect: launch_chunk_f32_v<kSegsumDirect>(Q, a, stream); break;
+    case kSegsumDiff: launch_chunk_f32_v<kSegsumDiff>(Q, a, stream); break;
+    default: launch_chunk_f32_v<kSegsumHierarchy>(Q, a, stream); break;
     }
 }
 

@@ -56,6 +56,7 @@ struct ChunkArgs {
     int dt_softplus;           // nonzero: dt <- softplus(dt)
     int dt_clamp;              // nonzero: dt <- min(max(dt, dt_lo), dt_hi)
     float dt_lo, dt_hi;
+    int segsum_variant;        // SegsumVariant of the intra-chunk mask (fp32 kernel only)
 };
 
 // Map from a raw per-token value to the step size dt of one head: plus the

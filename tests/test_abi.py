@@ -85,9 +85,14 @@ def test_argument_errors():
     o = ssd.Options(256)
     o.reserved[3] = 1
     assert _fwd(s, opts=o) == 3
-    o = ssd.Options(0, 2)             # unknown flag bit
+    o = ssd.Options(0, 8)             # unknown flag bit
     assert _fwd(s, opts=o) == 3
     assert b"flags" in ssd.load_library().ssd_last_error()
+    # segsum variants of the forward mask: fp32 io only, one at a time
+    assert _fwd(s, io=1, opts=ssd.Options(0, 2)) == 3
+    assert b"segsum" in ssd.load_library().ssd_last_error()
+    assert _fwd(s, io=0, opts=ssd.Options(0, 6)) == 3
+    assert _fwd(s, io=0, opts=ssd.Options(0, 4)) == 5   # accepted: reaches the workspace check
     o = ssd.Options(256)              # 4 splits -> workspace required
     assert _fwd(s, opts=o) == 5
     assert b"workspace" in ssd.load_library().ssd_last_error()
