@@ -26,12 +26,18 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 METRIC = "SSD fwd tokens/s + HBM GB/s (% of peak), Mamba-2 2.7B layer, L=2048"
+HEAD_KERNEL_SOURCES = ("ssd_api.cpp", "ssd_common.hpp", "ssd_scan_bf16.hpp", "ssd_scan_bf16_q64.hip",
+                       "ssd_scan_bf16_q128.hip", "ssd_scan_bf16_q256.hip", "ssd_segsum.hpp",
+                       "ssd_tiles.hpp")
+
+
 def kernel_source_digest() -> str:
-    """Digest of every kernel source (the counters are only valid for it)."""
+    """Digest of the sources that define the bf16 head kernel and its launch
+    (the counters are only valid for them)."""
     csrc = os.path.join(ROOT, "ssd_chunked_scan_amd", "csrc")
     h = hashlib.sha256()
     for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".hpp", ".cpp")):
+        if f in HEAD_KERNEL_SOURCES:
             h.update(f.encode())
             with open(os.path.join(csrc, f), "rb") as fh:
                 h.update(fh.read())
