@@ -26,6 +26,9 @@ Contents
                      clamped to [lo, hi].
   gate(...)          the element-wise output gate y * silu(z), silu(z) =
                      z / (1 + e^-z).
+  ssd_backward(...)  gradients of the forward pass w.r.t. every input, by
+                     reverse-mode differentiation of the same recurrence
+                     (fp64, small inputs).
   ssd_forward_fused(...)  dt_prologue, then ssd_forward, then gate: the scan
                      with the lightweight element-wise work around it that
                      page "NVIDIA Accelerates Mamba-2 Forward Kernel with
@@ -235,3 +238,77 @@ def ssd_forward_fused(x, dt_raw, A, B, C, D=None, seq_idx=None, init_states=None
     if z is not None:
         y = gate(y, z)
     return y, fs
+
+
+def ssd_backward(x, dt, A, B, C, D, dy, seq_idx=None, init_states=None, dfinal=None):
+    """Gradients of the forward pass, fp64, by reverse-mode differentiation of
+    the recurrence (what a backward pass computes; pure-Python loop over
+    tokens, small inputs only).
+
+    With y, final_states = ssd_forward(x, dt, A, B, C, D, seq_idx, init_states)
+    and the scalar J = <dy, y> + <dfinal, final_states> (dfinal None = 0),
+    returns a dict of dJ/d(input): dx [b,L,H,P], ddt [b,L,H], dA [H],
+    dB, dC [b,L,G,N], dD [H] (None if D is None), dinit [b,H,P,N] (None if
+    init_states is None).  The recurrence is the one of ssd_forward: with
+    a_t = exp(dt_t A_h), set to 0 where a document starts (page "Parallel
+    Scan and Hardware-Aware SSM Kernels", "When it breaks": no gradient flows
+    through a reset), h_t = a_t h_{t-1} + dt_t x_t B_t^T and
+    y_t = h_t C_t + D_h x_t (page "State Space Duality and Mamba-2", "The
+    Mathematical Bridge").  Walking t from the end: g_t = dJ/dh_t collects
+    dy_t C_t^T, feeds dx_t, dB_t, ddt_t through the input term and
+    dJ/da_t = <g_t, h_{t-1}> through the decay (a_t A_h into ddt_t,
+    a_t dt_t into dA_h), then g_{t-1} = a_t g_t."""
+    x = np.asarray(x, dtype=np.float64)
+    dt = np.asarray(dt, dtype=np.float64)
+    A = np.asarray(A, dtype=np.float64)
+    B = np.asarray(B, dtype=np.float64)
+    C = np.asarray(C, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    hpg = H // G
+    grp = np.arange(H) // hpg
+    Bh = B[:, :, grp, :]                                   # [b, L, H, N]
+    Ch = C[:, :, grp, :]
+    a = np.exp(dt * A[None, None, :])                      # [b, L, H]
+    if seq_idx is not None:
+        si = np.asarray(seq_idx)
+        reset = np.zeros((b, L), dtype=bool)
+        reset[:, 1:] = si[:, 1:] != si[:, :-1]
+        a = np.where(reset[:, :, None], 0.0, a)
+    h0 = (np.zeros((b, H, P, N)) if init_states is None
+          else np.asarray(init_states, dtype=np.float64).copy())
+    # forward, keeping every state
+    hs = np.empty((b, L, H, P, N))
+    h = h0.copy()
+    for t in range(L):
+        h = a[:, t, :, None, None] * h + (dt[:, t, :, None, None] * x[:, t, :, :, None]) * Bh[:, t, :, None, :]
+        hs[:, t] = h
+    # reverse
+    g = np.zeros((b, H, P, N)) if dfinal is None else np.asarray(dfinal, dtype=np.float64).copy()
+    dx = np.zeros_like(x)
+    ddt = np.zeros_like(dt)
+    dA = np.zeros(H)
+    dBh = np.zeros((b, L, H, N))
+    dCh = np.zeros((b, L, H, N))
+    for t in range(L - 1, -1, -1):
+        g = g + dy[:, t, :, :, None] * Ch[:, t, :, None, :]                   # y_t = h_t C_t
+        dCh[:, t] = np.einsum("bhpn,bhp->bhn", hs[:, t], dy[:, t])
+        gB = np.einsum("bhpn,bhn->bhp", g, Bh[:, t])                           # g_t B_t
+        dx[:, t] = dt[:, t, :, None] * gB
+        dBh[:, t] = dt[:, t, :, None] * np.einsum("bhpn,bhp->bhn", g, x[:, t])
+        ddt[:, t] = np.einsum("bhp,bhp->bh", gB, x[:, t])                      # input term
+        hprev = hs[:, t - 1] if t > 0 else h0
+        ga = np.einsum("bhpn,bhpn->bh", g, hprev) * a[:, t]                   # dJ/da_t * a_t
+        ddt[:, t] += ga * A[None, :]
+        dA += (ga * dt[:, t]).sum(axis=0)
+        g = a[:, t, :, None, None] * g                                         # dJ/dh_{t-1}
+    dD = None
+    if D is not None:
+        D = np.asarray(D, dtype=np.float64)
+        dx += D[None, None, :, None] * dy
+        dD = np.einsum("blhp,blhp->h", dy, x)
+    dB = dBh.reshape(b, L, G, hpg, N).sum(axis=3)
+    dC = dCh.reshape(b, L, G, hpg, N).sum(axis=3)
+    return {"dx": dx, "ddt": ddt, "dA": dA, "dB": dB, "dC": dC, "dD": dD,
+            "dinit": None if init_states is None else g}
