@@ -262,6 +262,31 @@ ssd_status_t ssd_decode_step_fused(const ssd_shape_t *shape, ssd_dtype_t io,
                                    float *state, void *y, const ssd_fused_t *fused,
                                    void *stream);
 
+/* Backward pass: the gradients of J = <dy, y> + <dfinal, final_states> with
+ * respect to every input of ssd_fwd (same shapes and layouts, no fused
+ * prologue/epilogue), i.e. what training needs from this layer.  The method
+ * differentiates the chunked decomposition of page "State Space Duality and
+ * Mamba-2" ("The SSD Block Decomposition Algorithm"): the chunk-entering
+ * states come from the forward pass's split-local pass and affine scan with
+ * one split per 64-token chunk, then one reverse walk over the chunks per
+ * (batch row, head) carries the adjoint of the state (fp32, vector ALU).
+ *   dy [b, L, H, P] io dtype, 16-byte aligned; dfinal [b, H, P, N] fp32 or NULL;
+ *   outputs, all fp32: dx [b, L, H, P], ddt [b, L, H], dA [H], dB and dC
+ *   [b, L, G, N], dD [H] (NULL exactly when D is NULL), dinit [b, H, P, N]
+ *   (NULL, or the gradient of init_states, which must then be given).
+ * Supported set and errors as ssd_fwd (chunk 64 internally); the workspace
+ * (ssd_bwd_workspace_bytes) is the forward's for 64-token splits plus
+ * 8 b L H N + 8 b H bytes. */
+size_t ssd_bwd_workspace_bytes(const ssd_shape_t *shape, ssd_dtype_t io);
+ssd_status_t ssd_bwd(const ssd_shape_t *shape, ssd_dtype_t io,
+                     const void *x, const float *dt, const float *A,
+                     const void *B, const void *C, const float *D,
+                     const int32_t *seq_idx, const float *init_states,
+                     const void *dy, const float *dfinal,
+                     float *dx, float *ddt, float *dA, float *dB, float *dC,
+                     float *dD, float *dinit,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
 const char *ssd_status_str(ssd_status_t status);
 
 /* Detail of the last failure on the calling thread ("" if none). */

@@ -19,7 +19,7 @@ import os
 from typing import Optional, Tuple
 
 __all__ = [
-    "ssd_fwd", "prepare_fwd", "ssd_fwd_workspace_bytes", "ssd_plan_split_len", "ssd_debug_chunk_mask",
+    "ssd_fwd", "prepare_fwd", "ssd_bwd", "ssd_fwd_workspace_bytes", "ssd_plan_split_len", "ssd_debug_chunk_mask",
     "ssd_decode_step",
     "SsdError", "library_path", "load_library", "STATUS", "EXPORTS",
 ]
@@ -34,8 +34,8 @@ EXPORTS = ["ssd_fwd_workspace_bytes", "ssd_fwd", "ssd_fwd_ex_workspace_bytes", "
            "ssd_fwd_fused",
            "ssd_plan_split_len", "ssd_plan_headdim_block", "ssd_debug_chunk_mask",
            "ssd_debug_chunk_mask_ex",
-           "ssd_decode_step", "ssd_decode_step_fused", "ssd_status_str", "ssd_last_error",
-           "ssd_version"]
+           "ssd_decode_step", "ssd_decode_step_fused", "ssd_bwd_workspace_bytes", "ssd_bwd",
+           "ssd_status_str", "ssd_last_error", "ssd_version"]
 # segsum evaluations of the mask export (ssd.h SSD_SEGSUM_*)
 SEGSUM = {"hierarchy": 0, "direct": 1, "diff": 2}
 
@@ -110,6 +110,10 @@ def load_library():
     lib.ssd_decode_step_fused.argtypes = [shp, i32, vp, vp, vp, vp, vp, vp, vp, vp,
                                           ctypes.POINTER(Fused), vp]
     lib.ssd_decode_step_fused.restype = i32
+    lib.ssd_bwd_workspace_bytes.argtypes = [shp, i32]
+    lib.ssd_bwd_workspace_bytes.restype = sz
+    lib.ssd_bwd.argtypes = [shp, i32] + [vp] * 18 + [sz, vp]
+    lib.ssd_bwd.restype = i32
     lib.ssd_status_str.argtypes = [i32]
     lib.ssd_status_str.restype = ctypes.c_char_p
     lib.ssd_last_error.argtypes = []
@@ -357,3 +361,52 @@ def ssd_decode_step(x, dt, A, B, C, D, state, y=None, stream=None, dt_bias=None,
                                        ctypes.byref(fused), stream)
     _check(st)
     return y
+
+
+def ssd_bwd(x, dt, A, B, C, D, dy, seq_idx=None, init_states=None, dfinal=None, stream=None):
+    """Gradients of J = <dy, y> + <dfinal, final_states> for y, final_states =
+    ssd_fwd(x, dt, A, B, C, D, seq_idx, init_states=init_states): returns a
+    dict of fp32 tensors dx, ddt, dA, dB, dC, dD (None if D is None) and
+    dinit (None if init_states is None).  dy has x's dtype; dfinal is fp32
+    [b, H, P, N] or None."""
+    import torch
+    lib = load_library()
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("ssd_bwd runs on the GPU only (x is on %s)" % dev)
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    io = _io_code(x.dtype)
+    _need(x, "x", (b, L, H, P), x.dtype, dev)
+    _need(dy, "dy", (b, L, H, P), x.dtype, dev)
+    _need(dt, "dt", (b, L, H), torch.float32, dev)
+    _need(A, "A", (H,), torch.float32, dev)
+    _need(B, "B", (b, L, G, N), x.dtype, dev)
+    _need(C, "C", (b, L, G, N), x.dtype, dev)
+    if D is not None:
+        _need(D, "D", (H,), torch.float32, dev)
+    if seq_idx is not None:
+        _need(seq_idx, "seq_idx", (b, L), torch.int32, dev)
+    if init_states is not None:
+        _need(init_states, "init_states", (b, H, P, N), torch.float32, dev)
+    if dfinal is not None:
+        _need(dfinal, "dfinal", (b, H, P, N), torch.float32, dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = {"dx": torch.empty((b, L, H, P), **f32), "ddt": torch.empty((b, L, H), **f32),
+           "dA": torch.empty((H,), **f32), "dB": torch.empty((b, L, G, N), **f32),
+           "dC": torch.empty((b, L, G, N), **f32),
+           "dD": None if D is None else torch.empty((H,), **f32),
+           "dinit": None if init_states is None else torch.empty((b, H, P, N), **f32)}
+    shape = Shape(b, L, H, P, N, G)
+    with torch.cuda.device(dev):
+        ws_bytes = int(lib.ssd_bwd_workspace_bytes(ctypes.byref(shape), io))
+        ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+        if stream is None:
+            stream = torch.cuda.current_stream(dev).cuda_stream
+        st = lib.ssd_bwd(ctypes.byref(shape), io, _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+                         _ptr(D), _ptr(seq_idx), _ptr(init_states), _ptr(dy), _ptr(dfinal),
+                         _ptr(out["dx"]), _ptr(out["ddt"]), _ptr(out["dA"]), _ptr(out["dB"]),
+                         _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dinit"]), _ptr(ws), ws_bytes,
+                         stream)
+    _check(st)
+    return out

@@ -20,6 +20,7 @@ bool launch_scan_bf16_q256(int N, int PB, const ChunkArgs &a, hipStream_t stream
 bool launch_cb(int Q, int N, const CbArgs &a, hipStream_t stream);
 size_t cb_s_elems(int Q);
 void launch_chunk_f32(int Q, const ChunkArgs &a, hipStream_t stream);
+void launch_bwd(bool bf16_io, const BwdArgs &a, hipStream_t stream);
 void launch_split_scan(const float *init_states, float *ws_states, const float *ws_decay,
                        int batch, int nheads, int nsplits, int pn, hipStream_t stream);
 void launch_mask(int Q, const MaskArgs &m, hipStream_t stream);
@@ -287,21 +288,28 @@ int64_t ssd_plan_headdim_block(const ssd_shape_t *shape, int64_t chunk_size, ssd
     return pl.pblock;
 }
 
-ssd_status_t ssd_fwd_fused(const ssd_shape_t *shape, ssd_dtype_t io, const void *x, const float *dt,
-                           const float *A, const void *B, const void *C, const float *D,
-                           const int32_t *seq_idx, int64_t chunk_size, const float *init_states,
-                           void *y, float *final_states, const ssd_fused_t *fused,
-                           void *workspace, size_t workspace_bytes, const ssd_options_t *opts,
-                           void *stream) {
-    g_last_error.clear();
+}  // extern "C"
+
+namespace {
+
+// The forward pass; with states_only, only what gives every split its
+// entering state (per-group operands, split-local pass, affine scan): the
+// outputs are not computed and y may be NULL (the backward pass uses this
+// with one split per chunk).
+ssd_status_t fwd_impl(const ssd_shape_t *shape, ssd_dtype_t io, const void *x, const float *dt,
+                      const float *A, const void *B, const void *C, const float *D,
+                      const int32_t *seq_idx, int64_t chunk_size, const float *init_states,
+                      void *y, float *final_states, const ssd_fused_t *fused,
+                      void *workspace, size_t workspace_bytes, const ssd_options_t *opts,
+                      void *stream, bool states_only) {
     ssd_status_t st = check_problem(shape, chunk_size, io, opts);
     if (st != SSD_OK) return st;
     st = check_fused(fused, 16);
     if (st != SSD_OK) return st;
-    if (!x || !dt || !A || !B || !C || !y)
+    if (!x || !dt || !A || !B || !C || (!y && !states_only))
         return fail(SSD_ERR_NULL, "x, dt, A, B, C and y are required");
     const size_t io_align = 16;
-    if (!aligned(x, io_align) || !aligned(B, io_align) || !aligned(C, io_align) || !aligned(y, io_align))
+    if (!aligned(x, io_align) || !aligned(B, io_align) || !aligned(C, io_align) || (y && !aligned(y, io_align)))
         return fail(SSD_ERR_ALIGN, "x, B, C and y must be 16-byte aligned");
     if (!aligned(dt, 4) || !aligned(A, 4) || (D && !aligned(D, 4)) || (seq_idx && !aligned(seq_idx, 4)))
         return fail(SSD_ERR_ALIGN, "dt, A, D and seq_idx must be 4-byte aligned");
@@ -404,10 +412,120 @@ ssd_status_t ssd_fwd_fused(const ssd_shape_t *shape, ssd_dtype_t io, const void 
         e = hipGetLastError();
         if (e != hipSuccess) return fail(SSD_ERR_HIP, "split-scan launch: %s", hipGetErrorString(e));
     }
+    if (states_only) return SSD_OK;
     a.mode = ssd::kModeFull;
     if (!launch(a)) return fail(SSD_ERR_UNSUPPORTED, "no kernel for this shape");
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(SSD_ERR_HIP, "chunk launch: %s", hipGetErrorString(e));
+    return SSD_OK;
+}
+
+// Backward workspace: the forward's (one split per 64-token chunk), then the
+// per-head dB and dC and the per-row dA and dD partial sums.
+struct BwdPlan {
+    Plan fwd;
+    size_t dbh_bytes, part_bytes, ws_bytes;
+};
+
+ssd_status_t make_bwd_plan(const ssd_shape_t *s, ssd_dtype_t io, BwdPlan *bp) {
+    ssd_options_t o;
+    memset(&o, 0, sizeof(o));
+    o.split_len = ssd::kBwdQ;
+    ssd_status_t st = make_plan(s, ssd::kBwdQ, io, &o, &bp->fwd);
+    if (st != SSD_OK) return st;
+    bp->dbh_bytes = round_up((size_t)s->batch * s->seqlen * s->nheads * s->dstate * sizeof(float), 256);
+    bp->part_bytes = round_up((size_t)s->batch * s->nheads * sizeof(float), 256);
+    bp->ws_bytes = bp->fwd.ws_bytes + 2 * bp->dbh_bytes + 2 * bp->part_bytes;
+    return SSD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ssd_status_t ssd_fwd_fused(const ssd_shape_t *shape, ssd_dtype_t io, const void *x, const float *dt,
+                           const float *A, const void *B, const void *C, const float *D,
+                           const int32_t *seq_idx, int64_t chunk_size, const float *init_states,
+                           void *y, float *final_states, const ssd_fused_t *fused,
+                           void *workspace, size_t workspace_bytes, const ssd_options_t *opts,
+                           void *stream) {
+    g_last_error.clear();
+    return fwd_impl(shape, io, x, dt, A, B, C, D, seq_idx, chunk_size, init_states, y, final_states,
+                    fused, workspace, workspace_bytes, opts, stream, false);
+}
+
+size_t ssd_bwd_workspace_bytes(const ssd_shape_t *shape, ssd_dtype_t io) {
+    BwdPlan bp;
+    if (make_bwd_plan(shape, io, &bp) != SSD_OK) return 0;
+    return bp.ws_bytes;
+}
+
+ssd_status_t ssd_bwd(const ssd_shape_t *shape, ssd_dtype_t io, const void *x, const float *dt,
+                     const float *A, const void *B, const void *C, const float *D,
+                     const int32_t *seq_idx, const float *init_states, const void *dy,
+                     const float *dfinal, float *dx, float *ddt, float *dA, float *dB, float *dC,
+                     float *dD, float *dinit, void *workspace, size_t workspace_bytes,
+                     void *stream) {
+    g_last_error.clear();
+    BwdPlan bp;
+    ssd_status_t st = make_bwd_plan(shape, io, &bp);
+    if (st != SSD_OK) return st;
+    if (!x || !dt || !A || !B || !C || !dy || !dx || !ddt || !dA || !dB || !dC)
+        return fail(SSD_ERR_NULL, "x, dt, A, B, C, dy, dx, ddt, dA, dB and dC are required");
+    if ((D == nullptr) != (dD == nullptr)) return fail(SSD_ERR_NULL, "D and dD go together");
+    if (dinit && !init_states) return fail(SSD_ERR_NULL, "dinit needs init_states");
+    const size_t esz = io == SSD_BF16 ? 2 : 4;
+    if (!aligned(dy, 16)) return fail(SSD_ERR_ALIGN, "dy must be 16-byte aligned");
+    if (!aligned(dx, 4) || !aligned(ddt, 4) || !aligned(dA, 4) || !aligned(dB, 4) || !aligned(dC, 4) ||
+        (dD && !aligned(dD, 4)) || (dinit && !aligned(dinit, 4)) || (dfinal && !aligned(dfinal, 4)))
+        return fail(SSD_ERR_ALIGN, "gradient buffers and dfinal must be 4-byte aligned");
+    (void)esz;
+    if (!workspace || workspace_bytes < bp.ws_bytes)
+        return fail(SSD_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given%s", bp.ws_bytes,
+                    workspace_bytes, workspace ? "" : " (NULL)");
+    if (!aligned(workspace, 16)) return fail(SSD_ERR_ALIGN, "workspace must be 16-byte aligned");
+    ssd_options_t o;
+    memset(&o, 0, sizeof(o));
+    o.split_len = ssd::kBwdQ;
+    st = fwd_impl(shape, io, x, dt, A, B, C, D, seq_idx, ssd::kBwdQ, init_states, nullptr, nullptr,
+                  nullptr, workspace, bp.fwd.ws_bytes, &o, stream, true);
+    if (st != SSD_OK) return st;
+    char *wsb = (char *)workspace + bp.fwd.ws_bytes;
+    ssd::BwdArgs a;
+    memset(&a, 0, sizeof(a));
+    a.x = x;
+    a.B = B;
+    a.C = C;
+    a.dy = dy;
+    a.dt = dt;
+    a.A = A;
+    a.D = D;
+    a.seq_idx = seq_idx;
+    a.states = bp.fwd.nsplits > 1 ? (const float *)workspace : nullptr;
+    a.init_states = init_states;
+    a.dfinal = dfinal;
+    a.dx = dx;
+    a.ddt = ddt;
+    a.dB_head = (float *)wsb;
+    a.dC_head = (float *)(wsb + bp.dbh_bytes);
+    a.dA_part = (float *)(wsb + 2 * bp.dbh_bytes);
+    a.dD_part = (float *)(wsb + 2 * bp.dbh_bytes + bp.part_bytes);
+    a.dB = dB;
+    a.dC = dC;
+    a.dA = dA;
+    a.dD = dD;
+    a.dinit = dinit;
+    a.batch = (int)shape->batch;
+    a.seqlen = (int)shape->seqlen;
+    a.nheads = (int)shape->nheads;
+    a.headdim = (int)shape->headdim;
+    a.dstate = (int)shape->dstate;
+    a.ngroups = (int)shape->ngroups;
+    a.nchunks = bp.fwd.nchunks;
+    (void)hipGetLastError();
+    ssd::launch_bwd(io == SSD_BF16, a, (hipStream_t)stream);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(SSD_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
     return SSD_OK;
 }
 

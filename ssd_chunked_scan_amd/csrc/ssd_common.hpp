@@ -157,6 +157,23 @@ struct DecodeArgs {
     float dt_lo, dt_hi;
 };
 
+// Arguments of the backward pass (fp32 gradients).
+constexpr int kBwdQ = 64;   // tokens per backward chunk (= the states' split length)
+struct BwdArgs {
+    const void *x, *B, *C, *dy;       // io dtype
+    const float *dt, *A, *D;          // D nullable
+    const int32_t *seq_idx;           // nullable
+    const float *states;              // [batch][nheads][nchunks][headdim][dstate] entering states,
+                                      // nullable when there is one chunk
+    const float *init_states;         // nullable
+    const float *dfinal;              // nullable
+    float *dx, *ddt;                  // [b][L][H][P], [b][L][H]
+    float *dB_head, *dC_head;         // [b][L][H][N] workspace
+    float *dA_part, *dD_part;         // [b][H] workspace
+    float *dB, *dC, *dA, *dD, *dinit; // dD, dinit nullable
+    int batch, seqlen, nheads, headdim, dstate, ngroups, nchunks;
+};
+
 struct Unit {
     int b, h, s, pb;
     int half;   // -1: the whole headdim block; 0 or 1: that half of it

@@ -250,3 +250,17 @@ def test_plan_queries():
     assert ssd.ssd_plan_split_len(s, 256, 1) == 2048
     assert ssd.ssd_plan_headdim_block(s, 256, 0) == 64
     assert lib.ssd_plan_headdim_block(None, 256, 1) == 0
+
+
+def test_binding_argument_counts_match_the_header():
+    """Every function the binding declares takes as many arguments as ssd.h
+    gives it (a short argtypes list would pass trailing pointers as 32-bit
+    ints)."""
+    src = open(os.path.join(ROOT, "include", "ssd.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    lib = ssd.load_library()
+    for name, params in re.findall(r"\b(ssd_[a-z0-9_]+)\s*\(([^;{]*?)\)\s*;", src):
+        n = 0 if params.strip() in ("", "void") else params.count(",") + 1
+        argtypes = getattr(lib, name).argtypes
+        assert argtypes is not None, name
+        assert len(argtypes) == n, f"{name}: header {n} parameters, binding {len(argtypes)}"
