@@ -164,6 +164,51 @@ def decode_step_bench(wl, inp, args):
                      "frac": gbs / 8000.0, "bytes_per_launch": nbytes}}), flush=True)
 
 
+def backward_bench(wl, inp, args):
+    """One JSON line: the backward pass (ssd_bwd) at the workload's sizes,
+    per-launch time with HIP events on its stream; roofline against HBM with
+    the algorithmic bytes of the gradients' inputs and outputs (x, dy, B, C,
+    dt, D read; dx, ddt, dB, dC written in fp32; the entering states the
+    pass writes and reads once each)."""
+    import numpy as np
+    import torch
+    import ssd_chunked_scan_amd as ssd
+    dev = torch.device("cuda:0")
+    io = torch.bfloat16 if wl.io == "bf16" else torch.float32
+    t = lambda a, d=torch.float32: torch.from_numpy(a).to(dev).to(d).contiguous()
+    x, dt, A, B, C, D = t(inp.x, io), t(inp.dt), t(inp.A), t(inp.B, io), t(inp.C, io), t(inp.D)
+    dy = t(np.random.default_rng(1).standard_normal(inp.x.shape).astype(np.float32), io)
+    for _ in range(args.warmup):
+        ssd.ssd_bwd(x, dt, A, B, C, D, dy)
+    torch.cuda.synchronize(dev)
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        ssd.ssd_bwd(x, dt, A, B, C, D, dy)
+        e1.record(stream)
+    torch.cuda.synchronize(dev)
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    avg = sum(ms) / len(ms)
+    b, L, H, P, N, G = wl.batch, wl.seqlen, wl.nheads, wl.headdim, wl.dstate, wl.ngroups
+    esz = 2 if wl.io == "bf16" else 4
+    nch = (L + 63) // 64
+    alg = (2 * b * L * H * P * esz + 2 * b * L * G * N * esz + b * L * H * 4     # x, dy, B, C, dt
+           + b * L * H * P * 4 + b * L * H * 4 + 2 * b * L * G * N * 4          # dx, ddt, dB, dC
+           + 2 * b * H * nch * P * N * 4)                                       # states
+    gbs = alg / (avg * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "SSD backward time per launch", "unit": "us", "value": avg * 1e3,
+        "higher_is_better": False, "steps": args.steps, "warmup": args.warmup, "dtype": wl.io,
+        "data": "synthetic", "tokens_per_s": wl.tokens / (avg * 1e-3),
+        "config": {"workload": wl.name, "batch": b, "seqlen": L, "nheads": H, "headdim": P,
+                   "dstate": N, "ngroups": G, "backward_chunk": 64},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": alg},
+        "p10_us": ms[len(ms) // 10] * 1e3, "p90_us": ms[(9 * len(ms)) // 10] * 1e3}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -178,6 +223,8 @@ def main():
                     help="instead of the forward pass: time the three segsum evaluations of the "
                          "decay mask (hierarchy-aware, dense direct, prefix difference) on the "
                          "workload's dt and A, every chunk, mask evaluated but not written")
+    ap.add_argument("--backward", action="store_true",
+                    help="instead of the forward pass: time the backward pass (ssd_bwd)")
     ap.add_argument("--fused", action="store_true",
                     help="time the forward pass with the fused prologue (raw dt + bias, softplus) "
                          "and the silu(z) output gate; z counts as algorithmic bytes")
@@ -201,6 +248,9 @@ def main():
         return
     if args.decode:
         decode_step_bench(wl, inp, args)
+        return
+    if args.backward:
+        backward_bench(wl, inp, args)
         return
     dev = torch.device("cuda:0")
     io = torch.bfloat16 if wl.io == "bf16" else torch.float32
