@@ -35,15 +35,21 @@ __device__ inline float bwd_ld(const void *p, int64_t i) {
     return (float)((const IO *)p)[i];
 }
 
+// 16 waves: one workgroup fills a CU (its LDS allows one per CU), so that
+// four waves per SIMD cover the latency of the global-memory operands.
+constexpr int kBwdThreads = 1024;
+
 template <typename IO>
-__global__ __launch_bounds__(kThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
     constexpr int Q = kBwdQ, NB = Q / 16;
+    constexpr int LQ = Q + 1;               // padded row pitch: a lane per row hits its own bank
     constexpr int kMaxPN = 128 * 128;
     __shared__ __attribute__((aligned(16))) SegLds<Q> sg;
     __shared__ float sG[kMaxPN];           // adjoint of the state at the chunk end, [P][N]
-    __shared__ float sL[Q * Q];             // decay mask L[i][j]
-    __shared__ float sS[Q * Q];             // (C B^T)[i][j]
-    __shared__ float sR[Q * Q];             // V[i][j] = dy_i . x_j, then R, then row prefix sums of R
+    __shared__ float sL[Q * LQ];            // decay mask L[i][j]
+    __shared__ float sS[Q * LQ];            // (C B^T)[i][j]
+    __shared__ float sR[Q * LQ];            // V[i][j] = dy_i . x_j, then R, then row prefix sums of R
+    __shared__ float sT[Q * 129];           // staged rows of B, then of x (pitch +1)
     __shared__ float sw[Q];                 // decay from token j to the chunk end
     __shared__ float sq[Q], sp[Q], sxdX[Q], sdl[Q];
     __shared__ float sK, sDD, sDA;
@@ -63,7 +69,7 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
     auto Bi = [&](int t, int n) { return bwd_ld<IO>(a.B, (((int64_t)b * L + t) * G + grp) * N + n); };
     auto Ci = [&](int t, int n) { return bwd_ld<IO>(a.C, (((int64_t)b * L + t) * G + grp) * N + n); };
 
-    for (int e = tid; e < PN; e += kThreads)
+    for (int e = tid; e < PN; e += kBwdThreads)
         sG[e] = a.dfinal ? a.dfinal[(int64_t)bh * PN + e] : 0.f;
     if (tid == 0) {
         sDD = 0.f;
@@ -110,63 +116,100 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
             for (int j = i; j >= 0; --j) {
                 float v = (sg.rs[i] > j) ? 0.f : __builtin_amdgcn_exp2f(sum);
                 if (i >= nvalid) v = 0.f;
-                sL[i * Q + j] = v;
+                sL[i * LQ + j] = v;
                 sum = __fadd_rn(sum, sg.d[j]);
             }
-            for (int j = i + 1; j < Q; ++j) sL[i * Q + j] = 0.f;
+            for (int j = i + 1; j < Q; ++j) sL[i * LQ + j] = 0.f;
         }
-        for (int e = tid; e < Q * Q; e += kThreads) {
+        // S = C B^T with B's rows staged in LDS (the lanes of a wave take
+        // different j), then V = dY X^T with x's rows staged in the same place
+        for (int e = tid; e < Q * N; e += kBwdThreads) {
+            const int j = e / N, n = e % N;
+            sT[j * (N + 1) + n] = (j < nvalid) ? Bi(t0 + j, n) : 0.f;
+        }
+        __syncthreads();
+        for (int e = tid; e < Q * Q; e += kBwdThreads) {
             const int i = e / Q, j = e % Q;
-            float s = 0.f, v = 0.f;
-            if (j <= i && i < nvalid) {
-                for (int n = 0; n < N; ++n) s = fmaf(Ci(t0 + i, n), Bi(t0 + j, n), s);
-                for (int p = 0; p < P; ++p) v = fmaf(dyi(t0 + i, p), xi(t0 + j, p), v);
-            }
-            sS[e] = s;
-            sR[e] = v;
+            float s = 0.f;
+            if (j <= i && i < nvalid)
+                
+#pragma unroll 8
+                for (int n = 0; n < N; ++n) s = fmaf(Ci(t0 + i, n), sT[j * (N + 1) + n], s);
+            sS[i * LQ + j] = s;
+        }
+        __syncthreads();
+        for (int e = tid; e < Q * P; e += kBwdThreads) {
+            const int j = e / P, p = e % P;
+            sT[j * (P + 1) + p] = (j < nvalid) ? xi(t0 + j, p) : 0.f;
+        }
+        __syncthreads();
+        for (int e = tid; e < Q * Q; e += kBwdThreads) {
+            const int i = e / Q, j = e % Q;
+            float v = 0.f;
+            if (j <= i && i < nvalid)
+                
+#pragma unroll 8
+                for (int p = 0; p < P; ++p) v = fmaf(dyi(t0 + i, p), sT[j * (P + 1) + p], v);
+            sR[i * LQ + j] = v;
         }
         __syncthreads();
 
-        // ---- dX (and x . dX, p_r), dx
-        for (int e = tid; e < Q * P; e += kThreads) {
+        // ---- dX (and x . dX, p_r), dx, and dy . x for dD
+        float ddsum = 0.f;
+        for (int e = tid; e < Q * P; e += kBwdThreads) {
             const int j = e / P, p = e % P;
             if (j >= nvalid) continue;
             float acc = 0.f;
-            for (int i = j; i < nvalid; ++i) acc = fmaf(sL[i * Q + j] * sS[i * Q + j], dyi(t0 + i, p), acc);
+            
+#pragma unroll 8
+                for (int i = j; i < nvalid; ++i) acc = fmaf(sL[i * LQ + j] * sS[i * LQ + j], dyi(t0 + i, p), acc);
             float gb = 0.f;
-            for (int n = 0; n < N; ++n) gb = fmaf(sG[p * N + n], Bi(t0 + j, n), gb);
+            
+#pragma unroll 8
+                for (int n = 0; n < N; ++n) gb = fmaf(sG[p * N + n], Bi(t0 + j, n), gb);
             const float dX = fmaf(sw[j], gb, acc);
             const float xv = xi(t0 + j, p);
             const float dtj = sg.dt[j];
-            a.dx[(((int64_t)b * L + t0 + j) * H + h) * P + p] = fmaf(dtj, dX, D_h * dyi(t0 + j, p));
+            const float dyv = dyi(t0 + j, p);
+            a.dx[(((int64_t)b * L + t0 + j) * H + h) * P + p] = fmaf(dtj, dX, D_h * dyv);
             atomicAdd(&sxdX[j], xv * dX);
+            ddsum = fmaf(dyv, xv, ddsum);
             atomicAdd(&sp[j], sg.wcd[j] * xv * gb);
         }
         // ---- dB (per head), dC (per head) and q_s
-        for (int e = tid; e < Q * N; e += kThreads) {
+        for (int e = tid; e < Q * N; e += kBwdThreads) {
             const int t = e / N, n = e % N;
             if (t >= nvalid) continue;
             // dB_t: column t of the masked products, and the state term
             float accb = 0.f;
-            for (int i = t; i < nvalid; ++i) accb = fmaf(sL[i * Q + t] * sR[i * Q + t], Ci(t0 + i, n), accb);
+            
+#pragma unroll 8
+                for (int i = t; i < nvalid; ++i) accb = fmaf(sL[i * LQ + t] * sR[i * LQ + t], Ci(t0 + i, n), accb);
             float gx = 0.f;
-            for (int p = 0; p < P; ++p) gx = fmaf(sG[p * N + n], xi(t0 + t, p), gx);
+            
+#pragma unroll 8
+                for (int p = 0; p < P; ++p) gx = fmaf(sG[p * N + n], xi(t0 + t, p), gx);
             const float dtt = sg.dt[t];
             a.dB_head[(((int64_t)b * L + t0 + t) * H + h) * N + n] = dtt * fmaf(sw[t], gx, accb);
             // dC_t: row t of the masked products, and the state term
             float accc = 0.f;
-            for (int j = 0; j <= t; ++j) accc = fmaf(sL[t * Q + j] * sg.dt[j] * sR[t * Q + j], Bi(t0 + j, n), accc);
+            
+#pragma unroll 8
+                for (int j = 0; j <= t; ++j) accc = fmaf(sL[t * LQ + j] * sg.dt[j] * sR[t * LQ + j], Bi(t0 + j, n), accc);
             float hdy = 0.f;
             if (Hs)
+                
+#pragma unroll 8
                 for (int p = 0; p < P; ++p) hdy = fmaf(Hs[p * N + n], dyi(t0 + t, p), hdy);
             a.dC_head[(((int64_t)b * L + t0 + t) * H + h) * N + n] = fmaf(sg.u[t], hdy, accc);
             atomicAdd(&sq[t], sg.u[t] * hdy * Ci(t0 + t, n));
         }
+        atomicAdd(&sDD, ddsum);
         // ---- T <G, H>
         {
             float k = 0.f;
             if (Hs)
-                for (int e = tid; e < PN; e += kThreads) k = fmaf(sG[e], Hs[e], k);
+                for (int e = tid; e < PN; e += kBwdThreads) k = fmaf(sG[e], Hs[e], k);
             atomicAdd(&sK, k);
         }
         __syncthreads();
@@ -176,8 +219,8 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
             const int s = tid;
             float run = 0.f;
             for (int r = 0; r < Q; ++r) {
-                const float R = (r <= s) ? sL[s * Q + r] * sg.dt[r] * sS[s * Q + r] * sR[s * Q + r] : 0.f;
-                sR[s * Q + r] = run;          // sum_{r' < r} R_{s r'}
+                const float R = (r <= s) ? sL[s * LQ + r] * sg.dt[r] * sS[s * LQ + r] * sR[s * LQ + r] : 0.f;
+                sR[s * LQ + r] = run;          // sum_{r' < r} R_{s r'}
                 run += R;
             }
         }
@@ -186,7 +229,7 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
             const int t = tid;
             float dl = 0.f;
             if (t < nvalid) {
-                for (int s = t; s < Q; ++s) dl += sR[s * Q + t] + sq[s];
+                for (int s = t; s < Q; ++s) dl += sR[s * LQ + t] + sq[s];
                 for (int r = 0; r < t; ++r) dl += sp[r];
                 dl += sg.T * sK;
                 if (sg.flag[t]) dl = 0.f;   // a_t is 0 there, not exp(dt A)
@@ -199,22 +242,20 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
             float s = 0.f;
             for (int t = 0; t < Q; ++t) s += sdl[t];
             sDA += s;
-            float d = 0.f;
-            for (int t = 0; t < nvalid; ++t)
-                for (int p = 0; p < P; ++p) d = fmaf(dyi(t0 + t, p), xi(t0 + t, p), d);
-            sDD += d;
         }
         // ---- G_{c-1} = T G_c + sum_i u_i dy_i C_i^T
-        for (int e = tid; e < PN; e += kThreads) {
+        for (int e = tid; e < PN; e += kBwdThreads) {
             const int p = e / N, n = e % N;
             float acc = sg.T * sG[e];
-            for (int i = 0; i < nvalid; ++i) acc = fmaf(sg.u[i] * dyi(t0 + i, p), Ci(t0 + i, n), acc);
+            
+#pragma unroll 8
+                for (int i = 0; i < nvalid; ++i) acc = fmaf(sg.u[i] * dyi(t0 + i, p), Ci(t0 + i, n), acc);
             sG[e] = acc;
         }
         __syncthreads();
     }
     if (a.dinit)
-        for (int e = tid; e < PN; e += kThreads) a.dinit[(int64_t)bh * PN + e] = sG[e];
+        for (int e = tid; e < PN; e += kBwdThreads) a.dinit[(int64_t)bh * PN + e] = sG[e];
     if (tid == 0) {
         a.dA_part[bh] = sDA;
         a.dD_part[bh] = sDD;
@@ -253,7 +294,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_reduce_kernel(BwdArgs a) {
 }
 
 void launch_bwd(bool bf16_io, const BwdArgs &a, hipStream_t stream) {
-    const dim3 grid(a.batch * a.nheads), block(kThreads);
+    const dim3 grid(a.batch * a.nheads), block(kBwdThreads);
     if (bf16_io) hipLaunchKernelGGL(ssd_bwd_kernel<bf16>, grid, block, 0, stream, a);
     else hipLaunchKernelGGL(ssd_bwd_kernel<float>, grid, block, 0, stream, a);
     const int64_t total = (int64_t)a.batch * a.seqlen * a.ngroups * a.dstate + a.nheads;
