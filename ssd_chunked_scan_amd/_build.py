@@ -67,6 +67,9 @@ _REG = re.compile(r"([vas])\[(\d+):(\d+)\]|\b([vas])(\d+)\b")
 # read as the accumulator of a following MFMA (same registers) need none, and
 # v_accvgpr_read of an AGPR destination is interlocked (measured: valid at 0).
 MFMA_READ_WAIT_STATES = 8
+# v_mfma_f32_16x16x4_f32 takes twice the passes (8): a result read needs
+# passes + 3 wait states.
+MFMA_READ_WAIT_STATES_BY_OP = {"v_mfma_f32_16x16x4_f32": 11}
 
 
 def _regs(text: str):
@@ -118,10 +121,11 @@ def check_mfma_result_reads(asm_text: str, where: str) -> int:
             n += 1
             ops = [o.strip() for o in text.split(None, 1)[1].split(",")]
             dst = _regs(ops[0])
+            need = MFMA_READ_WAIT_STATES_BY_OP.get(text.split()[0], MFMA_READ_WAIT_STATES)
             stack, seen = [(i + 1, 0)], set()
             while stack:
                 j, ws = stack.pop()
-                while j < len(items) and ws < MFMA_READ_WAIT_STATES:
+                while j < len(items) and ws < need:
                     if (j, ws) in seen:
                         break
                     seen.add((j, ws))
@@ -258,7 +262,7 @@ def build(verbose: bool = True, jobs: int = 0) -> str:
         n_mfma = sum(f.result() for f in chk)
     if verbose:
         print(f"  checked {n_mfma} MFMA instructions: every read of a result is at least "
-              f"{MFMA_READ_WAIT_STATES} wait states away on every path", file=sys.stderr)
+              f"{MFMA_READ_WAIT_STATES} wait states (fp32 MFMA: 11) away on every path", file=sys.stderr)
     tmp = LIB + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

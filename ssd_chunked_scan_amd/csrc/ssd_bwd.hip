@@ -35,42 +35,79 @@ __device__ inline float bwd_ld(const void *p, int64_t i) {
     return (float)((const IO *)p)[i];
 }
 
-// 16 waves: one workgroup fills a CU (its LDS allows one per CU), so that
-// four waves per SIMD cover the latency of the global-memory operands.
+// Four consecutive elements from index i (i a multiple of 4).
+template <typename IO>
+__device__ inline float4 bwd_ld4(const void *p, int64_t i);
+template <>
+__device__ inline float4 bwd_ld4<float>(const void *p, int64_t i) {
+    return *(const float4 *)((const float *)p + i);
+}
+template <>
+__device__ inline float4 bwd_ld4<bf16>(const void *p, int64_t i) {
+    const uint2 u = *(const uint2 *)((const bf16 *)p + i);
+    return float4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                  __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
+}
+
+// Sum over aligned groups of W lanes (W a power of two, at most 64).  Every
+// lane of the wave takes part.
+__device__ inline float lane_group_sum(float v, int W) {
+    for (int off = 1; off < W; off <<= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// D = A B + C on v_mfma_f32_16x16x4_f32: lane l gives A[l % 16][l / 16] and
+// B[l / 16][l % 16] and holds D[4 (l / 16) + r][l % 16] in element r.  The
+// contraction index of a step is the lane group l / 16; which four values of
+// the true index a step covers is free, as long as A and B agree.
+__device__ inline f32x4 mfma_f32(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// The fp32 MFMA takes more passes than the bf16 one the shared fence is sized
+// for: 8 + 4 wait states before vector code reads a result.
+__device__ inline void mfma_f32_fence(f32x4 &a, f32x4 &b) {
+    asm volatile("s_nop 7\n\ts_nop 3" : "+v"(a), "+v"(b));
+}
+
+// 16 waves: one workgroup fills a CU (its LDS allows one per CU).
 constexpr int kBwdThreads = 1024;
 
 template <typename IO>
 __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
     constexpr int Q = kBwdQ, NB = Q / 16;
-    constexpr int LQ = Q + 1;               // padded row pitch: a lane per row hits its own bank
-    constexpr int kMaxPN = 128 * 128;
+    // Row pitch of the Q x Q matrices: odd, so a lane per row hits its own
+    // bank, and 17 mod 64, so the MFMA operand patterns (16 consecutive
+    // columns in 4 rows, or 16 rows in 4 consecutive columns) barely collide.
+    constexpr int LQ = Q + 17;
+    constexpr int kMaxGN = 128 * (128 + 4);
     __shared__ __attribute__((aligned(16))) SegLds<Q> sg;
-    __shared__ float sG[kMaxPN];           // adjoint of the state at the chunk end, [P][N]
+    __shared__ __attribute__((aligned(16))) float sG[kMaxGN];  // adjoint of the state at the chunk end, [P][N + 4]
     __shared__ float sL[Q * LQ];            // decay mask L[i][j]
-    __shared__ float sS[Q * LQ];            // (C B^T)[i][j]
-    __shared__ float sR[Q * LQ];            // V[i][j] = dy_i . x_j, then R, then row prefix sums of R
-    __shared__ float sT[Q * 129];           // staged rows of B, then of x (pitch +1)
+    __shared__ float sS[Q * LQ];            // (L o C B^T)[i][j]
+    __shared__ float sV[Q * LQ];            // V[i][j] = dy_i . x_j, then row prefix sums of R
     __shared__ float sw[Q];                 // decay from token j to the chunk end
     __shared__ float sq[Q], sp[Q], sxdX[Q], sdl[Q];
     __shared__ float sK, sDD, sDA;
 
     const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
     const int bh = blockIdx.x;
     const int b = bh / a.nheads, h = bh % a.nheads;
     const int L = a.seqlen, H = a.nheads, G = a.ngroups, P = a.headdim, N = a.dstate;
     const int PN = P * N;
+    const int GN = N + 4;                   // row pitch of sG (16-byte rows, 4 mod 64 banks)
     const int grp = h / (H / G);
     const float A_h = a.A[h];
     const float D_h = a.D ? a.D[h] : 0.f;
     const float *dt_row = a.dt + (int64_t)b * L * H + h;
     const int32_t *seq_row = a.seq_idx ? a.seq_idx + (int64_t)b * L : nullptr;
-    auto xi = [&](int t, int p) { return bwd_ld<IO>(a.x, (((int64_t)b * L + t) * H + h) * P + p); };
-    auto dyi = [&](int t, int p) { return bwd_ld<IO>(a.dy, (((int64_t)b * L + t) * H + h) * P + p); };
-    auto Bi = [&](int t, int n) { return bwd_ld<IO>(a.B, (((int64_t)b * L + t) * G + grp) * N + n); };
-    auto Ci = [&](int t, int n) { return bwd_ld<IO>(a.C, (((int64_t)b * L + t) * G + grp) * N + n); };
+    // element offsets of token t's rows
+    auto xo = [&](int t) { return (((int64_t)b * L + t) * H + h) * P; };
+    auto bo = [&](int t) { return (((int64_t)b * L + t) * G + grp) * N; };
 
     for (int e = tid; e < PN; e += kBwdThreads)
-        sG[e] = a.dfinal ? a.dfinal[(int64_t)bh * PN + e] : 0.f;
+        sG[(e / N) * GN + e % N] = a.dfinal ? a.dfinal[(int64_t)bh * PN + e] : 0.f;
     if (tid == 0) {
         sDD = 0.f;
         sDA = 0.f;
@@ -83,6 +120,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
         // H_{c-1}: from the forward's scan, or (a single chunk) the initial state or 0
         const float *Hs = a.states ? a.states + ((int64_t)bh * a.nchunks + c) * PN
                                    : (a.init_states ? a.init_states + (int64_t)bh * PN : nullptr);
+        // operand row of token t0 + t, or none past the end of the row
+        auto ok = [&](int t) { return t < nvalid; };
 
         // ---- segsum values of the chunk (the forward kernels' helpers)
         int flag_any = 0;
@@ -109,7 +148,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
         }
         __syncthreads();
 
-        // ---- mask rows (nested sums leftwards from the diagonal), S and V
+        // ---- mask rows (nested sums leftwards from the diagonal)
         if (tid < Q) {
             const int i = tid;
             float sum = 0.f;
@@ -121,96 +160,166 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
             }
             for (int j = i + 1; j < Q; ++j) sL[i * LQ + j] = 0.f;
         }
-        // S = C B^T with B's rows staged in LDS (the lanes of a wave take
-        // different j), then V = dY X^T with x's rows staged in the same place
-        for (int e = tid; e < Q * N; e += kBwdThreads) {
-            const int j = e / N, n = e % N;
-            sT[j * (N + 1) + n] = (j < nvalid) ? Bi(t0 + j, n) : 0.f;
-        }
         __syncthreads();
-        for (int e = tid; e < Q * Q; e += kBwdThreads) {
-            const int i = e / Q, j = e % Q;
-            float s = 0.f;
-            if (j <= i && i < nvalid)
-                
-#pragma unroll 8
-                for (int n = 0; n < N; ++n) s = fmaf(Ci(t0 + i, n), sT[j * (N + 1) + n], s);
-            sS[i * LQ + j] = s;
-        }
-        __syncthreads();
-        for (int e = tid; e < Q * P; e += kBwdThreads) {
-            const int j = e / P, p = e % P;
-            sT[j * (P + 1) + p] = (j < nvalid) ? xi(t0 + j, p) : 0.f;
-        }
-        __syncthreads();
-        for (int e = tid; e < Q * Q; e += kBwdThreads) {
-            const int i = e / Q, j = e % Q;
-            float v = 0.f;
-            if (j <= i && i < nvalid)
-                
-#pragma unroll 8
-                for (int p = 0; p < P; ++p) v = fmaf(dyi(t0 + i, p), sT[j * (P + 1) + p], v);
-            sR[i * LQ + j] = v;
+
+        // ---- S = C B^T (stored masked) and V = dY X^T, lower 16 x 16 tiles
+        // only (upper tiles are never read).  Both operands are rows of
+        // token-major arrays: a lane reads four consecutive elements of its
+        // row and feeds them to four steps.
+        {
+            constexpr int NT = NB * (NB + 1) / 2;
+            for (int job = wave; job < 2 * NT; job += kBwdThreads / 64) {
+                const bool isS = job < NT;
+                int k = isS ? job : job - NT, I = 0;
+                while (k > I) k -= ++I;
+                const int J = k;                              // tile (I, J), J <= I
+                const int i = I * 16 + l16, j = J * 16 + l16;
+                const int K = isS ? N : P;
+                const void *Ap = isS ? a.C : a.dy;
+                const void *Bp = isS ? a.B : a.x;
+                const int64_t ai = isS ? bo(t0 + i) : xo(t0 + i);
+                const int64_t bj = isS ? bo(t0 + j) : xo(t0 + j);
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
+                for (int k0 = 0; k0 < K; k0 += 32) {
+                    // two independent chains, 16 contraction indices each
+                    const float4 av = ok(i) ? bwd_ld4<IO>(Ap, ai + k0 + 4 * g) : float4{0.f, 0.f, 0.f, 0.f};
+                    const float4 bv = ok(j) ? bwd_ld4<IO>(Bp, bj + k0 + 4 * g) : float4{0.f, 0.f, 0.f, 0.f};
+                    float4 av2 = {0.f, 0.f, 0.f, 0.f}, bv2 = {0.f, 0.f, 0.f, 0.f};
+                    if (k0 + 16 < K) {
+                        if (ok(i)) av2 = bwd_ld4<IO>(Ap, ai + k0 + 16 + 4 * g);
+                        if (ok(j)) bv2 = bwd_ld4<IO>(Bp, bj + k0 + 16 + 4 * g);
+                    }
+                    acc = mfma_f32(av.x, bv.x, acc);
+                    acc2 = mfma_f32(av2.x, bv2.x, acc2);
+                    acc = mfma_f32(av.y, bv.y, acc);
+                    acc2 = mfma_f32(av2.y, bv2.y, acc2);
+                    acc = mfma_f32(av.z, bv.z, acc);
+                    acc2 = mfma_f32(av2.z, bv2.z, acc2);
+                    acc = mfma_f32(av.w, bv.w, acc);
+                    acc2 = mfma_f32(av2.w, bv2.w, acc2);
+                }
+                mfma_f32_fence(acc, acc2);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int ii = I * 16 + 4 * g + r, jj = J * 16 + l16;
+                    const float v = acc[r] + acc2[r];
+                    if (isS) sS[ii * LQ + jj] = sL[ii * LQ + jj] * v;
+                    else sV[ii * LQ + jj] = v;
+                }
+            }
         }
         __syncthreads();
 
-        // ---- dX (and x . dX, p_r), dx, and dy . x for dD
         float ddsum = 0.f;
-        for (int e = tid; e < Q * P; e += kBwdThreads) {
-            const int j = e / P, p = e % P;
-            if (j >= nvalid) continue;
-            float acc = 0.f;
-            
-#pragma unroll 8
-                for (int i = j; i < nvalid; ++i) acc = fmaf(sL[i * LQ + j] * sS[i * LQ + j], dyi(t0 + i, p), acc);
-            float gb = 0.f;
-            
-#pragma unroll 8
-                for (int n = 0; n < N; ++n) gb = fmaf(sG[p * N + n], Bi(t0 + j, n), gb);
-            const float dX = fmaf(sw[j], gb, acc);
-            const float xv = xi(t0 + j, p);
-            const float dtj = sg.dt[j];
-            const float dyv = dyi(t0 + j, p);
-            a.dx[(((int64_t)b * L + t0 + j) * H + h) * P + p] = fmaf(dtj, dX, D_h * dyv);
-            atomicAdd(&sxdX[j], xv * dX);
-            ddsum = fmaf(dyv, xv, ddsum);
-            atomicAdd(&sp[j], sg.wcd[j] * xv * gb);
+        // ---- dX (and x . dX, p_r), dx, and dy . x for dD: tiles over (j, p)
+        //   acc  = sum_{i >= j} (L o S)[i][j] dy_i[p]     (i: LDS column, dy rows)
+        //   acc2 = (B G^T)[j][p] = G B_j                  (n: B rows, G rows)
+        for (int job = wave; job < NB * (P / 16); job += kBwdThreads / 64) {
+            const int J = job % NB, Pb = job / NB;
+            const int p = Pb * 16 + l16, jr = J * 16 + l16;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
+            for (int k = J * 16; k < Q; k += 4) {
+                const int i = k + g;
+                const float dyv = ok(i) ? bwd_ld<IO>(a.dy, xo(t0 + i) + p) : 0.f;
+                acc = mfma_f32(sS[i * LQ + jr], dyv, acc);
+            }
+            const int64_t bj = bo(t0 + jr);
+            for (int n0 = 0; n0 < N; n0 += 16) {
+                const float4 bv = ok(jr) ? bwd_ld4<IO>(a.B, bj + n0 + 4 * g) : float4{0.f, 0.f, 0.f, 0.f};
+                const float4 gv = *(const float4 *)&sG[p * GN + n0 + 4 * g];
+                acc2 = mfma_f32(bv.x, gv.x, acc2);
+                acc2 = mfma_f32(bv.y, gv.y, acc2);
+                acc2 = mfma_f32(bv.z, gv.z, acc2);
+                acc2 = mfma_f32(bv.w, gv.w, acc2);
+            }
+            mfma_f32_fence(acc, acc2);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = J * 16 + 4 * g + r;
+                float xd = 0.f, pr = 0.f;
+                if (ok(j)) {
+                    const float dX = fmaf(sw[j], acc2[r], acc[r]);
+                    const float xv = bwd_ld<IO>(a.x, xo(t0 + j) + p);
+                    const float dyv = bwd_ld<IO>(a.dy, xo(t0 + j) + p);
+                    a.dx[xo(t0 + j) + p] = fmaf(sg.dt[j], dX, D_h * dyv);
+                    xd = xv * dX;
+                    pr = sg.wcd[j] * xv * acc2[r];
+                    ddsum = fmaf(dyv, xv, ddsum);
+                }
+                xd = lane_group_sum(xd, 16);
+                pr = lane_group_sum(pr, 16);
+                if (l16 == 0 && ok(j)) {
+                    atomicAdd(&sxdX[j], xd);
+                    atomicAdd(&sp[j], pr);
+                }
+            }
         }
-        // ---- dB (per head), dC (per head) and q_s
-        for (int e = tid; e < Q * N; e += kBwdThreads) {
-            const int t = e / N, n = e % N;
-            if (t >= nvalid) continue;
-            // dB_t: column t of the masked products, and the state term
-            float accb = 0.f;
-            
-#pragma unroll 8
-                for (int i = t; i < nvalid; ++i) accb = fmaf(sL[i * LQ + t] * sR[i * LQ + t], Ci(t0 + i, n), accb);
-            float gx = 0.f;
-            
-#pragma unroll 8
-                for (int p = 0; p < P; ++p) gx = fmaf(sG[p * N + n], xi(t0 + t, p), gx);
-            const float dtt = sg.dt[t];
-            a.dB_head[(((int64_t)b * L + t0 + t) * H + h) * N + n] = dtt * fmaf(sw[t], gx, accb);
-            // dC_t: row t of the masked products, and the state term
-            float accc = 0.f;
-            
-#pragma unroll 8
-                for (int j = 0; j <= t; ++j) accc = fmaf(sL[t * LQ + j] * sg.dt[j] * sR[t * LQ + j], Bi(t0 + j, n), accc);
-            float hdy = 0.f;
-            if (Hs)
-                
-#pragma unroll 8
-                for (int p = 0; p < P; ++p) hdy = fmaf(Hs[p * N + n], dyi(t0 + t, p), hdy);
-            a.dC_head[(((int64_t)b * L + t0 + t) * H + h) * N + n] = fmaf(sg.u[t], hdy, accc);
-            atomicAdd(&sq[t], sg.u[t] * hdy * Ci(t0 + t, n));
+        // ---- dB, dC (per head) and q_s: tiles over (t, n)
+        //   dB: acc = sum_{i >= t} (L o V)[i][t] C_i[n],  acc2 = (X G)[t][n] = G^T x_t
+        //   dC: acc = sum_{j <= t} (L o dt o V)[t][j] B_j[n],  acc2 = (dY H)[t][n] = H^T dy_t
+        for (int job = wave; job < NB * (N / 16); job += kBwdThreads / 64) {
+            const int T = job % NB, Nb = job / NB;
+            const int n = Nb * 16 + l16, tr = T * 16 + l16;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
+            for (int k = T * 16; k < Q; k += 4) {
+                const int i = k + g;
+                const float cv = ok(i) ? bwd_ld<IO>(a.C, bo(t0 + i) + n) : 0.f;
+                acc = mfma_f32(sL[i * LQ + tr] * sV[i * LQ + tr], cv, acc);
+            }
+            const int64_t xt = xo(t0 + tr);
+            for (int p0 = 0; p0 < P; p0 += 16) {
+                const float4 xv = ok(tr) ? bwd_ld4<IO>(a.x, xt + p0 + 4 * g) : float4{0.f, 0.f, 0.f, 0.f};
+                const float *gr = &sG[(p0 + 4 * g) * GN + n];
+                acc2 = mfma_f32(xv.x, gr[0], acc2);
+                acc2 = mfma_f32(xv.y, gr[GN], acc2);
+                acc2 = mfma_f32(xv.z, gr[2 * GN], acc2);
+                acc2 = mfma_f32(xv.w, gr[3 * GN], acc2);
+            }
+            mfma_f32_fence(acc, acc2);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = T * 16 + 4 * g + r;
+                if (ok(t)) a.dB_head[(((int64_t)b * L + t0 + t) * H + h) * N + n] = sg.dt[t] * fmaf(sw[t], acc2[r], acc[r]);
+            }
+            acc = f32x4{0.f, 0.f, 0.f, 0.f};
+            acc2 = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int k = 0; k < T * 16 + 16; k += 4) {
+                const int j = k + g;
+                const float bv = ok(j) ? bwd_ld<IO>(a.B, bo(t0 + j) + n) : 0.f;
+                acc = mfma_f32(sL[tr * LQ + j] * sg.dt[j] * sV[tr * LQ + j], bv, acc);
+            }
+            if (Hs) {
+                for (int p0 = 0; p0 < P; p0 += 16) {
+                    const float4 dv = ok(tr) ? bwd_ld4<IO>(a.dy, xt + p0 + 4 * g) : float4{0.f, 0.f, 0.f, 0.f};
+                    const float *hr = Hs + (int64_t)(p0 + 4 * g) * N + n;
+                    acc2 = mfma_f32(dv.x, hr[0], acc2);
+                    acc2 = mfma_f32(dv.y, hr[N], acc2);
+                    acc2 = mfma_f32(dv.z, hr[2 * N], acc2);
+                    acc2 = mfma_f32(dv.w, hr[3 * N], acc2);
+                }
+            }
+            mfma_f32_fence(acc, acc2);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = T * 16 + 4 * g + r;
+                float qv = 0.f;
+                if (ok(t)) {
+                    a.dC_head[(((int64_t)b * L + t0 + t) * H + h) * N + n] = fmaf(sg.u[t], acc2[r], acc[r]);
+                    qv = sg.u[t] * acc2[r] * bwd_ld<IO>(a.C, bo(t0 + t) + n);
+                }
+                qv = lane_group_sum(qv, 16);
+                if (l16 == 0 && ok(t)) atomicAdd(&sq[t], qv);
+            }
         }
-        atomicAdd(&sDD, ddsum);
+        ddsum = lane_group_sum(ddsum, 64);
+        if (lane == 0) atomicAdd(&sDD, ddsum);
         // ---- T <G, H>
         {
             float k = 0.f;
             if (Hs)
-                for (int e = tid; e < PN; e += kBwdThreads) k = fmaf(sG[e], Hs[e], k);
-            atomicAdd(&sK, k);
+                for (int e = tid; e < PN; e += kBwdThreads) k = fmaf(sG[(e / N) * GN + e % N], Hs[e], k);
+            k = lane_group_sum(k, 64);
+            if (lane == 0) atomicAdd(&sK, k);
         }
         __syncthreads();
 
@@ -219,8 +328,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
             const int s = tid;
             float run = 0.f;
             for (int r = 0; r < Q; ++r) {
-                const float R = (r <= s) ? sL[s * LQ + r] * sg.dt[r] * sS[s * LQ + r] * sR[s * LQ + r] : 0.f;
-                sR[s * LQ + r] = run;          // sum_{r' < r} R_{s r'}
+                const float R = (r <= s) ? sS[s * LQ + r] * sg.dt[r] * sV[s * LQ + r] : 0.f;
+                sV[s * LQ + r] = run;          // sum_{r' < r} R_{s r'}
                 run += R;
             }
         }
@@ -229,7 +338,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
             const int t = tid;
             float dl = 0.f;
             if (t < nvalid) {
-                for (int s = t; s < Q; ++s) dl += sR[s * LQ + t] + sq[s];
+                for (int s = t; s < Q; ++s) dl += sV[s * LQ + t] + sq[s];
                 for (int r = 0; r < t; ++r) dl += sp[r];
                 dl += sg.T * sK;
                 if (sg.flag[t]) dl = 0.f;   // a_t is 0 there, not exp(dt A)
@@ -237,25 +346,37 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
             }
             sdl[t] = (t < nvalid) ? sg.dt[t] * dl : 0.f;
         }
+        // ---- G_{c-1} = T G_c + sum_i u_i dy_i C_i^T: tiles over (p, n)
+        for (int job = wave; job < (P / 16) * (N / 16); job += kBwdThreads / 64) {
+            const int Pb = job % (P / 16), Nb = job / (P / 16);
+            const int p = Pb * 16 + l16, n = Nb * 16 + l16;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
+            for (int k = 0; k < nvalid; k += 8) {
+                const int i = k + g, i2 = k + 4 + g;
+                const float dv = ok(i) ? sg.u[i] * bwd_ld<IO>(a.dy, xo(t0 + i) + p) : 0.f;
+                const float cv = ok(i) ? bwd_ld<IO>(a.C, bo(t0 + i) + n) : 0.f;
+                const float dv2 = ok(i2) ? sg.u[i2] * bwd_ld<IO>(a.dy, xo(t0 + i2) + p) : 0.f;
+                const float cv2 = ok(i2) ? bwd_ld<IO>(a.C, bo(t0 + i2) + n) : 0.f;
+                acc = mfma_f32(dv, cv, acc);
+                acc2 = mfma_f32(dv2, cv2, acc2);
+            }
+            mfma_f32_fence(acc, acc2);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float *gp = &sG[(Pb * 16 + 4 * g + r) * GN + n];
+                *gp = fmaf(sg.T, *gp, acc[r] + acc2[r]);
+            }
+        }
         __syncthreads();
         if (tid == 0) {
             float s = 0.f;
             for (int t = 0; t < Q; ++t) s += sdl[t];
             sDA += s;
         }
-        // ---- G_{c-1} = T G_c + sum_i u_i dy_i C_i^T
-        for (int e = tid; e < PN; e += kBwdThreads) {
-            const int p = e / N, n = e % N;
-            float acc = sg.T * sG[e];
-            
-#pragma unroll 8
-                for (int i = 0; i < nvalid; ++i) acc = fmaf(sg.u[i] * dyi(t0 + i, p), Ci(t0 + i, n), acc);
-            sG[e] = acc;
-        }
-        __syncthreads();
     }
+    __syncthreads();
     if (a.dinit)
-        for (int e = tid; e < PN; e += kBwdThreads) a.dinit[(int64_t)bh * PN + e] = sG[e];
+        for (int e = tid; e < PN; e += kBwdThreads) a.dinit[(int64_t)bh * PN + e] = sG[(e / N) * GN + e % N];
     if (tid == 0) {
         a.dA_part[bh] = sDA;
         a.dD_part[bh] = sDD;

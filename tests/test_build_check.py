@@ -123,3 +123,19 @@ def test_marker_does_not_count_as_a_wait_state():
                "v_mul_f32_e32 v20, v1, v21")
     with pytest.raises(RuntimeError):
         _build.check_mfma_result_reads(asm, "t")
+
+
+def test_fp32_mfma_needs_eleven_wait_states():
+    """The fp32 MFMA's result is read after 8 wait states: enough for the bf16
+    op, not for this one."""
+    asm = "\n".join([
+        "k:",
+        "v_mfma_f32_16x16x4_f32 v[0:3], v4, v5, v[0:3]",
+        "s_nop 7",
+        "v_add_f32_e32 v6, v0, v1",
+        "s_endpgm",
+    ])
+    with pytest.raises(RuntimeError, match="after only 8"):
+        _build.check_mfma_result_reads(asm, "t")
+    ok = asm.replace("s_nop 7", "s_nop 7\ns_nop 2")
+    assert _build.check_mfma_result_reads(ok, "t") == 1
