@@ -28,6 +28,8 @@
 #include "ssd_common.hpp"
 #include "ssd_segsum.hpp"
 
+#include <type_traits>
+
 namespace ssd {
 
 template <typename IO>
@@ -35,18 +37,39 @@ __device__ inline float bwd_ld(const void *p, int64_t i) {
     return (float)((const IO *)p)[i];
 }
 
-// Four consecutive elements from index i (i a multiple of 4).
-template <typename IO>
-__device__ inline float4 bwd_ld4(const void *p, int64_t i);
-template <>
-__device__ inline float4 bwd_ld4<float>(const void *p, int64_t i) {
-    return *(const float4 *)((const float *)p + i);
+// Element `off` of a row base: the offset is unsigned and 32-bit, so the
+// load takes the base in scalar registers and one offset register.
+template <typename T>
+__device__ inline const T *at_off(const T *p, unsigned off) {
+    return (const T *)((const char *)p + off * (unsigned)sizeof(T));
 }
+__device__ inline float ld1(const float *p, unsigned off) { return *at_off(p, off); }
+__device__ inline float ld1(const bf16 *p, unsigned off) { return (float)*at_off(p, off); }
+
+// Four consecutive elements (16-byte fp32 or 8-byte bf16 load), kept packed
+// until the MFMA steps take them one by one.
+template <typename IO>
+struct Pack;
 template <>
-__device__ inline float4 bwd_ld4<bf16>(const void *p, int64_t i) {
-    const uint2 u = *(const uint2 *)((const bf16 *)p + i);
-    return float4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
-                  __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
+struct Pack<float> {
+    float4 v;
+};
+template <>
+struct Pack<bf16> {
+    uint2 v;
+};
+template <typename IO>
+__device__ inline Pack<IO> ld_pack(const IO *p, unsigned off) {
+    return Pack<IO>{*(const decltype(Pack<IO>::v) *)at_off(p, off)};
+}
+template <int E>
+__device__ inline float pack_el(const Pack<float> &q) {
+    return E == 0 ? q.v.x : E == 1 ? q.v.y : E == 2 ? q.v.z : q.v.w;
+}
+template <int E>
+__device__ inline float pack_el(const Pack<bf16> &q) {
+    const unsigned w = (E < 2) ? q.v.x : q.v.y;
+    return __uint_as_float((E & 1) ? (w & 0xffff0000u) : (w << 16));
 }
 
 // Sum over aligned groups of W lanes (W a power of two, at most 64).  Every
@@ -54,6 +77,19 @@ __device__ inline float4 bwd_ld4<bf16>(const void *p, int64_t i) {
 __device__ inline float lane_group_sum(float v, int W) {
     for (int off = 1; off < W; off <<= 1) v += __shfl_xor(v, off, 64);
     return v;
+}
+
+// Sum over each row of 16 lanes, every lane receiving it, on DPP (vector
+// ALU, no LDS round trip): swaps within pairs and quads, then rotations of
+// the row by 4 and by 8.
+__device__ inline float row_sum16(float v) {
+    auto step = [](float x, auto ctrl) {
+        return x + __builtin_bit_cast(float, dpp_row<decltype(ctrl)::value>(__builtin_bit_cast(int, x)));
+    };
+    v = step(v, std::integral_constant<int, 0xB1>{});    // quad_perm [1, 0, 3, 2]
+    v = step(v, std::integral_constant<int, 0x4E>{});    // quad_perm [2, 3, 0, 1]
+    v = step(v, std::integral_constant<int, 0x124>{});   // row_ror 4
+    return step(v, std::integral_constant<int, 0x128>{});  // row_ror 8
 }
 
 // D = A B + C on v_mfma_f32_16x16x4_f32: lane l gives A[l % 16][l / 16] and
@@ -64,23 +100,36 @@ __device__ inline f32x4 mfma_f32(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// Four steps over the packed elements of a and b (same contraction indices).
+template <typename IO>
+__device__ inline f32x4 mfma_pack4(const Pack<IO> &a, const Pack<IO> &b, f32x4 c) {
+    c = mfma_f32(pack_el<0>(a), pack_el<0>(b), c);
+    c = mfma_f32(pack_el<1>(a), pack_el<1>(b), c);
+    c = mfma_f32(pack_el<2>(a), pack_el<2>(b), c);
+    return mfma_f32(pack_el<3>(a), pack_el<3>(b), c);
+}
+
 // The fp32 MFMA takes more passes than the bf16 one the shared fence is sized
 // for: 8 + 4 wait states before vector code reads a result.
 __device__ inline void mfma_f32_fence(f32x4 &a, f32x4 &b) {
     asm volatile("s_nop 7\n\ts_nop 3" : "+v"(a), "+v"(b));
 }
 
-// 16 waves: one workgroup fills a CU (its LDS allows one per CU).
-constexpr int kBwdThreads = 1024;
+// 8 waves: one workgroup per CU (its LDS allows one), two waves per SIMD
+// with 256 registers each; batched operand loads cover the memory latency.
+constexpr int kBwdThreads = 512;
 
-template <typename IO>
+// One instantiation per headdim P (the loops over P have fixed trip counts).
+template <typename IO, int P>
 __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
     constexpr int Q = kBwdQ, NB = Q / 16;
     // Row pitch of the Q x Q matrices: odd, so a lane per row hits its own
     // bank, and 17 mod 64, so the MFMA operand patterns (16 consecutive
     // columns in 4 rows, or 16 rows in 4 consecutive columns) barely collide.
     constexpr int LQ = Q + 17;
-    constexpr int kMaxGN = 128 * (128 + 4);
+    constexpr int kMaxK = 128;              // largest headdim and dstate
+    constexpr int kMaxGN = P * (kMaxK + 4);
+    constexpr int PU = P / 16;              // 16-column blocks of headdim
     __shared__ __attribute__((aligned(16))) SegLds<Q> sg;
     __shared__ __attribute__((aligned(16))) float sG[kMaxGN];  // adjoint of the state at the chunk end, [P][N + 4]
     __shared__ float sL[Q * LQ];            // decay mask L[i][j]
@@ -91,10 +140,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
     __shared__ float sK, sDD, sDA;
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: job branches are scalar
     const int bh = blockIdx.x;
     const int b = bh / a.nheads, h = bh % a.nheads;
-    const int L = a.seqlen, H = a.nheads, G = a.ngroups, P = a.headdim, N = a.dstate;
+    const int L = a.seqlen, H = a.nheads, G = a.ngroups, N = a.dstate;
     const int PN = P * N;
     const int GN = N + 4;                   // row pitch of sG (16-byte rows, 4 mod 64 banks)
     const int grp = h / (H / G);
@@ -105,6 +154,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
     // element offsets of token t's rows
     auto xo = [&](int t) { return (((int64_t)b * L + t) * H + h) * P; };
     auto bo = [&](int t) { return (((int64_t)b * L + t) * G + grp) * N; };
+    const int xs = H * P, bs = G * N;
 
     for (int e = tid; e < PN; e += kBwdThreads)
         sG[(e / N) * GN + e % N] = a.dfinal ? a.dfinal[(int64_t)bh * PN + e] : 0.f;
@@ -114,20 +164,66 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
     }
     __syncthreads();
 
+    // token values (dt, reset flag) of the next chunk in the walk are fetched
+    // one chunk ahead, so their memory latency overlaps a chunk's work
+    float dt_next = 0.f;
+    int flag_next = 0;
+    if (tid < Q) {
+        const int cl0 = a.nchunks - 1;
+        seg_fetch_token(tid, cl0 * Q, min(Q, L - cl0 * Q), dt_row, H, seq_row, dt_next, flag_next);
+    }
+    // H_{c-1}: from the forward's scan, or (a single chunk) the initial state or 0
+    auto hs_of = [&](int cc) -> const float * {
+        return a.states ? a.states + ((int64_t)bh * a.nchunks + cc) * PN
+                        : (a.init_states ? a.init_states + (int64_t)bh * PN : nullptr);
+    };
+    // A wave keeps one block of 16 state columns over its dB/dC jobs (the
+    // block count divides the wave count), so it reads those columns of H
+    // once per chunk, and a chunk ahead: the read is issued after the jobs
+    // of the chunk before.
+    static_assert(kBwdThreads / 64 == 8, "n-block ownership assumes 8 waves");
+    float hv[4 * PU];
+    auto load_hv = [&](int cc, int l16_, int g_) {
+        const float *Hc = hs_of(cc);
+        const int n = (wave % (N / 16)) * 16 + l16_;
+#pragma unroll
+        for (int u = 0; u < PU; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                hv[4 * u + e] = Hc ? *at_off(Hc, (16 * u + 4 * g_ + e) * N + n) : 0.f;
+    };
+    load_hv(a.nchunks - 1, tid & 15, (tid & 63) >> 4);
     for (int c = a.nchunks - 1; c >= 0; --c) {
         const int t0 = c * Q;
         const int nvalid = min(Q, L - t0);
-        // H_{c-1}: from the forward's scan, or (a single chunk) the initial state or 0
-        const float *Hs = a.states ? a.states + ((int64_t)bh * a.nchunks + c) * PN
-                                   : (a.init_states ? a.init_states + (int64_t)bh * PN : nullptr);
+        const float *Hs = hs_of(c);
         // operand row of token t0 + t, or none past the end of the row
         auto ok = [&](int t) { return t < nvalid; };
+        // The lane index, opaque to the compiler here: the per-lane offsets
+        // of the unrolled operand loads are recomputed per chunk rather than
+        // hoisted out of the loop and kept live (they would spill).
+        int lane = tid & 63;
+        asm volatile("" : "+v"(lane));
+        const int l16 = lane & 15, g = lane >> 4;
+        // Operand rows past the end of the row are read at the last valid
+        // token instead: every product they enter is zeroed by the mask, by
+        // dt = 0, or by the output row's own guard (the state update zeroes
+        // them explicitly).
+        auto cl = [&](int t) { return min(t, nvalid - 1); };
+        // the chunk's first token rows; tokens step by xs (x, dy) or bs (B, C)
+        // elements, so in-chunk offsets fit 32 bits and the loads take a
+        // scalar base
+        const IO *xc = (const IO *)a.x + xo(t0);
+        const IO *dyc = (const IO *)a.dy + xo(t0);
+        const IO *Bc = (const IO *)a.B + bo(t0);
+        const IO *Cc = (const IO *)a.C + bo(t0);
 
         // ---- segsum values of the chunk (the forward kernels' helpers)
         int flag_any = 0;
         if (tid < Q) {
-            seg_load_token<Q>(sg, tid, t0, nvalid, dt_row, H, A_h, seq_row, dt_map_identity());
-            flag_any = sg.flag[tid];
+            seg_store_token<Q>(sg, tid, dt_next, A_h, flag_next);
+            flag_any = flag_next;
+            if (c > 0) seg_fetch_token(tid, t0 - Q, Q, dt_row, H, seq_row, dt_next, flag_next);
         }
         flag_any = __syncthreads_or(flag_any);
         if (tid == 0) {
@@ -148,24 +244,36 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
         }
         __syncthreads();
 
-        // ---- mask rows (nested sums leftwards from the diagonal)
-        if (tid < Q) {
-            const int i = tid;
-            float sum = 0.f;
-            for (int j = i; j >= 0; --j) {
-                float v = (sg.rs[i] > j) ? 0.f : __builtin_amdgcn_exp2f(sum);
-                if (i >= nvalid) v = 0.f;
-                sL[i * LQ + j] = v;
-                sum = __fadd_rn(sum, sg.d[j]);
+        // ---- mask, built as the forward kernels build it: nested sums inside
+        // 16-token sub-blocks, rank-one factors across them.  A wave takes a
+        // 16-row tile, a lane row i and columns 16 jt + 4 g + r.
+        for (int I = wave; I < NB; I += kBwdThreads / 64) {
+            const int i = I * 16 + l16;
+            const int rs_i = sg.rs[i];
+            float e[4];
+            const float sum0 = seg_diag_row(sg.d, I * 16, i, g, e);
+            float F = seg_chain_start(sum0, I * 16, rs_i);
+            for (int jt = NB - 1; jt >= 0; --jt) {
+                float v[4] = {0.f, 0.f, 0.f, 0.f};
+                if (jt == I) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) v[r] = seg_diag_value(e[r], i, jt * 16 + 4 * g + r, rs_i);
+                } else if (jt < I) {
+                    if (jt < I - 1) F = seg_chain_step(F, sg.Tb[jt + 1]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) v[r] = seg_offdiag(F, sg.W[jt * 16 + 4 * g + r]);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sL[i * LQ + jt * 16 + 4 * g + r] = (i < nvalid) ? v[r] : 0.f;
             }
-            for (int j = i + 1; j < Q; ++j) sL[i * LQ + j] = 0.f;
         }
         __syncthreads();
 
         // ---- S = C B^T (stored masked) and V = dY X^T, lower 16 x 16 tiles
         // only (upper tiles are never read).  Both operands are rows of
         // token-major arrays: a lane reads four consecutive elements of its
-        // row and feeds them to four steps.
+        // row and feeds them to four steps.  All loads of a batch are issued
+        // before its MFMAs.
         {
             constexpr int NT = NB * (NB + 1) / 2;
             for (int job = wave; job < 2 * NT; job += kBwdThreads / 64) {
@@ -175,28 +283,21 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
                 const int J = k;                              // tile (I, J), J <= I
                 const int i = I * 16 + l16, j = J * 16 + l16;
                 const int K = isS ? N : P;
-                const void *Ap = isS ? a.C : a.dy;
-                const void *Bp = isS ? a.B : a.x;
-                const int64_t ai = isS ? bo(t0 + i) : xo(t0 + i);
-                const int64_t bj = isS ? bo(t0 + j) : xo(t0 + j);
+                const IO *Ab = isS ? Cc : dyc, *Bb = isS ? Bc : xc;   // chunk bases
+                const unsigned ao = cl(i) * (isS ? bs : xs), bo_ = cl(j) * (isS ? bs : xs);
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
-                for (int k0 = 0; k0 < K; k0 += 32) {
-                    // two independent chains, 16 contraction indices each
-                    const float4 av = ok(i) ? bwd_ld4<IO>(Ap, ai + k0 + 4 * g) : float4{0.f, 0.f, 0.f, 0.f};
-                    const float4 bv = ok(j) ? bwd_ld4<IO>(Bp, bj + k0 + 4 * g) : float4{0.f, 0.f, 0.f, 0.f};
-                    float4 av2 = {0.f, 0.f, 0.f, 0.f}, bv2 = {0.f, 0.f, 0.f, 0.f};
-                    if (k0 + 16 < K) {
-                        if (ok(i)) av2 = bwd_ld4<IO>(Ap, ai + k0 + 16 + 4 * g);
-                        if (ok(j)) bv2 = bwd_ld4<IO>(Bp, bj + k0 + 16 + 4 * g);
-                    }
-                    acc = mfma_f32(av.x, bv.x, acc);
-                    acc2 = mfma_f32(av2.x, bv2.x, acc2);
-                    acc = mfma_f32(av.y, bv.y, acc);
-                    acc2 = mfma_f32(av2.y, bv2.y, acc2);
-                    acc = mfma_f32(av.z, bv.z, acc);
-                    acc2 = mfma_f32(av2.z, bv2.z, acc2);
-                    acc = mfma_f32(av.w, bv.w, acc);
-                    acc2 = mfma_f32(av2.w, bv2.w, acc2);
+                Pack<IO> av[kMaxK / 16], bv[kMaxK / 16];
+#pragma unroll
+                for (int u = 0; u < kMaxK / 16; ++u) {
+                    const bool in = 16 * u < K;
+                    av[u] = in ? ld_pack<IO>(Ab, ao + 16 * u + 4 * g) : Pack<IO>{};
+                    bv[u] = in ? ld_pack<IO>(Bb, bo_ + 16 * u + 4 * g) : Pack<IO>{};
+                }
+#pragma unroll
+                for (int u = 0; u < kMaxK / 16; u += 2) {
+                    if (16 * u >= K) break;
+                    acc = mfma_pack4(av[u], bv[u], acc);
+                    acc2 = mfma_pack4(av[u + 1], bv[u + 1], acc2);
                 }
                 mfma_f32_fence(acc, acc2);
 #pragma unroll
@@ -218,19 +319,33 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
             const int J = job % NB, Pb = job / NB;
             const int p = Pb * 16 + l16, jr = J * 16 + l16;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
-            for (int k = J * 16; k < Q; k += 4) {
-                const int i = k + g;
-                const float dyv = ok(i) ? bwd_ld<IO>(a.dy, xo(t0 + i) + p) : 0.f;
-                acc = mfma_f32(sS[i * LQ + jr], dyv, acc);
+            const int ksteps = 4 * (NB - J);          // steps of 4 over i = 16 J .. Q - 1
+            float dyv[4 * NB];
+            Pack<IO> bv[kMaxK / 16];
+            const unsigned brow = cl(jr) * bs;
+#pragma unroll
+            for (int st = 0; st < 4 * NB; ++st) {
+                const int i = J * 16 + 4 * st + g;
+                dyv[st] = ld1(dyc, cl(i) * xs + p);
             }
-            const int64_t bj = bo(t0 + jr);
-            for (int n0 = 0; n0 < N; n0 += 16) {
-                const float4 bv = ok(jr) ? bwd_ld4<IO>(a.B, bj + n0 + 4 * g) : float4{0.f, 0.f, 0.f, 0.f};
-                const float4 gv = *(const float4 *)&sG[p * GN + n0 + 4 * g];
-                acc2 = mfma_f32(bv.x, gv.x, acc2);
-                acc2 = mfma_f32(bv.y, gv.y, acc2);
-                acc2 = mfma_f32(bv.z, gv.z, acc2);
-                acc2 = mfma_f32(bv.w, gv.w, acc2);
+#pragma unroll
+            for (int u = 0; u < kMaxK / 16; ++u)
+                bv[u] = (16 * u < N) ? ld_pack<IO>(Bc, brow + 16 * u + 4 * g) : Pack<IO>{};
+#pragma unroll
+            for (int st = 0; st < 4 * NB; ++st)
+            {
+                // steps past the range read a valid row and contribute 0
+                const float sv = sS[min(J * 16 + 4 * st + g, Q - 1) * LQ + jr];
+                acc = mfma_f32(st < ksteps ? sv : 0.f, dyv[st], acc);
+            }
+#pragma unroll
+            for (int u = 0; u < kMaxK / 16; ++u) {
+                // blocks past N: B is 0 there, G read at a valid column
+                const float4 gv = *(const float4 *)&sG[p * GN + min(16 * u, N - 16) + 4 * g];
+                acc2 = mfma_f32(pack_el<0>(bv[u]), gv.x, acc2);
+                acc2 = mfma_f32(pack_el<1>(bv[u]), gv.y, acc2);
+                acc2 = mfma_f32(pack_el<2>(bv[u]), gv.z, acc2);
+                acc2 = mfma_f32(pack_el<3>(bv[u]), gv.w, acc2);
             }
             mfma_f32_fence(acc, acc2);
 #pragma unroll
@@ -239,15 +354,15 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
                 float xd = 0.f, pr = 0.f;
                 if (ok(j)) {
                     const float dX = fmaf(sw[j], acc2[r], acc[r]);
-                    const float xv = bwd_ld<IO>(a.x, xo(t0 + j) + p);
-                    const float dyv = bwd_ld<IO>(a.dy, xo(t0 + j) + p);
+                    const float xv = ld1(xc, j * xs + p);
+                    const float dyv = ld1(dyc, j * xs + p);
                     a.dx[xo(t0 + j) + p] = fmaf(sg.dt[j], dX, D_h * dyv);
                     xd = xv * dX;
                     pr = sg.wcd[j] * xv * acc2[r];
                     ddsum = fmaf(dyv, xv, ddsum);
                 }
-                xd = lane_group_sum(xd, 16);
-                pr = lane_group_sum(pr, 16);
+                xd = row_sum16(xd);
+                pr = row_sum16(pr);
                 if (l16 == 0 && ok(j)) {
                     atomicAdd(&sxdX[j], xd);
                     atomicAdd(&sp[j], pr);
@@ -257,23 +372,53 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
         // ---- dB, dC (per head) and q_s: tiles over (t, n)
         //   dB: acc = sum_{i >= t} (L o V)[i][t] C_i[n],  acc2 = (X G)[t][n] = G^T x_t
         //   dC: acc = sum_{j <= t} (L o dt o V)[t][j] B_j[n],  acc2 = (dY H)[t][n] = H^T dy_t
+        // the first wave on each block of state columns adds its share of T <G, H>
+        if (Hs && wave < N / 16) {
+            const int n = (wave % (N / 16)) * 16 + l16;
+            float k = 0.f;
+#pragma unroll
+            for (int u = 0; u < PU; ++u)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) k = fmaf(sG[(16 * u + 4 * g + e) * GN + n], hv[4 * u + e], k);
+            k = lane_group_sum(k, 64);
+            if (lane == 0) atomicAdd(&sK, k);
+        }
         for (int job = wave; job < NB * (N / 16); job += kBwdThreads / 64) {
-            const int T = job % NB, Nb = job / NB;
+            const int Nb = job % (N / 16), T = job / (N / 16);
             const int n = Nb * 16 + l16, tr = T * 16 + l16;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
-            for (int k = T * 16; k < Q; k += 4) {
-                const int i = k + g;
-                const float cv = ok(i) ? bwd_ld<IO>(a.C, bo(t0 + i) + n) : 0.f;
-                acc = mfma_f32(sL[i * LQ + tr] * sV[i * LQ + tr], cv, acc);
+            // every global operand of the job, issued before its first MFMA
+            const int kb = 4 * (NB - T), kc = 4 * (T + 1);   // dB: i = 16 T .. Q - 1; dC: j = 0 .. 16 T + 15
+            const unsigned trow = cl(tr) * xs;
+            float cv[4 * NB], bv[4 * NB], cq[4];
+            Pack<IO> xr[PU], dr[PU];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) cq[r] = ld1(Cc, cl(T * 16 + 4 * g + r) * bs + n);
+#pragma unroll
+            for (int st = 0; st < 4 * NB; ++st) {
+                const int i = T * 16 + 4 * st + g, j = 4 * st + g;
+                cv[st] = ld1(Cc, cl(i) * bs + n);
+                bv[st] = ld1(Bc, cl(j) * bs + n);
             }
-            const int64_t xt = xo(t0 + tr);
-            for (int p0 = 0; p0 < P; p0 += 16) {
-                const float4 xv = ok(tr) ? bwd_ld4<IO>(a.x, xt + p0 + 4 * g) : float4{0.f, 0.f, 0.f, 0.f};
-                const float *gr = &sG[(p0 + 4 * g) * GN + n];
-                acc2 = mfma_f32(xv.x, gr[0], acc2);
-                acc2 = mfma_f32(xv.y, gr[GN], acc2);
-                acc2 = mfma_f32(xv.z, gr[2 * GN], acc2);
-                acc2 = mfma_f32(xv.w, gr[3 * GN], acc2);
+#pragma unroll
+            for (int u = 0; u < PU; ++u) {
+                xr[u] = ld_pack<IO>(xc, trow + 16 * u + 4 * g);
+                dr[u] = Hs ? ld_pack<IO>(dyc, trow + 16 * u + 4 * g) : Pack<IO>{};
+            }
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st < 4 * NB; ++st) {
+                const int i = T * 16 + 4 * st + g;
+                const int ic = min(i, Q - 1);
+                const float lv = sL[ic * LQ + tr] * sV[ic * LQ + tr];
+                acc = mfma_f32(st < kb ? lv : 0.f, cv[st], acc);
+            }
+#pragma unroll
+            for (int u = 0; u < PU; ++u) {
+                const float *gr = &sG[(16 * u + 4 * g) * GN + n];
+                acc2 = mfma_f32(pack_el<0>(xr[u]), gr[0], acc2);
+                acc2 = mfma_f32(pack_el<1>(xr[u]), gr[GN], acc2);
+                acc2 = mfma_f32(pack_el<2>(xr[u]), gr[2 * GN], acc2);
+                acc2 = mfma_f32(pack_el<3>(xr[u]), gr[3 * GN], acc2);
             }
             mfma_f32_fence(acc, acc2);
 #pragma unroll
@@ -283,20 +428,17 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
             }
             acc = f32x4{0.f, 0.f, 0.f, 0.f};
             acc2 = f32x4{0.f, 0.f, 0.f, 0.f};
-            for (int k = 0; k < T * 16 + 16; k += 4) {
-                const int j = k + g;
-                const float bv = ok(j) ? bwd_ld<IO>(a.B, bo(t0 + j) + n) : 0.f;
-                acc = mfma_f32(sL[tr * LQ + j] * sg.dt[j] * sV[tr * LQ + j], bv, acc);
+#pragma unroll
+            for (int st = 0; st < 4 * NB; ++st) {
+                const int j = 4 * st + g;
+                acc = mfma_f32(st < kc ? sL[tr * LQ + j] * sg.dt[j] * sV[tr * LQ + j] : 0.f, bv[st], acc);
             }
-            if (Hs) {
-                for (int p0 = 0; p0 < P; p0 += 16) {
-                    const float4 dv = ok(tr) ? bwd_ld4<IO>(a.dy, xt + p0 + 4 * g) : float4{0.f, 0.f, 0.f, 0.f};
-                    const float *hr = Hs + (int64_t)(p0 + 4 * g) * N + n;
-                    acc2 = mfma_f32(dv.x, hr[0], acc2);
-                    acc2 = mfma_f32(dv.y, hr[N], acc2);
-                    acc2 = mfma_f32(dv.z, hr[2 * N], acc2);
-                    acc2 = mfma_f32(dv.w, hr[3 * N], acc2);
-                }
+#pragma unroll
+            for (int u = 0; u < PU; ++u) {
+                acc2 = mfma_f32(pack_el<0>(dr[u]), hv[4 * u], acc2);
+                acc2 = mfma_f32(pack_el<1>(dr[u]), hv[4 * u + 1], acc2);
+                acc2 = mfma_f32(pack_el<2>(dr[u]), hv[4 * u + 2], acc2);
+                acc2 = mfma_f32(pack_el<3>(dr[u]), hv[4 * u + 3], acc2);
             }
             mfma_f32_fence(acc, acc2);
 #pragma unroll
@@ -305,60 +447,80 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
                 float qv = 0.f;
                 if (ok(t)) {
                     a.dC_head[(((int64_t)b * L + t0 + t) * H + h) * N + n] = fmaf(sg.u[t], acc2[r], acc[r]);
-                    qv = sg.u[t] * acc2[r] * bwd_ld<IO>(a.C, bo(t0 + t) + n);
+                    qv = sg.u[t] * acc2[r] * cq[r];
                 }
-                qv = lane_group_sum(qv, 16);
+                qv = row_sum16(qv);
                 if (l16 == 0 && ok(t)) atomicAdd(&sq[t], qv);
             }
         }
+        if (c > 0) load_hv(c - 1, l16, g);
         ddsum = lane_group_sum(ddsum, 64);
         if (lane == 0) atomicAdd(&sDD, ddsum);
-        // ---- T <G, H>
-        {
-            float k = 0.f;
-            if (Hs)
-                for (int e = tid; e < PN; e += kBwdThreads) k = fmaf(sG[(e / N) * GN + e % N], Hs[e], k);
-            k = lane_group_sum(k, 64);
-            if (lane == 0) atomicAdd(&sK, k);
-        }
         __syncthreads();
 
         // ---- R = L o dt o S o V, then prefix sums of each row over r < t
-        if (tid < Q) {
-            const int s = tid;
-            float run = 0.f;
-            for (int r = 0; r < Q; ++r) {
-                const float R = (r <= s) ? sS[s * LQ + r] * sg.dt[r] * sV[s * LQ + r] : 0.f;
-                sV[s * LQ + r] = run;          // sum_{r' < r} R_{s r'}
-                run += R;
+        // (eight lanes per row, eight columns each)
+        static_assert(kBwdThreads == 8 * Q, "eight lanes per row of the chunk");
+        {
+            const int s = tid >> 3, q = tid & 7;
+            float Rv[8], loc = 0.f;
+#pragma unroll
+            for (int c8 = 0; c8 < 8; ++c8) {
+                const int r = 8 * q + c8;
+                Rv[c8] = (r <= s) ? sS[s * LQ + r] * sg.dt[r] * sV[s * LQ + r] : 0.f;
+                loc += Rv[c8];
+            }
+            float incl = loc;
+#pragma unroll
+            for (int off = 1; off < 8; off <<= 1) {
+                const float o = __shfl_up(incl, off, 8);
+                if (q >= off) incl += o;
+            }
+            float run = incl - loc;
+#pragma unroll
+            for (int c8 = 0; c8 < 8; ++c8) {
+                sV[s * LQ + 8 * q + c8] = run;   // sum_{r' < r} R_{s r'}
+                run += Rv[c8];
             }
         }
         __syncthreads();
-        if (tid < Q) {
-            const int t = tid;
+        {
+            const int t = tid >> 3, q = tid & 7;
             float dl = 0.f;
-            if (t < nvalid) {
-                for (int s = t; s < Q; ++s) dl += sV[s * LQ + t] + sq[s];
-                for (int r = 0; r < t; ++r) dl += sp[r];
-                dl += sg.T * sK;
-                if (sg.flag[t]) dl = 0.f;   // a_t is 0 there, not exp(dt A)
-                a.ddt[((int64_t)b * L + t0 + t) * H + h] = fmaf(A_h, dl, sxdX[t]);
+#pragma unroll
+            for (int k8 = 0; k8 < 8; ++k8) {
+                const int s = q + 8 * k8;
+                if (s >= t) dl += sV[s * LQ + t] + sq[s];
+                else dl += sp[s];
             }
-            sdl[t] = (t < nvalid) ? sg.dt[t] * dl : 0.f;
+            dl = lane_group_sum(dl, 8);
+            if (q == 0) {
+                if (t < nvalid) {
+                    dl += sg.T * sK;
+                    if (sg.flag[t]) dl = 0.f;   // a_t is 0 there, not exp(dt A)
+                    a.ddt[((int64_t)b * L + t0 + t) * H + h] = fmaf(A_h, dl, sxdX[t]);
+                }
+                sdl[t] = (t < nvalid) ? sg.dt[t] * dl : 0.f;
+            }
         }
         // ---- G_{c-1} = T G_c + sum_i u_i dy_i C_i^T: tiles over (p, n)
         for (int job = wave; job < (P / 16) * (N / 16); job += kBwdThreads / 64) {
             const int Pb = job % (P / 16), Nb = job / (P / 16);
             const int p = Pb * 16 + l16, n = Nb * 16 + l16;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
-            for (int k = 0; k < nvalid; k += 8) {
-                const int i = k + g, i2 = k + 4 + g;
-                const float dv = ok(i) ? sg.u[i] * bwd_ld<IO>(a.dy, xo(t0 + i) + p) : 0.f;
-                const float cv = ok(i) ? bwd_ld<IO>(a.C, bo(t0 + i) + n) : 0.f;
-                const float dv2 = ok(i2) ? sg.u[i2] * bwd_ld<IO>(a.dy, xo(t0 + i2) + p) : 0.f;
-                const float cv2 = ok(i2) ? bwd_ld<IO>(a.C, bo(t0 + i2) + n) : 0.f;
-                acc = mfma_f32(dv, cv, acc);
-                acc2 = mfma_f32(dv2, cv2, acc2);
+            float dv[4 * NB], cv[4 * NB];
+#pragma unroll
+            for (int st = 0; st < 4 * NB; ++st) {
+                const int i = 4 * st + g;
+                dv[st] = ld1(dyc, cl(i) * xs + p);
+                cv[st] = ld1(Cc, cl(i) * bs + n);
+            }
+#pragma unroll
+            for (int st = 0; st < 4 * NB; st += 2) {
+                if (4 * st >= nvalid) break;
+                const int i = 4 * st + g;
+                acc = mfma_f32((ok(i) ? sg.u[i] : 0.f) * dv[st], cv[st], acc);
+                acc2 = mfma_f32((ok(i + 4) ? sg.u[i + 4] : 0.f) * dv[st + 1], cv[st + 1], acc2);
             }
             mfma_f32_fence(acc, acc2);
 #pragma unroll
@@ -416,8 +578,13 @@ __global__ __launch_bounds__(256) void ssd_bwd_reduce_kernel(BwdArgs a) {
 
 void launch_bwd(bool bf16_io, const BwdArgs &a, hipStream_t stream) {
     const dim3 grid(a.batch * a.nheads), block(kBwdThreads);
-    if (bf16_io) hipLaunchKernelGGL(ssd_bwd_kernel<bf16>, grid, block, 0, stream, a);
-    else hipLaunchKernelGGL(ssd_bwd_kernel<float>, grid, block, 0, stream, a);
+    auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, block, 0, stream, a); };
+    switch (a.headdim) {   // the API admits 16, 32, 64 and 128
+    case 16: bf16_io ? go(ssd_bwd_kernel<bf16, 16>) : go(ssd_bwd_kernel<float, 16>); break;
+    case 32: bf16_io ? go(ssd_bwd_kernel<bf16, 32>) : go(ssd_bwd_kernel<float, 32>); break;
+    case 64: bf16_io ? go(ssd_bwd_kernel<bf16, 64>) : go(ssd_bwd_kernel<float, 64>); break;
+    default: bf16_io ? go(ssd_bwd_kernel<bf16, 128>) : go(ssd_bwd_kernel<float, 128>); break;
+    }
     const int64_t total = (int64_t)a.batch * a.seqlen * a.ngroups * a.dstate + a.nheads;
     hipLaunchKernelGGL(ssd_bwd_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
                        stream, a);
