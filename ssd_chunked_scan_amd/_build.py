@@ -171,6 +171,7 @@ def check_mfma_result_reads(asm_text: str, where: str) -> int:
 _VMEM = ("global_load", "global_store", "buffer_load", "buffer_store", "scratch_load",
          "scratch_store", "flat_load", "flat_store", "global_atomic", "buffer_atomic")
 _WAIT_VM = re.compile(r"s_waitcnt\s+vmcnt\((\d+)\)")
+VMCNT_MAX = 63
 
 
 def check_counted_barrier_waits(asm_text: str, where: str) -> int:
@@ -185,7 +186,9 @@ def check_counted_barrier_waits(asm_text: str, where: str) -> int:
             if kind != "ins":
                 continue
             m = _WAIT_VM.search(text)
-            if not m or int(m.group(1)) == 0:
+            # vmcnt(0): waits for all; vmcnt(63), the field's maximum on gfx9,
+            # waits for none (the wait is for other counters)
+            if not m or int(m.group(1)) in (0, VMCNT_MAX):
                 continue
             nxt = next((t for k, t in items[i + 1:] if k == "ins"), "")
             if not nxt.startswith("s_barrier"):

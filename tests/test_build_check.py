@@ -139,3 +139,16 @@ def test_fp32_mfma_needs_eleven_wait_states():
         _build.check_mfma_result_reads(asm, "t")
     ok = asm.replace("s_nop 7", "s_nop 7\ns_nop 2")
     assert _build.check_mfma_result_reads(ok, "t") == 1
+
+
+def test_barrier_wait_at_vmcnt_max_waits_for_no_vector_memory():
+    """s_waitcnt vmcnt(63) (the field's maximum) leaves every vector-memory
+    operation in flight on purpose: it is not a counted wait."""
+    asm = "\n".join([
+        "k:",
+        "global_load_lds_dwordx4 v1, s[0:1]",
+        "s_waitcnt vmcnt(63) expcnt(7) lgkmcnt(0)",
+        "s_barrier",
+        "s_endpgm",
+    ])
+    _build.check_counted_barrier_waits(asm, "t")
