@@ -140,6 +140,14 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
     __shared__ float sw[Q];                 // decay from token j to the chunk end
     __shared__ float sq[Q], sp[Q], sxdX[Q], sdl[Q];
     __shared__ float sK, sDD, sDA;
+    // bf16 inputs with headdim <= 64: the chunk's x, dy, B and C rows are
+    // staged in LDS (56 KB), read there by every job.  Row pitches of 40 and
+    // 72 dwords (8 mod 32 banks) keep four rows of 16 consecutive columns on
+    // distinct banks.
+    constexpr bool STAGE = std::is_same<IO, bf16>::value && P <= 64;
+    constexpr int XPe = 80, BPe = 144;
+    __shared__ __attribute__((aligned(16))) bf16 sXs[STAGE ? Q * XPe : 8], sDYs[STAGE ? Q * XPe : 8];
+    __shared__ __attribute__((aligned(16))) bf16 sBs[STAGE ? Q * BPe : 8], sCs[STAGE ? Q * BPe : 8];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: job branches are scalar
@@ -156,7 +164,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
     // element offsets of token t's rows
     auto xo = [&](int t) { return (((int64_t)b * L + t) * H + h) * P; };
     auto bo = [&](int t) { return (((int64_t)b * L + t) * G + grp) * N; };
-    const int xs = H * P, bs = G * N;
+    const int gxs = H * P, gbs = G * N;     // token strides in global memory
+    const int xs = STAGE ? XPe : gxs, bs = STAGE ? BPe : gbs;   // ... where operands are read
 
     for (int e = tid; e < PN; e += kBwdThreads)
         sG[(e / N) * GN + e % N] = a.dfinal ? a.dfinal[(int64_t)bh * PN + e] : 0.f;
@@ -195,6 +204,53 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
                 hv[4 * u + e] = Hc ? *at_off(Hc, (16 * u + 4 * g_ + e) * N + n) : 0.f;
     };
     load_hv(a.nchunks - 1, tid & 15, (tid & 63) >> 4);
+    // staging payload of a chunk, 16 bytes a piece, loaded a chunk ahead into
+    // registers (rows past the end of the row hold the last valid token)
+    constexpr int NXS = (Q * (P / 8) + kBwdThreads - 1) / kBwdThreads;
+    constexpr int NBS = (Q * 16 + kBwdThreads - 1) / kBwdThreads;
+    uint4 stx[NXS], sty[NXS], stb[NBS], stc[NBS];
+    auto stage_load = [&](int cc) {
+        const int t0c = cc * Q, nv = min(Q, L - t0c);
+#pragma unroll
+        for (int k = 0; k < NXS; ++k) {
+            const int e = tid + k * kBwdThreads;
+            if (e < Q * (P / 8)) {
+                const int t = t0c + min(e / (P / 8), nv - 1), q8 = e % (P / 8);
+                stx[k] = *(const uint4 *)((const bf16 *)a.x + xo(t) + q8 * 8);
+                sty[k] = *(const uint4 *)((const bf16 *)a.dy + xo(t) + q8 * 8);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < NBS; ++k) {
+            const int e = tid + k * kBwdThreads;
+            if (e < Q * (N / 8)) {
+                const int t = t0c + min(e / (N / 8), nv - 1), q8 = e % (N / 8);
+                stb[k] = *(const uint4 *)((const bf16 *)a.B + bo(t) + q8 * 8);
+                stc[k] = *(const uint4 *)((const bf16 *)a.C + bo(t) + q8 * 8);
+            }
+        }
+    };
+    auto stage_store = [&]() {
+#pragma unroll
+        for (int k = 0; k < NXS; ++k) {
+            const int e = tid + k * kBwdThreads;
+            if (e < Q * (P / 8)) {
+                const int r = e / (P / 8), q8 = e % (P / 8);
+                *(uint4 *)&sXs[r * XPe + q8 * 8] = stx[k];
+                *(uint4 *)&sDYs[r * XPe + q8 * 8] = sty[k];
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < NBS; ++k) {
+            const int e = tid + k * kBwdThreads;
+            if (e < Q * (N / 8)) {
+                const int r = e / (N / 8), q8 = e % (N / 8);
+                *(uint4 *)&sBs[r * BPe + q8 * 8] = stb[k];
+                *(uint4 *)&sCs[r * BPe + q8 * 8] = stc[k];
+            }
+        }
+    };
+    if constexpr (STAGE) stage_load(a.nchunks - 1);
     for (int c = a.nchunks - 1; c >= 0; --c) {
         const int t0 = c * Q;
         const int nvalid = min(Q, L - t0);
@@ -215,10 +271,21 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
         // the chunk's first token rows; tokens step by xs (x, dy) or bs (B, C)
         // elements, so in-chunk offsets fit 32 bits and the loads take a
         // scalar base
-        const IO *xc = (const IO *)a.x + xo(t0);
-        const IO *dyc = (const IO *)a.dy + xo(t0);
-        const IO *Bc = (const IO *)a.B + bo(t0);
-        const IO *Cc = (const IO *)a.C + bo(t0);
+        const IO *xc, *dyc, *Bc, *Cc;
+        if constexpr (STAGE) {
+            // the previous chunk's last reads of the staged rows are behind
+            // its final barrier
+            stage_store();
+            xc = (const IO *)sXs;
+            dyc = (const IO *)sDYs;
+            Bc = (const IO *)sBs;
+            Cc = (const IO *)sCs;
+        } else {
+            xc = (const IO *)a.x + xo(t0);
+            dyc = (const IO *)a.dy + xo(t0);
+            Bc = (const IO *)a.B + bo(t0);
+            Cc = (const IO *)a.C + bo(t0);
+        }
 
         // ---- segsum values of the chunk (the forward kernels' helpers)
         int flag_any = 0;
@@ -506,6 +573,11 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
                 sdl[t] = (t < nvalid) ? sg.dt[t] * dl : 0.f;
             }
         }
+        // The next chunk's rows go into flight here, after this chunk's last
+        // global store: vmcnt also counts stores, and the wait for these loads
+        // at the next chunk's start then finds nothing younger to drain.
+        if constexpr (STAGE)
+            if (c > 0) stage_load(c - 1);
         // ---- G_{c-1} = T G_c + sum_i u_i dy_i C_i^T: tiles over (p, n)
         for (int job = wave; job < (P / 16) * (N / 16); job += kBwdThreads / 64) {
             const int Pb = job % (P / 16), Nb = job / (P / 16);
