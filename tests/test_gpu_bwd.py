@@ -84,31 +84,47 @@ def test_bwd_without_optional_inputs(io):
     _check(g, ref, TOL[io], wl.name)
 
 
-def test_bwd_full_layer_sampled_heads():
-    """The 2.7B-shaped layer (batch 8, seqlen 2048, 80 heads, headdim 64,
-    dstate 128, bf16) in the launch configuration bench.py --backward times.
-    Heads are independent in the forward pass, so dx and ddt of one (row,
-    head) are the oracle's gradients of that head alone: three sampled heads
-    (first, middle, last workgroup) against the fp64 oracle on their slices."""
+def _sampled_heads_vs_oracle(wl_name, heads, seed):
+    """ssd_bwd over a whole workload; dx and ddt of sampled (row, head)
+    pairs against the oracle on those heads alone (heads are independent in
+    the forward pass, so these are the same gradients)."""
     import torch
     import ssd_chunked_scan_amd as ssd
-    wl = workloads.WORKLOADS["layer27b"]
+    wl = workloads.WORKLOADS[wl_name]
     inp = workloads.make_inputs(wl, seed=0)
     t = to_device(inp)
-    dy = workloads.bf16_round(np.random.default_rng(11).standard_normal(inp.x.shape).astype(np.float32))
+    dy = workloads.bf16_round(np.random.default_rng(seed).standard_normal(inp.x.shape).astype(np.float32))
+    seq = None if inp.seq_idx is None else torch.from_numpy(inp.seq_idx).cuda()
     g = ssd.ssd_bwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"],
-                    torch.from_numpy(dy).cuda().to(torch.bfloat16))
+                    torch.from_numpy(dy).cuda().to(torch.bfloat16), seq)
     torch.cuda.synchronize()
     dx, ddt = g["dx"].cpu().numpy(), g["ddt"].cpu().numpy()
     assert np.isfinite(dx).all() and np.isfinite(ddt).all()
     hpg = wl.nheads // wl.ngroups
-    for b, h in [(0, 0), (3, 41), (wl.batch - 1, wl.nheads - 1)]:
+    for b, h in heads:
         grp = h // hpg
+        sq = None if inp.seq_idx is None else inp.seq_idx[b:b + 1]
         ref = oracle.ssd_backward(inp.x[b:b + 1, :, h:h + 1], inp.dt[b:b + 1, :, h:h + 1],
                                   inp.A[h:h + 1], inp.B[b:b + 1, :, grp:grp + 1],
                                   inp.C[b:b + 1, :, grp:grp + 1], inp.D[h:h + 1],
-                                  dy[b:b + 1, :, h:h + 1], None, None, None)
+                                  dy[b:b + 1, :, h:h + 1], sq, None, None)
         e_dx = max_rel(dx[b:b + 1, :, h:h + 1], ref["dx"])
         e_dt = max_rel(ddt[b:b + 1, :, h:h + 1], ref["ddt"])
-        print(f"layer27b bwd (b={b}, h={h}): dx {e_dx:.1e} ddt {e_dt:.1e}")
+        print(f"{wl_name} bwd (b={b}, h={h}): dx {e_dx:.1e} ddt {e_dt:.1e}")
         assert e_dx <= TOL["bf16"] and e_dt <= TOL["bf16"], (b, h, e_dx, e_dt)
+
+
+def test_bwd_packed_documents_sampled_heads():
+    """The packed-document workload (1 x 32768 tokens, 32 heads, headdim 128,
+    dstate 64, 8 groups, 8..64 documents): resets inside and across chunks,
+    heads of different groups, and the kernel's unstaged operand path
+    (headdim above 64)."""
+    _sampled_heads_vs_oracle("packed", [(0, 0), (0, 29)], seed=12)
+
+
+def test_bwd_full_layer_sampled_heads():
+    """The 2.7B-shaped layer (batch 8, seqlen 2048, 80 heads, headdim 64,
+    dstate 128, bf16) in the launch configuration bench.py --backward times
+    (the kernel's LDS-staged operand path): first, middle and last
+    workgroup's heads."""
+    _sampled_heads_vs_oracle("layer27b", [(0, 0), (3, 41), (7, 79)], seed=11)
