@@ -355,18 +355,42 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
                 const IO *Ab = isS ? Cc : dyc, *Bb = isS ? Bc : xc;   // chunk bases
                 const unsigned ao = cl(i) * (isS ? bs : xs), bo_ = cl(j) * (isS ? bs : xs);
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
-                Pack<IO> av[kMaxK / 16], bv[kMaxK / 16];
+                if constexpr (STAGE) {
+                    // bf16 rows in LDS: v_mfma_f32_16x16x32_bf16, a lane
+                    // giving eight consecutive elements of its row (products
+                    // of bf16 values are exact, accumulation fp32 as above)
 #pragma unroll
-                for (int u = 0; u < kMaxK / 16; ++u) {
-                    const bool in = 16 * u < K;
-                    av[u] = in ? ld_pack<IO>(Ab, ao + 16 * u + 4 * g) : Pack<IO>{};
-                    bv[u] = in ? ld_pack<IO>(Bb, bo_ + 16 * u + 4 * g) : Pack<IO>{};
-                }
+                    for (int u = 0; u < kMaxK / 32; u += 2) {
+                        if (32 * u >= K) break;
+                        const bf16x8 a0 = *(const bf16x8 *)at_off(Ab, ao + 32 * u + 8 * g);
+                        const bf16x8 b0 = *(const bf16x8 *)at_off(Bb, bo_ + 32 * u + 8 * g);
+                        acc = mfma_bf16(a0, b0, acc);
+                        if (32 * (u + 1) < K) {
+                            const bf16x8 a1 = *(const bf16x8 *)at_off(Ab, ao + 32 * (u + 1) + 8 * g);
+                            const bf16x8 b1 = *(const bf16x8 *)at_off(Bb, bo_ + 32 * (u + 1) + 8 * g);
+                            acc2 = mfma_bf16(a1, b1, acc2);
+                        }
+                    }
+                    if (K == 16) {   // a half step: the upper eight of the 32 contraction slots are 0
+                        const bf16x8 z = {};
+                        const bf16x8 a0 = g < 2 ? *(const bf16x8 *)at_off(Ab, ao + 8 * g) : z;
+                        const bf16x8 b0 = g < 2 ? *(const bf16x8 *)at_off(Bb, bo_ + 8 * g) : z;
+                        acc = mfma_bf16(a0, b0, acc);
+                    }
+                } else {
+                    Pack<IO> av[kMaxK / 16], bv[kMaxK / 16];
 #pragma unroll
-                for (int u = 0; u < kMaxK / 16; u += 2) {
-                    if (16 * u >= K) break;
-                    acc = mfma_pack4(av[u], bv[u], acc);
-                    acc2 = mfma_pack4(av[u + 1], bv[u + 1], acc2);
+                    for (int u = 0; u < kMaxK / 16; ++u) {
+                        const bool in = 16 * u < K;
+                        av[u] = in ? ld_pack<IO>(Ab, ao + 16 * u + 4 * g) : Pack<IO>{};
+                        bv[u] = in ? ld_pack<IO>(Bb, bo_ + 16 * u + 4 * g) : Pack<IO>{};
+                    }
+#pragma unroll
+                    for (int u = 0; u < kMaxK / 16; u += 2) {
+                        if (16 * u >= K) break;
+                        acc = mfma_pack4(av[u], bv[u], acc);
+                        acc2 = mfma_pack4(av[u + 1], bv[u + 1], acc2);
+                    }
                 }
                 mfma_f32_fence(acc, acc2);
 #pragma unroll
@@ -605,10 +629,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
             }
         }
         __syncthreads();
-        if (tid == 0) {
-            float s = 0.f;
-            for (int t = 0; t < Q; ++t) s += sdl[t];
-            sDA += s;
+        static_assert(Q == 64, "one token a lane of wave 0");
+        if (tid < 64) {
+            const float s = lane_group_sum(sdl[tid], 64);
+            if (tid == 0) sDA += s;
         }
     }
     __syncthreads();
