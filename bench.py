@@ -25,6 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix
 METRIC = "SSD fwd tokens/s + HBM GB/s (% of peak), Mamba-2 2.7B layer, L=2048"
 HEAD_KERNEL_SOURCES = ("ssd_api.cpp", "ssd_common.hpp", "ssd_scan_bf16.hpp", "ssd_scan_bf16_q64.hip",
                        "ssd_scan_bf16_q128.hip", "ssd_scan_bf16_q256.hip", "ssd_segsum.hpp",
@@ -198,6 +199,21 @@ def backward_bench(wl, inp, args):
            + b * L * H * P * 4 + b * L * H * 4 + 2 * b * L * G * N * 4          # dx, ddt, dB, dC
            + 2 * b * H * nch * P * N * 4)                                       # states
     gbs = alg / (avg * 1e-3) / 1e9
+    # MFMA work the backward kernel executes (padding steps included), per
+    # 64-token chunk and (batch row, head): fp32 16x16x4 steps (2048 flop)
+    # for the products with fp32 operands; C B^T and dY X^T on bf16 16x16x32
+    # steps (16384 flop) when bf16 rows are staged (bf16 inputs, headdim <= 64),
+    # else fp32 steps.
+    nb, ntri = 4, 10                          # 16-row blocks per chunk, lower tiles
+    f32 = (nb * (P // 16) * (16 + N // 4)                 # dX: (L o S)^T dY, G B_j
+           + nb * (N // 16) * (2 * 16 + 2 * (P // 4))     # dB, dC with their state terms
+           + (P // 16) * (N // 16) * 16)                  # state adjoint update
+    staged = wl.io == "bf16" and P <= 64
+    bf = ntri * (max(1, N // 32) + max(1, P // 32)) if staged else 0
+    if not staged:
+        f32 += ntri * (N // 4 + P // 4)
+    flop = b * H * nch * (f32 * 2048 + bf * 16384)
+    tflops = flop / (avg * 1e-3) / 1e12
     print(json.dumps({
         "metric": "SSD backward time per launch", "unit": "us", "value": avg * 1e3,
         "higher_is_better": False, "steps": args.steps, "warmup": args.warmup, "dtype": wl.io,
@@ -206,6 +222,11 @@ def backward_bench(wl, inp, args):
                    "dstate": N, "ngroups": G, "backward_chunk": 64},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": alg},
+        # the backward kernel is bound by MFMA issue and latency, not HBM:
+        # executed MFMA flops over the whole pass's time (a lower bound for the
+        # kernel alone) against the fp32 matrix peak
+        "mfma": {"flop_per_launch": flop, "achieved": tflops, "peak": FP32_MFMA_PEAK_TFLOPS,
+                 "unit": "TFLOP/s", "frac": tflops / FP32_MFMA_PEAK_TFLOPS},
         "p10_us": ms[len(ms) // 10] * 1e3, "p90_us": ms[(9 * len(ms)) // 10] * 1e3}), flush=True)
 
 

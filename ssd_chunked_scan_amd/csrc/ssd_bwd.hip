@@ -1,5 +1,5 @@
-// Backward pass of the SSD forward pass (gradients of every input), fp32 on
-// the vector ALU, chunk by chunk in reverse.
+// Backward pass of the SSD forward pass (gradients of every input), chunk by
+// chunk in reverse, every product on 16x16 MFMA tiles with fp32 accumulation.
 //
 // With the chunk-entering states H_{c-1} (from the forward machinery's
 // split-local pass and affine scan, one split per 64-token chunk) and the
@@ -21,9 +21,9 @@
 //
 // where dl_t = a_t <g_t, h_{t-1}> is the gradient through the log-decay of
 // token t (zero at a document boundary: every factor spanning it is 0).  The
-// mask is evaluated row by row as nested sums leftwards from the diagonal
-// (values in [0, 1], non-increasing away from the diagonal).  One workgroup
-// per (batch row, head); dB and dC are written per head and summed over the
+// mask is built as the forward kernels build it (nested sums inside 16-token
+// sub-blocks, rank-one factors across them).  One workgroup per (batch row,
+// head) walks the chunks; dB and dC are written per head and summed over the
 // heads of a group by ssd_bwd_reduce_kernel, as are dA and dD over rows.
 #include "ssd_common.hpp"
 #include "ssd_segsum.hpp"
@@ -31,11 +31,6 @@
 #include <type_traits>
 
 namespace ssd {
-
-template <typename IO>
-__device__ inline float bwd_ld(const void *p, int64_t i) {
-    return (float)((const IO *)p)[i];
-}
 
 // Element `off` of a row base: the offset is unsigned and 32-bit, so the
 // load takes the base in scalar registers and one offset register.
