@@ -471,74 +471,89 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
             k = lane_group_sum(k, 64);
             if (lane == 0) atomicAdd(&sK, k);
         }
-        for (int job = wave; job < NB * (N / 16); job += kBwdThreads / 64) {
-            const int Nb = job % (N / 16), T = job / (N / 16);
-            const int n = Nb * 16 + l16, tr = T * 16 + l16;
-            // every global operand of the job, issued before its first MFMA
-            const int kb = 4 * (NB - T), kc = 4 * (T + 1);   // dB: i = 16 T .. Q - 1; dC: j = 0 .. 16 T + 15
-            const unsigned trow = cl(tr) * xs;
-            float cv[4 * NB], bv[4 * NB], cq[4];
-            Pack<IO> xr[PU], dr[PU];
+        // A wave takes one block of 16 state columns n and NT consecutive
+        // 16-row blocks T of it (NT = 4 at dstate 128: the whole chunk).  The
+        // B operands of those tiles (C and B columns, G columns) are the same
+        // for every T and are read once.  Steps outside a tile's triangle are
+        // removed by a select (upper tiles of V are never written).
+        {
+            const int NT = max(1, N / 32);
+            const int Nb = wave % (N / 16), T0 = (wave / (N / 16)) * NT;
+            const int n = Nb * 16 + l16;
+            if (T0 < NB) {
+                float cvs[4 * NB], bvs[4 * NB], gq[4 * PU];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) cq[r] = ld1(Cc, cl(T * 16 + 4 * g + r) * bs + n);
-#pragma unroll
-            for (int st = 0; st < 4 * NB; ++st) {
-                const int i = T * 16 + 4 * st + g, j = 4 * st + g;
-                cv[st] = ld1(Cc, cl(i) * bs + n);
-                bv[st] = ld1(Bc, cl(j) * bs + n);
-            }
-#pragma unroll
-            for (int u = 0; u < PU; ++u) {
-                xr[u] = ld_pack<IO>(xc, trow + 16 * u + 4 * g);
-                dr[u] = Hs ? ld_pack<IO>(dyc, trow + 16 * u + 4 * g) : Pack<IO>{};
-            }
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int st = 0; st < 4 * NB; ++st) {
-                const int i = T * 16 + 4 * st + g;
-                const int ic = min(i, Q - 1);
-                const float lv = sL[ic * LQ + tr] * sV[ic * LQ + tr];
-                acc = mfma_f32(st < kb ? lv : 0.f, cv[st], acc);
-            }
-#pragma unroll
-            for (int u = 0; u < PU; ++u) {
-                const float *gr = &sG[(16 * u + 4 * g) * GN + n];
-                acc2 = mfma_f32(pack_el<0>(xr[u]), gr[0], acc2);
-                acc2 = mfma_f32(pack_el<1>(xr[u]), gr[GN], acc2);
-                acc2 = mfma_f32(pack_el<2>(xr[u]), gr[2 * GN], acc2);
-                acc2 = mfma_f32(pack_el<3>(xr[u]), gr[3 * GN], acc2);
-            }
-            mfma_f32_fence(acc, acc2);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = T * 16 + 4 * g + r;
-                if (ok(t)) a.dB_head[(((int64_t)b * L + t0 + t) * H + h) * N + n] = sg.dt[t] * fmaf(sw[t], acc2[r], acc[r]);
-            }
-            acc = f32x4{0.f, 0.f, 0.f, 0.f};
-            acc2 = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int st = 0; st < 4 * NB; ++st) {
-                const int j = 4 * st + g;
-                acc = mfma_f32(st < kc ? sL[tr * LQ + j] * sg.dt[j] * sV[tr * LQ + j] : 0.f, bv[st], acc);
-            }
-#pragma unroll
-            for (int u = 0; u < PU; ++u) {
-                acc2 = mfma_f32(pack_el<0>(dr[u]), hv[4 * u], acc2);
-                acc2 = mfma_f32(pack_el<1>(dr[u]), hv[4 * u + 1], acc2);
-                acc2 = mfma_f32(pack_el<2>(dr[u]), hv[4 * u + 2], acc2);
-                acc2 = mfma_f32(pack_el<3>(dr[u]), hv[4 * u + 3], acc2);
-            }
-            mfma_f32_fence(acc, acc2);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = T * 16 + 4 * g + r;
-                float qv = 0.f;
-                if (ok(t)) {
-                    a.dC_head[(((int64_t)b * L + t0 + t) * H + h) * N + n] = fmaf(sg.u[t], acc2[r], acc[r]);
-                    qv = sg.u[t] * acc2[r] * cq[r];
+                for (int st = 0; st < 4 * NB; ++st) {
+                    const int i = 4 * st + g;
+                    cvs[st] = ld1(Cc, cl(i) * bs + n);
+                    bvs[st] = ld1(Bc, cl(i) * bs + n);
                 }
-                qv = row_sum16(qv);
-                if (l16 == 0 && ok(t)) atomicAdd(&sq[t], qv);
+#pragma unroll
+                for (int u = 0; u < PU; ++u)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) gq[4 * u + e] = sG[(16 * u + 4 * g + e) * GN + n];
+                for (int T = T0; T < T0 + NT; ++T) {
+                    const int tr = T * 16 + l16;
+                    const unsigned trow = cl(tr) * xs;
+                    Pack<IO> xr[PU], dr[PU];
+                    float cq[4];
+#pragma unroll
+                    for (int u = 0; u < PU; ++u) {
+                        xr[u] = ld_pack<IO>(xc, trow + 16 * u + 4 * g);
+                        dr[u] = Hs ? ld_pack<IO>(dyc, trow + 16 * u + 4 * g) : Pack<IO>{};
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) cq[r] = ld1(Cc, cl(T * 16 + 4 * g + r) * bs + n);
+                    // dB: i = 16 T .. Q - 1;  G^T x_t
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int st = 0; st < 4 * NB; ++st) {
+                        const int i = 4 * st + g;
+                        const float lv = sL[i * LQ + tr] * sV[i * LQ + tr];
+                        acc = mfma_f32(st >= 4 * T ? lv : 0.f, cvs[st], acc);
+                    }
+#pragma unroll
+                    for (int u = 0; u < PU; ++u) {
+                        acc2 = mfma_f32(pack_el<0>(xr[u]), gq[4 * u], acc2);
+                        acc2 = mfma_f32(pack_el<1>(xr[u]), gq[4 * u + 1], acc2);
+                        acc2 = mfma_f32(pack_el<2>(xr[u]), gq[4 * u + 2], acc2);
+                        acc2 = mfma_f32(pack_el<3>(xr[u]), gq[4 * u + 3], acc2);
+                    }
+                    mfma_f32_fence(acc, acc2);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int t = T * 16 + 4 * g + r;
+                        if (ok(t)) a.dB_head[(((int64_t)b * L + t0 + t) * H + h) * N + n] = sg.dt[t] * fmaf(sw[t], acc2[r], acc[r]);
+                    }
+                    // dC: j = 0 .. 16 T + 15;  H^T dy_t
+                    acc = f32x4{0.f, 0.f, 0.f, 0.f};
+                    acc2 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int st = 0; st < 4 * NB; ++st) {
+                        const int j = 4 * st + g;
+                        const float lv = sL[tr * LQ + j] * sg.dt[j] * sV[tr * LQ + j];
+                        acc = mfma_f32(st < 4 * (T + 1) ? lv : 0.f, bvs[st], acc);
+                    }
+#pragma unroll
+                    for (int u = 0; u < PU; ++u) {
+                        acc2 = mfma_f32(pack_el<0>(dr[u]), hv[4 * u], acc2);
+                        acc2 = mfma_f32(pack_el<1>(dr[u]), hv[4 * u + 1], acc2);
+                        acc2 = mfma_f32(pack_el<2>(dr[u]), hv[4 * u + 2], acc2);
+                        acc2 = mfma_f32(pack_el<3>(dr[u]), hv[4 * u + 3], acc2);
+                    }
+                    mfma_f32_fence(acc, acc2);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int t = T * 16 + 4 * g + r;
+                        float qv = 0.f;
+                        if (ok(t)) {
+                            a.dC_head[(((int64_t)b * L + t0 + t) * H + h) * N + n] = fmaf(sg.u[t], acc2[r], acc[r]);
+                            qv = sg.u[t] * acc2[r] * cq[r];
+                        }
+                        qv = row_sum16(qv);
+                        if (l16 == 0 && ok(t)) atomicAdd(&sq[t], qv);
+                    }
+                }
             }
         }
         if (c > 0) load_hv(c - 1, l16, g);
