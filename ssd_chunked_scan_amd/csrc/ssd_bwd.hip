@@ -403,57 +403,63 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
         // ---- dX (and x . dX, p_r), dx, and dy . x for dD: tiles over (j, p)
         //   acc  = sum_{i >= j} (L o S)[i][j] dy_i[p]     (i: LDS column, dy rows)
         //   acc2 = (B G^T)[j][p] = G B_j                  (n: B rows, G rows)
-        for (int job = wave; job < NB * (P / 16); job += kBwdThreads / 64) {
-            const int J = job % NB, Pb = job / NB;
-            const int p = Pb * 16 + l16, jr = J * 16 + l16;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
-            const int ksteps = 4 * (NB - J);          // steps of 4 over i = 16 J .. Q - 1
-            float dyv[4 * NB];
-            Pack<IO> bv[kMaxK / 16];
-            const unsigned brow = cl(jr) * bs;
+        // A wave takes one block of 16 headdim columns p and NJ consecutive
+        // 16-row blocks J of it; dy's columns and G's rows for p are read once
+        // for all of them.  Steps above a tile's triangle are removed by a
+        // select (upper tiles of S are never written).
+        {
+            const int NJ = max(1, PU / 2);
+            const int Pb = wave % PU, J0 = (wave / PU) * NJ;
+            const int p = Pb * 16 + l16;
+            if (J0 < NB) {
+                float dyv[4 * NB];
+                float4 gv[kMaxK / 16];
 #pragma unroll
-            for (int st = 0; st < 4 * NB; ++st) {
-                const int i = J * 16 + 4 * st + g;
-                dyv[st] = ld1(dyc, cl(i) * xs + p);
-            }
+                for (int st = 0; st < 4 * NB; ++st) dyv[st] = ld1(dyc, cl(4 * st + g) * xs + p);
 #pragma unroll
-            for (int u = 0; u < kMaxK / 16; ++u)
-                bv[u] = (16 * u < N) ? ld_pack<IO>(Bc, brow + 16 * u + 4 * g) : Pack<IO>{};
+                for (int u = 0; u < kMaxK / 16; ++u)   // blocks past N: B is 0 there, G read at a valid column
+                    gv[u] = *(const float4 *)&sG[p * GN + min(16 * u, N - 16) + 4 * g];
+                for (int J = J0; J < J0 + NJ; ++J) {
+                    const int jr = J * 16 + l16;
+                    const unsigned brow = cl(jr) * bs;
+                    Pack<IO> bv[kMaxK / 16];
 #pragma unroll
-            for (int st = 0; st < 4 * NB; ++st)
-            {
-                // steps past the range read a valid row and contribute 0
-                const float sv = sS[min(J * 16 + 4 * st + g, Q - 1) * LQ + jr];
-                acc = mfma_f32(st < ksteps ? sv : 0.f, dyv[st], acc);
-            }
+                    for (int u = 0; u < kMaxK / 16; ++u)
+                        bv[u] = (16 * u < N) ? ld_pack<IO>(Bc, brow + 16 * u + 4 * g) : Pack<IO>{};
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int u = 0; u < kMaxK / 16; ++u) {
-                // blocks past N: B is 0 there, G read at a valid column
-                const float4 gv = *(const float4 *)&sG[p * GN + min(16 * u, N - 16) + 4 * g];
-                acc2 = mfma_f32(pack_el<0>(bv[u]), gv.x, acc2);
-                acc2 = mfma_f32(pack_el<1>(bv[u]), gv.y, acc2);
-                acc2 = mfma_f32(pack_el<2>(bv[u]), gv.z, acc2);
-                acc2 = mfma_f32(pack_el<3>(bv[u]), gv.w, acc2);
-            }
-            mfma_f32_fence(acc, acc2);
+                    for (int st = 0; st < 4 * NB; ++st) {   // i = 16 J .. Q - 1
+                        const float sv = sS[(4 * st + g) * LQ + jr];
+                        acc = mfma_f32(st >= 4 * J ? sv : 0.f, dyv[st], acc);
+                    }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int j = J * 16 + 4 * g + r;
-                float xd = 0.f, pr = 0.f;
-                if (ok(j)) {
-                    const float dX = fmaf(sw[j], acc2[r], acc[r]);
-                    const float xv = ld1(xc, j * xs + p);
-                    const float dyv = ld1(dyc, j * xs + p);
-                    a.dx[xo(t0 + j) + p] = fmaf(sg.dt[j], dX, D_h * dyv);
-                    xd = xv * dX;
-                    pr = sg.wcd[j] * xv * acc2[r];
-                    ddsum = fmaf(dyv, xv, ddsum);
-                }
-                xd = row_sum16(xd);
-                pr = row_sum16(pr);
-                if (l16 == 0 && ok(j)) {
-                    atomicAdd(&sxdX[j], xd);
-                    atomicAdd(&sp[j], pr);
+                    for (int u = 0; u < kMaxK / 16; ++u) {
+                        acc2 = mfma_f32(pack_el<0>(bv[u]), gv[u].x, acc2);
+                        acc2 = mfma_f32(pack_el<1>(bv[u]), gv[u].y, acc2);
+                        acc2 = mfma_f32(pack_el<2>(bv[u]), gv[u].z, acc2);
+                        acc2 = mfma_f32(pack_el<3>(bv[u]), gv[u].w, acc2);
+                    }
+                    mfma_f32_fence(acc, acc2);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int j = J * 16 + 4 * g + r;
+                        float xd = 0.f, pr = 0.f;
+                        if (ok(j)) {
+                            const float dX = fmaf(sw[j], acc2[r], acc[r]);
+                            const float xv = ld1(xc, j * xs + p);
+                            const float dyj = ld1(dyc, j * xs + p);
+                            a.dx[xo(t0 + j) + p] = fmaf(sg.dt[j], dX, D_h * dyj);
+                            xd = xv * dX;
+                            pr = sg.wcd[j] * xv * acc2[r];
+                            ddsum = fmaf(dyj, xv, ddsum);
+                        }
+                        xd = row_sum16(xd);
+                        pr = row_sum16(pr);
+                        if (l16 == 0 && ok(j)) {
+                            atomicAdd(&sxdX[j], xd);
+                            atomicAdd(&sp[j], pr);
+                        }
+                    }
                 }
             }
         }
@@ -613,29 +619,37 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
         if constexpr (STAGE)
             if (c > 0) stage_load(c - 1);
         // ---- G_{c-1} = T G_c + sum_i u_i dy_i C_i^T: tiles over (p, n)
-        for (int job = wave; job < (P / 16) * (N / 16); job += kBwdThreads / 64) {
-            const int Pb = job % (P / 16), Nb = job / (P / 16);
-            const int p = Pb * 16 + l16, n = Nb * 16 + l16;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
-            float dv[4 * NB], cv[4 * NB];
+        // A wave keeps one block of 16 headdim rows p (the block count divides
+        // the wave count) over its tiles, so u o dy for those rows is read once.
+        {
+            constexpr int kWaves = kBwdThreads / 64;
+            static_assert(kWaves % 8 == 0, "headdim blocks divide the wave count");
+            const int Pb = wave % PU;
+            const int p = Pb * 16 + l16;
+            float dv[4 * NB];
 #pragma unroll
             for (int st = 0; st < 4 * NB; ++st) {
                 const int i = 4 * st + g;
-                dv[st] = ld1(dyc, cl(i) * xs + p);
-                cv[st] = ld1(Cc, cl(i) * bs + n);
+                dv[st] = (ok(i) ? sg.u[i] : 0.f) * ld1(dyc, cl(i) * xs + p);
             }
+            for (int Nb = wave / PU; Nb < N / 16; Nb += kWaves / PU) {
+                const int n = Nb * 16 + l16;
+                float cv[4 * NB];
 #pragma unroll
-            for (int st = 0; st < 4 * NB; st += 2) {
-                if (4 * st >= nvalid) break;
-                const int i = 4 * st + g;
-                acc = mfma_f32((ok(i) ? sg.u[i] : 0.f) * dv[st], cv[st], acc);
-                acc2 = mfma_f32((ok(i + 4) ? sg.u[i + 4] : 0.f) * dv[st + 1], cv[st + 1], acc2);
-            }
-            mfma_f32_fence(acc, acc2);
+                for (int st = 0; st < 4 * NB; ++st) cv[st] = ld1(Cc, cl(4 * st + g) * bs + n);
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float *gp = &sG[(Pb * 16 + 4 * g + r) * GN + n];
-                *gp = fmaf(sg.T, *gp, acc[r] + acc2[r]);
+                for (int st = 0; st < 4 * NB; st += 2) {
+                    if (4 * st >= nvalid) break;
+                    acc = mfma_f32(dv[st], cv[st], acc);
+                    acc2 = mfma_f32(dv[st + 1], cv[st + 1], acc2);
+                }
+                mfma_f32_fence(acc, acc2);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float *gp = &sG[(Pb * 16 + 4 * g + r) * GN + n];
+                    *gp = fmaf(sg.T, *gp, acc[r] + acc2[r]);
+                }
             }
         }
         __syncthreads();
