@@ -199,50 +199,51 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
                 hv[4 * u + e] = Hc ? *at_off(Hc, (16 * u + 4 * g_ + e) * N + n) : 0.f;
     };
     load_hv(a.nchunks - 1, tid & 15, (tid & 63) >> 4);
-    // staging payload of a chunk, 16 bytes a piece, loaded a chunk ahead into
-    // registers (rows past the end of the row hold the last valid token)
-    constexpr int NXS = (Q * (P / 8) + kBwdThreads - 1) / kBwdThreads;
-    constexpr int NBS = (Q * 16 + kBwdThreads - 1) / kBwdThreads;
-    uint4 stx[NXS], sty[NXS], stb[NBS], stc[NBS];
+    // Staging payload of a chunk, 16 bytes a piece, loaded a chunk ahead into
+    // registers (rows past the end of the row hold the last valid token): one
+    // piece of x and of dy (Q * P / 8 <= 512 pieces at headdim <= 64) and two
+    // of B and of C (Q * N / 8 <= 1024) per thread.  Named registers, not
+    // arrays: arrays held across the chunk loop were placed in scratch memory.
+    static_assert(!STAGE || (Q * (P / 8) <= kBwdThreads && Q * 16 <= 2 * kBwdThreads),
+                  "staging pieces per thread");
+    uint4 stx0 = {}, sty0 = {}, stb0 = {}, stb1 = {}, stc0 = {}, stc1 = {};
     auto stage_load = [&](int cc) {
         const int t0c = cc * Q, nv = min(Q, L - t0c);
-#pragma unroll
-        for (int k = 0; k < NXS; ++k) {
-            const int e = tid + k * kBwdThreads;
-            if (e < Q * (P / 8)) {
-                const int t = t0c + min(e / (P / 8), nv - 1), q8 = e % (P / 8);
-                stx[k] = *(const uint4 *)((const bf16 *)a.x + xo(t) + q8 * 8);
-                sty[k] = *(const uint4 *)((const bf16 *)a.dy + xo(t) + q8 * 8);
-            }
+        if (tid < Q * (P / 8)) {
+            const int t = t0c + min(tid / (P / 8), nv - 1), q8 = tid % (P / 8);
+            stx0 = *(const uint4 *)((const bf16 *)a.x + xo(t) + q8 * 8);
+            sty0 = *(const uint4 *)((const bf16 *)a.dy + xo(t) + q8 * 8);
         }
-#pragma unroll
-        for (int k = 0; k < NBS; ++k) {
-            const int e = tid + k * kBwdThreads;
-            if (e < Q * (N / 8)) {
-                const int t = t0c + min(e / (N / 8), nv - 1), q8 = e % (N / 8);
-                stb[k] = *(const uint4 *)((const bf16 *)a.B + bo(t) + q8 * 8);
-                stc[k] = *(const uint4 *)((const bf16 *)a.C + bo(t) + q8 * 8);
-            }
+        const int nb8 = N / 8;
+        if (tid < Q * nb8) {
+            const int t = t0c + min(tid / nb8, nv - 1), q8 = tid % nb8;
+            stb0 = *(const uint4 *)((const bf16 *)a.B + bo(t) + q8 * 8);
+            stc0 = *(const uint4 *)((const bf16 *)a.C + bo(t) + q8 * 8);
+        }
+        if (tid + kBwdThreads < Q * nb8) {
+            const int e = tid + kBwdThreads;
+            const int t = t0c + min(e / nb8, nv - 1), q8 = e % nb8;
+            stb1 = *(const uint4 *)((const bf16 *)a.B + bo(t) + q8 * 8);
+            stc1 = *(const uint4 *)((const bf16 *)a.C + bo(t) + q8 * 8);
         }
     };
     auto stage_store = [&]() {
-#pragma unroll
-        for (int k = 0; k < NXS; ++k) {
-            const int e = tid + k * kBwdThreads;
-            if (e < Q * (P / 8)) {
-                const int r = e / (P / 8), q8 = e % (P / 8);
-                *(uint4 *)&sXs[r * XPe + q8 * 8] = stx[k];
-                *(uint4 *)&sDYs[r * XPe + q8 * 8] = sty[k];
-            }
+        if (tid < Q * (P / 8)) {
+            const int r = tid / (P / 8), q8 = tid % (P / 8);
+            *(uint4 *)&sXs[r * XPe + q8 * 8] = stx0;
+            *(uint4 *)&sDYs[r * XPe + q8 * 8] = sty0;
         }
-#pragma unroll
-        for (int k = 0; k < NBS; ++k) {
-            const int e = tid + k * kBwdThreads;
-            if (e < Q * (N / 8)) {
-                const int r = e / (N / 8), q8 = e % (N / 8);
-                *(uint4 *)&sBs[r * BPe + q8 * 8] = stb[k];
-                *(uint4 *)&sCs[r * BPe + q8 * 8] = stc[k];
-            }
+        const int nb8 = N / 8;
+        if (tid < Q * nb8) {
+            const int r = tid / nb8, q8 = tid % nb8;
+            *(uint4 *)&sBs[r * BPe + q8 * 8] = stb0;
+            *(uint4 *)&sCs[r * BPe + q8 * 8] = stc0;
+        }
+        if (tid + kBwdThreads < Q * nb8) {
+            const int e = tid + kBwdThreads;
+            const int r = e / nb8, q8 = e % nb8;
+            *(uint4 *)&sBs[r * BPe + q8 * 8] = stb1;
+            *(uint4 *)&sCs[r * BPe + q8 * 8] = stc1;
         }
     };
     if constexpr (STAGE) stage_load(a.nchunks - 1);
