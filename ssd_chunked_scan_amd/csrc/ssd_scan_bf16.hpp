@@ -285,7 +285,10 @@ __device__ __attribute__((always_inline)) inline void scan_body(
             const int cc = ypc ^ swz<CPRY>(r);
             const char *src = zbase + (int64_t)(t0 + k * RB) * row_bytes + (yrow_off + cc * 16);
             if (t0 + Q > L && t0 + r >= L) src = (const char *)kZeroChunk;
-            zr[k - KB0] = *(const bf16x8 *)src;
+            // a global load: z and the zero chunk are both global memory, but
+            // the select of the two would otherwise be a flat load, which also
+            // counts against the LDS wait counter
+            zr[k - KB0] = *(const __attribute__((address_space(1))) bf16x8 *)src;
         };
         auto store_y = [&](int c, int k) __attribute__((always_inline)) {
             constexpr int RB = 64 / CPRY;
@@ -424,13 +427,7 @@ __device__ __attribute__((always_inline)) inline void scan_body(
     // sXstage -> fragments (between the two barriers of a hand-over): fragment
     // (m, pt) holds, for lane (p = 16 pt + l16, g), X[j][p] at the slot tokens
     // j = 32m + 4g + (e%4) + 16(e/4); sXs holds the same times the X'' factor.
-    auto make_fragments = [&](const SegBuf<Q> &sg, int cx) __attribute__((always_inline)) {
-        // X_cx's staging buffer (always sXstage in the full pass)
-        const bf16 *xs_src = sXstage;
-        if constexpr (LOCAL) {
-            const int sel = cx % 3;
-            xs_src = sel == 0 ? sXstage : (sel == 1 ? (const bf16 *)sXr : (const bf16 *)sY);
-        }
+    auto make_fragments_from = [&](const SegBuf<Q> &sg, const bf16 *xs_src) __attribute__((always_inline)) {
         // wave w makes the fragments of pairs w, w + W, ...: the pair's X''
         // factors are read and multiplied once for all its headdim tiles
 #pragma unroll
@@ -458,6 +455,20 @@ __device__ __attribute__((always_inline)) inline void scan_body(
                 if constexpr (!LOCAL) sXr[(m * PT + pt) * 64 + lane] = xr;   // a staging buffer when LOCAL
                 sXs[(m * PT + pt) * 64 + lane] = xs;
             }
+        }
+    };
+    auto make_fragments = [&](const SegBuf<Q> &sg, int cx) __attribute__((always_inline)) {
+        // X_cx's staging buffer (always sXstage in the full pass).  One copy
+        // of the code per buffer, each naming its array: a pointer selected
+        // at run time was lowered to a table of generic pointers in scratch
+        // memory and flat loads.
+        if constexpr (LOCAL) {
+            const int sel = cx % 3;
+            if (sel == 0) make_fragments_from(sg, sXstage);
+            else if (sel == 1) make_fragments_from(sg, (const bf16 *)sXr);
+            else make_fragments_from(sg, (const bf16 *)sY);
+        } else {
+            make_fragments_from(sg, sXstage);
         }
     };
     // C_c rows of this wave's row tiles (B operand of the state projection,
