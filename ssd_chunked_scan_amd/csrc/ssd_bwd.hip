@@ -357,11 +357,11 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
                     // of bf16 values are exact, accumulation fp32 as above)
 #pragma unroll
                     for (int u = 0; u < kMaxK / 32; u += 2) {
-                        if (32 * u >= K) break;
+                        if (32 * u + 32 > K) break;   // whole 32-wide steps only (K = 16: the half step below)
                         const bf16x8 a0 = *(const bf16x8 *)at_off(Ab, ao + 32 * u + 8 * g);
                         const bf16x8 b0 = *(const bf16x8 *)at_off(Bb, bo_ + 32 * u + 8 * g);
                         acc = mfma_bf16(a0, b0, acc);
-                        if (32 * (u + 1) < K) {
+                        if (32 * (u + 1) + 32 <= K) {
                             const bf16x8 a1 = *(const bf16x8 *)at_off(Ab, ao + 32 * (u + 1) + 8 * g);
                             const bf16x8 b1 = *(const bf16x8 *)at_off(Bb, bo_ + 32 * (u + 1) + 8 * g);
                             acc2 = mfma_bf16(a1, b1, acc2);

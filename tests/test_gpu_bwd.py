@@ -54,6 +54,10 @@ CASES = [
     ("f32", 130, 2, 64, 128, 1),
     ("bf16", 300, 4, 64, 64, 2),
     ("bf16", 257, 2, 128, 128, 1),
+    # LDS-staged rows (bf16, headdim <= 64) with small headdim and dstate:
+    # fewer column blocks than waves in every job mapping
+    ("bf16", 150, 2, 32, 32, 1),
+    ("bf16", 100, 2, 16, 16, 1),
 ]
 
 
