@@ -58,6 +58,8 @@ CASES = [
     # fewer column blocks than waves in every job mapping
     ("bf16", 150, 2, 32, 32, 1),
     ("bf16", 100, 2, 16, 16, 1),
+    ("bf16", 140, 2, 16, 128, 1),    # staged, one headdim block, eight state blocks
+    ("bf16", 90, 4, 128, 16, 2),     # unstaged, eight headdim blocks, one state block
 ]
 
 
