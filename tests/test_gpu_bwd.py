@@ -60,6 +60,7 @@ CASES = [
     ("bf16", 100, 2, 16, 16, 1),
     ("bf16", 140, 2, 16, 128, 1),    # staged, one headdim block, eight state blocks
     ("bf16", 90, 4, 128, 16, 2),     # unstaged, eight headdim blocks, one state block
+    ("bf16", 40, 2, 64, 128, 1),     # one partial chunk: the entering state is init_states
 ]
 
 
