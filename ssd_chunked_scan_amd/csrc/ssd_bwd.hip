@@ -129,9 +129,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
     constexpr int PU = P / 16;              // 16-column blocks of headdim
     __shared__ __attribute__((aligned(16))) SegLds<Q> sg;
     __shared__ __attribute__((aligned(16))) float sG[kMaxGN];  // adjoint of the state at the chunk end, [P][N + 4]
-    __shared__ float sL[Q * LQ];            // decay mask L[i][j]
+    __shared__ float sL[Q * LQ];            // decay mask L[i][j], then V[i][j] = dy_i . x_j
     __shared__ float sS[Q * LQ];            // (L o C B^T)[i][j]
-    __shared__ float sV[Q * LQ];            // V[i][j] = dy_i . x_j, then row prefix sums of R
+    __shared__ float sV[Q * LQ];            // (L o V)[i][j], then row prefix sums of R
     __shared__ float sw[Q];                 // decay from token j to the chunk end
     __shared__ float sq[Q], sp[Q], sxdX[Q], sdl[Q];
     __shared__ float sK, sDD, sDA;
@@ -334,22 +334,16 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
         }
         __syncthreads();
 
-        // ---- S = C B^T (stored masked) and V = dY X^T, lower 16 x 16 tiles
-        // only (upper tiles are never read).  Both operands are rows of
-        // token-major arrays: a lane reads four consecutive elements of its
-        // row and feeds them to four steps.  All loads of a batch are issued
-        // before its MFMAs.
+        // ---- S = C B^T and V = dY X^T on the lower 16 x 16 tiles (upper tiles
+        // are never read), one job per tile computing both.  Stored: L o S in
+        // sS, L o V in sV (what dX, dB and dC read), and V itself over L in
+        // sL (only the R walk reads it; L is not read again in the chunk).
+        // Both operands are rows of token-major arrays: a lane reads
+        // consecutive elements of its row and feeds them to its steps; all
+        // loads of a product are issued before its MFMAs.
         {
-            constexpr int NT = NB * (NB + 1) / 2;
-            for (int job = wave; job < 2 * NT; job += kBwdThreads / 64) {
-                const bool isS = job < NT;
-                int k = isS ? job : job - NT, I = 0;
-                while (k > I) k -= ++I;
-                const int J = k;                              // tile (I, J), J <= I
-                const int i = I * 16 + l16, j = J * 16 + l16;
-                const int K = isS ? N : P;
-                const IO *Ab = isS ? Cc : dyc, *Bb = isS ? Bc : xc;   // chunk bases
-                const unsigned ao = cl(i) * (isS ? bs : xs), bo_ = cl(j) * (isS ? bs : xs);
+            auto product = [&](const IO *Ab, const IO *Bb, unsigned ao, unsigned bo_, int K)
+                    __attribute__((always_inline)) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
                 if constexpr (STAGE) {
                     // bf16 rows in LDS: v_mfma_f32_16x16x32_bf16, a lane
@@ -389,12 +383,23 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
                     }
                 }
                 mfma_f32_fence(acc, acc2);
+                return f32x4{acc[0] + acc2[0], acc[1] + acc2[1], acc[2] + acc2[2], acc[3] + acc2[3]};
+            };
+            constexpr int NT = NB * (NB + 1) / 2;
+            for (int job = wave; job < NT; job += kBwdThreads / 64) {
+                int k = job, I = 0;
+                while (k > I) k -= ++I;
+                const int J = k;                              // tile (I, J), J <= I
+                const int i = I * 16 + l16, j = J * 16 + l16;
+                const f32x4 sv = product(Cc, Bc, cl(i) * bs, cl(j) * bs, N);
+                const f32x4 vv = product(dyc, xc, cl(i) * xs, cl(j) * xs, P);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int ii = I * 16 + 4 * g + r, jj = J * 16 + l16;
-                    const float v = acc[r] + acc2[r];
-                    if (isS) sS[ii * LQ + jj] = sL[ii * LQ + jj] * v;
-                    else sV[ii * LQ + jj] = v;
+                    const int e = (I * 16 + 4 * g + r) * LQ + J * 16 + l16;
+                    const float l = sL[e];
+                    sS[e] = l * sv[r];
+                    sV[e] = l * vv[r];
+                    sL[e] = vv[r];
                 }
             }
         }
@@ -516,7 +521,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
 #pragma unroll
                     for (int st = 0; st < 4 * NB; ++st) {
                         const int i = 4 * st + g;
-                        const float lv = sL[i * LQ + tr] * sV[i * LQ + tr];
+                        const float lv = sV[i * LQ + tr];   // (L o V)[i][t]
                         acc = mfma_f32(st >= 4 * T ? lv : 0.f, cvs[st], acc);
                     }
 #pragma unroll
@@ -538,7 +543,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
 #pragma unroll
                     for (int st = 0; st < 4 * NB; ++st) {
                         const int j = 4 * st + g;
-                        const float lv = sL[tr * LQ + j] * sg.dt[j] * sV[tr * LQ + j];
+                        const float lv = sg.dt[j] * sV[tr * LQ + j];   // (L o dt o V)[t][j]
                         acc = mfma_f32(st < 4 * (T + 1) ? lv : 0.f, bvs[st], acc);
                     }
 #pragma unroll
@@ -578,7 +583,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
 #pragma unroll
             for (int c8 = 0; c8 < CPL; ++c8) {
                 const int r = CPL * q + c8;
-                Rv[c8] = (r <= s) ? sS[s * LQ + r] * sg.dt[r] * sV[s * LQ + r] : 0.f;
+                Rv[c8] = (r <= s) ? sS[s * LQ + r] * sg.dt[r] * sL[s * LQ + r] : 0.f;   // (L o S) dt V
                 loc += Rv[c8];
             }
             float incl = loc;
