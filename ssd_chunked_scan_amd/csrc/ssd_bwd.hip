@@ -433,10 +433,17 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
                     for (int u = 0; u < kMaxK / 16; ++u)
                         bv[u] = (16 * u < N) ? ld_pack<IO>(Bc, brow + 16 * u + 4 * g) : Pack<IO>{};
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
+                    // i = 16 J .. Q - 1: whole 16-row blocks I >= J (one uniform
+                    // branch per block; inside the diagonal block L is 0 above
+                    // the diagonal)
 #pragma unroll
-                    for (int st = 0; st < 4 * NB; ++st) {   // i = 16 J .. Q - 1
-                        const float sv = sS[(4 * st + g) * LQ + jr];
-                        acc = mfma_f32(st >= 4 * J ? sv : 0.f, dyv[st], acc);
+                    for (int blk = 0; blk < NB; ++blk) {
+                        if (blk < J) continue;
+#pragma unroll
+                        for (int s4 = 0; s4 < 4; ++s4) {
+                            const int st = 4 * blk + s4;
+                            acc = mfma_f32(sS[(4 * st + g) * LQ + jr], dyv[st], acc);
+                        }
                     }
 #pragma unroll
                     for (int u = 0; u < kMaxK / 16; ++u) {
@@ -519,10 +526,13 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
                     // dB: i = 16 T .. Q - 1;  G^T x_t
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int st = 0; st < 4 * NB; ++st) {
-                        const int i = 4 * st + g;
-                        const float lv = sV[i * LQ + tr];   // (L o V)[i][t]
-                        acc = mfma_f32(st >= 4 * T ? lv : 0.f, cvs[st], acc);
+                    for (int blk = 0; blk < NB; ++blk) {   // whole blocks I >= T
+                        if (blk < T) continue;
+#pragma unroll
+                        for (int s4 = 0; s4 < 4; ++s4) {
+                            const int st = 4 * blk + s4;
+                            acc = mfma_f32(sV[(4 * st + g) * LQ + tr], cvs[st], acc);   // (L o V)[i][t]
+                        }
                     }
 #pragma unroll
                     for (int u = 0; u < PU; ++u) {
@@ -541,10 +551,13 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
                     acc = f32x4{0.f, 0.f, 0.f, 0.f};
                     acc2 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int st = 0; st < 4 * NB; ++st) {
-                        const int j = 4 * st + g;
-                        const float lv = sg.dt[j] * sV[tr * LQ + j];   // (L o dt o V)[t][j]
-                        acc = mfma_f32(st < 4 * (T + 1) ? lv : 0.f, bvs[st], acc);
+                    for (int blk = 0; blk < NB; ++blk) {   // whole blocks J <= T
+                        if (blk > T) break;
+#pragma unroll
+                        for (int s4 = 0; s4 < 4; ++s4) {
+                            const int j = 4 * (4 * blk + s4) + g;
+                            acc = mfma_f32(sg.dt[j] * sV[tr * LQ + j], bvs[4 * blk + s4], acc);   // (L o dt o V)[t][j]
+                        }
                     }
 #pragma unroll
                     for (int u = 0; u < PU; ++u) {

@@ -52,6 +52,7 @@ CASES = [
     ("f32", 200, 4, 32, 32, 2),
     ("f32", 64, 2, 16, 16, 1),       # one chunk
     ("f32", 130, 2, 64, 128, 1),
+    ("f32", 100, 2, 128, 64, 1),
     ("bf16", 300, 4, 64, 64, 2),
     ("bf16", 257, 2, 128, 128, 1),
     # LDS-staged rows (bf16, headdim <= 64) with small headdim and dstate:
