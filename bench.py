@@ -199,15 +199,17 @@ def backward_bench(wl, inp, args):
            + b * L * H * P * 4 + b * L * H * 4 + 2 * b * L * G * N * 4          # dx, ddt, dB, dC
            + 2 * b * H * nch * P * N * 4)                                       # states
     gbs = alg / (avg * 1e-3) / 1e9
-    # MFMA work the backward kernel executes (padding steps included), per
-    # 64-token chunk and (batch row, head): fp32 16x16x4 steps (2048 flop)
-    # for the products with fp32 operands; C B^T and dY X^T on bf16 16x16x32
-    # steps (16384 flop) when bf16 rows are staged (bf16 inputs, headdim <= 64),
+    # MFMA work the backward kernel executes, per 64-token chunk and (batch
+    # row, head): fp32 16x16x4 steps (2048 flop) for the products with fp32
+    # operands, the triangular ones over whole 16-row blocks (4 steps each,
+    # diagonal blocks in full); C B^T and dY X^T on bf16 16x16x32 steps
+    # (16384 flop) when bf16 rows are staged (bf16 inputs, headdim <= 64),
     # else fp32 steps.
     nb, ntri = 4, 10                          # 16-row blocks per chunk, lower tiles
-    f32 = (nb * (P // 16) * (16 + N // 4)                 # dX: (L o S)^T dY, G B_j
-           + nb * (N // 16) * (2 * 16 + 2 * (P // 4))     # dB, dC with their state terms
-           + (P // 16) * (N // 16) * 16)                  # state adjoint update
+    tri = 4 * ntri                            # steps of one column tile's triangle
+    f32 = ((P // 16) * tri + nb * (P // 16) * (N // 4)          # dX: (L o S)^T dY, G B_j
+           + (N // 16) * 2 * tri + nb * (N // 16) * 2 * (P // 4)  # dB, dC and their state terms
+           + (P // 16) * (N // 16) * 16)                        # state adjoint update
     staged = wl.io == "bf16" and P <= 64
     bf = ntri * (max(1, N // 32) + max(1, P // 32)) if staged else 0
     if not staged:
