@@ -7,10 +7,13 @@ seeded synthetic inputs already resident in HBM; the default workload is the
 Mamba-2 2.7B-shaped layer: batch 8, seqlen 2048, 80 heads, headdim 64, dstate
 128, 1 group, chunk 256, x/B/C/y in bf16, dt/A/D and the states in fp32.
 
-Prints one JSON line with the throughput (tokens/s), the HBM roofline of the
-dominant kernel (algorithmic bytes per launch over its average launch time,
-measured with HIP events on the stream the kernel runs on), and the fp64 CPU
-oracle timed on the host cores as a reported baseline.
+Prints one JSON line with the throughput (tokens/s over K back-to-back
+steps), the HBM roofline of the forward pass (algorithmic bytes per call over
+its average duration, each call timed cold -- a 512 MiB scratch buffer written
+before it, so that neither L2 nor the Infinity Cache holds its inputs -- with
+HIP events on the stream the kernels run on; the head kernel alone and the
+back-to-back figures beside it), and the fp64 CPU oracle timed on the host
+cores as a reported baseline.
 """
 from __future__ import annotations
 
@@ -27,14 +30,14 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix
 METRIC = "SSD fwd tokens/s + HBM GB/s (% of peak), Mamba-2 2.7B layer, L=2048"
-HEAD_KERNEL_SOURCES = ("ssd_api.cpp", "ssd_common.hpp", "ssd_scan_bf16.hpp", "ssd_scan_bf16_q64.hip",
-                       "ssd_scan_bf16_q128.hip", "ssd_scan_bf16_q256.hip", "ssd_segsum.hpp",
-                       "ssd_tiles.hpp")
+HEAD_KERNEL_SOURCES = ("ssd_api.cpp", "ssd_cb.hip", "ssd_common.hpp", "ssd_scan_bf16.hpp",
+                       "ssd_scan_bf16_q64.hip", "ssd_scan_bf16_q128.hip", "ssd_scan_bf16_q256.hip",
+                       "ssd_segsum.hpp", "ssd_tiles.hpp")
 
 
 def kernel_source_digest() -> str:
-    """Digest of the sources that define the bf16 head kernel and its launch
-    (the counters are only valid for them)."""
+    """Digest of the sources that define the bf16 forward kernels and their
+    launch (the counters are only valid for them)."""
     csrc = os.path.join(ROOT, "ssd_chunked_scan_amd", "csrc")
     h = hashlib.sha256()
     for f in sorted(os.listdir(csrc)):
@@ -46,9 +49,10 @@ def kernel_source_digest() -> str:
 
 
 def counter_traffic(workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary of
-    this workload, if it was taken on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"ssd_scan_bf16_{workload}_counters.txt")
+    """HBM bytes per forward pass (both kernels) from the committed rocprofv3
+    counter summary of this workload, if it was taken on the current kernel
+    sources."""
+    path = os.path.join(ROOT, "profiles", f"ssd_fwd_{workload}_counters.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -59,14 +63,27 @@ def counter_traffic(workload: str):
     if vals.get("kernel_source_digest") != kernel_source_digest():
         return None
     try:
-        return float(vals["hbm_bytes_per_launch"])
+        return float(vals["hbm_bytes_per_forward"])
     except (KeyError, ValueError):
         return None
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(inp, repeats: int = 3):
     """The fp64 oracle on the host cores over the whole workload (every batch
-    row and head); median of ``repeats`` runs."""
+    row and head); median of ``repeats`` runs.  The oracle parallelises over
+    the independent (batch row, head) pairs with OpenMP, so the threads it
+    uses are the smaller of its thread count and that pair count."""
     import oracle
     threads = oracle.max_threads()
     units = inp.wl.batch * inp.wl.nheads
@@ -78,7 +95,8 @@ def cpu_baseline(inp, repeats: int = 3):
     times.sort()
     med = times[len(times) // 2]
     return {"value": inp.wl.tokens / med, "unit": "tokens/s", "cores": min(threads, units),
-            "kind": "oracle",
+            "kind": "oracle", "omp_threads": threads, "os_cpu_count": os.cpu_count(),
+            "cpu_model": cpu_model(),
             "sample": f"whole workload ({inp.wl.batch}x{inp.wl.seqlen} tokens x {inp.wl.nheads} "
                       f"heads), fp64 recurrence, median of {repeats} runs of {med:.2f} s"}
 
@@ -248,6 +266,10 @@ def main():
                          "workload's dt and A, every chunk, mask evaluated but not written")
     ap.add_argument("--backward", action="store_true",
                     help="instead of the forward pass: time the backward pass (ssd_bwd)")
+    ap.add_argument("--cold-only", action="store_true",
+                    help="only the cold per-call timing of the forward pass (a 512 MiB scratch "
+                         "write before each call): the command the rocprofv3 kernel statistics "
+                         "and counters are taken with, so that every profiled call is a cold one")
     ap.add_argument("--fused", action="store_true",
                     help="time the forward pass with the fused prologue (raw dt + bias, softplus) "
                          "and the silu(z) output gate; z counts as algorithmic bytes")
@@ -311,6 +333,26 @@ def main():
         step()
     torch.cuda.synchronize(dev)
 
+    stream = torch.cuda.current_stream(dev)
+    if args.cold_only:
+        flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for k, (e0, e1) in enumerate(ev):
+            flush_buf.fill_(k & 0xFF)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+        torch.cuda.synchronize(dev)
+        ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+        avg = sum(ms) / len(ms)
+        print(json.dumps({"metric": "forward pass time per call, cold", "unit": "us",
+                          "workload": wl.name, "steps": args.steps, "avg_us": avg * 1e3,
+                          "median_us": ms[len(ms) // 2] * 1e3,
+                          "gbs": (wl.algorithmic_bytes() + extra_bytes) / (avg * 1e-3) / 1e9}),
+              flush=True)
+        return
+
     # Whole-job timing: K back-to-back steps between two synchronisations.
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -320,10 +362,9 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
 
     # Per-launch timing with HIP events on the stream the kernels run on: the
-    # whole forward pass, and the head kernel alone (the dominant kernel: the
-    # same call told that the workspace already holds the per-group operands,
-    # which the previous step wrote).
-    stream = torch.cuda.current_stream(dev)
+    # whole forward pass, and the head kernel alone (the same call told that
+    # the workspace already holds the per-group operands, which the previous
+    # step wrote).
 
     def event_times(fn):
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -365,44 +406,77 @@ def main():
     print(f"bench: graph replay {graph_ms_per_step * 1e3:.1f} us/step (eager {ms_per_step * 1e3:.1f})",
           file=sys.stderr, flush=True)
 
-    step_ms = event_times(step)
-    avg_step_ms = sum(step_ms) / len(step_ms)
-    head_only = wl.io == "bf16" and split_len >= wl.seqlen
+    # Cold timing: before every timed call a 512 MiB scratch buffer is
+    # written (outside the events), which evicts the inputs and the
+    # per-group operands from L2 and from the 256 MB Infinity Cache, so each
+    # call streams x from HBM.  Per-call HIP events on the kernels' stream.
+    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
 
+    def cold_times(fn, n):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        for k, (e0, e1) in enumerate(ev):
+            flush_buf.fill_(k & 0xFF)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize(dev)
+        return sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+
+    def summary(ms):
+        n = len(ms)
+        return {"avg_us": sum(ms) / n * 1e3, "median_us": ms[n // 2] * 1e3,
+                "p10_us": ms[n // 10] * 1e3, "p90_us": ms[(9 * n) // 10] * 1e3}
+
+    alg_bytes = wl.algorithmic_bytes() + extra_bytes
+    head_only = wl.io == "bf16" and split_len >= wl.seqlen
     head_step, _, _ = ssd.prepare_fwd(x, dt, A, B, C, D, seq, chunk_size=wl.chunk_size, y=y,
                                       final_states=fs, workspace=ws, reuse_group_operands=True,
                                       **fused_kw)
-
-    launch_ms = event_times(head_step) if head_only else step_ms
-    avg_launch_ms = sum(launch_ms) / len(launch_ms)
-    print(f"bench: wall {ms_per_step * 1e3:.1f} us/step; forward event avg {avg_step_ms * 1e3:.1f} us; "
-          f"head kernel avg {avg_launch_ms * 1e3:.1f} us "
-          f"(p10 {launch_ms[len(launch_ms) // 10] * 1e3:.1f}, "
-          f"p90 {launch_ms[(9 * len(launch_ms)) // 10] * 1e3:.1f})", file=sys.stderr, flush=True)
-
-    alg_bytes = wl.algorithmic_bytes() + extra_bytes
-    achieved = alg_bytes / (avg_launch_ms * 1e-3) / 1e9
+    fwd_cold = summary(cold_times(step, args.steps))
+    fwd_warm = summary(event_times(step))
+    head_cold = summary(cold_times(head_step, args.steps)) if head_only else None
+    head_warm = summary(event_times(head_step)) if head_only else None
+    gbs = lambda us: alg_bytes / (us * 1e-6) / 1e9
+    print(f"bench: wall {ms_per_step * 1e3:.1f} us/step back to back; forward pass cold "
+          f"avg {fwd_cold['avg_us']:.1f} us (median {fwd_cold['median_us']:.1f}, p10 "
+          f"{fwd_cold['p10_us']:.1f}, p90 {fwd_cold['p90_us']:.1f}), warm avg {fwd_warm['avg_us']:.1f} us",
+          file=sys.stderr, flush=True)
+    if head_only:
+        print(f"bench: head kernel cold avg {head_cold['avg_us']:.1f} us (median "
+              f"{head_cold['median_us']:.1f}), warm avg {head_warm['avg_us']:.1f} us",
+              file=sys.stderr, flush=True)
+    achieved = gbs(fwd_cold["avg_us"])
 
     # Measured device-to-device copy moving the same number of bytes (half
-    # read, half written): the attainable-bandwidth reference, and the plain
-    # copy kernel whose counters calibrate the HBM-traffic counters.
+    # read, half written), timed cold like the forward pass: the attainable-
+    # bandwidth reference, and the plain copy kernel whose counters calibrate
+    # the HBM-traffic counters.
     copy_src = torch.empty(alg_bytes // 2, dtype=torch.uint8, device=dev)
     copy_dst = torch.empty_like(copy_src)
     for _ in range(3):
         copy_dst.copy_(copy_src)
-    cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(max(10, args.steps // 2))]
-    for e0, e1 in cev:
-        e0.record(stream)
-        copy_dst.copy_(copy_src)
-        e1.record(stream)
-    torch.cuda.synchronize(dev)
-    copy_ms = sum(e0.elapsed_time(e1) for e0, e1 in cev) / len(cev)
-    copy_gbs = alg_bytes / (copy_ms * 1e-3) / 1e9
-    del copy_src, copy_dst
-    print(f"bench: kernel {achieved:.0f} GB/s algorithmic; copy of the same bytes {copy_gbs:.0f} GB/s",
-          file=sys.stderr, flush=True)
+    copy_cold = summary(cold_times(lambda: copy_dst.copy_(copy_src), max(10, args.steps // 2)))
+    copy_gbs = gbs(copy_cold["avg_us"])
+    del copy_src, copy_dst, flush_buf
+    print(f"bench: forward pass {achieved:.0f} GB/s algorithmic (cold); copy of the same bytes "
+          f"{copy_gbs:.0f} GB/s (cold)", file=sys.stderr, flush=True)
     traffic = None if args.fused else counter_traffic(wl.name)
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                "kernel": ("forward pass: ssd_cb_kernel + ssd_scan_bf16_kernel" if wl.io == "bf16"
+                           else "forward pass: ssd_chunk_f32_kernel"),
+                "timing": "cold: 512 MiB scratch written before each call; HIP events per call, average",
+                "algorithmic_bytes_per_launch": alg_bytes,
+                "avg_launch_us": fwd_cold["avg_us"], "median_us": fwd_cold["median_us"],
+                "p10_us": fwd_cold["p10_us"], "p90_us": fwd_cold["p90_us"],
+                "back_to_back": {"avg_us": fwd_warm["avg_us"], "frac": gbs(fwd_warm["avg_us"]) / HBM_PEAK_GBS}}
+    if head_only:
+        roofline["head_kernel"] = {
+            "kernel": "ssd_scan_bf16_kernel (per-group operands already in the workspace)",
+            "cold": dict(head_cold, frac=gbs(head_cold["avg_us"]) / HBM_PEAK_GBS,
+                         frac_median=gbs(head_cold["median_us"]) / HBM_PEAK_GBS),
+            "back_to_back": dict(head_warm, frac=gbs(head_warm["avg_us"]) / HBM_PEAK_GBS)}
     out = {
         "metric": METRIC,
         "value": wl.tokens / (ms_per_step * 1e-3),
@@ -424,15 +498,12 @@ def main():
                    "seqlen": wl.seqlen, "nheads": wl.nheads, "headdim": wl.headdim,
                    "dstate": wl.dstate, "ngroups": wl.ngroups, "chunk_size": wl.chunk_size,
                    "split_len": split_len, "parallelism": "single GPU"},
+        "tokens_per_s_cold": wl.tokens / (fwd_cold["avg_us"] * 1e-6),
         "hbm_gbs": alg_bytes / (ms_per_step * 1e-3) / 1e9,
         "hbm_frac_of_peak": alg_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "ssd_scan_bf16_kernel" if head_only else "forward pass",
-                     "algorithmic_bytes_per_launch": alg_bytes,
-                     "avg_launch_us": avg_launch_ms * 1e3,
-                     "forward_avg_us": avg_step_ms * 1e3},
-        "copy_reference": {"gbs": copy_gbs, "bytes": alg_bytes, "frac_of_copy": achieved / copy_gbs},
+        "roofline": roofline,
+        "copy_reference": {"gbs": copy_gbs, "bytes": alg_bytes, "timing": "cold",
+                           "frac_of_copy": achieved / copy_gbs},
     }
     if not args.no_cpu_baseline and not args.fused:
         print("bench: timing the fp64 CPU oracle", file=sys.stderr, flush=True)

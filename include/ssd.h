@@ -46,9 +46,16 @@
  * stream), reentrant, and make no implicit synchronisation.  Concurrent calls
  * must not share a workspace.
  *
- * Errors: arguments are validated on the host before any HIP call; on failure
- * the call returns a status, launches nothing and records a message readable
- * with ssd_last_error() (thread-local).  A failed launch returns SSD_ERR_HIP.
+ * Planning: the split plan (and so the workspace size) depends on the
+ * compute-unit count of the device that `stream` belongs to (the current
+ * device for the NULL stream); the *_workspace_bytes and ssd_plan_* queries,
+ * which take no stream, plan for the current device.
+ *
+ * Errors: every argument is validated on the host before any kernel is
+ * launched; the only HIP calls made before that are the planner's queries of
+ * the stream's device and of its compute-unit count.  On failure the call
+ * returns a status, launches nothing and records a message readable with
+ * ssd_last_error() (thread-local).  A failed launch returns SSD_ERR_HIP.
  * Device-side faults surface at the caller's next synchronisation.  NaN or
  * Inf inputs propagate; the hot path does not check values.
  *
@@ -80,7 +87,10 @@ typedef enum {
 
 typedef enum {
     SSD_F32 = 0,   /* x, B, C, y in fp32; fp32 arithmetic throughout          */
-    SSD_BF16 = 1   /* x, B, C, y in bf16; bf16 MFMA with fp32 accumulation    */
+    SSD_BF16 = 1,  /* x, B, C, y in bf16; bf16 MFMA with fp32 accumulation    */
+    SSD_DTYPE_RANGE_ = 0x7fffffff  /* not a dtype: makes every non-negative int
+                                      a valid value of the type, so that an
+                                      unknown one is rejected, not undefined */
 } ssd_dtype_t;
 
 typedef struct {
@@ -118,15 +128,18 @@ typedef struct {
  * pointer required).  Returns 0 when no workspace is needed, and also for an
  * invalid problem (ssd_fwd then reports the error).  The workspace holds,
  * each part rounded up to 256 bytes:
- *   - with more than one sequence split: the splits' states and decays,
- *     4 * batch * nheads * nsplits * (headdim * dstate + 1) bytes;
- *   - bf16 io: the per-group C B^T blocks of every chunk (the lower triangle
- *     of C_c B_c^T in 16 x 32-token blocks, 1 KiB each, (Q/32)(Q/32+1)
- *     blocks per chunk), B token-transposed and C in operand order, i.e.
- *     batch * ngroups * nchunks * (1024 (Q/32)(Q/32+1) + 2 Q dstate) bytes
- *     + batch * ngroups * nchunks * 2 Q max(dstate, 32) bytes (C; dstate 16
- *     is padded to 32 columns).
- * The contents are scratch: nothing survives the call. */
+ *   - bf16 io, first: the per-group C B^T blocks of every chunk (the lower
+ *     triangle of C_c B_c^T in 16 x 32-token blocks, 1 KiB each,
+ *     (Q/32)(Q/32+1) blocks per chunk), B token-transposed and C in operand
+ *     order, i.e. batch * ngroups * nchunks * (1024 (Q/32)(Q/32+1) +
+ *     2 Q dstate) bytes + batch * ngroups * nchunks * 2 Q max(dstate, 32)
+ *     bytes (C; dstate 16 is padded to 32 columns);
+ *   - then, with more than one sequence split: the splits' states and
+ *     decays, 4 * batch * nheads * nsplits * (headdim * dstate + 1) bytes.
+ * Every byte the kernels read is written earlier in the same call, so the
+ * workspace needs no clearing.  Only the per-group operands survive a bf16
+ * call (for SSD_OPT_REUSE_GROUP_OPERANDS; their offsets depend on the shape
+ * and chunk size only); everything else is scratch. */
 size_t ssd_fwd_workspace_bytes(const ssd_shape_t *shape, int64_t chunk_size,
                                ssd_dtype_t io);
 
@@ -269,7 +282,9 @@ ssd_status_t ssd_decode_step_fused(const ssd_shape_t *shape, ssd_dtype_t io,
  * Mamba-2" ("The SSD Block Decomposition Algorithm"): the chunk-entering
  * states come from the forward pass's split-local pass and affine scan with
  * one split per 64-token chunk, then one reverse walk over the chunks per
- * (batch row, head) carries the adjoint of the state (fp32, vector ALU).
+ * (batch row, head) carries the adjoint of the state (fp32 arithmetic; the
+ * products on fp32 MFMA tiles, C B^T and dY X^T on bf16 MFMA when the inputs
+ * are bf16).
  *   dy [b, L, H, P] io dtype, 16-byte aligned; dfinal [b, H, P, N] fp32 or NULL;
  *   outputs, all fp32: dx [b, L, H, P], ddt [b, L, H], dA [H], dB and dC
  *   [b, L, G, N], dD [H] (NULL exactly when D is NULL), dinit [b, H, P, N]
@@ -286,6 +301,56 @@ ssd_status_t ssd_bwd(const ssd_shape_t *shape, ssd_dtype_t io,
                      float *dx, float *ddt, float *dA, float *dB, float *dC,
                      float *dD, float *dinit,
                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---- Debug exports (tests only) ---------------------------------------
+ *
+ * Segsum factor records.  The hierarchy-aware segsum (page "GPU Hierarchy
+ * Meets Structured Matrices", abstract) reduces each chunk of each head to
+ * per-token and per-sub-block factors (16-token sub-blocks): one record of
+ * ssd_segsum_record_words(chunk_size) 32-bit words per (batch row, head,
+ * chunk), records ordered [batch][nheads][nchunks], each holding
+ *   d[Q]       log2-decay dt_t A_h log2(e) (0 past the end of the row)
+ *   dt[Q]      dt_t (0 past the end)
+ *   wd[Q]      W_t dt_t, W_t the decay from t to the end of its sub-block
+ *   last1[Q]   int32: 1 + the last reset position <= t inside t's sub-block, 0 if none
+ *   Tb[Q/16]   whole-sub-block decay (0 if a reset lies inside)
+ *   blast1[Q/16]  int32: 1 + the last reset position inside the sub-block, 0 if none
+ *   Tp[Q/32]   Tb[2m] Tb[2m+1]
+ * All decays are exp2 of nested sequential sums of non-positive terms.  0 for
+ * an invalid chunk size. */
+int64_t ssd_segsum_record_words(int64_t chunk_size);
+
+/* The factors as the mask export (ssd_debug_chunk_mask) builds them, with
+ * sequential per-token sums: out holds batch * nheads * nchunks records.
+ * Validation and errors as ssd_debug_chunk_mask; at most 65535 chunks. */
+ssd_status_t ssd_debug_segsum_factors(const ssd_shape_t *shape, const float *dt,
+                                      const float *A, const int32_t *seq_idx,
+                                      int64_t chunk_size, float *out, void *stream);
+
+/* ssd_fwd_ex (bf16 io only) that also writes the factors exactly as the bf16
+ * head kernel builds them for its own use (row-shift sums across the lanes of
+ * a wave): out holds batch * nheads * nchunks records.  y and final_states
+ * are computed as by ssd_fwd_ex. */
+ssd_status_t ssd_debug_fwd_segsum_factors(const ssd_shape_t *shape, ssd_dtype_t io,
+                                          const void *x, const float *dt, const float *A,
+                                          const void *B, const void *C, const float *D,
+                                          const int32_t *seq_idx, int64_t chunk_size,
+                                          const float *init_states,
+                                          void *y, float *final_states,
+                                          void *workspace, size_t workspace_bytes,
+                                          const ssd_options_t *opts, float *out,
+                                          void *stream);
+
+/* Exhaustive check of the device's exp2 (the only exponential the decay
+ * factors use; their [0, 1] range and monotonicity rest on it, page "GPU
+ * Hierarchy Meets Structured Matrices", abstract) over the fp32 bit patterns
+ * [first_bits, first_bits + count), which must lie in [0x80000000,
+ * 0xff800000] (-0 down to -inf).  counts: device array of 3 * nthreads
+ * uint32; thread t writes, for its share of the patterns, the number of
+ * increases of exp2 as the argument decreases, of values above 1, and of
+ * values below 0 or NaN.  nthreads in [1, 2^24]. */
+ssd_status_t ssd_debug_exp2_probe(uint32_t first_bits, uint32_t count, uint32_t *counts,
+                                  uint32_t nthreads, void *stream);
 
 const char *ssd_status_str(ssd_status_t status);
 

@@ -35,6 +35,8 @@ EXPORTS = ["ssd_fwd_workspace_bytes", "ssd_fwd", "ssd_fwd_ex_workspace_bytes", "
            "ssd_plan_split_len", "ssd_plan_headdim_block", "ssd_debug_chunk_mask",
            "ssd_debug_chunk_mask_ex",
            "ssd_decode_step", "ssd_decode_step_fused", "ssd_bwd_workspace_bytes", "ssd_bwd",
+           "ssd_segsum_record_words", "ssd_debug_segsum_factors", "ssd_debug_fwd_segsum_factors",
+           "ssd_debug_exp2_probe",
            "ssd_status_str", "ssd_last_error", "ssd_version"]
 # segsum evaluations of the mask export (ssd.h SSD_SEGSUM_*)
 SEGSUM = {"hierarchy": 0, "direct": 1, "diff": 2}
@@ -114,6 +116,15 @@ def load_library():
     lib.ssd_bwd_workspace_bytes.restype = sz
     lib.ssd_bwd.argtypes = [shp, i32] + [vp] * 18 + [sz, vp]
     lib.ssd_bwd.restype = i32
+    lib.ssd_segsum_record_words.argtypes = [i64]
+    lib.ssd_segsum_record_words.restype = i64
+    lib.ssd_debug_segsum_factors.argtypes = [shp, vp, vp, vp, i64, vp, vp]
+    lib.ssd_debug_segsum_factors.restype = i32
+    lib.ssd_debug_fwd_segsum_factors.argtypes = fwd_args + [opt, vp, vp]
+    lib.ssd_debug_fwd_segsum_factors.restype = i32
+    u32 = ctypes.c_uint32
+    lib.ssd_debug_exp2_probe.argtypes = [u32, u32, vp, u32, vp]
+    lib.ssd_debug_exp2_probe.restype = i32
     lib.ssd_status_str.argtypes = [i32]
     lib.ssd_status_str.restype = ctypes.c_char_p
     lib.ssd_last_error.argtypes = []
@@ -315,6 +326,86 @@ def ssd_debug_chunk_mask(dt, A, seq_idx=None, chunk_size: int = 256, chunk_begin
                                          _ptr(out), _ptr(sums), torch.cuda.current_stream(dev).cuda_stream)
     _check(st)
     return sums if sums_only else out
+
+
+def ssd_debug_segsum_factors(dt, A, seq_idx=None, chunk_size: int = 256):
+    """Segsum factor records (ssd.h) of every chunk as the mask export builds
+    them: int32 view [b, H, nchunks, ssd_segsum_record_words(chunk_size)]
+    (the words are fp32 values except last1 and blast1, which are int32)."""
+    import torch
+    lib = load_library()
+    b, L, H = dt.shape
+    dev = dt.device
+    _need(dt, "dt", (b, L, H), torch.float32, dev)
+    _need(A, "A", (H,), torch.float32, dev)
+    if seq_idx is not None:
+        _need(seq_idx, "seq_idx", (b, L), torch.int32, dev)
+    words = int(lib.ssd_segsum_record_words(chunk_size))
+    nchunks = (L + chunk_size - 1) // chunk_size
+    out = torch.empty((b, H, nchunks, max(words, 1)), dtype=torch.int32, device=dev)
+    shape = Shape(b, L, H, 16, 16, 1)
+    with torch.cuda.device(dev):
+        st = lib.ssd_debug_segsum_factors(ctypes.byref(shape), _ptr(dt), _ptr(A), _ptr(seq_idx),
+                                          chunk_size, _ptr(out), torch.cuda.current_stream(dev).cuda_stream)
+    _check(st)
+    return out
+
+
+def ssd_debug_fwd_segsum_factors(x, dt, A, B, C, D=None, seq_idx=None, chunk_size: int = 256,
+                                 init_states=None, split_len: int = 0, headdim_block: int = 0):
+    """The bf16 forward pass with the head kernel's own segsum factor records:
+    returns (y, final_states, records), records as ssd_debug_segsum_factors."""
+    import torch
+    lib = load_library()
+    dev = x.device
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    if x.dtype != torch.bfloat16:
+        raise TypeError("the head kernel's segsum factor export is a bf16-path debug aid")
+    _need(x, "x", (b, L, H, P), x.dtype, dev)
+    _need(dt, "dt", (b, L, H), torch.float32, dev)
+    _need(A, "A", (H,), torch.float32, dev)
+    _need(B, "B", (b, L, G, N), x.dtype, dev)
+    _need(C, "C", (b, L, G, N), x.dtype, dev)
+    if D is not None:
+        _need(D, "D", (H,), torch.float32, dev)
+    if seq_idx is not None:
+        _need(seq_idx, "seq_idx", (b, L), torch.int32, dev)
+    if init_states is not None:
+        _need(init_states, "init_states", (b, H, P, N), torch.float32, dev)
+    words = int(lib.ssd_segsum_record_words(chunk_size))
+    nchunks = (L + chunk_size - 1) // chunk_size
+    rec = torch.empty((b, H, nchunks, max(words, 1)), dtype=torch.int32, device=dev)
+    y = torch.empty_like(x)
+    fs = torch.empty((b, H, P, N), dtype=torch.float32, device=dev)
+    shape = Shape(b, L, H, P, N, G)
+    opts = Options(split_len, 0, headdim_block)
+    with torch.cuda.device(dev):
+        ws_bytes = int(lib.ssd_fwd_ex_workspace_bytes(ctypes.byref(shape), chunk_size, SSD_BF16,
+                                                      ctypes.byref(opts)))
+        ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+        st = lib.ssd_debug_fwd_segsum_factors(
+            ctypes.byref(shape), SSD_BF16, _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+            _ptr(seq_idx), chunk_size, _ptr(init_states), _ptr(y), _ptr(fs), _ptr(ws), ws_bytes,
+            ctypes.byref(opts), _ptr(rec), torch.cuda.current_stream(dev).cuda_stream)
+    _check(st)
+    return y, fs, rec
+
+
+def ssd_debug_exp2_probe(first_bits: int, count: int, nthreads: int = 1 << 18, device="cuda"):
+    """Run the device exp2 probe (ssd.h) over fp32 bit patterns [first_bits,
+    first_bits + count); returns the summed counts (increases as the argument
+    decreases, values above 1, values below 0 or NaN)."""
+    import torch
+    lib = load_library()
+    counts = torch.zeros(3 * nthreads, dtype=torch.int32, device=device)
+    dev = counts.device
+    with torch.cuda.device(dev):
+        st = lib.ssd_debug_exp2_probe(first_bits, count, _ptr(counts), nthreads,
+                                      torch.cuda.current_stream(dev).cuda_stream)
+    _check(st)
+    c = counts.view(nthreads, 3).to(torch.int64).sum(0).cpu().tolist()
+    return {"increases": c[0], "above_one": c[1], "negative_or_nan": c[2]}
 
 
 def ssd_decode_step(x, dt, A, B, C, D, state, y=None, stream=None, dt_bias=None,

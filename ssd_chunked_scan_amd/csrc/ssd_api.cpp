@@ -25,6 +25,8 @@ void launch_split_scan(const float *init_states, float *ws_states, const float *
                        int batch, int nheads, int nsplits, int pn, hipStream_t stream);
 void launch_mask(int Q, const MaskArgs &m, hipStream_t stream);
 bool launch_decode(bool bf16_io, int N, const DecodeArgs &a, hipStream_t stream);
+void launch_exp2_probe(uint32_t first, uint32_t count, uint32_t span, uint32_t *out, uint32_t nthreads,
+                       hipStream_t stream);
 }  // namespace ssd
 
 namespace {
@@ -77,14 +79,23 @@ ssd_status_t check_shape(const ssd_shape_t *s, int64_t chunk) {
 int g_cu_cache[64];
 std::atomic<int> g_cu_ready[64];
 
-// Compute units of the current device (cached; 256 when no device answers,
-// so that planning also works in host-only tests).
-int device_cus() {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+// Compute units of the device that `stream` belongs to (the current device
+// for the null stream; cached per device; 256 when no device answers, so
+// that planning also works in host-only tests).  The only HIP queries the
+// planner makes.
+int device_cus(hipStream_t stream) {
+    int dev = -1;
+    if (stream != nullptr) {
+        if (hipStreamGetDevice(stream, &dev) != hipSuccess) {
+            (void)hipGetLastError();
+            dev = -1;
+        }
+    }
+    if (dev < 0 && hipGetDevice(&dev) != hipSuccess) {
         (void)hipGetLastError();
         return 256;
     }
+    if (dev < 0 || dev >= 64) return 256;
     if (g_cu_ready[dev].load(std::memory_order_acquire)) return g_cu_cache[dev];
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
@@ -96,13 +107,18 @@ int device_cus() {
     return cus;
 }
 
+// Workspace layout: the per-group operands first (their offsets depend only
+// on the shape and the chunk size, so that a call with
+// SSD_OPT_REUSE_GROUP_OPERANDS finds them whatever its split plan), then the
+// split states and decays.
 struct Plan {
-    int nchunks, nsplits, split_chunks, npblocks, pblock;
-    size_t split_bytes;   // split states + decays (nsplits > 1)
+    int nchunks, nsplits, split_chunks, npblocks, pblock, units, half_units;
     size_t s_bytes;       // per-group C B^T blocks (bf16)
     size_t bt_bytes;      // per-group token-transposed B (bf16)
     size_t c_bytes;       // per-group C in operand order (bf16)
+    size_t split_bytes;   // split states + decays (nsplits > 1)
     size_t ws_bytes;
+    size_t group_bytes() const { return s_bytes + bt_bytes + c_bytes; }
 };
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -123,10 +139,10 @@ int64_t bf16_lds_bytes(int64_t Q, int64_t N, int64_t PB) {
 // workgroups resident per device, U units take ceil(U / W) rounds and the last
 // one holds T = U - (rounds - 1) W; when 2T <= W, halving those T units fills
 // that round with workgroups of about half the work.
-int bf16_half_units(int64_t units, int64_t Q, int64_t N, int64_t PB) {
+int bf16_half_units(int64_t units, int64_t Q, int64_t N, int64_t PB, int64_t cus) {
     if (PB < 32) return 0;
     const int64_t per_cu = std::max<int64_t>(1, (160 * 1024) / bf16_lds_bytes(Q, N, PB));
-    const int64_t slots = device_cus() * per_cu;
+    const int64_t slots = cus * per_cu;
     const int64_t rounds = (units + slots - 1) / slots;
     const int64_t tail = units - (rounds - 1) * slots;
     return (rounds >= 2 && 2 * tail <= slots) ? (int)tail : 0;
@@ -185,9 +201,13 @@ ssd_status_t check_fused(const ssd_fused_t *fused, size_t z_align) {
     return SSD_OK;
 }
 
-// Split plan and workspace size of a validated problem.
+// Largest grid (workgroups along x) any launch of the library may make.
+constexpr int64_t kMaxGrid = 0x7fffffff;
+
+// Split plan and workspace size of a validated problem; `stream` names the
+// device whose compute-unit count the plan is made for.
 ssd_status_t make_plan(const ssd_shape_t *s, int64_t chunk, ssd_dtype_t io,
-                       const ssd_options_t *opts, Plan *pl) {
+                       const ssd_options_t *opts, Plan *pl, hipStream_t stream) {
     ssd_status_t st = check_problem(s, chunk, io, opts);
     if (st != SSD_OK) return st;
     pl->nchunks = (int)((s->seqlen + chunk - 1) / chunk);
@@ -195,7 +215,7 @@ ssd_status_t make_plan(const ssd_shape_t *s, int64_t chunk, ssd_dtype_t io,
     if (opts && opts->headdim_block > 0) pl->pblock = (int)opts->headdim_block;
     pl->npblocks = (int)(s->headdim / pl->pblock);
     int nsplits = 1;
-    const int64_t cus = device_cus();
+    const int64_t cus = device_cus(stream);
     const bool forced_pb = opts && opts->headdim_block > 0;
     if (io == SSD_BF16 && !forced_pb && !(opts && opts->split_len > 0)) {
         // Too few (batch row, head) units for one workgroup per CU: halve the
@@ -227,6 +247,13 @@ ssd_status_t make_plan(const ssd_shape_t *s, int64_t chunk, ssd_dtype_t io,
     }
     pl->split_chunks = (pl->nchunks + nsplits - 1) / nsplits;
     pl->nsplits = (pl->nchunks + pl->split_chunks - 1) / pl->split_chunks;
+    // Every grid must fit the launch limit and every unit index an int.
+    const int64_t units = s->batch * s->nheads * (int64_t)pl->nsplits * pl->npblocks;
+    if (units > kMaxGrid / 2 || s->batch * s->nheads > kMaxGrid / 2 ||
+        s->batch * s->ngroups * (int64_t)pl->nchunks * (chunk / 64) > kMaxGrid)
+        return fail(SSD_ERR_UNSUPPORTED, "problem too large: %lld work units", (long long)units);
+    pl->units = (int)units;
+    pl->half_units = (io == SSD_BF16) ? bf16_half_units(units, chunk, s->dstate, pl->pblock, cus) : 0;
     pl->split_bytes = 0;
     if (pl->nsplits > 1) {
         const size_t states = (size_t)s->batch * s->nheads * pl->nsplits * s->headdim * s->dstate;
@@ -240,7 +267,7 @@ ssd_status_t make_plan(const ssd_shape_t *s, int64_t chunk, ssd_dtype_t io,
         pl->bt_bytes = round_up(bgc * (size_t)chunk * s->dstate * 2, 256);
         pl->c_bytes = round_up(bgc * (size_t)chunk * std::max<int64_t>(s->dstate, 32) * 2, 256);
     }
-    pl->ws_bytes = pl->split_bytes + pl->s_bytes + pl->bt_bytes + pl->c_bytes;
+    pl->ws_bytes = pl->group_bytes() + pl->split_bytes;
     return SSD_OK;
 }
 
@@ -268,7 +295,7 @@ const char *ssd_version(void) { return "ssd-mi355x 0.1 (gfx950)"; }
 size_t ssd_fwd_ex_workspace_bytes(const ssd_shape_t *shape, int64_t chunk_size, ssd_dtype_t io,
                                   const ssd_options_t *opts) {
     Plan pl;
-    if (make_plan(shape, chunk_size, io, opts, &pl) != SSD_OK) return 0;
+    if (make_plan(shape, chunk_size, io, opts, &pl, nullptr) != SSD_OK) return 0;
     return pl.ws_bytes;
 }
 
@@ -278,13 +305,13 @@ size_t ssd_fwd_workspace_bytes(const ssd_shape_t *shape, int64_t chunk_size, ssd
 
 int64_t ssd_plan_split_len(const ssd_shape_t *shape, int64_t chunk_size, ssd_dtype_t io) {
     Plan pl;
-    if (make_plan(shape, chunk_size, io, nullptr, &pl) != SSD_OK) return 0;
+    if (make_plan(shape, chunk_size, io, nullptr, &pl, nullptr) != SSD_OK) return 0;
     return (int64_t)pl.split_chunks * chunk_size;
 }
 
 int64_t ssd_plan_headdim_block(const ssd_shape_t *shape, int64_t chunk_size, ssd_dtype_t io) {
     Plan pl;
-    if (make_plan(shape, chunk_size, io, nullptr, &pl) != SSD_OK) return 0;
+    if (make_plan(shape, chunk_size, io, nullptr, &pl, nullptr) != SSD_OK) return 0;
     return pl.pblock;
 }
 
@@ -295,13 +322,14 @@ namespace {
 // The forward pass; with states_only, only what gives every split its
 // entering state (per-group operands, split-local pass, affine scan): the
 // outputs are not computed and y may be NULL (the backward pass uses this
-// with one split per chunk).
+// with one split per chunk).  dbg_seg (bf16 io, nullable): the head kernel
+// also writes each chunk's segsum factors there.
 ssd_status_t fwd_impl(const ssd_shape_t *shape, ssd_dtype_t io, const void *x, const float *dt,
                       const float *A, const void *B, const void *C, const float *D,
                       const int32_t *seq_idx, int64_t chunk_size, const float *init_states,
                       void *y, float *final_states, const ssd_fused_t *fused,
                       void *workspace, size_t workspace_bytes, const ssd_options_t *opts,
-                      void *stream, bool states_only) {
+                      void *stream, bool states_only, float *dbg_seg = nullptr) {
     ssd_status_t st = check_problem(shape, chunk_size, io, opts);
     if (st != SSD_OK) return st;
     st = check_fused(fused, 16);
@@ -315,15 +343,14 @@ ssd_status_t fwd_impl(const ssd_shape_t *shape, ssd_dtype_t io, const void *x, c
         return fail(SSD_ERR_ALIGN, "dt, A, D and seq_idx must be 4-byte aligned");
     if ((init_states && !aligned(init_states, 16)) || (final_states && !aligned(final_states, 16)))
         return fail(SSD_ERR_ALIGN, "init_states and final_states must be 16-byte aligned");
+    if (workspace && !aligned(workspace, 16)) return fail(SSD_ERR_ALIGN, "workspace must be 16-byte aligned");
+    hipStream_t s = (hipStream_t)stream;
     Plan pl;
-    st = make_plan(shape, chunk_size, io, opts, &pl);
+    st = make_plan(shape, chunk_size, io, opts, &pl, s);
     if (st != SSD_OK) return st;
-    if (pl.ws_bytes > 0) {
-        if (!workspace || workspace_bytes < pl.ws_bytes)
-            return fail(SSD_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given%s", pl.ws_bytes,
-                        workspace_bytes, workspace ? "" : " (NULL)");
-        if (!aligned(workspace, 16)) return fail(SSD_ERR_ALIGN, "workspace must be 16-byte aligned");
-    }
+    if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes))
+        return fail(SSD_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given%s", pl.ws_bytes,
+                    workspace_bytes, workspace ? "" : " (NULL)");
 
     ssd::ChunkArgs a;
     memset(&a, 0, sizeof(a));
@@ -337,14 +364,14 @@ ssd_status_t fwd_impl(const ssd_shape_t *shape, ssd_dtype_t io, const void *x, c
     a.init_states = init_states;
     a.y = y;
     a.final_states = final_states;
-    float *ws = (float *)workspace;
     char *wsb = (char *)workspace;
-    a.ws_S = pl.s_bytes ? wsb + pl.split_bytes : nullptr;
-    a.ws_BT = pl.bt_bytes ? wsb + pl.split_bytes + pl.s_bytes : nullptr;
-    a.ws_C = pl.c_bytes ? wsb + pl.split_bytes + pl.s_bytes + pl.bt_bytes : nullptr;
-    a.ws_states = pl.nsplits > 1 ? ws : nullptr;
+    a.ws_S = pl.s_bytes ? wsb : nullptr;
+    a.ws_BT = pl.bt_bytes ? wsb + pl.s_bytes : nullptr;
+    a.ws_C = pl.c_bytes ? wsb + pl.s_bytes + pl.bt_bytes : nullptr;
+    float *ws_split = pl.nsplits > 1 ? (float *)(wsb + pl.group_bytes()) : nullptr;
+    a.ws_states = ws_split;
     a.ws_decay = pl.nsplits > 1
-                     ? ws + (size_t)shape->batch * shape->nheads * pl.nsplits * shape->headdim * shape->dstate
+                     ? ws_split + (size_t)shape->batch * shape->nheads * pl.nsplits * shape->headdim * shape->dstate
                      : nullptr;
     a.batch = (int)shape->batch;
     a.seqlen = (int)shape->seqlen;
@@ -358,8 +385,9 @@ ssd_status_t fwd_impl(const ssd_shape_t *shape, ssd_dtype_t io, const void *x, c
     a.split_chunks = pl.split_chunks;
     a.npblocks = pl.npblocks;
     a.pblock = pl.pblock;
-    a.units = a.batch * a.nheads * a.nsplits * a.npblocks;
-    a.half_units = (io == SSD_BF16) ? bf16_half_units(a.units, chunk_size, a.dstate, a.pblock) : 0;
+    a.units = pl.units;
+    a.half_units = pl.half_units;
+    a.dbg_seg = dbg_seg;
     if (opts && (opts->flags & SSD_OPT_SEGSUM_DIRECT)) a.segsum_variant = ssd::kSegsumDirect;
     if (opts && (opts->flags & SSD_OPT_SEGSUM_DIFF)) a.segsum_variant = ssd::kSegsumDiff;
     if (fused) {
@@ -370,7 +398,6 @@ ssd_status_t fwd_impl(const ssd_shape_t *shape, ssd_dtype_t io, const void *x, c
         a.dt_lo = fused->dt_min;
         a.dt_hi = fused->dt_max;
     }
-    hipStream_t s = (hipStream_t)stream;
 
     auto launch = [&](const ssd::ChunkArgs &args) -> bool {
         if (io == SSD_F32) {
@@ -390,9 +417,9 @@ ssd_status_t fwd_impl(const ssd_shape_t *shape, ssd_dtype_t io, const void *x, c
         ssd::CbArgs cb;
         cb.B = B;
         cb.C = C;
-        cb.ws_S = wsb + pl.split_bytes;
-        cb.ws_BT = wsb + pl.split_bytes + pl.s_bytes;
-        cb.ws_C = wsb + pl.split_bytes + pl.s_bytes + pl.bt_bytes;
+        cb.ws_S = wsb;
+        cb.ws_BT = wsb + pl.s_bytes;
+        cb.ws_C = wsb + pl.s_bytes + pl.bt_bytes;
         cb.batch = a.batch;
         cb.seqlen = a.seqlen;
         cb.ngroups = a.ngroups;
@@ -427,11 +454,11 @@ struct BwdPlan {
     size_t dbh_bytes, part_bytes, ws_bytes;
 };
 
-ssd_status_t make_bwd_plan(const ssd_shape_t *s, ssd_dtype_t io, BwdPlan *bp) {
+ssd_status_t make_bwd_plan(const ssd_shape_t *s, ssd_dtype_t io, BwdPlan *bp, hipStream_t stream) {
     ssd_options_t o;
     memset(&o, 0, sizeof(o));
     o.split_len = ssd::kBwdQ;
-    ssd_status_t st = make_plan(s, ssd::kBwdQ, io, &o, &bp->fwd);
+    ssd_status_t st = make_plan(s, ssd::kBwdQ, io, &o, &bp->fwd, stream);
     if (st != SSD_OK) return st;
     bp->dbh_bytes = round_up((size_t)s->batch * s->seqlen * s->nheads * s->dstate * sizeof(float), 256);
     bp->part_bytes = round_up((size_t)s->batch * s->nheads * sizeof(float), 256);
@@ -456,7 +483,7 @@ ssd_status_t ssd_fwd_fused(const ssd_shape_t *shape, ssd_dtype_t io, const void 
 
 size_t ssd_bwd_workspace_bytes(const ssd_shape_t *shape, ssd_dtype_t io) {
     BwdPlan bp;
-    if (make_bwd_plan(shape, io, &bp) != SSD_OK) return 0;
+    if (make_bwd_plan(shape, io, &bp, nullptr) != SSD_OK) return 0;
     return bp.ws_bytes;
 }
 
@@ -468,7 +495,7 @@ ssd_status_t ssd_bwd(const ssd_shape_t *shape, ssd_dtype_t io, const void *x, co
                      void *stream) {
     g_last_error.clear();
     BwdPlan bp;
-    ssd_status_t st = make_bwd_plan(shape, io, &bp);
+    ssd_status_t st = make_bwd_plan(shape, io, &bp, (hipStream_t)stream);
     if (st != SSD_OK) return st;
     if (!x || !dt || !A || !B || !C || !dy || !dx || !ddt || !dA || !dB || !dC)
         return fail(SSD_ERR_NULL, "x, dt, A, B, C, dy, dx, ddt, dA, dB and dC are required");
@@ -484,6 +511,9 @@ ssd_status_t ssd_bwd(const ssd_shape_t *shape, ssd_dtype_t io, const void *x, co
         return fail(SSD_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given%s", bp.ws_bytes,
                     workspace_bytes, workspace ? "" : " (NULL)");
     if (!aligned(workspace, 16)) return fail(SSD_ERR_ALIGN, "workspace must be 16-byte aligned");
+    // the gradient reduction runs one thread per (row, token, group, state) element
+    if ((shape->batch * shape->seqlen * shape->ngroups * shape->dstate + shape->nheads) / 256 >= kMaxGrid)
+        return fail(SSD_ERR_UNSUPPORTED, "problem too large for the gradient reduction grid");
     ssd_options_t o;
     memset(&o, 0, sizeof(o));
     o.split_len = ssd::kBwdQ;
@@ -501,7 +531,7 @@ ssd_status_t ssd_bwd(const ssd_shape_t *shape, ssd_dtype_t io, const void *x, co
     a.A = A;
     a.D = D;
     a.seq_idx = seq_idx;
-    a.states = bp.fwd.nsplits > 1 ? (const float *)workspace : nullptr;
+    a.states = bp.fwd.nsplits > 1 ? (const float *)((const char *)workspace + bp.fwd.group_bytes()) : nullptr;
     a.init_states = init_states;
     a.dfinal = dfinal;
     a.dx = dx;
@@ -611,6 +641,8 @@ ssd_status_t ssd_decode_step_fused(const ssd_shape_t *shape, ssd_dtype_t io, con
     if (st != SSD_OK) return st;
     if (shape->seqlen != 1) return fail(SSD_ERR_SHAPE, "a decode step takes one token (seqlen %lld)",
                                         (long long)shape->seqlen);
+    if (shape->batch * shape->nheads > kMaxGrid)
+        return fail(SSD_ERR_UNSUPPORTED, "batch * nheads above the launch limit");
     if (!x || !dt || !A || !B || !C || !state || !y)
         return fail(SSD_ERR_NULL, "x, dt, A, B, C, state and y are required");
     const size_t esz = io == SSD_BF16 ? 2 : 4;
@@ -649,6 +681,74 @@ ssd_status_t ssd_decode_step_fused(const ssd_shape_t *shape, ssd_dtype_t io, con
         return fail(SSD_ERR_UNSUPPORTED, "no decode kernel for dstate %d", a.dstate);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(SSD_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+    return SSD_OK;
+}
+
+
+int64_t ssd_segsum_record_words(int64_t chunk_size) {
+    if (chunk_size != 64 && chunk_size != 128 && chunk_size != 256) return 0;
+    return 4 * chunk_size + 2 * (chunk_size / 16) + chunk_size / 32;
+}
+
+ssd_status_t ssd_debug_segsum_factors(const ssd_shape_t *shape, const float *dt, const float *A,
+                                      const int32_t *seq_idx, int64_t chunk_size, float *out,
+                                      void *stream) {
+    g_last_error.clear();
+    ssd_status_t st = check_shape(shape, chunk_size);
+    if (st != SSD_OK) return st;
+    if (!dt || !A || !out) return fail(SSD_ERR_NULL, "dt, A and out are required");
+    if (!aligned(dt, 4) || !aligned(A, 4) || (seq_idx && !aligned(seq_idx, 4)) || !aligned(out, 4))
+        return fail(SSD_ERR_ALIGN, "dt, A, seq_idx and out must be 4-byte aligned");
+    const int64_t nchunks = (shape->seqlen + chunk_size - 1) / chunk_size;
+    if (nchunks > 65535) return fail(SSD_ERR_UNSUPPORTED, "more than 65535 chunks");
+    ssd::MaskArgs m;
+    memset(&m, 0, sizeof(m));
+    m.dt = dt;
+    m.A = A;
+    m.seq_idx = seq_idx;
+    m.factors = out;
+    m.variant = SSD_SEGSUM_HIERARCHY;
+    m.batch = (int)shape->batch;
+    m.seqlen = (int)shape->seqlen;
+    m.nheads = (int)shape->nheads;
+    m.chunk_begin = 0;
+    m.count = (int)nchunks;
+    (void)hipGetLastError();
+    ssd::launch_mask((int)chunk_size, m, (hipStream_t)stream);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(SSD_ERR_HIP, "segsum factor launch: %s", hipGetErrorString(e));
+    return SSD_OK;
+}
+
+ssd_status_t ssd_debug_fwd_segsum_factors(const ssd_shape_t *shape, ssd_dtype_t io, const void *x,
+                                          const float *dt, const float *A, const void *B,
+                                          const void *C, const float *D, const int32_t *seq_idx,
+                                          int64_t chunk_size, const float *init_states, void *y,
+                                          float *final_states, void *workspace,
+                                          size_t workspace_bytes, const ssd_options_t *opts,
+                                          float *out, void *stream) {
+    g_last_error.clear();
+    if (io != SSD_BF16) return fail(SSD_ERR_UNSUPPORTED, "the segsum factor export is a bf16-path debug aid");
+    if (!out) return fail(SSD_ERR_NULL, "out is required");
+    if (!aligned(out, 4)) return fail(SSD_ERR_ALIGN, "out must be 4-byte aligned");
+    return fwd_impl(shape, io, x, dt, A, B, C, D, seq_idx, chunk_size, init_states, y, final_states,
+                    nullptr, workspace, workspace_bytes, opts, stream, false, out);
+}
+
+ssd_status_t ssd_debug_exp2_probe(uint32_t first_bits, uint32_t count, uint32_t *counts,
+                                  uint32_t nthreads, void *stream) {
+    g_last_error.clear();
+    if (!counts) return fail(SSD_ERR_NULL, "counts is required");
+    if (!aligned(counts, 4)) return fail(SSD_ERR_ALIGN, "counts must be 4-byte aligned");
+    if (first_bits < 0x80000000u || count == 0 || (uint64_t)first_bits + count - 1 > 0xFF800000u)
+        return fail(SSD_ERR_UNSUPPORTED, "the probe covers non-positive fp32 patterns in "
+                    "[0x80000000, 0xff800000] (-0 .. -inf)");
+    if (nthreads == 0 || nthreads > (1u << 24)) return fail(SSD_ERR_UNSUPPORTED, "nthreads must be in [1, 2^24]");
+    const uint32_t span = (uint32_t)(((uint64_t)count + nthreads - 1) / nthreads);
+    (void)hipGetLastError();
+    ssd::launch_exp2_probe(first_bits, count, span, counts, nthreads, (hipStream_t)stream);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(SSD_ERR_HIP, "exp2 probe launch: %s", hipGetErrorString(e));
     return SSD_OK;
 }
 

@@ -102,9 +102,24 @@ __global__ __launch_bounds__(kThreads) void ssd_mask_kernel(MaskArgs m) {
     if (tid == 0) sg.any_reset = flag_any;
     if (tid < Q) seg_block_sums<Q>(sg, tid);
     __syncthreads();
+    if (m.factors && tid < Q) {
+        // the block-sum path's factors in the head kernel's terms (before
+        // seg_chunk_products turns rs into chunk-wide reset positions)
+        using R = SegRecord<Q>;
+        float *rec = m.factors + (((int64_t)b * H + h) * m.count + ci) * R::WORDS;
+        const int t = tid;
+        rec[R::D + t] = sg.d[t];
+        rec[R::DT + t] = sg.dt[t];
+        rec[R::WD + t] = __fmul_rn(sg.W[t], sg.dt[t]);
+        rec[R::LAST1 + t] = __builtin_bit_cast(float, sg.rs[t] + 1);
+        if ((t & 15) == 0) rec[R::TB + (t >> 4)] = sg.Tb[t >> 4];
+        if ((t & 15) == 15) rec[R::BLAST1 + (t >> 4)] = __builtin_bit_cast(float, sg.blast[t >> 4] + 1);
+        if ((t & 31) == 0) rec[R::TP + (t >> 5)] = __fmul_rn(sg.Tb[t >> 4], sg.Tb[(t >> 4) + 1]);
+    }
     if (tid < Q) seg_chunk_products<Q>(sg, tid);
     __syncthreads();
 
+    if (!m.out && !m.sums) return;   // factors only
     if (tid == 0) block_sum = 0.f;
     float *out = m.out ? m.out + (((int64_t)b * H + h) * m.count + ci) * Q * Q : nullptr;
     float csum = 0.f;
@@ -192,6 +207,52 @@ void launch_mask(int Q, const MaskArgs &m, hipStream_t stream) {
     case 128: launch_mask_q<128>(m, stream); break;
     default: launch_mask_q<256>(m, stream); break;
     }
+}
+
+}  // namespace ssd
+
+namespace ssd {
+
+// Exhaustive check of the hardware exp2 (v_exp_f32, the only exponential the
+// decay factors use) over a range of fp32 bit patterns.  The mask stays in
+// [0, 1] and non-increasing along rows only if exp2 is monotone and <= 1 on
+// non-positive inputs (page "GPU Hierarchy Meets Structured Matrices",
+// abstract: segsum without monotonicity violations).  Thread t takes the
+// patterns [first + t span, first + (t+1) span) of the range [first, first +
+// count), plus the pattern before its first one, and counts, for patterns
+// u and u + 1 in its part: exp2(f(u+1)) > exp2(f(u)) when f(u+1) < f(u)
+// (negative floats: a larger pattern is a smaller value), values above 1,
+// values below 0 or NaN.  Plain vector stores of one counter triple per
+// thread; the host sums them.
+__global__ __launch_bounds__(256) void ssd_exp2_probe_kernel(uint32_t first, uint32_t count,
+                                                             uint32_t span, uint32_t *out,
+                                                             uint32_t nthreads) {
+    const uint32_t t = blockIdx.x * 256u + threadIdx.x;
+    if (t >= nthreads) return;
+    const uint64_t lo = (uint64_t)t * span;
+    const uint64_t hi = lo + span < (uint64_t)count ? lo + span : (uint64_t)count;
+    uint32_t up = 0, above = 0, bad = 0;
+    if (lo < hi) {
+        float prev = __builtin_amdgcn_exp2f(__builtin_bit_cast(float, first + (uint32_t)(lo > 0 ? lo - 1 : 0)));
+        for (uint64_t k = lo; k < hi; ++k) {
+            const float x = __builtin_bit_cast(float, first + (uint32_t)k);
+            const float v = __builtin_amdgcn_exp2f(x);
+            // within the negative range a larger bit pattern is a smaller x
+            if (k > 0 && v > prev) ++up;
+            if (v > 1.f) ++above;
+            if (!(v >= 0.f)) ++bad;
+            prev = v;
+        }
+    }
+    out[3 * (uint64_t)t + 0] = up;
+    out[3 * (uint64_t)t + 1] = above;
+    out[3 * (uint64_t)t + 2] = bad;
+}
+
+void launch_exp2_probe(uint32_t first, uint32_t count, uint32_t span, uint32_t *out, uint32_t nthreads,
+                       hipStream_t stream) {
+    hipLaunchKernelGGL(ssd_exp2_probe_kernel, dim3((nthreads + 255) / 256), dim3(256), 0, stream, first,
+                       count, span, out, nthreads);
 }
 
 }  // namespace ssd

@@ -57,6 +57,8 @@ struct ChunkArgs {
     int dt_clamp;              // nonzero: dt <- min(max(dt, dt_lo), dt_hi)
     float dt_lo, dt_hi;
     int segsum_variant;        // SegsumVariant of the intra-chunk mask (fp32 kernel only)
+    float *dbg_seg;            // nullable: the bf16 head kernel writes each chunk's segsum
+                               // factors here (SegRecord layout, [batch][nheads][nchunks])
 };
 
 // Map from a raw per-token value to the step size dt of one head: plus the
@@ -134,6 +136,7 @@ struct MaskArgs {
     const int32_t *seq_idx;
     float *out;          // [batch][nheads][count][Q][Q], nullable
     float *sums;         // [batch][nheads][count]: sum of each chunk's mask, nullable
+    float *factors;      // [batch][nheads][count] SegRecords of the block-sum path, nullable
     int variant;         // SegsumVariant
     int batch, seqlen, nheads;
     int chunk_begin, count;

@@ -198,14 +198,18 @@ __device__ __attribute__((always_inline)) inline void scan_body(
                 p_prev[k] = seq_row[max(tg - 1, 0)];
             }
         };
+        // Debug export of the factors (full pass, one workgroup per head).
+        const bool dbg = !LOCAL && a.dbg_seg != nullptr && pb == 0 && un.half <= 0;
         auto segsum = [&](int c, SegBuf<Q> &sgb) __attribute__((always_inline)) {
+            float *rec = dbg ? a.dbg_seg + (((int64_t)b * H + h) * a.nchunks + c) * SegRecord<Q>::WORDS
+                             : nullptr;
 #pragma unroll
             for (int k = pw; k < Q / 64; k += NPROD) {
                 const int t = k * 64 + lane, tg = c * Q + t;
                 const bool valid = tg < L;
                 const float dtv = valid ? dt_apply(dm, p_dt[k]) : 0.f;
                 const int flag = (resets && valid && tg > 0 && p_cur[k] != p_prev[k]) ? 1 : 0;
-                seg_tokens<Q>(sgb, t, dtv, flag, A_h, resets);
+                seg_tokens<Q>(sgb, t, dtv, flag, A_h, resets, rec);
             }
         };
         // HBM streams of the workgroup in 1 KB blocks (64 lanes x 16 bytes):

@@ -172,6 +172,17 @@ struct SegBuf {
     float Tp[NB / 2]; // decay over 32-token pair m: Tb[2m] * Tb[2m+1]
 };
 
+// Debug record of one chunk's segsum factors (32-bit words): the values the
+// bf16 head kernel keeps in SegBuf, in a layout both segsum paths can write,
+// so that the DPP sums of seg_tokens can be compared bit for bit with the
+// sequential sums of seg_block_sums.  last1 and blast1 are int32 words.
+template <int Q>
+struct SegRecord {
+    static constexpr int NB = Q / 16;
+    static constexpr int D = 0, DT = Q, WD = 2 * Q, LAST1 = 3 * Q, TB = 4 * Q, BLAST1 = 4 * Q + NB,
+                         TP = 4 * Q + 2 * NB, WORDS = 4 * Q + 2 * NB + NB / 2;
+};
+
 template <int CTRL>
 __device__ inline int dpp_row(int v) {
     // row_mask and bank_mask 0xf; lanes whose source lies outside the row read 0
@@ -187,9 +198,10 @@ __device__ inline float dpp_row_shl1(float v) {
 // Steps 1-2 for token t (thread t < Q; whole waves only): dtv and flag are
 // the token's dt and reset flag (0 past the end of the row).  resets is
 // uniform: false when the call has no seq_idx.
+// rec (nullable): the chunk's SegRecord in global memory, written as well.
 template <int Q>
 __device__ inline void seg_tokens(SegBuf<Q> &s, int t, float dtv, int flag, float A_h,
-                                  bool resets) {
+                                  bool resets, float *rec = nullptr) {
     const float d = __fmul_rn(__fmul_rn(dtv, A_h), kLog2e);
     float e = d;
 #pragma unroll
@@ -226,7 +238,18 @@ __device__ inline void seg_tokens(SegBuf<Q> &s, int t, float dtv, int flag, floa
     // the first lane of each 32-token pair takes the decay of the pair's
     // second sub-block from 16 lanes up (same wave: waves own 64 tokens)
     const float tb_hi = __shfl_down(tb, 16, 64);
-    if ((t & 31) == 0) s.Tp[t >> 5] = __fmul_rn(tb, tb_hi);
+    const float tp = __fmul_rn(tb, tb_hi);
+    if ((t & 31) == 0) s.Tp[t >> 5] = tp;
+    if (rec) {
+        using R = SegRecord<Q>;
+        rec[R::D + t] = d;
+        rec[R::DT + t] = dtv;
+        rec[R::WD + t] = __fmul_rn(W, dtv);
+        rec[R::LAST1 + t] = __builtin_bit_cast(float, last1);
+        if ((t & 15) == 0) rec[R::TB + (t >> 4)] = tb;
+        if ((t & 15) == 15) rec[R::BLAST1 + (t >> 4)] = __builtin_bit_cast(float, last1);
+        if ((t & 31) == 0) rec[R::TP + (t >> 5)] = tp;
+    }
 }
 
 // Step 3 in registers (every wave after a barrier): the cross-sub-block

@@ -17,3 +17,17 @@ def pytest_configure(config):
 def oracle_mod():
     import oracle
     return oracle
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    try:
+        from ssd_testlib import ERRORS
+    except ImportError:
+        return
+    if not ERRORS:
+        return
+    tr = terminalreporter
+    tr.write_sep("-", "parity: max|gpu - oracle| / max|oracle| over whole tensors")
+    for label, ey, ef, tol in ERRORS:
+        tr.write_line(f"{label:60s} y {ey:.3e}  final_states {ef:.3e}  (tol {tol:g}, "
+                      f"margin {tol / max(ey, ef, 1e-30):.1f}x)")

@@ -264,3 +264,52 @@ def test_binding_argument_counts_match_the_header():
         argtypes = getattr(lib, name).argtypes
         assert argtypes is not None, name
         assert len(argtypes) == n, f"{name}: header {n} parameters, binding {len(argtypes)}"
+
+
+def test_debug_export_host_validation():
+    lib = ssd.load_library()
+    s = good_shape()
+    assert lib.ssd_segsum_record_words(256) == 4 * 256 + 2 * 16 + 8
+    assert lib.ssd_segsum_record_words(64) == 4 * 64 + 2 * 4 + 2
+    assert lib.ssd_segsum_record_words(100) == 0
+    assert lib.ssd_debug_segsum_factors(ctypes.byref(s), FAKE, FAKE, None, 256, None, None) == 1
+    assert lib.ssd_debug_segsum_factors(ctypes.byref(s), FAKE, FAKE, None, 96, FAKE, None) == 3
+    assert lib.ssd_debug_segsum_factors(ctypes.byref(s), FAKE + 2, FAKE, None, 256, FAKE, None) == 4
+    o = ssd.Options()
+    # the head kernel's factor export is a bf16-path aid
+    assert lib.ssd_debug_fwd_segsum_factors(ctypes.byref(s), 0, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
+                                            256, None, FAKE, None, None, 0, ctypes.byref(o), FAKE,
+                                            None) == 3
+    assert lib.ssd_debug_fwd_segsum_factors(ctypes.byref(s), 1, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
+                                            256, None, FAKE, None, None, 0, ctypes.byref(o), None,
+                                            None) == 1
+    # without a workspace the bf16 call stops at the workspace check
+    assert lib.ssd_debug_fwd_segsum_factors(ctypes.byref(s), 1, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
+                                            256, None, FAKE, None, None, 0, ctypes.byref(o), FAKE,
+                                            None) == 5
+    # exp2 probe: non-positive patterns only, -0 .. -inf
+    assert lib.ssd_debug_exp2_probe(0, 16, FAKE, 64, None) == 3
+    assert lib.ssd_debug_exp2_probe(0xFF800000, 2, FAKE, 64, None) == 3
+    assert lib.ssd_debug_exp2_probe(0x80000000, 0, FAKE, 64, None) == 3
+    assert lib.ssd_debug_exp2_probe(0x80000000, 16, None, 64, None) == 1
+    assert lib.ssd_debug_exp2_probe(0x80000000, 16, FAKE, 0, None) == 3
+    assert lib.ssd_debug_exp2_probe(0x80000000, 16, FAKE + 2, 64, None) == 4
+
+
+def test_launch_limits_are_checked_on_the_host():
+    """Shapes whose work units or grids would not fit a launch (or an int) are
+    refused before anything is launched."""
+    huge = ssd.Shape(1 << 20, 1, 65536, 16, 16, 1)      # 2^36 (batch row, head) units
+    assert ssd.ssd_fwd_workspace_bytes(huge, 64, 1) == 0
+    assert _fwd(huge, chunk=64, ws=FAKE, ws_bytes=1 << 40) == 3
+    assert _fwd(huge, io=0, chunk=64, ws=FAKE, ws_bytes=1 << 40) == 3
+    lib = ssd.load_library()
+    dec = ssd.Shape(1 << 20, 1, 65536, 16, 16, 1)
+    assert lib.ssd_decode_step(ctypes.byref(dec), 1, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE,
+                               None) == 3
+
+
+def test_unknown_dtype_is_rejected():
+    s = good_shape()
+    for io in (2, 7, 1 << 20):
+        assert _fwd(s, io=io) == 3

@@ -136,3 +136,40 @@ def test_bwd_full_layer_sampled_heads():
     (the kernel's LDS-staged operand path): first, middle and last
     workgroup's heads."""
     _sampled_heads_vs_oracle("layer27b", [(0, 0), (3, 41), (7, 79)], seed=11)
+
+
+def test_bwd_every_gradient_at_a_layer_shaped_launch():
+    """Every gradient (dx, ddt, dA, dB, dC, dD) element by element at a shape
+    of the 2.7B layer that the oracle holds in memory: 1 x 2048 tokens, 8
+    heads of one group, headdim 64, dstate 128, bf16 (the kernel's LDS-staged
+    path, the one the layer-sized benchmark runs), so that dB and dC are the
+    sums over eight heads that the reduction kernel forms."""
+    wl = workloads.custom_workload(name="bwd_layer_shape", batch=1, seqlen=2048, nheads=8,
+                                   headdim=64, dstate=128, ngroups=1, chunk_size=64, io="bf16")
+    inp = workloads.make_inputs(wl, seed=21)
+    g, ref = _run(inp, seed=21)
+    errs = _check(g, ref, TOL["bf16"], wl.name)
+    print(wl.name, {k: f"{e:.1e}" for k, e in errs.items()})
+
+
+def test_bwd_full_layer_dA_dD_of_sampled_heads():
+    """dA and dD of sampled heads at the full 2.7B-shaped layer (8 x 2048, 80
+    heads): both are sums over the batch rows, so the oracle runs every row
+    of each sampled head (heads are independent in the forward pass)."""
+    import torch
+    import ssd_chunked_scan_amd as ssd
+    wl = workloads.WORKLOADS["layer27b"]
+    inp = workloads.make_inputs(wl, seed=0)
+    t = to_device(inp)
+    dy = workloads.bf16_round(np.random.default_rng(11).standard_normal(inp.x.shape).astype(np.float32))
+    g = ssd.ssd_bwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"],
+                    torch.from_numpy(dy).cuda().to(torch.bfloat16))
+    torch.cuda.synchronize()
+    dA, dD = g["dA"].cpu().numpy(), g["dD"].cpu().numpy()
+    for h in (0, 79):
+        ref = oracle.ssd_backward(inp.x[:, :, h:h + 1], inp.dt[:, :, h:h + 1], inp.A[h:h + 1],
+                                  inp.B, inp.C, inp.D[h:h + 1], dy[:, :, h:h + 1])
+        e_a = abs(dA[h] - ref["dA"][0]) / abs(ref["dA"][0])
+        e_d = abs(dD[h] - ref["dD"][0]) / abs(ref["dD"][0])
+        print(f"layer27b bwd head {h}: dA {e_a:.1e} dD {e_d:.1e}")
+        assert e_a <= TOL["bf16"] and e_d <= TOL["bf16"], (h, e_a, e_d)

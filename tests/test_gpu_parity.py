@@ -2,15 +2,17 @@
 
 Parity bar: max|y_gpu - y_ref| / max|y_ref| <= 1e-2 for bf16 inputs and
 <= 1e-4 for fp32 inputs, final_states held to the same bound, on identical
-seeded inputs.  Small cases compare every element; the full-size workloads
-compare every output of a sample of (batch row, head) pairs that the oracle
-computes independently.
+seeded inputs.  Every test compares every element of y and final_states
+with one oracle run over the whole call (the full-size workloads included,
+in the launch configuration the benchmark times); the outputs start out NaN,
+so an element the kernels never write fails.  The measured errors are listed
+in the terminal summary.
 """
 import numpy as np
 import pytest
 
 import workloads
-from ssd_testlib import TOL, max_rel, oracle_slice, run_gpu, to_device
+from ssd_testlib import TOL, max_rel, oracle_slice, record_error, run_gpu, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -19,10 +21,16 @@ def _case(name, **kw):
     return workloads.custom_workload(name=name, **kw)
 
 
-def _check_full(inp, y, fs, tol, init_states=None, skip=True):
-    b, H = inp.wl.batch, inp.wl.nheads
-    yr, fsr = oracle_slice(inp, range(b), range(H), init_states, skip=skip)
+def _check_full(inp, y, fs, tol, init_states=None, skip=True, label=None):
+    """Every element of y and final_states against the oracle over the whole
+    call."""
+    import oracle
+    h0 = None if init_states is None else np.asarray(init_states, np.float64)
+    yr, fsr = oracle.ssd_forward(inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D if skip else None,
+                                 inp.seq_idx, h0)
     ey, ef = max_rel(y, yr), max_rel(fs, fsr)
+    if label is not None:
+        record_error(label, ey, ef, tol)
     assert ey <= tol and ef <= tol, f"{inp.wl.name}: y err {ey:.3e}, final_states err {ef:.3e}"
     return ey, ef
 
@@ -103,40 +111,38 @@ def test_packed_documents_small(io):
 
 
 # ----------------------------------------------------------- full-size workloads
-
-def _sampled(inp, pairs, y, fs, tol, label, skip=True):
-    worst = 0.0
-    for b, h in pairs:
-        yr, fsr = oracle_slice(inp, [b], [h], skip=skip)
-        ey = max_rel(y[b:b + 1, :, h:h + 1], yr)
-        ef = max_rel(fs[b:b + 1, h:h + 1], fsr)
-        worst = max(worst, ey, ef)
-        assert ey <= tol and ef <= tol, f"{label} (b={b}, h={h}): y {ey:.3e} fs {ef:.3e}"
-    return worst
-
+# Each full-size call is compared element by element with one oracle run over
+# the whole call (every batch row and head; the fp64 recurrence takes well
+# under a second per workload on the host cores).
 
 @pytest.mark.parametrize("skip", [True, False], ids=["with_skip", "no_skip"])
-def test_layer27b_full_size_sampled(skip):
+def test_layer27b_full_size(skip):
+    """The benchmarked call: 8 x 2048 tokens, 80 heads, headdim 64, dstate 128,
+    chunk 256, bf16, every unit of the launch (whole-headdim workgroups and the
+    last round's half-headdim ones)."""
     inp = workloads.make_inputs(workloads.WORKLOADS["layer27b"], seed=0)
     y, fs = run_gpu(inp, skip=skip)
-    assert np.isfinite(y).all() and np.isfinite(fs).all()
-    pairs = [(0, 0), (3, 41), (7, 79), (5, 17)]
-    _sampled(inp, pairs, y, fs, TOL["bf16"], "layer27b", skip=skip)
+    _check_full(inp, y, fs, TOL["bf16"], skip=skip, label=f"layer27b {'skip' if skip else 'no skip'}")
+
+
+def test_layer27b_bitwise_determinism():
+    """Two calls of the benchmarked launch give identical bits."""
+    inp = workloads.make_inputs(workloads.WORKLOADS["layer27b"], seed=0)
+    a = run_gpu(inp)
+    b = run_gpu(inp)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
 @pytest.mark.parametrize("skip", [True, False], ids=["with_skip", "no_skip"])
 def test_partial_last_round_half_blocks(skip):
     """288 (batch row, head) units of one workgroup each on a 256-CU device: the
     last 32 units (batch row 1, heads 112..143) run as two workgroups of half
-    the headdim block each.  Samples on both sides of that boundary, ragged
-    tail chunk, two groups."""
+    the headdim block each.  Ragged tail chunk, two groups."""
     wl = _case("half_blocks", batch=2, seqlen=600, nheads=144, headdim=64, dstate=128, ngroups=2,
                chunk_size=256, io="bf16")
     inp = workloads.make_inputs(wl, seed=3)
     y, fs = run_gpu(inp, skip=skip)
-    assert np.isfinite(y).all() and np.isfinite(fs).all()
-    _sampled(inp, [(0, 5), (1, 111), (1, 112), (1, 127), (1, 143)], y, fs, TOL["bf16"],
-             "half blocks", skip=skip)
+    _check_full(inp, y, fs, TOL["bf16"], skip=skip, label=f"half blocks {'skip' if skip else 'no skip'}")
 
 
 def test_half_blocks_with_forced_splits_and_init_state():
@@ -149,29 +155,22 @@ def test_half_blocks_with_forced_splits_and_init_state():
     inp = workloads.make_inputs(wl, seed=5)
     h0 = np.random.default_rng(6).standard_normal((2, 144, 64, 128)).astype(np.float32) * 0.5
     y, fs = run_gpu(inp, init_states=h0, split_len=256)
-    assert np.isfinite(y).all() and np.isfinite(fs).all()
-    for b, h in [(0, 0), (1, 111), (1, 112), (1, 143)]:
-        yr, fsr = oracle_slice(inp, [b], [h], init_states=h0)
-        ey = max_rel(y[b:b + 1, :, h:h + 1], yr)
-        ef = max_rel(fs[b:b + 1, h:h + 1], fsr)
-        assert ey <= TOL["bf16"] and ef <= TOL["bf16"], f"(b={b}, h={h}): y {ey:.3e} fs {ef:.3e}"
+    _check_full(inp, y, fs, TOL["bf16"], init_states=h0, label="half blocks, 3 splits, h0")
 
 
 @pytest.mark.parametrize("skip", [True, False], ids=["with_skip", "no_skip"])
-def test_decay_stress_full_size_sampled(skip):
+def test_decay_stress_full_size(skip):
     inp = workloads.make_inputs(workloads.WORKLOADS["decay"], seed=0)
     y, fs = run_gpu(inp, skip=skip)
-    assert np.isfinite(y).all() and np.isfinite(fs).all()
-    _sampled(inp, [(0, 0), (0, 9)], y, fs, TOL["bf16"], "decay", skip=skip)
+    _check_full(inp, y, fs, TOL["bf16"], skip=skip, label=f"decay {'skip' if skip else 'no skip'}")
 
 
 @pytest.mark.parametrize("skip", [True, False], ids=["with_skip", "no_skip"])
-def test_packed_full_size_sampled_and_per_document(skip):
+def test_packed_full_size_and_per_document(skip):
     import oracle
     inp = workloads.make_inputs(workloads.WORKLOADS["packed"], seed=0)
     y, fs = run_gpu(inp, skip=skip)
-    assert np.isfinite(y).all()
-    _sampled(inp, [(0, 0), (0, 13), (0, 31)], y, fs, TOL["bf16"], "packed", skip=skip)
+    _check_full(inp, y, fs, TOL["bf16"], skip=skip, label=f"packed {'skip' if skip else 'no skip'}")
     # independent per-document oracle runs from a zero state, head 5 (group 1)
     lens = inp.doc_lens
     starts = np.concatenate([[0], np.cumsum(lens)])
@@ -189,10 +188,10 @@ def test_packed_full_size_sampled_and_per_document(skip):
 
 @pytest.mark.parametrize("b,L", workloads.SWEEP_SHAPES)
 @pytest.mark.parametrize("Q", [128, 256])
-def test_sweep_sampled(b, L, Q):
-    """Sampled with the skip for one head and without it (D = None) for another."""
+def test_sweep_full_size(b, L, Q):
+    """Every element, with the skip and without it (D = None)."""
     inp = workloads.make_inputs(workloads.WORKLOADS[f"sweep_b{b}_L{L}_q{Q}"], seed=0)
     y, fs = run_gpu(inp)
-    _sampled(inp, [(b - 1, 31), (0, 7)], y, fs, TOL["bf16"], f"sweep b{b} L{L} Q{Q}")
+    _check_full(inp, y, fs, TOL["bf16"], label=f"sweep b{b} L{L} Q{Q} skip")
     y, fs = run_gpu(inp, skip=False)
-    _sampled(inp, [(0, 3)], y, fs, TOL["bf16"], f"sweep b{b} L{L} Q{Q} no skip", skip=False)
+    _check_full(inp, y, fs, TOL["bf16"], skip=False, label=f"sweep b{b} L{L} Q{Q} no skip")

@@ -161,3 +161,29 @@ def test_headdim_block_invariance(Q):
         assert max_rel(ys, y0) <= TOL["bf16"] and max_rel(fs, f0) <= TOL["bf16"]
     yr, fr = oracle_slice(inp, range(2), range(4))
     assert max_rel(y0, yr) <= TOL["bf16"] and max_rel(f0, fr) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("split_len", [0, 128], ids=["one_split", "forced_splits"])
+def test_workspace_poison_does_not_change_outputs(split_len):
+    """Every workspace byte a kernel reads is written earlier in the same call:
+    a workspace filled with 0xff bytes (NaN as fp32 and as bf16) gives the
+    same bits as a zeroed one, with and without sequence splits (split states,
+    per-group C B^T, B^T and C operands)."""
+    import torch
+    import ssd_chunked_scan_amd as ssd
+    inp = workloads.make_inputs(_wl(), seed=16)
+    t = to_device(inp)
+    h0 = torch.from_numpy(np.random.default_rng(17).standard_normal((2, 4, 64, 64)).astype(np.float32)).cuda()
+    shape = ssd.Shape(2, 1100, 4, 64, 64, 2)
+    nbytes = ssd.ssd_fwd_workspace_bytes(shape, 128, 1, split_len=split_len)
+    assert nbytes > 0
+    outs = []
+    for fill in (0x00, 0xFF):
+        ws = torch.full((nbytes,), fill, dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+        y, f = ssd.ssd_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], None, chunk_size=128,
+                           init_states=h0, split_len=split_len, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append((y.clone(), f.clone()))
+    assert torch.isfinite(outs[0][0].float()).all()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
