@@ -415,6 +415,7 @@ ssd_status_t fwd_impl(const ssd_shape_t *shape, ssd_dtype_t io, const void *x, c
     const bool reuse = opts && (opts->flags & SSD_OPT_REUSE_GROUP_OPERANDS);
     if (io == SSD_BF16 && !reuse) {
         ssd::CbArgs cb;
+        memset(&cb, 0, sizeof(cb));
         cb.B = B;
         cb.C = C;
         cb.ws_S = wsb;
@@ -607,6 +608,7 @@ ssd_status_t ssd_debug_chunk_mask_ex(const ssd_shape_t *shape, const float *dt, 
         return fail(SSD_ERR_SHAPE, "chunk range [%lld, %lld) outside [0, %lld)", (long long)chunk_begin,
                     (long long)(chunk_begin + chunk_count), (long long)nchunks);
     ssd::MaskArgs m;
+    memset(&m, 0, sizeof(m));   // every field not set below (factors) stays null
     m.dt = dt;
     m.A = A;
     m.seq_idx = seq_idx;

@@ -90,6 +90,22 @@ static void run_fwd(const fwd_case *c) {
         CHECK(st == SSD_OK, "segsum factors (export): status %d", (int)st);
         free(rec);
     }
+    {
+        /* the mask exports: whole mask of the last chunk, and per-chunk sums */
+        const int64_t nch = (c->L + c->Q - 1) / c->Q;
+        float *mask = buf((size_t)(c->b * c->H * c->Q * c->Q) * 4);
+        float *sums = buf((size_t)(c->b * c->H * nch) * 4);
+        st = ssd_debug_chunk_mask(&s, dt, A, seq, c->Q, nch - 1, 1, mask, NULL);
+        CHECK(st == SSD_OK, "mask export: status %d", (int)st);
+        for (int v = 0; v < 3; ++v) {
+            st = ssd_debug_chunk_mask_ex(&s, dt, A, seq, c->Q, 0, nch, v, NULL, sums, NULL);
+            CHECK(st == SSD_OK, "mask sums, variant %d: status %d", v, (int)st);
+        }
+        st = ssd_debug_chunk_mask_ex(&s, dt, A, seq, c->Q, nch - 1, 2, 0, mask, NULL, NULL);
+        CHECK(st == SSD_ERR_SHAPE, "mask range past the end: status %d", (int)st);
+        free(mask);
+        free(sums);
+    }
     /* one byte too little workspace */
     if (ws_bytes) {
         st = ssd_fwd_ex(&s, c->io, x, dt, A, B, C, D, seq, c->Q, h0, y, fs, ws, ws_bytes - 1, &o, NULL);
@@ -197,7 +213,7 @@ int main(void) {
     run_decode(4, 8, 64, 128, 2, SSD_BF16, 0);
     run_decode(2, 4, 32, 16, 1, SSD_F32, 1);
     run_errors();
-    CHECK(stub_launches() > 40, "only %llu launches reached the stubs", (unsigned long long)stub_launches());
+    CHECK(stub_launches() > 80, "only %llu launches reached the stubs", (unsigned long long)stub_launches());
     if (g_fail) return 1;
     printf("abi driver: all checks passed (%llu launches)\n", (unsigned long long)stub_launches());
     return 0;

@@ -13,8 +13,10 @@
   identities that hold exactly in the recurrence
   (tests/host_sanitize/oracle_driver.c).
 
-The device code is not instrumented: each sanitizer flag reaches the host
-compiler only.
+The host code is also built with every local variable pattern-initialised,
+so that an argument-block field the API forgets to set reaches a stub as a
+wild pointer instead of a lucky zero.  The device code is not instrumented:
+each of these flags reaches the host compiler only.
 """
 import os
 import shutil
@@ -43,7 +45,9 @@ def _run(cmd, **kw):
 def _hipcc_host(src, obj):
     hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     host_san = []
-    for f in SAN:
+    # every local starts as a 0xaa pattern, so that a field of an argument
+    # block left unset becomes a wild pointer the stubs write through
+    for f in SAN + ["-ftrivial-auto-var-init=pattern"]:
         host_san += ["-Xarch_host", f]
     _run([hipcc, "--offload-arch=gfx950", "--cuda-host-only", "-x", "hip", "-std=c++17", "-O1", "-g",
           *host_san, "-I", CSRC, "-I", INCLUDE, "-c", src, "-o", obj])
