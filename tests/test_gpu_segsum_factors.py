@@ -67,11 +67,15 @@ def test_factors_forced_splits_and_half_headdim_blocks():
 
 def test_factors_decay_stress_full_size():
     """The decay-stress workload (1 x 65536, 16 heads, dt in [1e-2, 1], A in
-    -[4, 64]): most factors underflow to exactly 0."""
+    -[4, 64]): a 16-token sub-block decays by e^-74 on average, so many
+    sub-block decays underflow to exactly 0 (measured: 30%) and the pair
+    decays Tp, products of two of them, more often still."""
     inp = workloads.make_inputs(workloads.WORKLOADS["decay"], seed=0)
     rec = _compare(inp)
     tb = rec[..., 4 * 256:4 * 256 + 16].view(np.float32)
-    assert (tb == 0).mean() > 0.5 and (tb >= 0).all() and (tb <= 1).all()
+    tp = rec[..., 4 * 256 + 32:4 * 256 + 40].view(np.float32)
+    assert (tb == 0).mean() > 0.1 and (tb >= 0).all() and (tb <= 1).all()
+    assert (tp == 0).mean() >= (tb == 0).mean() and (tp >= 0).all() and (tp <= 1).all()
 
 
 def test_factors_packed_full_size():
