@@ -266,6 +266,9 @@ def main():
                          "workload's dt and A, every chunk, mask evaluated but not written")
     ap.add_argument("--backward", action="store_true",
                     help="instead of the forward pass: time the backward pass (ssd_bwd)")
+    ap.add_argument("--flush", choices=["write", "read"], default="read",
+                    help="how the caches are emptied before each cold call: write a 512 MiB scratch "
+                         "buffer (also leaves dirty lines to write back), or read one")
     ap.add_argument("--cold-only", action="store_true",
                     help="only the cold per-call timing of the forward pass (a 512 MiB scratch "
                          "write before each call): the command the rocprofv3 kernel statistics "
@@ -334,19 +337,27 @@ def main():
     torch.cuda.synchronize(dev)
 
     stream = torch.cuda.current_stream(dev)
+    flush_buf = torch.ones(512 << 18, dtype=torch.float32, device=dev)   # 512 MiB
+    flush_sink = torch.empty((), dtype=torch.float32, device=dev)
+
+    def flush(k):
+        if args.flush == "write":
+            flush_buf.fill_(float(k & 0xFF))
+        else:
+            torch.sum(flush_buf, dim=0, out=flush_sink)
+
     if args.cold_only:
-        flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(args.steps)]
         for k, (e0, e1) in enumerate(ev):
-            flush_buf.fill_(k & 0xFF)
+            flush(k)
             e0.record(stream)
             step()
             e1.record(stream)
         torch.cuda.synchronize(dev)
         ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
         avg = sum(ms) / len(ms)
-        print(json.dumps({"metric": "forward pass time per call, cold", "unit": "us",
+        print(json.dumps({"metric": "forward pass time per call, cold", "unit": "us", "flush": args.flush,
                           "workload": wl.name, "steps": args.steps, "avg_us": avg * 1e3,
                           "median_us": ms[len(ms) // 2] * 1e3,
                           "gbs": (wl.algorithmic_bytes() + extra_bytes) / (avg * 1e-3) / 1e9}),
@@ -407,16 +418,14 @@ def main():
           file=sys.stderr, flush=True)
 
     # Cold timing: before every timed call a 512 MiB scratch buffer is
-    # written (outside the events), which evicts the inputs and the
+    # written or read (outside the events), which evicts the inputs and the
     # per-group operands from L2 and from the 256 MB Infinity Cache, so each
     # call streams x from HBM.  Per-call HIP events on the kernels' stream.
-    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-
     def cold_times(fn, n):
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(n)]
         for k, (e0, e1) in enumerate(ev):
-            flush_buf.fill_(k & 0xFF)
+            flush(k)
             e0.record(stream)
             fn()
             e1.record(stream)
@@ -466,7 +475,8 @@ def main():
                 "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                 "kernel": ("forward pass: ssd_cb_kernel + ssd_scan_bf16_kernel" if wl.io == "bf16"
                            else "forward pass: ssd_chunk_f32_kernel"),
-                "timing": "cold: 512 MiB scratch written before each call; HIP events per call, average",
+                "timing": f"cold: 512 MiB scratch {'written' if args.flush == 'write' else 'read'} before "
+                          "each call; HIP events per call, average",
                 "algorithmic_bytes_per_launch": alg_bytes,
                 "avg_launch_us": fwd_cold["avg_us"], "median_us": fwd_cold["median_us"],
                 "p10_us": fwd_cold["p10_us"], "p90_us": fwd_cold["p90_us"],

@@ -37,7 +37,7 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_chunk_f32_kernel(ChunkArgs a)
     __shared__ float sRowD[16 * 16];    // diagonal sub-block mask values
 
     const int tid = threadIdx.x;
-    const Unit un = unit_of_block(a);
+    const Unit un = unit_of_block(a, (int)blockIdx.x);
     const int b = un.b, h = un.h, s = un.s;
     if (a.mode == kModeSplitLocal && s == a.nsplits - 1) return;
     const int L = a.seqlen, H = a.nheads, G = a.ngroups, P = a.headdim, N = a.dstate;

@@ -115,10 +115,10 @@ template <int Q>
 struct CbShape {
     static constexpr int TILES = Q / 16;
     static constexpr int NP = Q / 32;   // 32-token pairs
-    // blocks of row tiles 0 .. I-1
-    static __host__ __device__ constexpr int off(int I) {
-        return (I & 1) ? ((I + 1) / 2) * ((I + 1) / 2) : (I / 2) * (I / 2 + 1);
-    }
+    // blocks of row tiles 0 .. I-1: ((I+1)/2)^2 for odd I, (I/2)(I/2+1) for
+    // even I, written without a select (so that loads addressed with it stay
+    // on straight-line code)
+    static __host__ __device__ constexpr int off(int I) { return ((I >> 1) + 1) * ((I >> 1) + (I & 1)); }
     static constexpr int NBLK = off(TILES);
 };
 
@@ -187,9 +187,9 @@ struct Unit {
 // are ordered (batch, head, split, headdim block), so the heads of one batch
 // row that share its B/C rows run on one XCD and share its L2.  The last
 // half_units units come after all others, two blocks each (the blocks of the
-// last, partial round of workgroups: halving them fills that round).
-__device__ inline Unit unit_of_block(const ChunkArgs &a) {
-    const int blk = blockIdx.x;
+// last, partial round of workgroups: halving them fills that round); they are
+// launched as a kernel of their own, whose block k is block whole + k here.
+__device__ inline Unit unit_of_block(const ChunkArgs &a, int blk) {
     const int whole = a.units - a.half_units;
     int logical, half = -1;
     if (blk < whole) {

@@ -368,12 +368,48 @@ __device__ __attribute__((always_inline)) inline void scan_body(
         segsum(c_begin, segbuf[c_begin & 1]);
         vmem_lds_sync();
         lds_sync();
+        // y_{c-1} of a whole chunk in straight-line, unpredicated stores (the
+        // blocks are issued in the same order as by stream)
+        auto store_y_whole = [&](int cy) __attribute__((always_inline)) {
+#pragma unroll
+            for (int k = KB0; k < KB1; ++k) {
+                constexpr int RB = 64 / CPRY;
+                const int t0 = cy * Q, r = k * RB + yrow;
+                const int cc = ypc ^ swz<CPRY>(r);
+                const bf16x8 v = *(const bf16x8 *)&sY[(k * 64 + lane) * 8];
+                char *dst = ybase + (int64_t)(t0 + k * RB) * row_bytes + (yrow_off + cc * 16);
+                __builtin_nontemporal_store(v, (bf16x8 *)dst);
+            }
+        };
         for (int c = c_begin; c < c_end; ++c) {
             const bool more = c + 1 < c_end;
-            if (more) fetch_tokens(c + 1);
-            stream(more ? c + 1 : -1, (full && c > c_begin) ? c - 1 : -1, (full && gated) ? c : -1);
-            if (more) segsum(c + 1, segbuf[(c + 1) & 1]);
-            vmem_lds_sync();   // X_{c+1} and z_c have landed, sY is read
+            if (gated) {
+                if (more) fetch_tokens(c + 1);
+                stream(more ? c + 1 : -1, c > c_begin ? c - 1 : -1, c);
+                if (more) segsum(c + 1, segbuf[(c + 1) & 1]);
+                vmem_lds_sync();   // X_{c+1} and z_c have landed, sY is read
+                lds_sync();        // the compute waves write y_c to sY in between
+                continue;
+            }
+            // Without the gate: X_{c+1} first, then the segsum of chunk c+1,
+            // then the stores of y_{c-1}.  The barrier needs X_{c+1} in LDS and
+            // the y tile read out of sY, not the stores' completions: for a
+            // whole chunk it lets exactly those KB1 - KB0 newest operations,
+            // the stores, stay in flight (completions count in issue order).
+            if (more) {
+                fetch_tokens(c + 1);
+                stream(c + 1, -1, -1);
+                segsum(c + 1, segbuf[(c + 1) & 1]);
+            }
+            const int cy = c - 1;
+            if (full && c > c_begin && (cy + 1) * Q <= L) {
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                store_y_whole(cy);
+                vmem_lds_sync_keep<KB1 - KB0>();
+            } else {
+                if (full && c > c_begin) stream(-1, cy, -1);
+                vmem_lds_sync();
+            }
             lds_sync();        // the compute waves write y_c to sY in between
         }
         if (full) stream(-1, c_end - 1, -1);
@@ -503,13 +539,39 @@ __device__ __attribute__((always_inline)) inline void scan_body(
         }
     };
 
-    // ---- prologue: X fragments, state tile and C rows of the first chunk
-    // (the producer loads X and computes the segsum values meanwhile)
+    // Fragments of pair m of chunk c (C B^T blocks of the wave's row tiles and
+    // B^T of its state n-tiles) into slot m % NS, loaded unconditionally: a row
+    // tile whose diagonal pair lies left of m loads its diagonal pair again,
+    // so the last load of each row tile is its diagonal pair.
+    constexpr int PD = SSD_PAIR_PREFETCH;   // pairs loaded ahead of their use
+    constexpr int NS = PD + 1;               // fragment slots
+    bf16x8 sfr[NS][IT], bfr[NS][NTW];
+    auto load_pair_of = [&](int c, int m, const int (&Irow)[IT]) __attribute__((always_inline)) {
+        const bf16x8 *Sc = Sws + (int64_t)c * NBLK * 64;
+        const bf16x8 *BTc = BTws + (int64_t)c * NP * N * 4;
+        const int slot = m % NS;
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            if (IT == 2 && it == 0 && m >= NP / 2) continue;   // never reaches the pair
+            const int I = Irow[it];
+            sfr[slot][it] = Sc[(CbShape<Q>::off(I) + min(m, I >> 1)) * 64];
+        }
+#pragma unroll
+        for (int q = 0; q < NTW; ++q)
+            bfr[slot][q] = BTc[((int64_t)m * N + min(nt0 + q, NT - 1) * 16 + l16) * 4 + g];
+    };
+    // vector-memory operations load_pair_of issues for pair 0
+    constexpr int kPair0Loads = IT + NTW;
+
+    // ---- prologue: X fragments, state tile, C rows and the first pair's
+    // fragments of the first chunk (the producer loads X and computes the
+    // segsum values meanwhile)
     if constexpr (LOCAL) {
         vmem_lds_sync();                 // no C rows: the split-local pass has no outputs
     } else {
+        load_pair_of(c_begin, 0, Irow0);
         load_c(c_begin, Irow0);
-        vmem_lds_sync_keep<IT * KN>();   // the C rows may still be in flight
+        vmem_lds_sync_keep<IT * KN + kPair0Loads>();   // C rows and pair 0 may still be in flight
     }
     if (!state_zero) write_h();
     make_fragments(segbuf[c_begin & 1], c_begin);
@@ -529,29 +591,11 @@ __device__ __attribute__((always_inline)) inline void scan_body(
         const SegBuf<Q> &sg = segbuf[buf];
         const int cn = min(c + 1, c_end - 1);   // next chunk (the last one repeats itself)
 
-        // ---- 1. the first column pair's fragments
-        const bf16x8 *Sc = Sws + (int64_t)c * NBLK * 64;
-        const bf16x8 *BTc = BTws + (int64_t)c * NP * N * 4;
-        constexpr int PD = SSD_PAIR_PREFETCH;   // pairs loaded ahead of their use
-        constexpr int NS = PD + 1;               // fragment slots
-        bf16x8 sfr[NS][IT], bfr[NS][NTW];
-        // Fragments of pair m, loaded unconditionally: a row tile whose
-        // diagonal pair lies left of m loads its diagonal pair again, so the
-        // last load of each row tile is its diagonal pair.
-        auto load_pair = [&](int m) __attribute__((always_inline)) {
-            const int slot = m % NS;
+        // ---- 1. the first column pairs' fragments (in the full pass pair 0
+        // was loaded before the hand-over into this chunk)
+        auto load_pair = [&](int m) __attribute__((always_inline)) { load_pair_of(c, m, Irow); };
 #pragma unroll
-            for (int it = 0; it < IT; ++it) {
-                if (IT == 2 && it == 0 && m >= NP / 2) continue;   // never reaches the pair
-                const int I = Irow[it];
-                sfr[slot][it] = Sc[(CbShape<Q>::off(I) + min(m, I >> 1)) * 64];
-            }
-#pragma unroll
-            for (int q = 0; q < NTW; ++q)
-                bfr[slot][q] = BTc[((int64_t)m * N + min(nt0 + q, NT - 1) * 16 + l16) * 4 + g];
-        };
-#pragma unroll
-        for (int m = 0; m < PD && m < NP; ++m) load_pair(m);
+        for (int m = LOCAL ? 0 : 1; m < PD && m < NP; ++m) load_pair(m);
 
         // ---- 2. state projection Y^T = h^T C^T (the Horner steps below
         // give it the decay from the chunk start to the row tile)
@@ -711,8 +755,12 @@ __device__ __attribute__((always_inline)) inline void scan_body(
         if constexpr (LOCAL) {
             vmem_lds_sync();
         } else {
+            // slot 0 is free: the diagonal pairs (the last loads of each row
+            // tile) sit in slot 1 (NS = 2, NP even)
+            static_assert(NS == 2 && NP % 2 == 0, "pair 0 of the next chunk goes to a free slot");
+            load_pair_of(cn, 0, Irow);
             load_c(cn, Irow);
-            vmem_lds_sync_keep<IT * KN>();
+            vmem_lds_sync_keep<IT * KN + kPair0Loads>();
         }
         if (full) write_y(Irow);
         if (c + 1 < c_end) {
@@ -743,13 +791,19 @@ __device__ __attribute__((always_inline)) inline void scan_body(
     }
 }
 
-// The head kernel: one workgroup per unit, or per half unit for the units of
-// the last, partial round (see unit_of_block).  sXstage is written only by the
-// producer waves' asynchronous loads and read only between the two barriers of
-// a hand-over; the fragment sets sXr (unscaled) and sXs (X'') are separate LDS
-// objects, so that the compiler sees that their reads do not wait for the loads
-// in flight.  sY holds the y tile of one chunk (swizzled like the X stage).
-template <int Q, int N, int PB>
+// The head kernel: one workgroup per unit (HALF = false; grid = units -
+// half_units) or per half unit of the last, partial round (HALF = true; grid
+// = 2 half_units, launched after the first), for the full pass or the
+// split-local one.  Each (pass, HALF) is a kernel of its own: one function
+// holding several instantiations of the walk kept far more scalar values live
+// (measured: 90 scalar registers spilled to vector lanes, 21 without the
+// half-unit walk beside the whole-unit one).  sXstage is written only by the
+// producer waves' asynchronous loads and read only between the two barriers
+// of a hand-over; the fragment sets sXr (unscaled) and sXs (X'') are separate
+// LDS objects, so that the compiler sees that their reads do not wait for the
+// loads in flight.  sY holds the y tile of one chunk (swizzled like the X
+// stage).
+template <int Q, int N, int PB, bool LOCAL, bool HALF>
 __global__ __launch_bounds__(64 * (((Q == 256) ? 8 + SSD_NPROD_Q256 : 4 + 2))) void ssd_scan_bf16_kernel(ChunkArgs a) {
     using Cfg = ScanCfg<Q, N, PB>;
     __shared__ __attribute__((aligned(1024))) bf16 sXstage[Cfg::SX];
@@ -758,24 +812,33 @@ __global__ __launch_bounds__(64 * (((Q == 256) ? 8 + SSD_NPROD_Q256 : 4 + 2))) v
     __shared__ __attribute__((aligned(1024))) bf16 sY[Cfg::SX];
     __shared__ __attribute__((aligned(16))) bf16 sH[PB * Cfg::LDH];
     __shared__ __attribute__((aligned(16))) SegBuf<Q> segbuf[2];
-    const Unit un = unit_of_block(a);
-    if (a.mode == kModeSplitLocal) {
-        if constexpr (PB >= 32) {
-            if (un.half >= 0) {
-                scan_body<Q, N, PB / 2, true>(a, un, un.pb * PB + un.half * (PB / 2), sXstage, sXr, sXs, sY, sH, segbuf);
-                return;
-            }
-        }
-        scan_body<Q, N, PB, true>(a, un, un.pb * PB, sXstage, sXr, sXs, sY, sH, segbuf);
-        return;
+    if constexpr (HALF) {
+        static_assert(PB >= 32, "half units need a headdim block of at least 32");
+        const Unit un = unit_of_block(a, a.units - a.half_units + (int)blockIdx.x);
+        scan_body<Q, N, PB / 2, LOCAL>(a, un, un.pb * PB + un.half * (PB / 2), sXstage, sXr, sXs, sY, sH, segbuf);
+    } else {
+        const Unit un = unit_of_block(a, (int)blockIdx.x);
+        scan_body<Q, N, PB, LOCAL>(a, un, un.pb * PB, sXstage, sXr, sXs, sY, sH, segbuf);
+    }
+}
+
+// Launches of one pass (a.mode): the whole units, then the half units.
+template <int Q, int N, int PB>
+inline void launch_scan_bf16(const ChunkArgs &a, hipStream_t stream) {
+    const dim3 block(ScanCfg<Q, N, PB>::THREADS);
+    const unsigned whole = (unsigned)(a.units - a.half_units);
+    const bool local = a.mode == kModeSplitLocal;
+    if (whole > 0) {
+        if (local) hipLaunchKernelGGL((ssd_scan_bf16_kernel<Q, N, PB, true, false>), dim3(whole), block, 0, stream, a);
+        else hipLaunchKernelGGL((ssd_scan_bf16_kernel<Q, N, PB, false, false>), dim3(whole), block, 0, stream, a);
     }
     if constexpr (PB >= 32) {
-        if (un.half >= 0) {
-            scan_body<Q, N, PB / 2, false>(a, un, un.pb * PB + un.half * (PB / 2), sXstage, sXr, sXs, sY, sH, segbuf);
-            return;
+        if (a.half_units > 0) {
+            const dim3 grid((unsigned)(2 * a.half_units));
+            if (local) hipLaunchKernelGGL((ssd_scan_bf16_kernel<Q, N, PB, true, true>), grid, block, 0, stream, a);
+            else hipLaunchKernelGGL((ssd_scan_bf16_kernel<Q, N, PB, false, true>), grid, block, 0, stream, a);
         }
     }
-    scan_body<Q, N, PB, false>(a, un, un.pb * PB, sXstage, sXr, sXs, sY, sH, segbuf);
 }
 
 }  // namespace ssd

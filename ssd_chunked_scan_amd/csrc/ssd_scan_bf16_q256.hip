@@ -5,13 +5,11 @@ namespace ssd {
 
 #define SSD_SCAN_CASE(q, n, pb)                                                         \
     if (N == n && PB == pb) {                                                            \
-        hipLaunchKernelGGL((ssd_scan_bf16_kernel<q, n, pb>), grid,                      \
-                           dim3(ScanCfg<q, n, pb>::THREADS), 0, stream, a);              \
+        launch_scan_bf16<q, n, pb>(a, stream);                                          \
         return true;                                                                    \
     }
 
 bool launch_scan_bf16_q256(int N, int PB, const ChunkArgs &a, hipStream_t stream) {
-    const dim3 grid(a.units + a.half_units);
     SSD_SCAN_CASE(256, 16, 16)
     SSD_SCAN_CASE(256, 16, 32)
     SSD_SCAN_CASE(256, 16, 64)
