@@ -92,6 +92,12 @@ def _parse_functions(asm_text: str):
         if "ssd lookahead wait" in raw and cur is not None:
             cur.append(("mark", "ssd lookahead wait"))   # see vmem_lds_sync_lookahead
             continue
+        if "ssd touch wait" in raw and cur is not None:
+            cur.append(("mark", "ssd touch wait"))       # see vmem_lds_sync_touch
+            continue
+        if "ssd touch" in raw and cur is not None:
+            cur.append(("mark", "ssd touch"))            # see l2_touch
+            continue
         line = raw.split(";")[0].strip()
         if not line:
             continue
@@ -195,16 +201,45 @@ def check_counted_barrier_waits(asm_text: str, where: str) -> int:
                 continue
             need, j = int(m.group(1)), i - 1
             n += 1
-            # the marker of vmem_lds_sync_lookahead: before the wait, with no
-            # label or vector-memory operation in between
-            marked, q = False, i - 1
+            # the marker of vmem_lds_sync_lookahead / vmem_lds_sync_touch:
+            # before the wait, with no label or vector-memory operation in
+            # between
+            marked, touch, q = False, False, i - 1
             while q >= 0 and items[q][0] != "label":
-                if items[q][0] == "mark":
+                if items[q][0] == "mark" and items[q][1] in ("ssd lookahead wait", "ssd touch wait"):
                     marked = True
+                    touch = items[q][1] == "ssd touch wait"
                     break
-                if items[q][1].startswith(_VMEM):
+                if items[q][0] == "ins" and items[q][1].startswith(_VMEM):
                     break
                 q -= 1
+            if touch:
+                # the K newest vector-memory operations, on straight-line code,
+                # may be stores, ordinary loads or L2 prefetches; a
+                # direct-to-LDS load among them must be a prefetch: the
+                # nearest vector-memory item before it is its touch marker
+                while need > 0:
+                    if j < 0 or items[j][0] == "label":
+                        raise RuntimeError(f"{where}: {fname}: touch wait '{text}' reaches a label "
+                                           f"before {m.group(1)} vector-memory operations")
+                    k2, t = items[j]
+                    if k2 == "ins":
+                        op = t.split()[0] if t.split() else ""
+                        if op.startswith(("s_branch", "s_cbranch", "s_setpc")):
+                            raise RuntimeError(f"{where}: {fname}: touch wait '{text}' reaches a "
+                                               f"branch before {m.group(1)} vector-memory operations")
+                        if op.startswith(("global_load_lds", "buffer_load_lds")):
+                            q2 = j - 1
+                            while q2 >= 0 and items[q2][0] == "ins" and not items[q2][1].startswith(_VMEM):
+                                q2 -= 1
+                            if not (q2 >= 0 and items[q2] == ("mark", "ssd touch")):
+                                raise RuntimeError(f"{where}: {fname}: touch wait '{text}' would leave "
+                                                   f"a direct-to-LDS tile load in flight: {t}")
+                            need -= 1
+                        elif op.startswith(_VMEM):
+                            need -= 1
+                    j -= 1
+                continue
             if marked:
                 # run-ahead tile loads: the K newest vector-memory operations
                 # must be exactly direct-to-LDS loads on straight-line code

@@ -139,7 +139,7 @@ template <int Q, int N, int PB, bool LOCAL>
 __device__ __attribute__((always_inline)) inline void scan_body(
         const ChunkArgs &a, const Unit un, const int p_base, bf16 *__restrict__ sXstage,
         bf16x8 *__restrict__ sXr, bf16x8 *__restrict__ sXs, bf16 *__restrict__ sY,
-        bf16 *__restrict__ sH, SegBuf<Q> *__restrict__ segbuf) {
+        bf16 *__restrict__ sH, SegBuf<Q> *__restrict__ segbuf, bf16x8 *__restrict__ sTouch) {
     using Cfg = ScanCfg<Q, N, PB>;
     constexpr int W = Cfg::W, THREADS = Cfg::THREADS;
     constexpr int NT = Cfg::NT, PT = Cfg::PT, KN = Cfg::KN, IT = Cfg::IT, NP = Cfg::NP;
@@ -381,6 +381,46 @@ __device__ __attribute__((always_inline)) inline void scan_body(
                 __builtin_nontemporal_store(v, (bf16x8 *)dst);
             }
         };
+        // L2 prefetches one step further ahead than the loads that use them
+        // (direct-to-LDS loads into sTouch, which nothing reads):
+        //  * this producer's blocks of X_{c+2}, issued after the loads of
+        //    X_{c+1} and left in flight across the hand-over: the loads of
+        //    X_{c+2} during chunk c+1 then find them in L2;
+        //  * a slice of the per-group operands of chunk c+1 (the heads of a
+        //    group, which run on one XCD, take slices h mod 8 of it), issued
+        //    at the start of chunk c: the compute waves load them from the
+        //    hand-over on.
+        constexpr int kOpBlocks = NBLK + NP * N * 4 * 16 / 1024 + Cfg::TILES * KN;   // 1 KB blocks
+        constexpr int kOpSlices = 8;
+        constexpr int kOpPerSlice = (kOpBlocks + kOpSlices - 1) / kOpSlices;
+        constexpr int kOpTouch = (kOpPerSlice + NPROD - 1) / NPROD;
+        const int op_slice = h % kOpSlices;
+        auto touch_operands = [&](int co) __attribute__((always_inline)) {
+            const int64_t rec = bg * a.nchunks + co;
+#pragma unroll
+            for (int u = 0; u < kOpTouch; ++u) {
+                const int idx = min(op_slice * kOpPerSlice + pw * kOpTouch + u, kOpBlocks - 1);
+                const char *src;
+                if (idx < NBLK)
+                    src = (const char *)a.ws_S + (rec * NBLK + idx) * 1024;
+                else if (idx < NBLK + NP * N * 4 * 16 / 1024)
+                    src = (const char *)a.ws_BT + rec * (NP * N * 4 * 16) + (idx - NBLK) * 1024;
+                else
+                    src = (const char *)a.ws_C + (rec * Cfg::TILES * KN + (idx - NBLK - NP * N * 4 * 16 / 1024)) * 1024;
+                l2_touch(src + lane * 16, sTouch);
+            }
+        };
+        auto touch_x = [&](int cx) __attribute__((always_inline)) {
+            constexpr int RB = 64 / CPRX;
+#pragma unroll
+            for (int k = KB0; k < KB1; ++k) {
+                const int t0 = cx * Q, r = k * RB + xrow;
+                const int cc = xpc ^ swz<CPRX>(r);
+                const char *src = xbase + (int64_t)(t0 + k * RB) * row_bytes + (xrow_off + cc * 16);
+                if (t0 + Q > L && t0 + r >= L) src = (const char *)kZeroChunk;
+                l2_touch(src, sTouch);
+            }
+        };
         for (int c = c_begin; c < c_end; ++c) {
             const bool more = c + 1 < c_end;
             if (gated) {
@@ -397,22 +437,28 @@ __device__ __attribute__((always_inline)) inline void scan_body(
             // whole chunk it lets exactly those KB1 - KB0 newest operations,
             // the stores, stay in flight (completions count in issue order).
             if (more) {
+                touch_operands(c + 1);
                 fetch_tokens(c + 1);
                 stream(c + 1, -1, -1);
                 segsum(c + 1, segbuf[(c + 1) & 1]);
             }
             const int cy = c - 1;
-            if (full && c > c_begin && (cy + 1) * Q <= L) {
+            if (more && c > c_begin && (cy + 1) * Q <= L) {
+                // in flight across the barrier: the prefetches of X_{c+2}
+                // and the stores of y_{c-1}
                 __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                touch_x(min(c + 2, c_end - 1));
                 store_y_whole(cy);
-                vmem_lds_sync_keep<KB1 - KB0>();
+                vmem_lds_sync_touch<2 * (KB1 - KB0)>();
             } else {
-                if (full && c > c_begin) stream(-1, cy, -1);
+                if (c > c_begin) stream(-1, cy, -1);
                 vmem_lds_sync();
             }
             lds_sync();        // the compute waves write y_c to sY in between
         }
-        if (full) stream(-1, c_end - 1, -1);
+        stream(-1, c_end - 1, -1);
+        // nothing may land in this workgroup's LDS after it ends
+        __builtin_amdgcn_s_waitcnt(kWaitVmemLgkm0);
     };
     if (producer) {
         if (wave == W) run_producer(std::integral_constant<int, 0>{});
@@ -812,13 +858,14 @@ __global__ __launch_bounds__(64 * (((Q == 256) ? 8 + SSD_NPROD_Q256 : 4 + 2))) v
     __shared__ __attribute__((aligned(1024))) bf16 sY[Cfg::SX];
     __shared__ __attribute__((aligned(16))) bf16 sH[PB * Cfg::LDH];
     __shared__ __attribute__((aligned(16))) SegBuf<Q> segbuf[2];
+    __shared__ __attribute__((aligned(1024))) bf16x8 sTouch[64];   // target of the L2 prefetches
     if constexpr (HALF) {
         static_assert(PB >= 32, "half units need a headdim block of at least 32");
         const Unit un = unit_of_block(a, a.units - a.half_units + (int)blockIdx.x);
-        scan_body<Q, N, PB / 2, LOCAL>(a, un, un.pb * PB + un.half * (PB / 2), sXstage, sXr, sXs, sY, sH, segbuf);
+        scan_body<Q, N, PB / 2, LOCAL>(a, un, un.pb * PB + un.half * (PB / 2), sXstage, sXr, sXs, sY, sH, segbuf, sTouch);
     } else {
         const Unit un = unit_of_block(a, (int)blockIdx.x);
-        scan_body<Q, N, PB, LOCAL>(a, un, un.pb * PB, sXstage, sXr, sXs, sY, sH, segbuf);
+        scan_body<Q, N, PB, LOCAL>(a, un, un.pb * PB, sXstage, sXr, sXs, sY, sH, segbuf, sTouch);
     }
 }
 

@@ -99,6 +99,31 @@ __device__ inline void vmem_lds_sync_lookahead() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// An L2 prefetch: one direct-to-LDS load of a 1 KB block (64 lanes x 16
+// bytes) into a scratch LDS block that nothing reads, issued only to bring
+// the block's lines into L2 ahead of the load that uses them.  The marker
+// tells the build check that this direct-to-LDS load may stay in flight
+// across a barrier (vmem_lds_sync_touch).
+__device__ inline void l2_touch(const void *src, void *lds_scratch) {
+    asm volatile("; ssd touch" ::: "memory");
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                     (__attribute__((address_space(3))) void *)lds_scratch, 16, 0, 0);
+}
+
+// Barrier after which every vector-memory operation has completed except the
+// KEEP most recently issued ones, which are stores, ordinary loads or
+// l2_touch prefetches (nothing the barrier publishes).  The build check
+// verifies that every direct-to-LDS load among them follows a touch marker.
+template <int KEEP>
+__device__ inline void vmem_lds_sync_touch() {
+    static_assert(KEEP > 0 && KEEP < 64, "vmcnt range");
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    asm volatile("; ssd touch wait" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(KEEP));
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // 16 zero bytes in global memory: the source of the padding rows of a tile.
 static __device__ __attribute__((aligned(16))) const bf16 kZeroChunk[8] = {};
 
