@@ -302,6 +302,26 @@ ssd_status_t ssd_bwd(const ssd_shape_t *shape, ssd_dtype_t io,
                      float *dD, float *dinit,
                      void *workspace, size_t workspace_bytes, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): ssd_fwd
+ * with its workspace taken from a fixed array of SSD_NOALLOC_WORKSPACE_BYTES
+ * that the library holds in the memory of each GPU it runs on, from its first
+ * use until the process ends (its device address is looked up once per
+ * device).  The caller still passes inputs and outputs.  A problem whose
+ * workspace (ssd_fwd_workspace_bytes) exceeds the array returns
+ * SSD_ERR_WORKSPACE and launches nothing; no call allocates or frees memory.
+ * Every call on a GPU uses that GPU's one array: calls that overlap on one
+ * GPU (other streams, other threads) race and must be serialised by the
+ * caller.  The array needs no clearing between calls (every byte read is
+ * written earlier in the same call).  Otherwise as ssd_fwd. */
+#define SSD_NOALLOC_WORKSPACE_BYTES ((size_t)64 << 20)
+ssd_status_t ssd_fwd_noalloc(const ssd_shape_t *shape, ssd_dtype_t io,
+                             const void *x, const float *dt, const float *A,
+                             const void *B, const void *C, const float *D,
+                             const int32_t *seq_idx, int64_t chunk_size,
+                             const float *init_states,
+                             void *y, float *final_states, void *stream);
+
 /* ---- Debug exports (tests only) ---------------------------------------
  *
  * Segsum factor records.  The hierarchy-aware segsum (page "GPU Hierarchy

@@ -36,7 +36,7 @@ EXPORTS = ["ssd_fwd_workspace_bytes", "ssd_fwd", "ssd_fwd_ex_workspace_bytes", "
            "ssd_debug_chunk_mask_ex",
            "ssd_decode_step", "ssd_decode_step_fused", "ssd_bwd_workspace_bytes", "ssd_bwd",
            "ssd_segsum_record_words", "ssd_debug_segsum_factors", "ssd_debug_fwd_segsum_factors",
-           "ssd_debug_exp2_probe",
+           "ssd_debug_exp2_probe", "ssd_fwd_noalloc",
            "ssd_status_str", "ssd_last_error", "ssd_version"]
 # segsum evaluations of the mask export (ssd.h SSD_SEGSUM_*)
 SEGSUM = {"hierarchy": 0, "direct": 1, "diff": 2}
@@ -125,6 +125,8 @@ def load_library():
     u32 = ctypes.c_uint32
     lib.ssd_debug_exp2_probe.argtypes = [u32, u32, vp, u32, vp]
     lib.ssd_debug_exp2_probe.restype = i32
+    lib.ssd_fwd_noalloc.argtypes = fwd_args[:13] + [vp]
+    lib.ssd_fwd_noalloc.restype = i32
     lib.ssd_status_str.argtypes = [i32]
     lib.ssd_status_str.restype = ctypes.c_char_p
     lib.ssd_last_error.argtypes = []

@@ -27,6 +27,7 @@ void launch_mask(int Q, const MaskArgs &m, hipStream_t stream);
 bool launch_decode(bool bf16_io, int N, const DecodeArgs &a, hipStream_t stream);
 void launch_exp2_probe(uint32_t first, uint32_t count, uint32_t span, uint32_t *out, uint32_t nthreads,
                        hipStream_t stream);
+void *noalloc_scratch(int dev, std::string *err);
 }  // namespace ssd
 
 namespace {
@@ -686,6 +687,39 @@ ssd_status_t ssd_decode_step_fused(const ssd_shape_t *shape, ssd_dtype_t io, con
     return SSD_OK;
 }
 
+
+ssd_status_t ssd_fwd_noalloc(const ssd_shape_t *shape, ssd_dtype_t io, const void *x, const float *dt,
+                             const float *A, const void *B, const void *C, const float *D,
+                             const int32_t *seq_idx, int64_t chunk_size, const float *init_states,
+                             void *y, float *final_states, void *stream) {
+    g_last_error.clear();
+    ssd_status_t st = check_problem(shape, chunk_size, io, nullptr);
+    if (st != SSD_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    Plan pl;
+    st = make_plan(shape, chunk_size, io, nullptr, &pl, s);
+    if (st != SSD_OK) return st;
+    if (pl.ws_bytes > SSD_NOALLOC_WORKSPACE_BYTES)
+        return fail(SSD_ERR_WORKSPACE, "ssd_fwd_noalloc: this problem needs %zu bytes of workspace, "
+                    "above the fixed %zu bytes; use ssd_fwd with a caller-allocated workspace",
+                    pl.ws_bytes, (size_t)SSD_NOALLOC_WORKSPACE_BYTES);
+    void *ws = nullptr;
+    if (pl.ws_bytes > 0) {
+        int dev = -1;
+        if (s == nullptr || hipStreamGetDevice(s, &dev) != hipSuccess) {
+            (void)hipGetLastError();
+            if (hipGetDevice(&dev) != hipSuccess) {
+                (void)hipGetLastError();
+                return fail(SSD_ERR_HIP, "no current device");
+            }
+        }
+        std::string err;
+        ws = ssd::noalloc_scratch(dev, &err);
+        if (!ws) return fail(SSD_ERR_HIP, "%s", err.c_str());
+    }
+    return fwd_impl(shape, io, x, dt, A, B, C, D, seq_idx, chunk_size, init_states, y, final_states,
+                    nullptr, ws, ws ? (size_t)SSD_NOALLOC_WORKSPACE_BYTES : 0, nullptr, stream, false);
+}
 
 int64_t ssd_segsum_record_words(int64_t chunk_size) {
     if (chunk_size != 64 && chunk_size != 128 && chunk_size != 256) return 0;

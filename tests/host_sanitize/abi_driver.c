@@ -106,6 +106,14 @@ static void run_fwd(const fwd_case *c) {
         free(mask);
         free(sums);
     }
+    /* the allocation-free entry point: its fixed workspace, or a clear refusal */
+    if (!c->fused && c->split_len == 0 && c->headdim_block == 0) {
+        st = ssd_fwd_noalloc(&s, c->io, x, dt, A, B, C, D, seq, c->Q, h0, y, fs, NULL);
+        if (ws_bytes <= SSD_NOALLOC_WORKSPACE_BYTES)
+            CHECK(st == SSD_OK, "noalloc: status %d", (int)st);
+        else
+            CHECK(st == SSD_ERR_WORKSPACE, "noalloc beyond its array: status %d", (int)st);
+    }
     /* one byte too little workspace */
     if (ws_bytes) {
         st = ssd_fwd_ex(&s, c->io, x, dt, A, B, C, D, seq, c->Q, h0, y, fs, ws, ws_bytes - 1, &o, NULL);
@@ -206,6 +214,7 @@ int main(void) {
         {1, 256, 2, 16, 16, 1, 64, SSD_F32, 1, 0, 0, 1, 0, 0, 0},          /* fp32 */
         {2, 700, 4, 64, 64, 2, 128, SSD_F32, 1, 1, 1, 1, 256, 0, 1},
         {1, 1, 1, 16, 16, 1, 64, SSD_BF16, 0, 0, 0, 0, 0, 0, 0},           /* one token */
+        {1, 32768, 32, 128, 64, 8, 128, SSD_BF16, 1, 1, 0, 1, 0, 0, 0},   /* beyond the noalloc array */
     };
     for (size_t k = 0; k < sizeof(cases) / sizeof(cases[0]); ++k) run_fwd(&cases[k]);
     run_bwd(1, 300, 4, 64, 64, 2, SSD_BF16, 1);

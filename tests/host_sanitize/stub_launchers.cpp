@@ -7,6 +7,9 @@
 // caller's buffer or outside the workspace.
 #include <cstdint>
 #include <cstring>
+#include <string>
+
+#include "ssd.h"
 
 #include "ssd_common.hpp"
 
@@ -81,6 +84,13 @@ void chunk_pass(const ssd::ChunkArgs &a, size_t esz) {
 namespace ssd {
 
 size_t cb_s_elems(int Q) { return nblk(Q) * 64 * 8; }
+
+// The allocation-free entry point's fixed workspace, as a host object of the
+// documented size (ssd_noalloc.hip holds the device array).
+void *noalloc_scratch(int, std::string *) {
+    static unsigned char host_scratch[SSD_NOALLOC_WORKSPACE_BYTES];
+    return host_scratch;
+}
 
 bool launch_cb(int Q, int N, const CbArgs &cb, hipStream_t) {
     ++g_launches;
@@ -181,13 +191,13 @@ void launch_exp2_probe(uint32_t, uint32_t, uint32_t, uint32_t *out, uint32_t nth
 
 extern "C" uint64_t stub_launches(void) { return g_launches; }
 
-// The HIP runtime queries of the planner, answered as a host without a GPU
-// would (the planner then plans for 256 compute units); the sanitizer build
-// links no device runtime.
+// The HIP runtime queries of the planner, answered as for a device 0 that
+// reports no attributes (the planner then plans for 256 compute units); the
+// sanitizer build links no device runtime.
 extern "C" {
 hipError_t hipGetDevice(int *dev) {
-    if (dev) *dev = -1;
-    return hipErrorNoDevice;
+    if (dev) *dev = 0;
+    return hipSuccess;
 }
 hipError_t hipStreamGetDevice(hipStream_t, hipDevice_t *dev) {
     if (dev) *dev = -1;
@@ -198,5 +208,6 @@ hipError_t hipDeviceGetAttribute(int *v, hipDeviceAttribute_t, int) {
     return hipErrorNoDevice;
 }
 hipError_t hipGetLastError(void) { return hipSuccess; }
+
 const char *hipGetErrorString(hipError_t) { return "stub"; }
 }
