@@ -102,21 +102,84 @@ def cpu_baseline(inp, repeats: int = 3):
 
 
 def segsum_ablation(wl, inp, args):
-    """One JSON line: per-launch time of the mask evaluation over every
-    (batch row, head, chunk) of the workload for each segsum variant (HIP
-    events, sums-only export: no mask traffic), and the ratios to the
-    hierarchy-aware one (page "GPU Hierarchy Meets Structured Matrices",
-    abstract: direct segsum ~30% slower than the diff segsum; hierarchy-aware
-    1.35-1.40x faster than a naive direct one)."""
+    """One JSON line: the segsum ablation (page "GPU Hierarchy Meets
+    Structured Matrices", abstract: direct segsum ~30% slower than the diff
+    segsum; hierarchy-aware 1.35-1.40x faster than a naive direct one).
+
+    head_kernel: the bf16 head kernels of the forward pass (every launch but
+    the per-group operand kernel, whose output the workspace already holds)
+    with each evaluation of the mask on the output path, cold (the 512 MiB
+    flush before every call) and warm, per call on the kernels' stream; the
+    variants take turns call by call so that they see the same machine state.
+    mask_export: the mask evaluation alone over every (batch row, head, chunk),
+    through the sums-only mask export (no mask traffic)."""
     import torch
     import ssd_chunked_scan_amd as ssd
     dev = torch.device("cuda:0")
+    variants = ("hierarchy", "direct", "diff")
+    stream = torch.cuda.current_stream(dev)
+    res = {"workload": wl.name}
+    if wl.io == "bf16" and wl.chunk_size == 256:
+        t = lambda a, d=torch.float32: torch.from_numpy(a).to(dev).to(d).contiguous()
+        io = torch.bfloat16
+        x, dt, A, B, C, D = t(inp.x, io), t(inp.dt), t(inp.A), t(inp.B, io), t(inp.C, io), t(inp.D)
+        seq = None if inp.seq_idx is None else torch.from_numpy(inp.seq_idx).to(dev)
+        y = torch.empty_like(x)
+        fs = torch.empty((wl.batch, wl.nheads, wl.headdim, wl.dstate), dtype=torch.float32, device=dev)
+        shape = ssd.Shape(wl.batch, wl.seqlen, wl.nheads, wl.headdim, wl.dstate, wl.ngroups)
+        ws = torch.empty(max(ssd.ssd_fwd_workspace_bytes(shape, wl.chunk_size, 1), 16),
+                         dtype=torch.uint8, device=dev)
+        full, _, _ = ssd.prepare_fwd(x, dt, A, B, C, D, seq, chunk_size=wl.chunk_size, y=y,
+                                     final_states=fs, workspace=ws)
+        full()   # the per-group operands into the workspace
+        heads = {v: ssd.prepare_fwd(x, dt, A, B, C, D, seq, chunk_size=wl.chunk_size, y=y,
+                                    final_states=fs, workspace=ws, reuse_group_operands=True,
+                                    segsum=v)[0] for v in variants}
+        for _ in range(args.warmup):
+            for v in variants:
+                heads[v]()
+        torch.cuda.synchronize(dev)
+        flush_buf = torch.ones(512 << 18, dtype=torch.float32, device=dev)   # 512 MiB
+        flush_sink = torch.empty((), dtype=torch.float32, device=dev)
+        mk = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        cold = {v: [] for v in variants}
+        warm = {v: [] for v in variants}
+        for k in range(args.steps):
+            for v in variants:
+                torch.sum(flush_buf, dim=0, out=flush_sink)
+                e = mk()
+                e[0].record(stream)
+                heads[v]()
+                e[1].record(stream)
+                cold[v].append(e)
+        for k in range(args.steps):
+            for v in variants:
+                e = mk()
+                e[0].record(stream)
+                heads[v]()
+                e[1].record(stream)
+                warm[v].append(e)
+        torch.cuda.synchronize(dev)
+        del flush_buf
+        summ = lambda evs: (lambda ms: {"avg_us": sum(ms) / len(ms) * 1e3, "median_us": ms[len(ms) // 2] * 1e3,
+                                        "p10_us": ms[len(ms) // 10] * 1e3,
+                                        "p90_us": ms[(9 * len(ms)) // 10] * 1e3})(
+            sorted(a.elapsed_time(b) for a, b in evs))
+        hk = {"cold": {v: summ(cold[v]) for v in variants}, "warm": {v: summ(warm[v]) for v in variants}}
+        for kind in ("cold", "warm"):
+            u = {v: hk[kind][v]["avg_us"] for v in variants}
+            hk[kind]["direct_over_hierarchy"] = u["direct"] / u["hierarchy"]
+            hk[kind]["diff_over_hierarchy"] = u["diff"] / u["hierarchy"]
+            hk[kind]["direct_over_diff"] = u["direct"] / u["diff"]
+            print(f"bench: head kernels {kind}: " + ", ".join(f"{v} {u[v]:.1f} us" for v in variants),
+                  file=sys.stderr, flush=True)
+        res["head_kernel"] = hk
+        del heads, full, ws, x, B, C, y
     dt = torch.from_numpy(inp.dt).to(dev)
     A = torch.from_numpy(inp.A).to(dev)
     seq = None if inp.seq_idx is None else torch.from_numpy(inp.seq_idx).to(dev)
-    stream = torch.cuda.current_stream(dev)
-    res = {}
-    for v in ("hierarchy", "direct", "diff"):
+    mx = {}
+    for v in variants:
         run = lambda: ssd.ssd_debug_chunk_mask(dt, A, seq, chunk_size=wl.chunk_size, variant=v,
                                                sums_only=True)
         for _ in range(args.warmup):
@@ -129,16 +192,16 @@ def segsum_ablation(wl, inp, args):
             run()
             e1.record(stream)
         torch.cuda.synchronize(dev)
-        t = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in ev)
-        res[v] = sum(t) / len(t)
-        print(f"bench: segsum {v}: {res[v]:.1f} us per launch (p10 {t[len(t) // 10]:.1f})",
+        tt = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in ev)
+        mx[v] = sum(tt) / len(tt)
+        print(f"bench: mask export {v}: {mx[v]:.1f} us per launch (p10 {tt[len(tt) // 10]:.1f})",
               file=sys.stderr, flush=True)
     units = wl.batch * wl.nheads * ((wl.seqlen + wl.chunk_size - 1) // wl.chunk_size)
-    print(json.dumps({
-        "metric": "segsum evaluation time per launch (sums-only mask export)", "unit": "us",
-        "higher_is_better": False, "workload": wl.name, "chunk_units": units,
-        "us": res, "direct_over_hierarchy": res["direct"] / res["hierarchy"],
-        "diff_over_hierarchy": res["diff"] / res["hierarchy"]}), flush=True)
+    res["mask_export"] = {"us": mx, "chunk_units": units,
+                          "direct_over_hierarchy": mx["direct"] / mx["hierarchy"],
+                          "diff_over_hierarchy": mx["diff"] / mx["hierarchy"]}
+    print(json.dumps({"metric": "segsum ablation: time per call by mask evaluation", "unit": "us",
+                      "higher_is_better": False, **res}), flush=True)
 
 
 def decode_step_bench(wl, inp, args):
@@ -262,8 +325,8 @@ def main():
                          "workload's batch, heads and state size (state read and written once)")
     ap.add_argument("--segsum-ablation", action="store_true",
                     help="instead of the forward pass: time the three segsum evaluations of the "
-                         "decay mask (hierarchy-aware, dense direct, prefix difference) on the "
-                         "workload's dt and A, every chunk, mask evaluated but not written")
+                         "decay mask (hierarchy-aware, direct, prefix difference) inside the bf16 "
+                         "head kernel (chunk 256) and in the mask export alone")
     ap.add_argument("--backward", action="store_true",
                     help="instead of the forward pass: time the backward pass (ssd_bwd)")
     ap.add_argument("--flush", choices=["write", "read"], default="read",

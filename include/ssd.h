@@ -117,10 +117,16 @@ typedef struct {
  * library cannot check it. */
 #define SSD_OPT_REUSE_GROUP_OPERANDS 1
 
-/* flags (tests and benchmarks, fp32 io only; SSD_ERR_UNSUPPORTED with bf16):
- * evaluate the intra-chunk decay mask by the dense direct segsum or by the
- * diff segsum instead of the hierarchy-aware one (page "GPU Hierarchy Meets
- * Structured Matrices", abstract, compares the three).  At most one. */
+/* flags (segsum ablation, for tests and benchmarks): evaluate the
+ * intra-chunk decay mask by the direct segsum (each entry its own running
+ * sum) or by the diff segsum (difference of the chunk's prefix sums) instead
+ * of the hierarchy-aware one (page "GPU Hierarchy Meets Structured Matrices",
+ * abstract, compares the three).  At most one.  fp32 io: any shape.  bf16
+ * io: the head kernel's output path masks every C B^T block element by
+ * element instead of applying the rank-one factors; chunk_size 256, dstate 64
+ * or 128 and a headdim block of 32 or 64 only (SSD_ERR_UNSUPPORTED
+ * otherwise).  The chunk states and the decays of the state projection are
+ * the hierarchy-aware ones in every case. */
 #define SSD_OPT_SEGSUM_DIRECT 2
 #define SSD_OPT_SEGSUM_DIFF 4
 

@@ -60,7 +60,7 @@ class Options(ctypes.Structure):
 
 
 SSD_OPT_REUSE_GROUP_OPERANDS = 1
-SSD_OPT_SEGSUM = {"hierarchy": 0, "direct": 2, "diff": 4}   # forward mask evaluation (fp32 io)
+SSD_OPT_SEGSUM = {"hierarchy": 0, "direct": 2, "diff": 4}   # forward mask evaluation
 
 
 class Fused(ctypes.Structure):
@@ -222,8 +222,9 @@ def _marshal_fwd(x, dt, A, B, C, D, seq_idx, chunk_size, init_states, return_fin
     """Argument checks and marshalling of ssd_fwd / prepare_fwd.
     ``split_len`` forces the sequence-parallel split length (0 = planner);
     ``headdim_block`` the headdim columns per workgroup (0 = planner);
-    ``segsum`` ("hierarchy", "direct" or "diff"; fp32 io only) how the
-    intra-chunk decay mask is evaluated (an ablation for tests and benchmarks).
+    ``segsum`` ("hierarchy", "direct" or "diff") how the intra-chunk decay
+    mask is evaluated (an ablation for tests and benchmarks; bf16 io: chunk
+    256, dstate 64 or 128, headdim blocks of 32 or 64).
     Preallocated ``y`` / ``final_states`` / ``workspace`` (uint8) may be given.
     ``reuse_group_operands`` (bf16) skips the per-group C B^T / B^T kernel: the
     given ``workspace`` must hold them from an earlier call with the same B, C.

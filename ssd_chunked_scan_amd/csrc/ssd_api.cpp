@@ -17,6 +17,8 @@ namespace ssd {
 bool launch_scan_bf16_q64(int N, int PB, const ChunkArgs &a, hipStream_t stream);
 bool launch_scan_bf16_q128(int N, int PB, const ChunkArgs &a, hipStream_t stream);
 bool launch_scan_bf16_q256(int N, int PB, const ChunkArgs &a, hipStream_t stream);
+bool launch_scan_bf16_direct(int N, int PB, const ChunkArgs &a, hipStream_t stream);
+bool launch_scan_bf16_diff(int N, int PB, const ChunkArgs &a, hipStream_t stream);
 bool launch_cb(int Q, int N, const CbArgs &a, hipStream_t stream);
 size_t cb_s_elems(int Q);
 void launch_chunk_f32(int Q, const ChunkArgs &a, hipStream_t stream);
@@ -178,8 +180,10 @@ ssd_status_t check_problem(const ssd_shape_t *s, int64_t chunk, ssd_dtype_t io,
         if (opts->flags & ~known)
             return fail(SSD_ERR_UNSUPPORTED, "unknown option flags 0x%llx", (long long)opts->flags);
         const int64_t seg = opts->flags & (SSD_OPT_SEGSUM_DIRECT | SSD_OPT_SEGSUM_DIFF);
-        if (seg == (SSD_OPT_SEGSUM_DIRECT | SSD_OPT_SEGSUM_DIFF) || (seg && io != SSD_F32))
-            return fail(SSD_ERR_UNSUPPORTED, "segsum variants: one at a time, fp32 io only");
+        if (seg == (SSD_OPT_SEGSUM_DIRECT | SSD_OPT_SEGSUM_DIFF))
+            return fail(SSD_ERR_UNSUPPORTED, "segsum variants: one at a time");
+        if (seg && io == SSD_BF16 && (chunk != 256 || (s->dstate != 64 && s->dstate != 128)))
+            return fail(SSD_ERR_UNSUPPORTED, "bf16 segsum variants: chunk 256, dstate 64 or 128 only");
         if (opts->split_len < 0 || (opts->split_len > 0 && opts->split_len % chunk != 0))
             return fail(SSD_ERR_UNSUPPORTED, "split_len %lld must be 0 or a positive multiple of chunk_size",
                         (long long)opts->split_len);
@@ -255,6 +259,10 @@ ssd_status_t make_plan(const ssd_shape_t *s, int64_t chunk, ssd_dtype_t io,
         return fail(SSD_ERR_UNSUPPORTED, "problem too large: %lld work units", (long long)units);
     pl->units = (int)units;
     pl->half_units = (io == SSD_BF16) ? bf16_half_units(units, chunk, s->dstate, pl->pblock, cus) : 0;
+    if (io == SSD_BF16 && opts && (opts->flags & (SSD_OPT_SEGSUM_DIRECT | SSD_OPT_SEGSUM_DIFF)) &&
+        pl->pblock != 32 && pl->pblock != 64)
+        return fail(SSD_ERR_UNSUPPORTED, "bf16 segsum variants: headdim blocks of 32 or 64 only (planned %d)",
+                    pl->pblock);
     pl->split_bytes = 0;
     if (pl->nsplits > 1) {
         const size_t states = (size_t)s->batch * s->nheads * pl->nsplits * s->headdim * s->dstate;
@@ -405,6 +413,10 @@ ssd_status_t fwd_impl(const ssd_shape_t *shape, ssd_dtype_t io, const void *x, c
             ssd::launch_chunk_f32(args.chunk, args, s);
             return true;
         }
+        if (args.mode == ssd::kModeFull && args.segsum_variant == ssd::kSegsumDirect)
+            return ssd::launch_scan_bf16_direct(args.dstate, args.pblock, args, s);
+        if (args.mode == ssd::kModeFull && args.segsum_variant == ssd::kSegsumDiff)
+            return ssd::launch_scan_bf16_diff(args.dstate, args.pblock, args, s);
         switch (args.chunk) {
         case 64: return ssd::launch_scan_bf16_q64(args.dstate, args.pblock, args, s);
         case 128: return ssd::launch_scan_bf16_q128(args.dstate, args.pblock, args, s);

@@ -56,7 +56,8 @@ struct ChunkArgs {
     int dt_softplus;           // nonzero: dt <- softplus(dt)
     int dt_clamp;              // nonzero: dt <- min(max(dt, dt_lo), dt_hi)
     float dt_lo, dt_hi;
-    int segsum_variant;        // SegsumVariant of the intra-chunk mask (fp32 kernel only)
+    int segsum_variant;        // SegsumVariant of the intra-chunk mask (fp32 kernel; bf16
+                               // full pass at chunk 256)
     float *dbg_seg;            // nullable: the bf16 head kernel writes each chunk's segsum
                                // factors here (SegRecord layout, [batch][nheads][nchunks])
 };

@@ -135,11 +135,23 @@ struct ScanCfg {
 // One workgroup's walk over its chunks.  PB is the number of headdim columns
 // the workgroup owns (a whole headdim block, or half of one); the LDS arrays
 // belong to the kernel and are at least as large as this PB needs.
-template <int Q, int N, int PB, bool LOCAL>
+//
+// SEG selects how the output path evaluates the intra-chunk mask (segsum
+// ablation, page "GPU Hierarchy Meets Structured Matrices", abstract):
+// kSegsumHierarchy is the factorisation above.  kSegsumDirect and
+// kSegsumDiff mask every 32-token block of C B^T left of and on the diagonal
+// element by element, L_ij dt_j with L_ij = 2^s_ij, and multiply the unscaled
+// X: direct takes s_ij as its own running sum d_i + d_{i-1} + ... + d_{j+1}
+// (each lane walks its row leftwards from the diagonal), diff as cs_i - cs_j
+// of the chunk's inclusive prefix sums cs (an associative scan, in vcs).  The
+// state path, the row factor of the state projection and the chunk decay are
+// the hierarchy's in all three, so that only the mask evaluation differs.
+template <int Q, int N, int PB, bool LOCAL, int SEG>
 __device__ __attribute__((always_inline)) inline void scan_body(
         const ChunkArgs &a, const Unit un, const int p_base, bf16 *__restrict__ sXstage,
         bf16x8 *__restrict__ sXr, bf16x8 *__restrict__ sXs, bf16 *__restrict__ sY,
-        bf16 *__restrict__ sH, SegBuf<Q> *__restrict__ segbuf, bf16x8 *__restrict__ sTouch) {
+        bf16 *__restrict__ sH, SegBuf<Q> *__restrict__ segbuf, bf16x8 *__restrict__ sTouch,
+        float *__restrict__ vcs) {
     using Cfg = ScanCfg<Q, N, PB>;
     constexpr int W = Cfg::W, THREADS = Cfg::THREADS;
     constexpr int NT = Cfg::NT, PT = Cfg::PT, KN = Cfg::KN, IT = Cfg::IT, NP = Cfg::NP;
@@ -148,6 +160,8 @@ __device__ __attribute__((always_inline)) inline void scan_body(
     constexpr int CPRY = PB / 8;
     constexpr int NPROD = Cfg::NPROD;
     static_assert(THREADS == 64 * (((Q == 256) ? 8 + SSD_NPROD_Q256 : 4 + 2)), "launch bounds");
+    constexpr bool kVar = SEG != kSegsumHierarchy;   // per-element mask on the output path
+    static_assert(!kVar || (Q == 256 && !LOCAL && NP == W), "mask variants: chunk 256, full pass");
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -606,8 +620,48 @@ __device__ __attribute__((always_inline)) inline void scan_body(
         for (int q = 0; q < NTW; ++q)
             bfr[slot][q] = BTc[((int64_t)m * N + min(nt0 + q, NT - 1) * 16 + l16) * 4 + g];
     };
-    // vector-memory operations load_pair_of issues for pair 0
-    constexpr int kPair0Loads = IT + NTW;
+    // B^T fragments of pair m alone (the mask variants load their C B^T
+    // blocks in the output loop)
+    auto load_bt_of = [&](int c, int m) __attribute__((always_inline)) {
+        const bf16x8 *BTc = BTws + (int64_t)c * NP * N * 4;
+        const int slot = m % NS;
+#pragma unroll
+        for (int q = 0; q < NTW; ++q)
+            bfr[slot][q] = BTc[((int64_t)m * N + min(nt0 + q, NT - 1) * 16 + l16) * 4 + g];
+    };
+    // the first pair's fragments of chunk c, loaded before the hand-over into
+    // it, and the vector-memory operations that issues
+    auto load_pair0 = [&](int c, const int (&Irow)[IT]) __attribute__((always_inline)) {
+        if constexpr (kVar) load_bt_of(c, 0);
+        else load_pair_of(c, 0, Irow);
+    };
+    constexpr int kPair0Loads = (kVar ? 0 : IT) + NTW;
+
+    // Diff segsum: the inclusive prefix sums cs of the chunk's log2-decays
+    // (Kogge-Stone over the wave's lanes, four tokens per lane), computed by
+    // every compute wave; wave w stores those of pair w.  Written between the
+    // barriers of a hand-over, read during the next chunk.
+    auto make_cs = [&](const SegBuf<Q> &sg) __attribute__((always_inline)) {
+        if constexpr (SEG == kSegsumDiff) {
+            const f32x4 dv = *(const f32x4 *)&sg.d[4 * lane];
+            f32x4 cv;
+            cv[0] = dv[0];
+            cv[1] = __fadd_rn(cv[0], dv[1]);
+            cv[2] = __fadd_rn(cv[1], dv[2]);
+            cv[3] = __fadd_rn(cv[2], dv[3]);
+            float x = cv[3];
+#pragma unroll
+            for (int off = 1; off < 64; off *= 2) {
+                const float t = __shfl_up(x, off, 64);
+                if (lane >= off) x = __fadd_rn(x, t);
+            }
+            float ex = __shfl_up(x, 1, 64);
+            if (lane == 0) ex = 0.f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) cv[r] = __fadd_rn(ex, cv[r]);
+            if ((lane >> 3) == wave) *(f32x4 *)&vcs[4 * lane] = cv;
+        }
+    };
 
     // ---- prologue: X fragments, state tile, C rows and the first pair's
     // fragments of the first chunk (the producer loads X and computes the
@@ -615,11 +669,12 @@ __device__ __attribute__((always_inline)) inline void scan_body(
     if constexpr (LOCAL) {
         vmem_lds_sync();                 // no C rows: the split-local pass has no outputs
     } else {
-        load_pair_of(c_begin, 0, Irow0);
+        load_pair0(c_begin, Irow0);
         load_c(c_begin, Irow0);
         vmem_lds_sync_keep<IT * KN + kPair0Loads>();   // C rows and pair 0 may still be in flight
     }
     if (!state_zero) write_h();
+    make_cs(segbuf[c_begin & 1]);
     make_fragments(segbuf[c_begin & 1], c_begin);
     lds_sync();
 
@@ -639,7 +694,10 @@ __device__ __attribute__((always_inline)) inline void scan_body(
 
         // ---- 1. the first column pairs' fragments (in the full pass pair 0
         // was loaded before the hand-over into this chunk)
-        auto load_pair = [&](int m) __attribute__((always_inline)) { load_pair_of(c, m, Irow); };
+        auto load_pair = [&](int m) __attribute__((always_inline)) {
+            if constexpr (kVar) load_bt_of(c, m);
+            else load_pair_of(c, m, Irow);
+        };
 #pragma unroll
         for (int m = LOCAL ? 0 : 1; m < PD && m < NP; ++m) load_pair(m);
 
@@ -683,7 +741,7 @@ __device__ __attribute__((always_inline)) inline void scan_body(
             // loads stay where they were issued
 #pragma unroll
             for (int it = 0; it < IT; ++it)
-                if (!(IT == 2 && it == 0 && m >= NP / 2)) asm volatile("" ::"v"(sfr[slot][it]));
+                if (!kVar && !(IT == 2 && it == 0 && m >= NP / 2)) asm volatile("" ::"v"(sfr[slot][it]));
             const float tp = sg.Tp[m];
             Tchunk = __fmul_rn(Tchunk, tp);
             bf16x8 xf[PT];
@@ -714,7 +772,7 @@ __device__ __attribute__((always_inline)) inline void scan_body(
             }
 
             // output rows: Y^T <- Y^T * Tp_m + X''_m^T (C B^T)_{I,m}^T
-            if (full) {
+            if (full && !kVar) {
                 // the previous pair's output MFMAs may be only a branch away
                 // (ROCm 7.2 has been seen to miss the wait on that path)
                 if (m > 0) mfma_fence_all(acc);
@@ -736,10 +794,97 @@ __device__ __attribute__((always_inline)) inline void scan_body(
         }
         split_decay = __fmul_rn(split_decay, Tchunk);
 
+        // ---- 4'. mask variants, per row tile: the row factor on the state
+        // projection, then the blocks (I, m), m = I/2 down to 0, each masked
+        // element by element and multiplied with the unscaled X of pair m
+        if constexpr (kVar) {
+            if (full) {
+                const bf16x8 *Sc = Sws + (int64_t)c * NBLK * 64;
+#pragma unroll
+                for (int it = 0; it < IT; ++it) {
+                    const int I = Irow[it], I0 = I * 16, i = I0 + l16;
+                    const int md = I >> 1;
+                    const int rs = resets ? seg_last_reset<Q>(sg, i, I) : -1;
+                    const int blk0 = CbShape<Q>::off(I);
+                    bf16x8 snext = Sc[(blk0 + md) * 64];
+                    // decay from the chunk start through i: the pair decays
+                    // left of the diagonal pair, Tb_{I-1} for odd I, F_i
+                    float dd[16];
+#pragma unroll
+                    for (int k = 0; k < 16; k += 4) {
+                        const f32x4 v = *(const f32x4 *)&sg.d[I0 + k];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) dd[k + r] = v[r];
+                    }
+                    float ev[4];
+                    const float F0 = seg_chain_start(seg_diag_row_regs(dd, I0, i, g, ev), I0, rs);
+                    float V = 1.f;
+                    for (int mm = 0; mm < md; ++mm) V = __fmul_rn(V, sg.Tp[mm]);
+                    if (I & 1) V = __fmul_rn(V, sg.Tb[I - 1]);
+                    const float u = __fmul_rn(V, F0);
+                    mfma_fence_all(acc[it]);
+#pragma unroll
+                    for (int pt = 0; pt < PT; ++pt) acc[it][pt] *= u;
+                    const float csi = (SEG == kSegsumDiff) ? vcs[i] : 0.f;
+                    float run = 0.f;   // direct: sum of d over (start of the walk, i]
+                    auto block = [&](int m, bf16x8 sv, auto DIAG) __attribute__((always_inline)) {
+                        constexpr bool diag = decltype(DIAG)::value;
+                        // exponents s_ij of the lane's slots j = 32m + 4g + (e%4) + 16(e/4)
+                        float se[8];
+                        if constexpr (SEG == kSegsumDirect) {
+#pragma unroll
+                            for (int q = 7; q >= 0; --q) {
+                                const f32x4 dq = *(const f32x4 *)&sg.d[32 * m + 4 * q];
+#pragma unroll
+                                for (int r = 3; r >= 0; --r) {
+                                    const int kk = 4 * q + r;
+                                    if ((q & 3) == g) se[r + 4 * (q >> 2)] = run;
+                                    if (diag) run = (32 * m + kk <= i) ? __fadd_rn(run, dq[r]) : run;
+                                    else run = __fadd_rn(run, dq[r]);
+                                }
+                            }
+                        } else {
+                            const f32x4 clo = *(const f32x4 *)&vcs[32 * m + 4 * g];
+                            const f32x4 chi = *(const f32x4 *)&vcs[32 * m + 16 + 4 * g];
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                se[r] = __fsub_rn(csi, clo[r]);
+                                se[4 + r] = __fsub_rn(csi, chi[r]);
+                            }
+                        }
+                        const f32x4 dlo = *(const f32x4 *)&sg.dt[32 * m + 4 * g];
+                        const f32x4 dhi = *(const f32x4 *)&sg.dt[32 * m + 16 + 4 * g];
+                        bf16x8 pf;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const int j = 32 * m + 4 * g + (e & 3) + 16 * (e >> 2);
+                            const float dtj = e < 4 ? dlo[e] : dhi[e - 4];
+                            const bool zero = (diag && j > i) || j < rs;
+                            const float v = zero ? 0.f : __fmul_rn(__builtin_amdgcn_exp2f(se[e]), dtj);
+                            pf[e] = (bf16)fmaf((float)sv[e], v, (diag && j == i) ? D_h : 0.f);
+                        }
+#pragma unroll
+                        for (int pt = 0; pt < PT; ++pt)
+                            acc[it][pt] = mfma_bf16(sXr[(m * PT + pt) * 64 + lane], pf, acc[it][pt]);
+                    };
+                    {
+                        const bf16x8 sv = snext;
+                        if (md > 0) snext = Sc[(blk0 + md - 1) * 64];
+                        block(md, sv, std::true_type{});
+                    }
+                    for (int m = md - 1; m >= 0; --m) {
+                        const bf16x8 sv = snext;
+                        if (m > 0) snext = Sc[(blk0 + m - 1) * 64];
+                        block(m, sv, std::false_type{});
+                    }
+                }
+            }
+        }
+
         // ---- 4. per row tile: the row factor, then the diagonal pair
         //   F_i    decay from the start of row i's sub-block through i
         //   fdg    diagonal-sub-block factor L_ij dt_j
-        if (full) {
+        if (full && !kVar) {
 #pragma unroll
             for (int it = 0; it < IT; ++it) {
                 const int I = Irow[it], I0 = I * 16, i = I0 + l16;
@@ -804,7 +949,7 @@ __device__ __attribute__((always_inline)) inline void scan_body(
             // slot 0 is free: the diagonal pairs (the last loads of each row
             // tile) sit in slot 1 (NS = 2, NP even)
             static_assert(NS == 2 && NP % 2 == 0, "pair 0 of the next chunk goes to a free slot");
-            load_pair_of(cn, 0, Irow);
+            load_pair0(cn, Irow);
             load_c(cn, Irow);
             vmem_lds_sync_keep<IT * KN + kPair0Loads>();
         }
@@ -812,6 +957,7 @@ __device__ __attribute__((always_inline)) inline void scan_body(
         if (c + 1 < c_end) {
             mfma_fence_all(hs);
             write_h();
+            make_cs(segbuf[buf ^ 1]);
             make_fragments(segbuf[buf ^ 1], c + 1);
         }
         lds_sync();
@@ -849,7 +995,10 @@ __device__ __attribute__((always_inline)) inline void scan_body(
 // LDS objects, so that the compiler sees that their reads do not wait for the
 // loads in flight.  sY holds the y tile of one chunk (swizzled like the X
 // stage).
-template <int Q, int N, int PB, bool LOCAL, bool HALF>
+//
+// SEG != kSegsumHierarchy: the segsum ablation's mask variants (full pass,
+// chunk 256); the diff segsum keeps its prefix sums in one more LDS array.
+template <int Q, int N, int PB, bool LOCAL, bool HALF, int SEG = kSegsumHierarchy>
 __global__ __launch_bounds__(64 * (((Q == 256) ? 8 + SSD_NPROD_Q256 : 4 + 2))) void ssd_scan_bf16_kernel(ChunkArgs a) {
     using Cfg = ScanCfg<Q, N, PB>;
     __shared__ __attribute__((aligned(1024))) bf16 sXstage[Cfg::SX];
@@ -859,33 +1008,48 @@ __global__ __launch_bounds__(64 * (((Q == 256) ? 8 + SSD_NPROD_Q256 : 4 + 2))) v
     __shared__ __attribute__((aligned(16))) bf16 sH[PB * Cfg::LDH];
     __shared__ __attribute__((aligned(16))) SegBuf<Q> segbuf[2];
     __shared__ __attribute__((aligned(1024))) bf16x8 sTouch[64];   // target of the L2 prefetches
+    float *vcs = nullptr;
+    if constexpr (SEG == kSegsumDiff) {
+        __shared__ __attribute__((aligned(16))) float sCs[Q];
+        vcs = sCs;
+    }
     if constexpr (HALF) {
         static_assert(PB >= 32, "half units need a headdim block of at least 32");
         const Unit un = unit_of_block(a, a.units - a.half_units + (int)blockIdx.x);
-        scan_body<Q, N, PB / 2, LOCAL>(a, un, un.pb * PB + un.half * (PB / 2), sXstage, sXr, sXs, sY, sH, segbuf, sTouch);
+        scan_body<Q, N, PB / 2, LOCAL, SEG>(a, un, un.pb * PB + un.half * (PB / 2), sXstage, sXr, sXs, sY, sH,
+                                            segbuf, sTouch, vcs);
     } else {
         const Unit un = unit_of_block(a, (int)blockIdx.x);
-        scan_body<Q, N, PB, LOCAL>(a, un, un.pb * PB, sXstage, sXr, sXs, sY, sH, segbuf, sTouch);
+        scan_body<Q, N, PB, LOCAL, SEG>(a, un, un.pb * PB, sXstage, sXr, sXs, sY, sH, segbuf, sTouch, vcs);
     }
 }
 
-// Launches of one pass (a.mode): the whole units, then the half units.
-template <int Q, int N, int PB>
-inline void launch_scan_bf16(const ChunkArgs &a, hipStream_t stream) {
+// Launches of one pass (a.mode): the whole units, then the half units.  With
+// SEG (a mask variant) only the full pass: the split-local pass has no
+// outputs, so the hierarchy kernels serve all three (the caller launches
+// them), and each kernel is instantiated in one translation unit only.
+template <int Q, int N, int PB, int SEG = kSegsumHierarchy>
+inline bool launch_scan_bf16(const ChunkArgs &a, hipStream_t stream) {
     const dim3 block(ScanCfg<Q, N, PB>::THREADS);
     const unsigned whole = (unsigned)(a.units - a.half_units);
     const bool local = a.mode == kModeSplitLocal;
+    if (SEG != kSegsumHierarchy && local) return false;
     if (whole > 0) {
-        if (local) hipLaunchKernelGGL((ssd_scan_bf16_kernel<Q, N, PB, true, false>), dim3(whole), block, 0, stream, a);
-        else hipLaunchKernelGGL((ssd_scan_bf16_kernel<Q, N, PB, false, false>), dim3(whole), block, 0, stream, a);
+        if constexpr (SEG == kSegsumHierarchy) {
+            if (local) hipLaunchKernelGGL((ssd_scan_bf16_kernel<Q, N, PB, true, false>), dim3(whole), block, 0, stream, a);
+        }
+        if (!local) hipLaunchKernelGGL((ssd_scan_bf16_kernel<Q, N, PB, false, false, SEG>), dim3(whole), block, 0, stream, a);
     }
     if constexpr (PB >= 32) {
         if (a.half_units > 0) {
             const dim3 grid((unsigned)(2 * a.half_units));
-            if (local) hipLaunchKernelGGL((ssd_scan_bf16_kernel<Q, N, PB, true, true>), grid, block, 0, stream, a);
-            else hipLaunchKernelGGL((ssd_scan_bf16_kernel<Q, N, PB, false, true>), grid, block, 0, stream, a);
+            if constexpr (SEG == kSegsumHierarchy) {
+                if (local) hipLaunchKernelGGL((ssd_scan_bf16_kernel<Q, N, PB, true, true>), grid, block, 0, stream, a);
+            }
+            if (!local) hipLaunchKernelGGL((ssd_scan_bf16_kernel<Q, N, PB, false, true, SEG>), grid, block, 0, stream, a);
         }
     }
+    return true;
 }
 
 }  // namespace ssd

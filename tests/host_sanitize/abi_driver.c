@@ -78,6 +78,16 @@ static void run_fwd(const fwd_case *c) {
         o.flags = SSD_OPT_REUSE_GROUP_OPERANDS;
         st = ssd_fwd_ex(&s, c->io, x, dt, A, B, C, D, seq, c->Q, h0, y, fs, ws, ws_bytes, &o, NULL);
         CHECK(st == SSD_OK, "reuse: status %d", (int)st);
+        /* the segsum ablation's mask variants in the head kernel: chunk 256,
+           dstate 64 or 128, headdim blocks of 32 or 64 */
+        const int64_t pb = c->headdim_block ? c->headdim_block : ssd_plan_headdim_block(&s, c->Q, c->io);
+        const int var_ok = c->Q == 256 && (c->N == 64 || c->N == 128) && (pb == 32 || pb == 64);
+        for (int v = 0; v < 2; ++v) {
+            o.flags = SSD_OPT_REUSE_GROUP_OPERANDS | (v ? SSD_OPT_SEGSUM_DIFF : SSD_OPT_SEGSUM_DIRECT);
+            st = ssd_fwd_ex(&s, c->io, x, dt, A, B, C, D, seq, c->Q, h0, y, fs, ws, ws_bytes, &o, NULL);
+            CHECK(st == (var_ok ? SSD_OK : SSD_ERR_UNSUPPORTED), "segsum variant %d (pb %lld): status %d", v,
+                  (long long)pb, (int)st);
+        }
         o.flags = 0;
         /* the head kernel's segsum factors */
         const int64_t words = ssd_segsum_record_words(c->Q);

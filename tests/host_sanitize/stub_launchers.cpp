@@ -114,6 +114,16 @@ bool launch_cb(int Q, int N, const CbArgs &cb, hipStream_t) {
 bool launch_scan_bf16_q64(int, int, const ChunkArgs &a, hipStream_t) { chunk_pass(a, 2); return true; }
 bool launch_scan_bf16_q128(int, int, const ChunkArgs &a, hipStream_t) { chunk_pass(a, 2); return true; }
 bool launch_scan_bf16_q256(int, int, const ChunkArgs &a, hipStream_t) { chunk_pass(a, 2); return true; }
+bool launch_scan_bf16_direct(int, int, const ChunkArgs &a, hipStream_t) {
+    if (a.mode != kModeFull) return false;
+    chunk_pass(a, 2);
+    return true;
+}
+bool launch_scan_bf16_diff(int, int, const ChunkArgs &a, hipStream_t) {
+    if (a.mode != kModeFull) return false;
+    chunk_pass(a, 2);
+    return true;
+}
 void launch_chunk_f32(int, const ChunkArgs &a, hipStream_t) { chunk_pass(a, 4); }
 
 void launch_split_scan(const float *init_states, float *ws_states, const float *ws_decay, int batch,

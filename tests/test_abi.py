@@ -88,11 +88,18 @@ def test_argument_errors():
     o = ssd.Options(0, 8)             # unknown flag bit
     assert _fwd(s, opts=o) == 3
     assert b"flags" in ssd.load_library().ssd_last_error()
-    # segsum variants of the forward mask: fp32 io only, one at a time
-    assert _fwd(s, io=1, opts=ssd.Options(0, 2)) == 3
-    assert b"segsum" in ssd.load_library().ssd_last_error()
+    # segsum variants of the forward mask: one at a time; bf16 io only at
+    # chunk 256, dstate 64 or 128 and headdim blocks of 32 or 64
     assert _fwd(s, io=0, opts=ssd.Options(0, 6)) == 3
     assert _fwd(s, io=0, opts=ssd.Options(0, 4)) == 5   # accepted: reaches the workspace check
+    assert _fwd(s, io=1, opts=ssd.Options(0, 2)) == 5   # bf16, chunk 256, dstate 128: accepted
+    assert _fwd(s, io=1, chunk=128, opts=ssd.Options(0, 2)) == 3
+    assert b"segsum" in ssd.load_library().ssd_last_error()
+    assert _fwd(ssd.Shape(2, 1000, 8, 64, 32, 2), io=1, opts=ssd.Options(0, 4)) == 3
+    o = ssd.Options(0, 4)
+    o.headdim_block = 16
+    assert _fwd(s, io=1, opts=o) == 3
+    assert b"headdim blocks of 32 or 64" in ssd.load_library().ssd_last_error()
     o = ssd.Options(256)              # 4 splits -> workspace required
     assert _fwd(s, opts=o) == 5
     assert b"workspace" in ssd.load_library().ssd_last_error()

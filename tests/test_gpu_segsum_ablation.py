@@ -7,8 +7,9 @@ hierarchy-aware mask keeps the invariants (entries in [0, 1], non-increasing
 along a row away from the diagonal); the diff segsum loses accuracy to
 cancellation and breaks the invariants once the chunk's prefix sums are large
 next to the decays that follow.  The same three evaluations also run inside
-the fp32 forward pass (option flags of ssd_fwd_ex), against the fp64
-recurrence."""
+the fp32 forward pass and on the output path of the bf16 head kernel at
+chunk 256 (option flags of ssd_fwd_ex), against the fp64 recurrence; there a
+constructed chunk shows the prefix differences' cancellation in y."""
 import numpy as np
 import pytest
 
@@ -96,9 +97,9 @@ def test_sums_only_is_the_sum_of_the_mask(variant):
 # The same three evaluations inside the forward pass (fp32 path, ssd_fwd_ex
 # option flags): only the intra-chunk mask changes.
 
-def _fwd_variant(inp, variant, init_states=None):
+def _fwd_variant(inp, variant, init_states=None, **kw):
     from ssd_testlib import run_gpu
-    return run_gpu(inp, init_states=init_states, segsum=variant)
+    return run_gpu(inp, init_states=init_states, segsum=variant, **kw)
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
@@ -140,3 +141,91 @@ def test_forward_deep_decay_variants():
     # measured on gfx950: hierarchy and direct 6.3e-8, diff 6.8e-6 on y (the
     # final state does not go through the intra-chunk mask)
     assert errs["diff"][0] > 10 * errs["hierarchy"][0], errs
+
+
+# --------------------------------------------------------------------------
+# The bf16 head kernel at chunk 256 with each evaluation on its output path:
+# the hierarchy's rank-one factors, or every C B^T block masked element by
+# element (direct running sums, prefix differences).  The states are the
+# hierarchy's in all three.
+
+BF16_SHAPES = [
+    # (dstate, headdim, headdim_block, split_len)
+    (128, 64, 0, 0),       # whole headdim per workgroup, one split
+    (64, 128, 64, 256),    # two headdim blocks, a split per chunk (split-local
+                           # pass and split scan before the variant's full pass)
+    (128, 64, 32, 512),    # blocks of 32, two chunks per split
+]
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("N,P,hb,split", BF16_SHAPES,
+                         ids=[f"N{n}_P{p}_pb{b}_split{s}" for n, p, b, s in BF16_SHAPES])
+def test_bf16_forward_variants_match_oracle(variant, N, P, hb, split):
+    """Document resets inside and across chunks, a ragged tail, two groups and
+    an entering state: every element of y and final_states within the bf16
+    bound of the fp64 oracle."""
+    from ssd_testlib import TOL, max_rel, record_error
+    wl = workloads.custom_workload(name=f"bf16_seg_{variant}", batch=2, seqlen=4 * 256 - 29,
+                                   nheads=4, headdim=P, dstate=N, ngroups=2, chunk_size=256,
+                                   io="bf16", packed=True, doc_range=(20, 400), doc_count=(2, 400))
+    inp = workloads.make_inputs(wl, seed=13)
+    h0 = np.random.default_rng(14).standard_normal((2, 4, P, N)).astype(np.float32) * 0.5
+    y, fs = _fwd_variant(inp, variant, h0, split_len=split, headdim_block=hb)
+    yr, fsr = oracle.ssd_forward(inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D, inp.seq_idx,
+                                 h0.astype(np.float64))
+    ey, ef = max_rel(y, yr), max_rel(fs, fsr)
+    record_error(f"bf16 {variant} N{N} P{P} pb{hb} split{split}", ey, ef, TOL["bf16"])
+    assert ey <= TOL["bf16"] and ef <= TOL["bf16"], f"{variant}: y {ey:.2e} fs {ef:.2e}"
+
+
+@pytest.mark.parametrize("variant", ("direct", "diff"))
+def test_bf16_variants_half_headdim_units(variant):
+    """288 (batch row, head) units on a 256-CU device: the last round runs as
+    half-headdim workgroups, the variant's half-unit kernel among them."""
+    from ssd_testlib import TOL, max_rel, record_error
+    wl = workloads.custom_workload(name="bf16_seg_half", batch=2, seqlen=600, nheads=144,
+                                   headdim=64, dstate=128, ngroups=2, chunk_size=256, io="bf16")
+    inp = workloads.make_inputs(wl, seed=3)
+    y, fs = _fwd_variant(inp, variant)
+    yr, fsr = oracle.ssd_forward(inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D, inp.seq_idx)
+    ey, ef = max_rel(y, yr), max_rel(fs, fsr)
+    record_error(f"bf16 {variant} half units", ey, ef, TOL["bf16"])
+    assert ey <= TOL["bf16"] and ef <= TOL["bf16"], f"{variant}: y {ey:.2e} fs {ef:.2e}"
+
+
+@pytest.mark.parametrize("variant", ("direct", "diff"))
+@pytest.mark.parametrize("name", ("layer27b", "decay"))
+def test_bf16_variants_full_size(variant, name):
+    """The 2.7B-shaped layer and the decay-stress workload at full size, every
+    element against the fp64 oracle."""
+    from ssd_testlib import TOL, max_rel, record_error
+    inp = workloads.make_inputs(workloads.WORKLOADS[name], seed=0)
+    y, fs = _fwd_variant(inp, variant)
+    yr, fsr = oracle.ssd_forward(inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D, inp.seq_idx)
+    ey, ef = max_rel(y, yr), max_rel(fs, fsr)
+    record_error(f"bf16 {variant} {name}", ey, ef, TOL["bf16"])
+    assert ey <= TOL["bf16"] and ef <= TOL["bf16"], f"{variant} {name}: y {ey:.2e} fs {ef:.2e}"
+
+
+def test_bf16_diff_segsum_cancellation_in_the_forward_pass():
+    """One chunk whose first half decays by ~1.4e4 (log2) per token and whose
+    second half by 0.14: the prefix sums reach -1.8e6, where an fp32 ulp is
+    0.125, comparable with the second half's decays.  Rows of the second half
+    (no D term): the direct and hierarchy-aware evaluations stay within the
+    bf16 bound, the prefix differences lose several percent."""
+    from ssd_testlib import TOL, max_rel
+    wl = workloads.custom_workload(name="bf16_cancel", batch=1, seqlen=256, nheads=2, headdim=64,
+                                   dstate=64, chunk_size=256, io="bf16")
+    inp = workloads.make_inputs(wl, seed=17)
+    inp.dt = np.full_like(inp.dt, 1e-5)
+    inp.dt[:, :128] = 1.0
+    inp.A = np.full_like(inp.A, -1.0e4)
+    yr, _ = oracle.ssd_forward(inp.x, inp.dt, inp.A, inp.B, inp.C, None)
+    err = {}
+    for v in VARIANTS:
+        y, _ = _fwd_variant(inp, v, skip=False)
+        err[v] = max_rel(y[:, 128:], yr[:, 128:])
+    print("second-half errors:", err)
+    assert err["hierarchy"] <= TOL["bf16"] and err["direct"] <= TOL["bf16"], err
+    assert err["diff"] > 2 * TOL["bf16"], err
