@@ -395,35 +395,14 @@ __device__ __attribute__((always_inline)) inline void scan_body(
                 __builtin_nontemporal_store(v, (bf16x8 *)dst);
             }
         };
-        // L2 prefetches one step further ahead than the loads that use them
-        // (direct-to-LDS loads into sTouch, which nothing reads):
-        //  * this producer's blocks of X_{c+2}, issued after the loads of
-        //    X_{c+1} and left in flight across the hand-over: the loads of
-        //    X_{c+2} during chunk c+1 then find them in L2;
-        //  * a slice of the per-group operands of chunk c+1 (the heads of a
-        //    group, which run on one XCD, take slices h mod 8 of it), issued
-        //    at the start of chunk c: the compute waves load them from the
-        //    hand-over on.
-        constexpr int kOpBlocks = NBLK + NP * N * 4 * 16 / 1024 + Cfg::TILES * KN;   // 1 KB blocks
-        constexpr int kOpSlices = 8;
-        constexpr int kOpPerSlice = (kOpBlocks + kOpSlices - 1) / kOpSlices;
-        constexpr int kOpTouch = (kOpPerSlice + NPROD - 1) / NPROD;
-        const int op_slice = h % kOpSlices;
-        auto touch_operands = [&](int co) __attribute__((always_inline)) {
-            const int64_t rec = bg * a.nchunks + co;
-#pragma unroll
-            for (int u = 0; u < kOpTouch; ++u) {
-                const int idx = min(op_slice * kOpPerSlice + pw * kOpTouch + u, kOpBlocks - 1);
-                const char *src;
-                if (idx < NBLK)
-                    src = (const char *)a.ws_S + (rec * NBLK + idx) * 1024;
-                else if (idx < NBLK + NP * N * 4 * 16 / 1024)
-                    src = (const char *)a.ws_BT + rec * (NP * N * 4 * 16) + (idx - NBLK) * 1024;
-                else
-                    src = (const char *)a.ws_C + (rec * Cfg::TILES * KN + (idx - NBLK - NP * N * 4 * 16 / 1024)) * 1024;
-                l2_touch(src + lane * 16, sTouch);
-            }
-        };
+        // L2 prefetches of this producer's blocks of X_{c+2} (direct-to-LDS
+        // loads into sTouch, which nothing reads), issued after the loads of
+        // X_{c+1} and left in flight across the hand-over: the loads of
+        // X_{c+2} during chunk c+1 then find them in L2 (measured at the 2.7B
+        // layer, cold: forward 209 -> 201 us).  The per-group operands are not
+        // prefetched: in the forward pass the per-group kernel has just written
+        // them to L2, and a slice-wise prefetch of them only added traffic
+        // (201 -> 197 us).
         auto touch_x = [&](int cx) __attribute__((always_inline)) {
             constexpr int RB = 64 / CPRX;
 #pragma unroll
@@ -451,7 +430,6 @@ __device__ __attribute__((always_inline)) inline void scan_body(
             // whole chunk it lets exactly those KB1 - KB0 newest operations,
             // the stores, stay in flight (completions count in issue order).
             if (more) {
-                touch_operands(c + 1);
                 fetch_tokens(c + 1);
                 stream(c + 1, -1, -1);
                 segsum(c + 1, segbuf[(c + 1) & 1]);
@@ -483,6 +461,10 @@ __device__ __attribute__((always_inline)) inline void scan_body(
     }
 
     // ================= compute waves =================
+    // The compute waves hold the critical path of every chunk: they issue
+    // ahead of the producer waves on their SIMD (measured at the 2.7B layer,
+    // cold: 198 -> 196 us; the producers ahead instead: 202 us).
+    __builtin_amdgcn_s_setprio(1);
     // Row tiles of this wave: I0 = w < TILES/2 and, with two per wave,
     // I1 = TILES-1-w >= TILES/2.  So for pairs m >= NP/2 only I1 can reach
     // the pair, and for m < NP/2 the pair lies wholly left of I1's diagonal.
