@@ -333,9 +333,10 @@ def main():
                     help="how the caches are emptied before each cold call: write a 512 MiB scratch "
                          "buffer (also leaves dirty lines to write back), or read one")
     ap.add_argument("--cold-only", action="store_true",
-                    help="only the cold per-call timing of the forward pass (a 512 MiB scratch "
-                         "write before each call): the command the rocprofv3 kernel statistics "
-                         "and counters are taken with, so that every profiled call is a cold one")
+                    help="only the cold per-call timing of the forward pass (the flush before "
+                         "each call), then one 256 MiB device copy: the command the rocprofv3 "
+                         "kernel statistics and counters are taken with, so that every profiled "
+                         "call is a cold one and the copy calibrates the byte counters")
     ap.add_argument("--fused", action="store_true",
                     help="time the forward pass with the fused prologue (raw dt + bias, softplus) "
                          "and the silu(z) output gate; z counts as algorithmic bytes")
@@ -420,10 +421,20 @@ def main():
         torch.cuda.synchronize(dev)
         ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
         avg = sum(ms) / len(ms)
+        # a plain device copy of known size after the timed calls: under
+        # rocprofv3 --pmc its FETCH_SIZE / WRITE_SIZE give the factors from
+        # counter units to bytes
+        cal = 256 << 20
+        cal_src = torch.ones(cal, dtype=torch.uint8, device=dev)
+        cal_dst = torch.empty_like(cal_src)
+        cal_dst.copy_(cal_src)
+        torch.cuda.synchronize(dev)
         print(json.dumps({"metric": "forward pass time per call, cold", "unit": "us", "flush": args.flush,
                           "workload": wl.name, "steps": args.steps, "avg_us": avg * 1e3,
                           "median_us": ms[len(ms) // 2] * 1e3,
-                          "gbs": (wl.algorithmic_bytes() + extra_bytes) / (avg * 1e-3) / 1e9}),
+                          "p10_us": ms[len(ms) // 10] * 1e3, "p90_us": ms[(9 * len(ms)) // 10] * 1e3,
+                          "gbs": (wl.algorithmic_bytes() + extra_bytes) / (avg * 1e-3) / 1e9,
+                          "calibration_copy_bytes": cal}),
               flush=True)
         return
 
