@@ -584,7 +584,9 @@ __device__ __attribute__((always_inline)) inline void scan_body(
     // Fragments of pair m of chunk c (C B^T blocks of the wave's row tiles and
     // B^T of its state n-tiles) into slot m % NS, loaded unconditionally: a row
     // tile whose diagonal pair lies left of m loads its diagonal pair again,
-    // so the last load of each row tile is its diagonal pair.
+    // so the last load of each row tile is its diagonal pair (taking the
+    // fragment from the previous slot instead, behind a branch, measured
+    // slower: 197 -> 202 us at the 2.7B layer, the copy waits for the load).
     constexpr int PD = SSD_PAIR_PREFETCH;   // pairs loaded ahead of their use
     constexpr int NS = PD + 1;               // fragment slots
     bf16x8 sfr[NS][IT], bfr[NS][NTW];
@@ -676,8 +678,9 @@ __device__ __attribute__((always_inline)) inline void scan_body(
 
         // ---- 1. the first column pairs' fragments (in the full pass pair 0
         // was loaded before the hand-over into this chunk)
+        // (the split-local pass has no outputs: B^T only)
         auto load_pair = [&](int m) __attribute__((always_inline)) {
-            if constexpr (kVar) load_bt_of(c, m);
+            if constexpr (kVar || LOCAL) load_bt_of(c, m);
             else load_pair_of(c, m, Irow);
         };
 #pragma unroll
@@ -723,7 +726,7 @@ __device__ __attribute__((always_inline)) inline void scan_body(
             // loads stay where they were issued
 #pragma unroll
             for (int it = 0; it < IT; ++it)
-                if (!kVar && !(IT == 2 && it == 0 && m >= NP / 2)) asm volatile("" ::"v"(sfr[slot][it]));
+                if (!kVar && !LOCAL && !(IT == 2 && it == 0 && m >= NP / 2)) asm volatile("" ::"v"(sfr[slot][it]));
             const float tp = sg.Tp[m];
             Tchunk = __fmul_rn(Tchunk, tp);
             bf16x8 xf[PT];
