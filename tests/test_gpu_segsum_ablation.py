@@ -229,3 +229,20 @@ def test_bf16_diff_segsum_cancellation_in_the_forward_pass():
     print("second-half errors:", err)
     assert err["hierarchy"] <= TOL["bf16"] and err["direct"] <= TOL["bf16"], err
     assert err["diff"] > 2 * TOL["bf16"], err
+
+
+@pytest.mark.parametrize("variant", ("direct", "diff"))
+def test_bf16_variants_change_only_the_mask(variant):
+    """The mask variants share the hierarchy kernel's state path, so the final
+    states are bit-identical to the hierarchy-aware kernel's; y differs only by
+    the mask's rounding (a bf16 ulp at most where a rounding flips)."""
+    from ssd_testlib import TOL, max_rel
+    wl = workloads.custom_workload(name="bf16_seg_state", batch=2, seqlen=3 * 256 + 77, nheads=4,
+                                   headdim=64, dstate=128, ngroups=2, chunk_size=256, io="bf16",
+                                   packed=True, doc_range=(30, 500), doc_count=(2, 400))
+    inp = workloads.make_inputs(wl, seed=23)
+    h0 = np.random.default_rng(24).standard_normal((2, 4, 64, 128)).astype(np.float32)
+    yh, fh = _fwd_variant(inp, "hierarchy", h0)
+    yv, fv = _fwd_variant(inp, variant, h0)
+    assert np.array_equal(fh, fv)
+    assert max_rel(yv, yh) <= TOL["bf16"]
