@@ -38,7 +38,7 @@ def _check_full(inp, y, fs, tol, init_states=None, skip=True, label=None):
 def test_tiny_fp32_workload():
     inp = workloads.make_inputs(workloads.WORKLOADS["tiny"], seed=0)
     y, fs = run_gpu(inp)
-    _check_full(inp, y, fs, TOL["f32"])
+    _check_full(inp, y, fs, TOL["f32"], label="tiny fp32")
 
 
 SHAPES = [
