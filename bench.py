@@ -19,6 +19,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -35,16 +36,25 @@ HEAD_KERNEL_SOURCES = ("ssd_api.cpp", "ssd_cb.hip", "ssd_common.hpp", "ssd_scan_
                        "ssd_segsum.hpp", "ssd_tiles.hpp")
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and blank lines (a comment edit does not
+    change the kernels the counters were taken on)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def kernel_source_digest() -> str:
-    """Digest of the sources that define the bf16 forward kernels and their
-    launch (the counters are only valid for them)."""
+    """Digest of the code (comments stripped) of the sources that define the
+    bf16 forward kernels and their launch (the counters are only valid for
+    them)."""
     csrc = os.path.join(ROOT, "ssd_chunked_scan_amd", "csrc")
     h = hashlib.sha256()
     for f in sorted(os.listdir(csrc)):
         if f in HEAD_KERNEL_SOURCES:
             h.update(f.encode())
-            with open(os.path.join(csrc, f), "rb") as fh:
-                h.update(fh.read())
+            with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+                h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -74,10 +74,11 @@
 //
 // Per chunk, two barriers.  Between them X_{c+1} is turned into MFMA
 // fragments once for all compute waves (unscaled and X'', fragment-ordered so
-// that each operand is one 16-byte LDS read per lane), h_c goes to LDS as
-// bf16, and the producer reads the y tile of chunk c.  The C rows of chunk c+1
-// go out last and stay in flight across the first barrier (its wait counts
-// them out), and the C B^T and B^T fragments one pair ahead of their use.
+// that each operand is one 16-byte LDS read per lane), and h_c and y_c go to
+// LDS as bf16 (the producers store y_c during chunk c+1).  The first pair's
+// fragments and the C rows of chunk c+1 go out last before the first barrier
+// and stay in flight across it (its wait counts them out); the C B^T and B^T
+// fragments of the other pairs are loaded one pair ahead of their use.
 #pragma once
 
 #include <type_traits>
