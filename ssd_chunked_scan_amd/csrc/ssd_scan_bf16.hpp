@@ -78,7 +78,9 @@
 // LDS as bf16 (the producers store y_c during chunk c+1).  The first pair's
 // fragments and the C rows of chunk c+1 go out last before the first barrier
 // and stay in flight across it (its wait counts them out); the C B^T and B^T
-// fragments of the other pairs are loaded one pair ahead of their use.
+// fragments of the other pairs are loaded two pairs ahead of their use
+// (one pair ahead: 193.6 -> 190.7 us cold forward at the 2.7B layer, the
+// 32-head chunk-128 sweep 152.6 -> 145.2 us; three ahead spill).
 #pragma once
 
 #include <type_traits>
@@ -93,7 +95,7 @@ namespace ssd {
 #define SSD_PRODUCER_INFLIGHT 32
 #endif
 #ifndef SSD_PAIR_PREFETCH
-#define SSD_PAIR_PREFETCH 1
+#define SSD_PAIR_PREFETCH 2
 #endif
 #ifndef SSD_NPROD_Q256
 #define SSD_NPROD_Q256 4
@@ -744,9 +746,10 @@ __device__ __attribute__((always_inline)) inline void scan_body(
 #pragma unroll
                     for (int k = 0; k < PTW; ++k) xs[k] = sXs[(m * PT + pt0 + k) * 64 + lane];
                 }
-                // without the output steps in between, the previous pair's
-                // state MFMAs are only a few instructions back
-                if constexpr (LOCAL) mfma_fence_all(hs);
+                // without the output steps in between (the split-local pass,
+                // the mask variants), the previous pair's state MFMAs are only
+                // a few instructions back
+                if constexpr (LOCAL || kVar) mfma_fence_all(hs);
 #pragma unroll
                 for (int q = 0; q < NTW; ++q) {
 #pragma unroll
@@ -932,9 +935,9 @@ __device__ __attribute__((always_inline)) inline void scan_body(
         if constexpr (LOCAL) {
             vmem_lds_sync();
         } else {
-            // slot 0 is free: the diagonal pairs (the last loads of each row
-            // tile) sit in slot 1 (NS = 2, NP even)
-            static_assert(NS == 2 && NP % 2 == 0, "pair 0 of the next chunk goes to a free slot");
+            // slot 0 takes the next chunk's pair 0: the diagonal pairs (the
+            // last loads of each row tile) were read from their slots above
+            static_assert(NS >= 2, "pair 0 of the next chunk goes to slot 0");
             load_pair0(cn, Irow);
             load_c(cn, Irow);
             vmem_lds_sync_keep<IT * KN + kPair0Loads>();
