@@ -963,10 +963,17 @@ __device__ __attribute__((always_inline)) inline void scan_body(
     }
     if (dst) {
         mfma_fence_all(hs);
+        // the lane's row and column are recomputed here from a fresh lane
+        // index: the offsets of the entering-state loads are the same, and
+        // kept live across the chunk loop they (or the thread index) were
+        // spilled to scratch memory
+        int le;
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(le));
+        const int pl = le & 15, nl = 4 * (le >> 4);
 #pragma unroll
         for (int k = 0; k < ST; ++k) {
             const int nt = nt0 + k / PTW, pt = pt0 + k % PTW;
-            const int p = p_base + pt * 16 + l16, n = nt * 16 + 4 * g;
+            const int p = p_base + pt * 16 + pl, n = nt * 16 + nl;
             *(f32x4 *)(dst + (int64_t)p * N + n) = hs[k];
         }
     }
