@@ -353,29 +353,33 @@ __device__ __attribute__((always_inline)) inline void scan_body(
             }
         };
 
-        // chunk c: the token values of chunk c+1 (a short gather), X_{c+1}
-        // and y_{c-1} (written to sY by the compute waves between the
-        // barriers of the previous hand-over), then the segsum of chunk c+1,
-        // whose token values arrived long before.
+        // chunk c: X_{c+1} and y_{c-1} (written to sY by the compute waves
+        // between the barriers of the previous hand-over), the segsum of
+        // chunk c+1 from token values gathered during chunk c-1, and the
+        // gather of chunk c+2's token values after the first barrier (with
+        // the output gate: chunk c+1's, gathered just before its segsum).
         if constexpr (LOCAL) {
             // Split-local pass: X runs two chunks ahead (three staging
             // buffers), because this pass has too little work per chunk to
             // cover an HBM round trip.  At the first barrier of chunk c only
             // X_{c+1} must have landed: the loads of X_{c+2}, issued last,
             // may still be in flight (completions count in issue order).
+            // The token values of chunk c+1 are gathered one chunk ahead of
+            // its segsum: issued after the barrier that waits for X_{c+1} in
+            // the walk of chunk c-1, so that the segsum does not wait for
+            // their round trip (this pass has little else to hide it behind).
             fetch_tokens(c_begin);
             prefetch_local(c_begin, false);
             segsum(c_begin, segbuf[c_begin & 1]);
             if (c_begin + 1 < c_end) prefetch_local(c_begin + 1, true);   // X_{c_begin} has landed
             else vmem_lds_sync();
+            if (c_begin + 1 < c_end) fetch_tokens(c_begin + 1);
             lds_sync();
             for (int c = c_begin; c < c_end; ++c) {
-                if (c + 1 < c_end) {
-                    fetch_tokens(c + 1);
-                    segsum(c + 1, segbuf[(c + 1) & 1]);
-                }
+                if (c + 1 < c_end) segsum(c + 1, segbuf[(c + 1) & 1]);
                 if (c + 2 < c_end) prefetch_local(c + 2, true);   // X_{c+1} has landed
                 else vmem_lds_sync();
+                if (c + 2 < c_end) fetch_tokens(c + 2);
                 lds_sync();
             }
             return;
@@ -384,6 +388,7 @@ __device__ __attribute__((always_inline)) inline void scan_body(
         stream(c_begin, -1, -1);
         segsum(c_begin, segbuf[c_begin & 1]);
         vmem_lds_sync();
+        if (!gated && c_begin + 1 < c_end) fetch_tokens(c_begin + 1);
         lds_sync();
         // y_{c-1} of a whole chunk in straight-line, unpredicated stores (the
         // blocks are issued in the same order as by stream)
@@ -427,13 +432,15 @@ __device__ __attribute__((always_inline)) inline void scan_body(
                 lds_sync();        // the compute waves write y_c to sY in between
                 continue;
             }
-            // Without the gate: X_{c+1} first, then the segsum of chunk c+1,
-            // then the stores of y_{c-1}.  The barrier needs X_{c+1} in LDS and
+            // Without the gate: X_{c+1} first, then the segsum of chunk c+1
+            // (its token values were gathered after the previous chunk's
+            // first barrier, one chunk ahead, as in the split-local pass:
+            // packed 334 -> 319 us, decay stress 174 -> 167 us of the forward
+            // pass), then the stores of y_{c-1}.  The barrier needs X_{c+1} in LDS and
             // the y tile read out of sY, not the stores' completions: for a
             // whole chunk it lets exactly those KB1 - KB0 newest operations,
             // the stores, stay in flight (completions count in issue order).
             if (more) {
-                fetch_tokens(c + 1);
                 stream(c + 1, -1, -1);
                 segsum(c + 1, segbuf[(c + 1) & 1]);
             }
@@ -449,6 +456,7 @@ __device__ __attribute__((always_inline)) inline void scan_body(
                 if (c > c_begin) stream(-1, cy, -1);
                 vmem_lds_sync();
             }
+            if (c + 2 < c_end) fetch_tokens(c + 2);
             lds_sync();        // the compute waves write y_c to sY in between
         }
         stream(-1, c_end - 1, -1);
