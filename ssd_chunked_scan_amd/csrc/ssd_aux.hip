@@ -26,7 +26,7 @@ __global__ __launch_bounds__(256) void ssd_split_scan_kernel(const float *init_s
     // Groups of splits: all loads of a group are issued before its stores
     // (a store to ws_states could otherwise alias the next load, and each
     // split would wait a full memory round trip).
-    constexpr int GRP = 8;
+    constexpr int GRP = 16;   // the planner's split counts fit one group
     for (int s0 = 0; s0 < nsplits; s0 += GRP) {
         float loc[GRP], T[GRP];
 #pragma unroll
