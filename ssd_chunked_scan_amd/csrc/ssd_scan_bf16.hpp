@@ -468,11 +468,12 @@ __device__ __attribute__((always_inline)) inline void scan_body(
             // Without the gate: X_{c+1} first, then the segsum of chunk c+1
             // (its token values were gathered after the previous chunk's
             // first barrier, one chunk ahead, as in the split-local pass:
-            // packed 334 -> 319 us, decay stress 174 -> 167 us of the forward
-            // pass), then the stores of y_{c-1}.  The barrier needs X_{c+1} in LDS and
-            // the y tile read out of sY, not the stores' completions: for a
-            // whole chunk it lets exactly those KB1 - KB0 newest operations,
-            // the stores, stay in flight (completions count in issue order).
+            // packed 334 -> 319 us, decay stress 174 -> 167 us of the
+            // forward pass), then the stores of y_{c-1}.  The barrier needs
+            // X_{c+1} in LDS and the y tile read out of sY, not the stores'
+            // completions: for a whole chunk it lets exactly those KB1 - KB0
+            // newest operations, the stores, stay in flight (completions
+            // count in issue order).
             if (more) {
                 stream(c + 1, -1, -1);
                 segsum(c + 1, segbuf[(c + 1) & 1]);
