@@ -190,13 +190,17 @@ struct Unit {
 // per-group operands chunk by chunk, run on one XCD and share its L2
 // (measured on the decay-stress workload, 16 heads x 16 splits: ordered
 // (batch, head, split) every XCD walked all 256 chunks' operands, 838 MB of
-// reads against 290 MB of algorithmic bytes).  The last
-// half_units units come after all others, two blocks each (the blocks of the
-// last, partial round of workgroups: halving them fills that round); they are
-// launched as a kernel of their own, whose block k is block whole + k here,
-// and are dealt to the XCDs in contiguous ranges in the same way (measured at
-// the 2.7B layer: round-robin halves made every XCD read the per-group
-// operands of both batch rows of that round, 70 MB of extra L2 misses).
+// reads against 290 MB of algorithmic bytes).  Half units (the last,
+// partial round of workgroups, two blocks each: halving them fills that
+// round) are launched as a kernel of their own, whose block k is block
+// whole + k here.  When the whole and the half units both divide by the 8
+// XCDs, each XCD takes one contiguous range of units, the first part as
+// whole units and the rest as half units: at the 2.7B layer one batch row,
+// whose per-group operands its L2 then reads once (head kernels with the
+// operands evicted from the caches: 195 -> 180 us; round-robin halves had
+// made every XCD read the operands of both batch rows of that round, 70 MB
+// of extra L2 misses).  Otherwise whole and half units are each dealt in
+// contiguous ranges.
 __device__ inline int xcd_contiguous(int blk, int count) {
     const int per = count / 8, rem = count % 8;
     const int xcd = blk % 8, k = blk / 8;
@@ -206,7 +210,19 @@ __device__ inline int xcd_contiguous(int blk, int count) {
 __device__ inline Unit unit_of_block(const ChunkArgs &a, int blk) {
     const int whole = a.units - a.half_units;
     int logical, half = -1;
-    if (blk < whole) {
+    if (a.half_units > 0 && whole % 8 == 0 && a.half_units % 8 == 0) {
+        // Each XCD takes one contiguous range of units, whole and half
+        // alike: the first whole/8 of its range as whole units, the rest as
+        // half units (at the 2.7B layer one batch row per XCD).
+        const int per = a.units / 8, wper = whole / 8;
+        if (blk < whole) {
+            logical = (blk % 8) * per + blk / 8;
+        } else {
+            const int j = blk - whole, m = j / 8;
+            logical = (j % 8) * per + wper + (m >> 1);
+            half = m & 1;
+        }
+    } else if (blk < whole) {
         logical = xcd_contiguous(blk, whole);
     } else {
         const int j = xcd_contiguous(blk - whole, 2 * a.half_units);
