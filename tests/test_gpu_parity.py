@@ -145,6 +145,18 @@ def test_partial_last_round_half_blocks(skip):
     _check_full(inp, y, fs, TOL["bf16"], skip=skip, label=f"half blocks {'skip' if skip else 'no skip'}")
 
 
+def test_partial_last_round_half_blocks_uneven():
+    """276 units on a 256-CU device: the last 20 run as half-headdim
+    workgroups.  20 does not divide by the 8 XCDs, so the blocks take the
+    other unit order (whole and half units each dealt in contiguous ranges);
+    the 288-unit shapes above take the one-range-per-XCD order."""
+    wl = _case("half_blocks_uneven", batch=2, seqlen=600, nheads=138, headdim=64, dstate=128,
+               ngroups=2, chunk_size=256, io="bf16")
+    inp = workloads.make_inputs(wl, seed=11)
+    y, fs = run_gpu(inp)
+    _check_full(inp, y, fs, TOL["bf16"], label="half blocks, 20 of 276 units")
+
+
 def test_half_blocks_with_forced_splits_and_init_state():
     """The 288-unit shape in three sequence splits: 864 units, of which the last
     96 (batch row 1, heads 112..143, every split) run as half-headdim
