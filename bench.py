@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix
 METRIC = "SSD fwd tokens/s + HBM GB/s (% of peak), Mamba-2 2.7B layer, L=2048"
 HEAD_KERNEL_SOURCES = ("ssd_api.cpp", "ssd_cb.hip", "ssd_common.hpp", "ssd_scan_bf16.hpp",
                        "ssd_scan_bf16_q64.hip", "ssd_scan_bf16_q128.hip", "ssd_scan_bf16_q256.hip",
@@ -291,21 +292,37 @@ def backward_bench(wl, inp, args):
            + 2 * b * H * nch * P * N * 4)                                       # states
     gbs = alg / (avg * 1e-3) / 1e9
     # MFMA work the backward kernel executes, per 64-token chunk and (batch
-    # row, head): fp32 16x16x4 steps (2048 flop) for the products with fp32
-    # operands, the triangular ones over whole 16-row blocks (4 steps each,
-    # diagonal blocks in full); C B^T and dY X^T on bf16 16x16x32 steps
-    # (16384 flop) when bf16 rows are staged (bf16 inputs, headdim <= 64),
-    # else fp32 steps.
+    # row, head).  bf16 inputs: every product on bf16 16x16x32 steps (16384
+    # flop): the masked ones over the pairs of 16-row blocks a triangle
+    # touches, the ones with a carried state (B G^T, x G, dY H, u dy C^T) as
+    # hi + lo steps, C B^T and dY X^T over the lower tiles when bf16 rows are
+    # staged (headdim <= 64), else on fp32 steps.  fp32 inputs: fp32 16x16x4
+    # steps (2048 flop) throughout, the triangles over whole 16-row blocks.
     nb, ntri = 4, 10                          # 16-row blocks per chunk, lower tiles
-    tri = 4 * ntri                            # steps of one column tile's triangle
-    f32 = ((P // 16) * tri + nb * (P // 16) * (N // 4)          # dX: (L o S)^T dY, G B_j
-           + (N // 16) * 2 * tri + nb * (N // 16) * 2 * (P // 4)  # dB, dC and their state terms
-           + (P // 16) * (N // 16) * 16)                        # state adjoint update
-    staged = wl.io == "bf16" and P <= 64
-    bf = ntri * (max(1, N // 32) + max(1, P // 32)) if staged else 0
-    if not staged:
+    c32 = lambda k: (k + 31) // 32
+    if wl.io == "bf16":
+        m_up = sum(1 for j in range(nb) for q in range(nb // 2) if 2 * q + 1 >= j)   # dX, dB
+        m_lo = sum(1 for t in range(nb) for q in range(nb // 2) if 2 * q <= t)       # dC
+        bf = ((P // 16) * (m_up + nb * 2 * c32(N))                 # dX: masked, B G^T
+              + (N // 16) * (m_up + m_lo + 2 * nb * 2 * c32(P))    # dB, dC: masked, x G, dY H
+              + (P // 16) * (N // 16) * nb)                        # adjoint update
+        f32 = 0
+    else:
+        tri = 4 * ntri                        # steps of one column tile's triangle
+        bf = 0
+        f32 = ((P // 16) * tri + nb * (P // 16) * (N // 4)          # dX: (L o S)^T dY, G B_j
+               + (N // 16) * 2 * tri + nb * (N // 16) * 2 * (P // 4)  # dB, dC and their state terms
+               + (P // 16) * (N // 16) * 16)                        # state adjoint update
+    if wl.io == "bf16" and P <= 64:
+        bf += ntri * (max(1, N // 32) + max(1, P // 32))
+    else:
         f32 += ntri * (N // 4 + P // 4)
-    flop = b * H * nch * (f32 * 2048 + bf * 16384)
+    units = b * H * nch
+    flop = units * (f32 * 2048 + bf * 16384)
+    # the mix's peak: its flops over the time the matrix pipes take at their
+    # published rate for each step type, so frac is the pipes' busy fraction
+    pipe_s = units * (bf * 16384 / (BF16_MFMA_PEAK_TFLOPS * 1e12) + f32 * 2048 / (FP32_MFMA_PEAK_TFLOPS * 1e12))
+    peak = flop / pipe_s / 1e12
     tflops = flop / (avg * 1e-3) / 1e12
     print(json.dumps({
         "metric": "SSD backward time per launch", "unit": "us", "value": avg * 1e3,
@@ -315,11 +332,11 @@ def backward_bench(wl, inp, args):
                    "dstate": N, "ngroups": G, "backward_chunk": 64},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": alg},
-        # the backward kernel is bound by MFMA issue and latency, not HBM:
         # executed MFMA flops over the whole pass's time (a lower bound for the
-        # kernel alone) against the fp32 matrix peak
-        "mfma": {"flop_per_launch": flop, "achieved": tflops, "peak": FP32_MFMA_PEAK_TFLOPS,
-                 "unit": "TFLOP/s", "frac": tflops / FP32_MFMA_PEAK_TFLOPS},
+        # kernel alone) against the peak of the step mix (bf16 and fp32 steps
+        # each at their published dense rate)
+        "mfma": {"flop_per_launch": flop, "bf16_steps_per_chunk": bf, "fp32_steps_per_chunk": f32,
+                 "achieved": tflops, "peak": peak, "unit": "TFLOP/s", "frac": tflops / peak},
         "p10_us": ms[len(ms) // 10] * 1e3, "p90_us": ms[(9 * len(ms)) // 10] * 1e3}), flush=True)
 
 

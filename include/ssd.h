@@ -288,9 +288,11 @@ ssd_status_t ssd_decode_step_fused(const ssd_shape_t *shape, ssd_dtype_t io,
  * Mamba-2" ("The SSD Block Decomposition Algorithm"): the chunk-entering
  * states come from the forward pass's split-local pass and affine scan with
  * one split per 64-token chunk, then one reverse walk over the chunks per
- * (batch row, head) carries the adjoint of the state (fp32 arithmetic; the
- * products on fp32 MFMA tiles, C B^T and dY X^T on bf16 MFMA when the inputs
- * are bf16).
+ * (batch row, head) carries the adjoint of the state in fp32.  fp32 inputs:
+ * every product on fp32 MFMA tiles.  bf16 inputs: every product on bf16 MFMA
+ * with fp32 accumulation; the masked products take their fp32 operand
+ * rounded to bf16, the products with a carried state (adjoint or state) take
+ * that fp32 operand as a sum of two bf16 parts (about 16 bits kept).
  *   dy [b, L, H, P] io dtype, 16-byte aligned; dfinal [b, H, P, N] fp32 or NULL;
  *   outputs, all fp32: dx [b, L, H, P], ddt [b, L, H], dA [H], dB and dC
  *   [b, L, G, N], dD [H] (NULL exactly when D is NULL), dinit [b, H, P, N]

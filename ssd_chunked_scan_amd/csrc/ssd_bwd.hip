@@ -104,6 +104,30 @@ __device__ inline f32x4 mfma_pack4(const Pack<IO> &a, const Pack<IO> &b, f32x4 c
     return mfma_f32(pack_el<3>(a), pack_el<3>(b), c);
 }
 
+// Operands of one v_mfma_f32_16x16x32_bf16 step (eight contraction values a
+// lane, in the order of eight fp32 steps above): from eight fp32 values,
+// rounded to nearest even, or from two packs of four bf16, exact.
+__device__ inline bf16x8 bf16x8_of(const float (&v)[8]) {
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = (bf16)v[e];
+    return r;
+}
+__device__ inline bf16x8 bf16x8_of(const Pack<bf16> &lo, const Pack<bf16> &hi) {
+    return __builtin_bit_cast(bf16x8, uint4{lo.v.x, lo.v.y, hi.v.x, hi.v.y});
+}
+// Eight fp32 values as a sum of two bf16 operands: hi = the nearest bf16, lo =
+// the nearest bf16 to the remainder.  A product with an exact bf16 operand
+// then takes two bf16 steps and keeps about 16 bits of the fp32 value.
+__device__ inline void bf16x8_split(const float (&v)[8], bf16x8 &hi, bf16x8 &lo) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const bf16 h = (bf16)v[e];
+        hi[e] = h;
+        lo[e] = (bf16)(v[e] - (float)h);
+    }
+}
+
 // The fp32 MFMA takes more passes than the bf16 one the shared fence is sized
 // for: 8 + 4 wait states before vector code reads a result.
 __device__ inline void mfma_f32_fence(f32x4 &a, f32x4 &b) {
@@ -127,6 +151,13 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
     constexpr int kMaxK = 128;              // largest headdim and dstate
     constexpr int kMaxGN = P * (kMaxK + 4);
     constexpr int PU = P / 16;              // 16-column blocks of headdim
+    // bf16 inputs: every product of dX, dB, dC and the adjoint update runs on
+    // bf16 MFMA with fp32 accumulation.  The masked products take their fp32
+    // operand rounded to bf16 (the forward's precision class); the products
+    // with the carried states (B G^T, x G, dY H, u dy C^T) take it as hi + lo
+    // bf16, two steps, about 16 bits: they give the terms of dl, where sums of
+    // both signs magnify rounding.  fp32 inputs keep fp32 MFMA throughout.
+    constexpr bool kBf = std::is_same<IO, bf16>::value;
     __shared__ __attribute__((aligned(16))) SegLds<Q> sg;
     __shared__ __attribute__((aligned(16))) float sG[kMaxGN];  // adjoint of the state at the chunk end, [P][N + 4]
     __shared__ float sL[Q * LQ];            // decay mask L[i][j], then V[i][j] = dy_i . x_j
@@ -425,6 +456,15 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
 #pragma unroll
                 for (int u = 0; u < kMaxK / 16; ++u)   // blocks past N: B is 0 there, G read at a valid column
                     gv[u] = *(const float4 *)&sG[p * GN + min(16 * u, N - 16) + 4 * g];
+                bf16x8 ghi[kMaxK / 32], glo[kMaxK / 32];
+                if constexpr (kBf) {
+#pragma unroll
+                    for (int v = 0; v < kMaxK / 32; ++v) {
+                        const float w[8] = {gv[2 * v].x, gv[2 * v].y, gv[2 * v].z, gv[2 * v].w,
+                                            gv[2 * v + 1].x, gv[2 * v + 1].y, gv[2 * v + 1].z, gv[2 * v + 1].w};
+                        bf16x8_split(w, ghi[v], glo[v]);
+                    }
+                }
                 for (int J = J0; J < J0 + NJ; ++J) {
                     const int jr = J * 16 + l16;
                     const unsigned brow = cl(jr) * bs;
@@ -436,21 +476,51 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
                     // i = 16 J .. Q - 1: whole 16-row blocks I >= J (one uniform
                     // branch per block; inside the diagonal block L is 0 above
                     // the diagonal)
+                    if constexpr (kBf) {
+                        // one bf16 step per two 16-row blocks (slot e in block
+                        // 2q + e/4; a block left of J is zeroed)
 #pragma unroll
-                    for (int blk = 0; blk < NB; ++blk) {
-                        if (blk < J) continue;
+                        for (int q = 0; q < NB / 2; ++q) {
+                            if (2 * q + 1 < J) continue;
+                            float av[8], bw[8];
 #pragma unroll
-                        for (int s4 = 0; s4 < 4; ++s4) {
-                            const int st = 4 * blk + s4;
-                            acc = mfma_f32(sS[(4 * st + g) * LQ + jr], dyv[st], acc);
+                            for (int e = 0; e < 8; ++e) {
+                                const int st = 8 * q + e;
+                                av[e] = (2 * q + (e >> 2) < J) ? 0.f : sS[(4 * st + g) * LQ + jr];
+                                bw[e] = dyv[st];
+                            }
+                            acc = mfma_bf16(bf16x8_of(av), bf16x8_of(bw), acc);
+                        }
+                    } else {
+#pragma unroll
+                        for (int blk = 0; blk < NB; ++blk) {
+                            if (blk < J) continue;
+#pragma unroll
+                            for (int s4 = 0; s4 < 4; ++s4) {
+                                const int st = 4 * blk + s4;
+                                acc = mfma_f32(sS[(4 * st + g) * LQ + jr], dyv[st], acc);
+                            }
                         }
                     }
+                    // B G^T also gives p_r, a term of dl, where sums of both
+                    // signs magnify operand rounding (G rounded to bf16: dA
+                    // 1.5e-2 off at headdim 16): G as hi + lo bf16
+                    if constexpr (kBf) {
 #pragma unroll
-                    for (int u = 0; u < kMaxK / 16; ++u) {
-                        acc2 = mfma_f32(pack_el<0>(bv[u]), gv[u].x, acc2);
-                        acc2 = mfma_f32(pack_el<1>(bv[u]), gv[u].y, acc2);
-                        acc2 = mfma_f32(pack_el<2>(bv[u]), gv[u].z, acc2);
-                        acc2 = mfma_f32(pack_el<3>(bv[u]), gv[u].w, acc2);
+                        for (int v = 0; v < kMaxK / 32; ++v) {
+                            if (32 * v >= N) break;
+                            const bf16x8 bb = bf16x8_of(bv[2 * v], bv[2 * v + 1]);
+                            acc2 = mfma_bf16(bb, ghi[v], acc2);
+                            acc2 = mfma_bf16(bb, glo[v], acc2);
+                        }
+                    } else {
+#pragma unroll
+                        for (int u = 0; u < kMaxK / 16; ++u) {
+                            acc2 = mfma_f32(pack_el<0>(bv[u]), gv[u].x, acc2);
+                            acc2 = mfma_f32(pack_el<1>(bv[u]), gv[u].y, acc2);
+                            acc2 = mfma_f32(pack_el<2>(bv[u]), gv[u].z, acc2);
+                            acc2 = mfma_f32(pack_el<3>(bv[u]), gv[u].w, acc2);
+                        }
                     }
                     mfma_f32_fence(acc, acc2);
 #pragma unroll
@@ -511,6 +581,23 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
                 for (int u = 0; u < PU; ++u)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) gq[4 * u + e] = sG[(16 * u + 4 * g + e) * GN + n];
+                // bf16: G and H columns as hi + lo bf16 (see dX)
+                constexpr int PV = (PU + 1) / 2;
+                bf16x8 gqhi[PV], gqlo[PV], hvhi[PV], hvlo[PV];
+                if constexpr (kBf) {
+#pragma unroll
+                    for (int v = 0; v < PV; ++v) {
+                        float w[8], x8[8];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const bool in = 8 * v + e < 4 * PU;
+                            w[e] = in ? gq[min(8 * v + e, 4 * PU - 1)] : 0.f;
+                            x8[e] = in ? hv[min(8 * v + e, 4 * PU - 1)] : 0.f;
+                        }
+                        bf16x8_split(w, gqhi[v], gqlo[v]);
+                        bf16x8_split(x8, hvhi[v], hvlo[v]);
+                    }
+                }
                 for (int T = T0; T < T0 + NT; ++T) {
                     const int tr = T * 16 + l16;
                     const unsigned trow = cl(tr) * xs;
@@ -525,21 +612,43 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
                     for (int r = 0; r < 4; ++r) cq[r] = ld1(Cc, cl(T * 16 + 4 * g + r) * bs + n);
                     // dB: i = 16 T .. Q - 1;  G^T x_t
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
+                    if constexpr (kBf) {
 #pragma unroll
-                    for (int blk = 0; blk < NB; ++blk) {   // whole blocks I >= T
-                        if (blk < T) continue;
+                        for (int q = 0; q < NB / 2; ++q) {   // pairs of blocks, blocks I < T zeroed
+                            if (2 * q + 1 < T) continue;
+                            float av[8], bw[8];
 #pragma unroll
-                        for (int s4 = 0; s4 < 4; ++s4) {
-                            const int st = 4 * blk + s4;
-                            acc = mfma_f32(sV[(4 * st + g) * LQ + tr], cvs[st], acc);   // (L o V)[i][t]
+                            for (int e = 0; e < 8; ++e) {
+                                const int st = 8 * q + e;
+                                av[e] = (2 * q + (e >> 2) < T) ? 0.f : sV[(4 * st + g) * LQ + tr];   // (L o V)[i][t]
+                                bw[e] = cvs[st];
+                            }
+                            acc = mfma_bf16(bf16x8_of(av), bf16x8_of(bw), acc);
                         }
-                    }
 #pragma unroll
-                    for (int u = 0; u < PU; ++u) {
-                        acc2 = mfma_f32(pack_el<0>(xr[u]), gq[4 * u], acc2);
-                        acc2 = mfma_f32(pack_el<1>(xr[u]), gq[4 * u + 1], acc2);
-                        acc2 = mfma_f32(pack_el<2>(xr[u]), gq[4 * u + 2], acc2);
-                        acc2 = mfma_f32(pack_el<3>(xr[u]), gq[4 * u + 3], acc2);
+                        for (int v = 0; v < PV; ++v) {
+                            const Pack<IO> hi = (2 * v + 1 < PU) ? xr[min(2 * v + 1, PU - 1)] : Pack<IO>{};
+                            const bf16x8 xx = bf16x8_of(xr[2 * v], hi);   // x_t, G columns
+                            acc2 = mfma_bf16(xx, gqhi[v], acc2);
+                            acc2 = mfma_bf16(xx, gqlo[v], acc2);
+                        }
+                    } else {
+#pragma unroll
+                        for (int blk = 0; blk < NB; ++blk) {   // whole blocks I >= T
+                            if (blk < T) continue;
+#pragma unroll
+                            for (int s4 = 0; s4 < 4; ++s4) {
+                                const int st = 4 * blk + s4;
+                                acc = mfma_f32(sV[(4 * st + g) * LQ + tr], cvs[st], acc);   // (L o V)[i][t]
+                            }
+                        }
+#pragma unroll
+                        for (int u = 0; u < PU; ++u) {
+                            acc2 = mfma_f32(pack_el<0>(xr[u]), gq[4 * u], acc2);
+                            acc2 = mfma_f32(pack_el<1>(xr[u]), gq[4 * u + 1], acc2);
+                            acc2 = mfma_f32(pack_el<2>(xr[u]), gq[4 * u + 2], acc2);
+                            acc2 = mfma_f32(pack_el<3>(xr[u]), gq[4 * u + 3], acc2);
+                        }
                     }
                     mfma_f32_fence(acc, acc2);
 #pragma unroll
@@ -550,21 +659,47 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
                     // dC: j = 0 .. 16 T + 15;  H^T dy_t
                     acc = f32x4{0.f, 0.f, 0.f, 0.f};
                     acc2 = f32x4{0.f, 0.f, 0.f, 0.f};
+                    if constexpr (kBf) {
 #pragma unroll
-                    for (int blk = 0; blk < NB; ++blk) {   // whole blocks J <= T
-                        if (blk > T) break;
+                        for (int q = 0; q < NB / 2; ++q) {   // pairs of blocks, blocks J > T zeroed
+                            if (2 * q > T) break;
+                            float av[8], bw[8];
 #pragma unroll
-                        for (int s4 = 0; s4 < 4; ++s4) {
-                            const int j = 4 * (4 * blk + s4) + g;
-                            acc = mfma_f32(sg.dt[j] * sV[tr * LQ + j], bvs[4 * blk + s4], acc);   // (L o dt o V)[t][j]
+                            for (int e = 0; e < 8; ++e) {
+                                const int j = 4 * (8 * q + e) + g;
+                                av[e] = (2 * q + (e >> 2) > T) ? 0.f : sg.dt[j] * sV[tr * LQ + j];   // (L o dt o V)[t][j]
+                                bw[e] = bvs[8 * q + e];
+                            }
+                            acc = mfma_bf16(bf16x8_of(av), bf16x8_of(bw), acc);
+                        }
+                    } else {
+#pragma unroll
+                        for (int blk = 0; blk < NB; ++blk) {   // whole blocks J <= T
+                            if (blk > T) break;
+#pragma unroll
+                            for (int s4 = 0; s4 < 4; ++s4) {
+                                const int j = 4 * (4 * blk + s4) + g;
+                                acc = mfma_f32(sg.dt[j] * sV[tr * LQ + j], bvs[4 * blk + s4], acc);   // (L o dt o V)[t][j]
+                            }
                         }
                     }
+                    // dY H also gives q_s, a term of dl: H as hi + lo bf16
+                    if constexpr (kBf) {
 #pragma unroll
-                    for (int u = 0; u < PU; ++u) {
-                        acc2 = mfma_f32(pack_el<0>(dr[u]), hv[4 * u], acc2);
-                        acc2 = mfma_f32(pack_el<1>(dr[u]), hv[4 * u + 1], acc2);
-                        acc2 = mfma_f32(pack_el<2>(dr[u]), hv[4 * u + 2], acc2);
-                        acc2 = mfma_f32(pack_el<3>(dr[u]), hv[4 * u + 3], acc2);
+                        for (int v = 0; v < PV; ++v) {
+                            const Pack<IO> hi = (2 * v + 1 < PU) ? dr[min(2 * v + 1, PU - 1)] : Pack<IO>{};
+                            const bf16x8 dd = bf16x8_of(dr[2 * v], hi);   // dy_t, H columns
+                            acc2 = mfma_bf16(dd, hvhi[v], acc2);
+                            acc2 = mfma_bf16(dd, hvlo[v], acc2);
+                        }
+                    } else {
+#pragma unroll
+                        for (int u = 0; u < PU; ++u) {
+                            acc2 = mfma_f32(pack_el<0>(dr[u]), hv[4 * u], acc2);
+                            acc2 = mfma_f32(pack_el<1>(dr[u]), hv[4 * u + 1], acc2);
+                            acc2 = mfma_f32(pack_el<2>(dr[u]), hv[4 * u + 2], acc2);
+                            acc2 = mfma_f32(pack_el<3>(dr[u]), hv[4 * u + 3], acc2);
+                        }
                     }
                     mfma_f32_fence(acc, acc2);
 #pragma unroll
@@ -651,17 +786,42 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
                 const int i = 4 * st + g;
                 dv[st] = (ok(i) ? sg.u[i] : 0.f) * ld1(dyc, cl(i) * xs + p);
             }
+            // bf16: u o dy as hi + lo bf16 (G carries into every later chunk's
+            // terms of dl), C exact
+            bf16x8 dvhi[NB / 2], dvlo[NB / 2];
+            if constexpr (kBf) {
+#pragma unroll
+                for (int q = 0; q < NB / 2; ++q) {
+                    float w[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) w[e] = dv[8 * q + e];
+                    bf16x8_split(w, dvhi[q], dvlo[q]);
+                }
+            }
             for (int Nb = wave / PU; Nb < N / 16; Nb += kWaves / PU) {
                 const int n = Nb * 16 + l16;
                 float cv[4 * NB];
 #pragma unroll
                 for (int st = 0; st < 4 * NB; ++st) cv[st] = ld1(Cc, cl(4 * st + g) * bs + n);
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
+                if constexpr (kBf) {
 #pragma unroll
-                for (int st = 0; st < 4 * NB; st += 2) {
-                    if (4 * st >= nvalid) break;
-                    acc = mfma_f32(dv[st], cv[st], acc);
-                    acc2 = mfma_f32(dv[st + 1], cv[st + 1], acc2);
+                    for (int q = 0; q < NB / 2; ++q) {
+                        if (32 * q >= nvalid) break;
+                        float w[8];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) w[e] = cv[8 * q + e];
+                        const bf16x8 cc = bf16x8_of(w);
+                        acc = mfma_bf16(dvhi[q], cc, acc);
+                        acc2 = mfma_bf16(dvlo[q], cc, acc2);
+                    }
+                } else {
+#pragma unroll
+                    for (int st = 0; st < 4 * NB; st += 2) {
+                        if (4 * st >= nvalid) break;
+                        acc = mfma_f32(dv[st], cv[st], acc);
+                        acc2 = mfma_f32(dv[st + 1], cv[st + 1], acc2);
+                    }
                 }
                 mfma_f32_fence(acc, acc2);
 #pragma unroll
