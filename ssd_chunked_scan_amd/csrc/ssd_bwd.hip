@@ -67,24 +67,49 @@ __device__ inline float pack_el(const Pack<bf16> &q) {
     return __uint_as_float((E & 1) ? (w & 0xffff0000u) : (w << 16));
 }
 
-// Sum over aligned groups of W lanes (W a power of two, at most 64).  Every
-// lane of the wave takes part.
-__device__ inline float lane_group_sum(float v, int W) {
-    for (int off = 1; off < W; off <<= 1) v += __shfl_xor(v, off, 64);
+// Cross-lane sums and scans on DPP (vector ALU, no LDS round trip).
+template <int CTRL>
+__device__ inline float dpp_f(float x) {
+    return __builtin_bit_cast(float, dpp_row<CTRL>(__builtin_bit_cast(int, x)));
+}
+
+// Sum over each row of 16 lanes, every lane receiving it: swaps within pairs
+// and quads, then rotations of the row by 4 and by 8.
+__device__ inline float row_sum16(float v) {
+    v += dpp_f<0xB1>(v);     // quad_perm [1, 0, 3, 2]
+    v += dpp_f<0x4E>(v);     // quad_perm [2, 3, 0, 1]
+    v += dpp_f<0x124>(v);    // row_ror 4
+    return v + dpp_f<0x128>(v);   // row_ror 8
+}
+
+// Sum over each aligned group of 8 lanes, every lane receiving it: swaps
+// within pairs and quads, then the half-row mirror (lane i and 7 - i).
+__device__ inline float group8_sum(float v) {
+    v += dpp_f<0xB1>(v);
+    v += dpp_f<0x4E>(v);
+    return v + dpp_f<0x141>(v);   // row_half_mirror
+}
+
+// Inclusive prefix sum within each aligned group of 8 lanes; q = lane % 8.
+__device__ inline float group8_scan(float v, int q) {
+    float o = dpp_f<0x111>(v);    // row_shr 1
+    if (q >= 1) v += o;
+    o = dpp_f<0x112>(v);          // row_shr 2
+    if (q >= 2) v += o;
+    o = dpp_f<0x114>(v);          // row_shr 4
+    if (q >= 4) v += o;
     return v;
 }
 
-// Sum over each row of 16 lanes, every lane receiving it, on DPP (vector
-// ALU, no LDS round trip): swaps within pairs and quads, then rotations of
-// the row by 4 and by 8.
-__device__ inline float row_sum16(float v) {
-    auto step = [](float x, auto ctrl) {
-        return x + __builtin_bit_cast(float, dpp_row<decltype(ctrl)::value>(__builtin_bit_cast(int, x)));
-    };
-    v = step(v, std::integral_constant<int, 0xB1>{});    // quad_perm [1, 0, 3, 2]
-    v = step(v, std::integral_constant<int, 0x4E>{});    // quad_perm [2, 3, 0, 1]
-    v = step(v, std::integral_constant<int, 0x124>{});   // row_ror 4
-    return step(v, std::integral_constant<int, 0x128>{});  // row_ror 8
+// Sum over the whole wave, the same value in every lane: the row sums, then
+// lanes 0, 16, 32 and 48 read out and added in a fixed order.
+__device__ inline float wave_sum(float v) {
+    v = row_sum16(v);
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+    return (r0 + r1) + (r2 + r3);
 }
 
 // D = A B + C on v_mfma_f32_16x16x4_f32: lane l gives A[l % 16][l / 16] and
@@ -549,17 +574,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
         // ---- dB, dC (per head) and q_s: tiles over (t, n)
         //   dB: acc = sum_{i >= t} (L o V)[i][t] C_i[n],  acc2 = (X G)[t][n] = G^T x_t
         //   dC: acc = sum_{j <= t} (L o dt o V)[t][j] B_j[n],  acc2 = (dY H)[t][n] = H^T dy_t
-        // the first wave on each block of state columns adds its share of T <G, H>
-        if (Hs && wave < N / 16) {
-            const int n = (wave % (N / 16)) * 16 + l16;
-            float k = 0.f;
-#pragma unroll
-            for (int u = 0; u < PU; ++u)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) k = fmaf(sG[(16 * u + 4 * g + e) * GN + n], hv[4 * u + e], k);
-            k = lane_group_sum(k, 64);
-            if (lane == 0) atomicAdd(&sK, k);
-        }
+        // the first wave on each block of state columns (T0 = 0) adds its
+        // share of T <G, H> from the G columns it holds
         // A wave takes one block of 16 state columns n and NT consecutive
         // 16-row blocks T of it (NT = 4 at dstate 128: the whole chunk).  The
         // B operands of those tiles (C and B columns, G columns) are the same
@@ -581,6 +597,13 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
                 for (int u = 0; u < PU; ++u)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) gq[4 * u + e] = sG[(16 * u + 4 * g + e) * GN + n];
+                if (Hs && T0 == 0) {
+                    float k = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 4 * PU; ++e) k = fmaf(gq[e], hv[e], k);
+                    k = wave_sum(k);
+                    if (lane == 0) atomicAdd(&sK, k);
+                }
                 // bf16: G and H columns as hi + lo bf16 (see dX)
                 constexpr int PV = (PU + 1) / 2;
                 bf16x8 gqhi[PV], gqlo[PV], hvhi[PV], hvlo[PV];
@@ -717,14 +740,14 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
             }
         }
         if (c > 0) load_hv(c - 1, l16, g);
-        ddsum = lane_group_sum(ddsum, 64);
+        ddsum = wave_sum(ddsum);
         if (lane == 0) atomicAdd(&sDD, ddsum);
         __syncthreads();
 
         // ---- R = L o dt o S o V, then prefix sums of each row over r < t
         // (eight lanes per row, eight columns each)
         constexpr int LPR = kBwdThreads / Q, CPL = Q / LPR;   // lanes per row, columns per lane
-        static_assert(LPR * Q == kBwdThreads && LPR <= 64, "whole rows per thread group");
+        static_assert(LPR * Q == kBwdThreads && LPR == 8, "rows of 8 lanes (the DPP sums and scans)");
         {
             const int s = tid / LPR, q = tid % LPR;
             float Rv[CPL], loc = 0.f;
@@ -734,13 +757,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
                 Rv[c8] = (r <= s) ? sS[s * LQ + r] * sg.dt[r] * sL[s * LQ + r] : 0.f;   // (L o S) dt V
                 loc += Rv[c8];
             }
-            float incl = loc;
-#pragma unroll
-            for (int off = 1; off < LPR; off <<= 1) {
-                const float o = __shfl_up(incl, off, LPR);
-                if (q >= off) incl += o;
-            }
-            float run = incl - loc;
+            float run = group8_scan(loc, q) - loc;
 #pragma unroll
             for (int c8 = 0; c8 < CPL; ++c8) {
                 sV[s * LQ + CPL * q + c8] = run;   // sum_{r' < r} R_{s r'}
@@ -757,7 +774,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
                 if (s >= t) dl += sV[s * LQ + t] + sq[s];
                 else dl += sp[s];
             }
-            dl = lane_group_sum(dl, LPR);
+            dl = group8_sum(dl);
             if (q == 0) {
                 if (t < nvalid) {
                     dl += sg.T * sK;
@@ -834,7 +851,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
         __syncthreads();
         static_assert(Q == 64, "one token a lane of wave 0");
         if (tid < 64) {
-            const float s = lane_group_sum(sdl[tid], 64);
+            const float s = wave_sum(sdl[tid]);
             if (tid == 0) sDA += s;
         }
     }
