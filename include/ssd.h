@@ -285,10 +285,10 @@ ssd_status_t ssd_decode_step_fused(const ssd_shape_t *shape, ssd_dtype_t io,
  * respect to every input of ssd_fwd (same shapes and layouts, no fused
  * prologue/epilogue), i.e. what training needs from this layer.  The method
  * differentiates the chunked decomposition of page "State Space Duality and
- * Mamba-2" ("The SSD Block Decomposition Algorithm"): the chunk-entering
- * states come from the forward pass's split-local pass and affine scan with
- * one split per 64-token chunk, then one reverse walk over the chunks per
- * (batch row, head) carries the adjoint of the state in fp32.  fp32 inputs:
+ * Mamba-2" ("The SSD Block Decomposition Algorithm"): one pass per (batch
+ * row, head) walks the 64-token chunks in order and writes every
+ * chunk-entering state, then one reverse walk over the chunks per (batch
+ * row, head) carries the adjoint of the state in fp32.  fp32 inputs:
  * every product on fp32 MFMA tiles.  bf16 inputs: every product on bf16 MFMA
  * with fp32 accumulation; the masked products take their fp32 operand
  * rounded to bf16, the products with a carried state (adjoint or state) take
@@ -298,8 +298,9 @@ ssd_status_t ssd_decode_step_fused(const ssd_shape_t *shape, ssd_dtype_t io,
  *   [b, L, G, N], dD [H] (NULL exactly when D is NULL), dinit [b, H, P, N]
  *   (NULL, or the gradient of init_states, which must then be given).
  * Supported set and errors as ssd_fwd (chunk 64 internally); the workspace
- * (ssd_bwd_workspace_bytes) is the forward's for 64-token splits plus
- * 8 b L H N + 8 b H bytes. */
+ * (ssd_bwd_workspace_bytes, 16-byte aligned) holds the entering states,
+ * 4 b H ceil(L / 64) P N bytes when L > 64, then 8 b L H N + 8 b H bytes,
+ * each part rounded up to 256 bytes; nothing in it survives the call. */
 size_t ssd_bwd_workspace_bytes(const ssd_shape_t *shape, ssd_dtype_t io);
 ssd_status_t ssd_bwd(const ssd_shape_t *shape, ssd_dtype_t io,
                      const void *x, const float *dt, const float *A,

@@ -23,6 +23,7 @@ bool launch_cb(int Q, int N, const CbArgs &a, hipStream_t stream);
 size_t cb_s_elems(int Q);
 void launch_chunk_f32(int Q, const ChunkArgs &a, hipStream_t stream);
 void launch_bwd(bool bf16_io, const BwdArgs &a, hipStream_t stream);
+void launch_bwd_states(bool bf16_io, const BwdArgs &a, float *out, hipStream_t stream);
 void launch_split_scan(const float *init_states, float *ws_states, const float *ws_decay,
                        int batch, int nheads, int nsplits, int pn, hipStream_t stream);
 void launch_mask(int Q, const MaskArgs &m, hipStream_t stream);
@@ -338,7 +339,8 @@ ssd_status_t fwd_impl(const ssd_shape_t *shape, ssd_dtype_t io, const void *x, c
                       const int32_t *seq_idx, int64_t chunk_size, const float *init_states,
                       void *y, float *final_states, const ssd_fused_t *fused,
                       void *workspace, size_t workspace_bytes, const ssd_options_t *opts,
-                      void *stream, bool states_only, float *dbg_seg = nullptr) {
+                      void *stream, bool states_only, float *dbg_seg = nullptr,
+                      bool validate_only = false) {
     ssd_status_t st = check_problem(shape, chunk_size, io, opts);
     if (st != SSD_OK) return st;
     st = check_fused(fused, 16);
@@ -357,6 +359,7 @@ ssd_status_t fwd_impl(const ssd_shape_t *shape, ssd_dtype_t io, const void *x, c
     Plan pl;
     st = make_plan(shape, chunk_size, io, opts, &pl, s);
     if (st != SSD_OK) return st;
+    if (validate_only) return SSD_OK;
     if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes))
         return fail(SSD_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given%s", pl.ws_bytes,
                     workspace_bytes, workspace ? "" : " (NULL)");
@@ -461,11 +464,12 @@ ssd_status_t fwd_impl(const ssd_shape_t *shape, ssd_dtype_t io, const void *x, c
     return SSD_OK;
 }
 
-// Backward workspace: the forward's (one split per 64-token chunk), then the
-// per-head dB and dC and the per-row dA and dD partial sums.
+// Backward workspace: the chunk-entering states (when there is more than
+// one 64-token chunk), then the per-head dB and dC and the per-row dA and dD
+// partial sums.
 struct BwdPlan {
     Plan fwd;
-    size_t dbh_bytes, part_bytes, ws_bytes;
+    size_t states_bytes, dbh_bytes, part_bytes, ws_bytes;
 };
 
 ssd_status_t make_bwd_plan(const ssd_shape_t *s, ssd_dtype_t io, BwdPlan *bp, hipStream_t stream) {
@@ -474,9 +478,13 @@ ssd_status_t make_bwd_plan(const ssd_shape_t *s, ssd_dtype_t io, BwdPlan *bp, hi
     o.split_len = ssd::kBwdQ;
     ssd_status_t st = make_plan(s, ssd::kBwdQ, io, &o, &bp->fwd, stream);
     if (st != SSD_OK) return st;
+    bp->states_bytes = bp->fwd.nchunks > 1
+                           ? round_up((size_t)s->batch * s->nheads * bp->fwd.nchunks * s->headdim *
+                                          s->dstate * sizeof(float), 256)
+                           : 0;
     bp->dbh_bytes = round_up((size_t)s->batch * s->seqlen * s->nheads * s->dstate * sizeof(float), 256);
     bp->part_bytes = round_up((size_t)s->batch * s->nheads * sizeof(float), 256);
-    bp->ws_bytes = bp->fwd.ws_bytes + 2 * bp->dbh_bytes + 2 * bp->part_bytes;
+    bp->ws_bytes = bp->states_bytes + 2 * bp->dbh_bytes + 2 * bp->part_bytes;
     return SSD_OK;
 }
 
@@ -531,10 +539,11 @@ ssd_status_t ssd_bwd(const ssd_shape_t *shape, ssd_dtype_t io, const void *x, co
     ssd_options_t o;
     memset(&o, 0, sizeof(o));
     o.split_len = ssd::kBwdQ;
+    // the forward's checks of the shared inputs (nothing is launched)
     st = fwd_impl(shape, io, x, dt, A, B, C, D, seq_idx, ssd::kBwdQ, init_states, nullptr, nullptr,
-                  nullptr, workspace, bp.fwd.ws_bytes, &o, stream, true);
+                  nullptr, nullptr, 0, &o, stream, true, nullptr, true);
     if (st != SSD_OK) return st;
-    char *wsb = (char *)workspace + bp.fwd.ws_bytes;
+    char *wsb = (char *)workspace + bp.states_bytes;
     ssd::BwdArgs a;
     memset(&a, 0, sizeof(a));
     a.x = x;
@@ -545,7 +554,8 @@ ssd_status_t ssd_bwd(const ssd_shape_t *shape, ssd_dtype_t io, const void *x, co
     a.A = A;
     a.D = D;
     a.seq_idx = seq_idx;
-    a.states = bp.fwd.nsplits > 1 ? (const float *)((const char *)workspace + bp.fwd.group_bytes()) : nullptr;
+    float *states = bp.states_bytes ? (float *)workspace : nullptr;
+    a.states = states;
     a.init_states = init_states;
     a.dfinal = dfinal;
     a.dx = dx;
@@ -567,6 +577,11 @@ ssd_status_t ssd_bwd(const ssd_shape_t *shape, ssd_dtype_t io, const void *x, co
     a.ngroups = (int)shape->ngroups;
     a.nchunks = bp.fwd.nchunks;
     (void)hipGetLastError();
+    if (states) {   // H_{c-1} of every chunk, walked in order
+        ssd::launch_bwd_states(io == SSD_BF16, a, states, (hipStream_t)stream);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return fail(SSD_ERR_HIP, "backward states launch: %s", hipGetErrorString(e));
+    }
     ssd::launch_bwd(io == SSD_BF16, a, (hipStream_t)stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(SSD_ERR_HIP, "backward launch: %s", hipGetErrorString(e));

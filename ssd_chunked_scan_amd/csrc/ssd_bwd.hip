@@ -1,8 +1,8 @@
 // Backward pass of the SSD forward pass (gradients of every input), chunk by
 // chunk in reverse, every product on 16x16 MFMA tiles with fp32 accumulation.
 //
-// With the chunk-entering states H_{c-1} (from the forward machinery's
-// split-local pass and affine scan, one split per 64-token chunk) and the
+// With the chunk-entering states H_{c-1} (written by ssd_bwd_states_kernel
+// below, one pass over the chunks in order per (batch row, head)) and the
 // adjoint G_c = dJ/dH_c of the state at the end of chunk c, everything a
 // chunk contributes is a masked quadratic form plus state terms (page "State
 // Space Duality and Mamba-2", "The SSD Block Decomposition Algorithm", read
@@ -892,6 +892,253 @@ __global__ __launch_bounds__(256) void ssd_bwd_reduce_kernel(BwdArgs a) {
         }
         a.dA[h] = sa;
         if (a.dD) a.dD[h] = sd;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// The chunk-entering states the reverse walk reads: H_{c-1} for every
+// 64-token chunk c, as [batch][nheads][nchunks][headdim][dstate] fp32, entry 0
+// being the initial state (or 0).  One workgroup per (batch row, head) walks
+// the chunks in order with the state in MFMA accumulators,
+//   H_c = T_c H_{c-1} + sum_t w_t x_t B_t^T,
+// where w_t is dt_t times the decay from t (exclusive) to the chunk end and
+// T_c the chunk's decay, both 0 across a document boundary (page "State Space
+// Duality and Mamba-2", "The SSD Block Decomposition Algorithm": the chunk
+// states and their passing from chunk to chunk).  Each state is written to
+// memory once and nothing else is, where a parallel pass over chunks plus a
+// scan over them writes and reads every state again.  Per chunk the x and B
+// rows are staged in LDS transposed to [row][token], so an MFMA operand (8
+// consecutive tokens of a row, or 16 in fp32) is one or four 16-byte reads.
+// bf16 inputs: w_t x_t as hi + lo bf16 (about 16 bits of the product) against
+// the exact bf16 B rows, fp32 accumulation; fp32 inputs: fp32 MFMA.
+constexpr int kStThreads = 256;
+
+// MFMA results are read by vector code (the state stores, the decay) only
+// after this: 7 wait states after a bf16 16x16x32 step, 12 after fp32 16x16x4.
+// The empty statements place every accumulator's MFMAs before the wait (the
+// volatile statements keep their order); the memory clobber keeps the state
+// stores after it.
+template <bool F32, int K>
+__device__ inline void states_fence(f32x4 (&v)[K]) {
+#pragma unroll
+    for (int k = 1; k < K; ++k) asm volatile("" : "+v"(v[k]));
+    if constexpr (F32)
+        asm volatile("s_nop 7\n\ts_nop 3" : "+v"(v[0]) : : "memory");
+    else
+        asm volatile("s_nop 7" : "+v"(v[0]) : : "memory");
+}
+
+// One instantiation per (headdim, dstate): with the tile count known, the
+// common shapes are straight-line code and the compiler's memory-wait counts
+// stay exact (behind runtime-guarded tiles it waits for every store).  A
+// state is stored right after its update, so the accumulators are next
+// overwritten a whole chunk later: they are the stores' data registers, and
+// rewriting them waits for those stores.
+template <typename IO, int P, int N>
+__global__ __launch_bounds__(kStThreads, (P <= 32 || (P == 64 && std::is_same<IO, bf16>::value)) ? 3 : P == 64 ? 2 : 1)
+void ssd_bwd_states_kernel(BwdArgs a, float *out) {
+    constexpr int Q = kBwdQ, PBn = P / 16, NT = PBn * (N / 16);
+    constexpr bool kBf = std::is_same<IO, bf16>::value;
+    constexpr int MAXT = (NT + 3) / 4;                          // tiles per wave
+    constexpr int TP = kBf ? Q + 8 : Q + 4;                     // row pitch: 144 or 272 bytes
+    constexpr int EPV = 16 / (int)sizeof(IO);                   // elements per 16-byte piece
+    constexpr int XP = Q * P / EPV, BP = Q * N / EPV;           // pieces per chunk
+    constexpr int XPC = (XP + kStThreads - 1) / kStThreads, BPC = (BP + kStThreads - 1) / kStThreads;
+    __shared__ __attribute__((aligned(16))) IO sX[kBf ? 2 : 1][P * TP];   // w x (bf16: hi, lo)
+    __shared__ __attribute__((aligned(16))) IO sBt[N * TP];
+    __shared__ float sw[Q];
+    __shared__ float sT;
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+    const int H = a.nheads, L = a.seqlen, G = a.ngroups;
+    const int bh = blockIdx.x, b = bh / H, h = bh % H, grp = h / (H / G);
+    const int nch = a.nchunks;
+    constexpr int PN = P * N;
+    const float A_h = a.A[h];
+    const float *dt_row = a.dt + (int64_t)b * L * H + h;
+    const int32_t *seq_row = a.seq_idx ? a.seq_idx + (int64_t)b * L : nullptr;
+    float *outh = out + (int64_t)bh * nch * PN;
+    const IO *xg = (const IO *)a.x, *bg = (const IO *)a.B;
+
+    // this wave's tiles: i = wave + 4 j, rows of p block i % PBn, columns of
+    // n block i / PBn; lane holds rows 4 g + r, column l16
+    auto valid = [&](int j) { return NT % 4 == 0 || wave + 4 * j < NT; };
+    auto tile_off = [&](int j, int r) {
+        const int i = wave + 4 * j;
+        return ((i % PBn) * 16 + 4 * g + r) * N + (i / PBn) * 16 + l16;
+    };
+    f32x4 acc[MAXT];
+    const float *h0 = a.init_states ? a.init_states + (int64_t)bh * PN : nullptr;
+#pragma unroll
+    for (int j = 0; j < MAXT; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[j][r] = (h0 && valid(j)) ? h0[tile_off(j, r)] : 0.f;
+    auto store_state = [&](int c) {
+        float *oc = outh + (int64_t)c * PN;
+#pragma unroll
+        for (int j = 0; j < MAXT; ++j)
+            if (valid(j))
+#pragma unroll
+                for (int r = 0; r < 4; ++r) __builtin_nontemporal_store(acc[j][r], oc + tile_off(j, r));
+    };
+
+    // chunk operands in 16-byte pieces, loaded a chunk ahead; every chunk
+    // but the last is whole, and the last is never staged
+    uint4 rx[XPC], rb[BPC];
+    auto load_chunk = [&](int c) {
+        const int64_t r0 = (int64_t)b * L + c * Q;
+#pragma unroll
+        for (int k = 0; k < XPC; ++k) {
+            const int piece = tid + k * kStThreads;
+            if (XP % kStThreads == 0 || piece < XP) {
+                const int t = piece / (P / EPV), q = piece % (P / EPV);
+                rx[k] = *(const uint4 *)(xg + ((r0 + t) * H + h) * P + q * EPV);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < BPC; ++k) {
+            const int piece = tid + k * kStThreads;
+            if (BP % kStThreads == 0 || piece < BP) {
+                const int t = piece / (N / EPV), q = piece % (N / EPV);
+                rb[k] = *(const uint4 *)(bg + ((r0 + t) * G + grp) * N + q * EPV);
+            }
+        }
+    };
+    // token values of a chunk (thread t < Q: token t), a chunk ahead; the
+    // sequence indices are compared where the flag is used, so the loads need
+    // not complete before the chunk's stores are issued
+    float dtv = 0.f;
+    int sq_cur = 0, sq_prev = 0;
+    auto fetch_tokens = [&](int c) {
+        const int t = c * Q + tid;
+        dtv = dt_row[(int64_t)t * H];
+        if (seq_row) {
+            sq_cur = seq_row[t];
+            sq_prev = t > 0 ? seq_row[t - 1] : sq_cur;
+        }
+    };
+    if (nch > 1) {
+        load_chunk(0);
+        if (tid < Q) fetch_tokens(0);
+    }
+    store_state(0);
+    for (int c = 0; c + 1 < nch; ++c) {
+        // w_t and T of chunk c: wave 0, lane = token; log2 decays summed over
+        // the lanes after each one; a reset after t (or anywhere) zeroes w_t (T)
+        if (wave == 0) {
+            const int flag = sq_cur != sq_prev;   // token t starts a document
+            const float d = flag ? 0.f : __fmul_rn(__fmul_rn(dtv, A_h), kLog2e);
+            float sfx = d;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float o = __shfl_down(sfx, off, 64);
+                if (lane + off < 64) sfx += o;
+            }
+            const float after = __shfl_down(sfx, 1, 64);   // sum over (t, 63]
+            const unsigned long long m = __ballot(flag);
+            const bool cut = lane < 63 && (m >> (lane + 1)) != 0ull;
+            sw[lane] = cut ? 0.f : dtv * __builtin_amdgcn_exp2f(lane < 63 ? after : 0.f);
+            if (lane == 0) sT = m ? 0.f : __builtin_amdgcn_exp2f(sfx);
+        }
+        __syncthreads();   // the last chunk's MFMAs are done with the tiles; w and T visible
+        const float T = sT;
+#pragma unroll
+        for (int k = 0; k < XPC; ++k) {
+            const int piece = tid + k * kStThreads;
+            if (XP % kStThreads == 0 || piece < XP) {
+                const int t = piece / (P / EPV), q0 = (piece % (P / EPV)) * EPV;
+                const float wt = sw[t];
+                if constexpr (kBf) {
+                    const bf16x8 v8 = __builtin_bit_cast(bf16x8, rx[k]);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float v = (float)v8[e] * wt;
+                        const bf16 hi = (bf16)v;
+                        sX[0][(q0 + e) * TP + t] = hi;
+                        sX[1][(q0 + e) * TP + t] = (bf16)(v - (float)hi);
+                    }
+                } else {
+                    const float4 v4 = __builtin_bit_cast(float4, rx[k]);
+                    sX[0][(q0 + 0) * TP + t] = v4.x * wt;
+                    sX[0][(q0 + 1) * TP + t] = v4.y * wt;
+                    sX[0][(q0 + 2) * TP + t] = v4.z * wt;
+                    sX[0][(q0 + 3) * TP + t] = v4.w * wt;
+                }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < BPC; ++k) {
+            const int piece = tid + k * kStThreads;
+            if (BP % kStThreads == 0 || piece < BP) {
+                const int t = piece / (N / EPV), q0 = (piece % (N / EPV)) * EPV;
+                if constexpr (kBf) {
+                    const bf16x8 v8 = __builtin_bit_cast(bf16x8, rb[k]);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) sBt[(q0 + e) * TP + t] = v8[e];
+                } else {
+                    const float4 v4 = __builtin_bit_cast(float4, rb[k]);
+                    sBt[(q0 + 0) * TP + t] = v4.x;
+                    sBt[(q0 + 1) * TP + t] = v4.y;
+                    sBt[(q0 + 2) * TP + t] = v4.z;
+                    sBt[(q0 + 3) * TP + t] = v4.w;
+                }
+            }
+        }
+        if (c + 2 < nch) {   // chunk c + 1 is staged in the next pass
+            load_chunk(c + 1);
+            if (tid < Q) fetch_tokens(c + 1);
+        }
+        __syncthreads();   // staged tiles visible
+#pragma unroll
+        for (int j = 0; j < MAXT; ++j) {
+            if (!valid(j)) continue;
+            const int i = wave + 4 * j;
+            const int prow = ((i % PBn) * 16 + l16) * TP, nrow = ((i / PBn) * 16 + l16) * TP;
+            f32x4 v = acc[j] * T;
+            if constexpr (kBf) {
+#pragma unroll
+                for (int ks = 0; ks < Q / 32; ++ks) {
+                    const int k0 = 32 * ks + 8 * g;
+                    const bf16x8 bb = *(const bf16x8 *)&sBt[nrow + k0];
+                    v = mfma_bf16(*(const bf16x8 *)&sX[0][prow + k0], bb, v);
+                    v = mfma_bf16(*(const bf16x8 *)&sX[1][prow + k0], bb, v);
+                }
+            } else {
+                // step s, lane group g: token 16 g + s
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4) {
+                    const float4 xa = *(const float4 *)&sX[0][prow + 16 * g + 4 * s4];
+                    const float4 ba = *(const float4 *)&sBt[nrow + 16 * g + 4 * s4];
+                    v = mfma_f32(xa.x, ba.x, v);
+                    v = mfma_f32(xa.y, ba.y, v);
+                    v = mfma_f32(xa.z, ba.z, v);
+                    v = mfma_f32(xa.w, ba.w, v);
+                }
+            }
+            acc[j] = v;
+        }
+        states_fence<!kBf>(acc);
+        store_state(c + 1);
+    }
+}
+
+void launch_bwd_states(bool bf16_io, const BwdArgs &a, float *out, hipStream_t stream) {
+    const dim3 grid(a.batch * a.nheads), block(kStThreads);
+    auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, block, 0, stream, a, out); };
+    auto by_n = [&](auto pc) {   // the API admits dstate 16, 32, 64 and 128
+        constexpr int P = decltype(pc)::value;
+        switch (a.dstate) {
+        case 16: bf16_io ? go(ssd_bwd_states_kernel<bf16, P, 16>) : go(ssd_bwd_states_kernel<float, P, 16>); break;
+        case 32: bf16_io ? go(ssd_bwd_states_kernel<bf16, P, 32>) : go(ssd_bwd_states_kernel<float, P, 32>); break;
+        case 64: bf16_io ? go(ssd_bwd_states_kernel<bf16, P, 64>) : go(ssd_bwd_states_kernel<float, P, 64>); break;
+        default: bf16_io ? go(ssd_bwd_states_kernel<bf16, P, 128>) : go(ssd_bwd_states_kernel<float, P, 128>); break;
+        }
+    };
+    switch (a.headdim) {   // and headdim 16, 32, 64 and 128
+    case 16: by_n(std::integral_constant<int, 16>{}); break;
+    case 32: by_n(std::integral_constant<int, 32>{}); break;
+    case 64: by_n(std::integral_constant<int, 64>{}); break;
+    default: by_n(std::integral_constant<int, 128>{}); break;
     }
 }
 

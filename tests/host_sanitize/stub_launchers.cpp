@@ -164,6 +164,23 @@ bool launch_decode(bool bf16_io, int N, const DecodeArgs &a, hipStream_t) {
     return true;
 }
 
+void launch_bwd_states(bool bf16_io, const BwdArgs &a, float *out, hipStream_t) {
+    ++g_launches;
+    const size_t esz = bf16_io ? 2 : 4, b = a.batch, L = a.seqlen, H = a.nheads, P = a.headdim,
+                 N = a.dstate, G = a.ngroups;
+    // the chunks before the last (the last is never staged)
+    const size_t Ls = (size_t)(a.nchunks - 1) * kBwdQ;
+    for (size_t r = 0; r < b; ++r) {
+        rd((const char *)a.x + r * L * H * P * esz, Ls * H * P * esz);
+        rd((const char *)a.B + r * L * G * N * esz, Ls * G * N * esz);
+        rd(a.dt + r * L * H, Ls * H * 4);
+        rd(a.seq_idx ? a.seq_idx + r * L : nullptr, a.seq_idx ? Ls * 4 : 0);
+    }
+    rd(a.A, H * 4);
+    rd(a.init_states, a.init_states ? b * H * P * N * 4 : 0);
+    wr(out, b * H * a.nchunks * P * N * 4);
+}
+
 void launch_bwd(bool bf16_io, const BwdArgs &a, hipStream_t) {
     ++g_launches;
     const size_t esz = bf16_io ? 2 : 4, b = a.batch, L = a.seqlen, H = a.nheads, P = a.headdim,
