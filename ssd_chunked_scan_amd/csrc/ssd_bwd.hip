@@ -979,7 +979,7 @@ void ssd_bwd_states_kernel(BwdArgs a, float *out) {
         for (int j = 0; j < MAXT; ++j)
             if (valid(j))
 #pragma unroll
-                for (int r = 0; r < 4; ++r) __builtin_nontemporal_store(acc[j][r], oc + tile_off(j, r));
+                for (int r = 0; r < 4; ++r) oc[tile_off(j, r)] = acc[j][r];
     };
 
     // chunk operands in 16-byte pieces, loaded a chunk ahead; every chunk
