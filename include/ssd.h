@@ -298,9 +298,13 @@ ssd_status_t ssd_decode_step_fused(const ssd_shape_t *shape, ssd_dtype_t io,
  *   [b, L, G, N], dD [H] (NULL exactly when D is NULL), dinit [b, H, P, N]
  *   (NULL, or the gradient of init_states, which must then be given).
  * Supported set and errors as ssd_fwd (chunk 64 internally); the workspace
- * (ssd_bwd_workspace_bytes, 16-byte aligned) holds the entering states,
- * 4 b H ceil(L / 64) P N bytes when L > 64, then 8 b L H N + 8 b H bytes,
- * each part rounded up to 256 bytes; nothing in it survives the call. */
+ * (ssd_bwd_workspace_bytes, 16-byte aligned, queried with the device that
+ * will run the call current: its size depends on the compute-unit count)
+ * holds the entering states, 4 b H ceil(L / 64) P N bytes when L > 64, then
+ * 8 b L H N + 16 b H bytes, then, when the (batch row, head) walks of the
+ * last round are split in two, 4 P N bytes for each of them (at most half the
+ * compute units), each part rounded up to 256 bytes; nothing in it survives
+ * the call. */
 size_t ssd_bwd_workspace_bytes(const ssd_shape_t *shape, ssd_dtype_t io);
 ssd_status_t ssd_bwd(const ssd_shape_t *shape, ssd_dtype_t io,
                      const void *x, const float *dt, const float *A,

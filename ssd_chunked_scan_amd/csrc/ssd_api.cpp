@@ -465,11 +465,19 @@ ssd_status_t fwd_impl(const ssd_shape_t *shape, ssd_dtype_t io, const void *x, c
 }
 
 // Backward workspace: the chunk-entering states (when there is more than
-// one 64-token chunk), then the per-head dB and dC and the per-row dA and dD
-// partial sums.
+// one 64-token chunk), then the per-head dB and dC, the dA and dD partial
+// sums (two slots per walk) and the adjoints the tail walks start from.
+//
+// Tail split: the reverse walks are one workgroup per (batch row, head), one
+// per compute unit.  When they outnumber the CUs and the last round holds at
+// most half of them, each walk of that round runs as two workgroups over
+// half the chunks each, the earlier half starting from an adjoint computed
+// beforehand (by the states kernel, alongside the states): the last round
+// then takes about half as long.
 struct BwdPlan {
     Plan fwd;
-    size_t states_bytes, dbh_bytes, part_bytes, ws_bytes;
+    int whole_units, tail_units, split_chunk;
+    size_t states_bytes, dbh_bytes, part_bytes, tail_bytes, ws_bytes;
 };
 
 ssd_status_t make_bwd_plan(const ssd_shape_t *s, ssd_dtype_t io, BwdPlan *bp, hipStream_t stream) {
@@ -483,8 +491,15 @@ ssd_status_t make_bwd_plan(const ssd_shape_t *s, ssd_dtype_t io, BwdPlan *bp, hi
                                           s->dstate * sizeof(float), 256)
                            : 0;
     bp->dbh_bytes = round_up((size_t)s->batch * s->seqlen * s->nheads * s->dstate * sizeof(float), 256);
-    bp->part_bytes = round_up((size_t)s->batch * s->nheads * sizeof(float), 256);
-    bp->ws_bytes = bp->states_bytes + 2 * bp->dbh_bytes + 2 * bp->part_bytes;
+    bp->part_bytes = round_up((size_t)s->batch * s->nheads * 2 * sizeof(float), 256);
+    const int64_t units = s->batch * s->nheads, cus = device_cus(stream);
+    const int64_t tail = units % cus;
+    const bool split = units > cus && tail > 0 && 2 * tail <= cus && bp->fwd.nchunks >= 2;
+    bp->tail_units = split ? (int)tail : 0;
+    bp->whole_units = (int)(units - bp->tail_units);
+    bp->split_chunk = bp->fwd.nchunks / 2;
+    bp->tail_bytes = round_up((size_t)bp->tail_units * s->headdim * s->dstate * sizeof(float), 256);
+    bp->ws_bytes = bp->states_bytes + 2 * bp->dbh_bytes + 2 * bp->part_bytes + bp->tail_bytes;
     return SSD_OK;
 }
 
@@ -564,6 +579,10 @@ ssd_status_t ssd_bwd(const ssd_shape_t *shape, ssd_dtype_t io, const void *x, co
     a.dC_head = (float *)(wsb + bp.dbh_bytes);
     a.dA_part = (float *)(wsb + 2 * bp.dbh_bytes);
     a.dD_part = (float *)(wsb + 2 * bp.dbh_bytes + bp.part_bytes);
+    a.g_tail = bp.tail_units ? (float *)(wsb + 2 * bp.dbh_bytes + 2 * bp.part_bytes) : nullptr;
+    a.whole_units = bp.whole_units;
+    a.tail_units = bp.tail_units;
+    a.split_chunk = bp.split_chunk;
     a.dB = dB;
     a.dC = dC;
     a.dA = dA;

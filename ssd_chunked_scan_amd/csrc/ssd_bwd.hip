@@ -202,10 +202,26 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: job branches are scalar
-    const int bh = blockIdx.x;
-    const int b = bh / a.nheads, h = bh % a.nheads;
     const int L = a.seqlen, H = a.nheads, G = a.ngroups, N = a.dstate;
     const int PN = P * N;
+    // The walk: a whole (batch row, head), or one half of a tail walk (chunks
+    // [split, nchunks) from dfinal, or [0, split) from the adjoint the states
+    // kernel left for it); dA and dD partial sums go to slot 0 or 1
+    int bh = blockIdx.x, c_lo = 0, c_hi = a.nchunks, slot = 0;
+    const float *g0 = nullptr;
+    if (bh >= a.whole_units) {
+        const int k = (bh - a.whole_units) >> 1;
+        slot = (bh - a.whole_units) & 1;
+        bh = a.whole_units + k;
+        if (slot == 0)
+            c_lo = a.split_chunk;
+        else {
+            c_hi = a.split_chunk;
+            g0 = a.g_tail + (int64_t)k * PN;
+        }
+    }
+    if (slot == 0 && a.dfinal) g0 = a.dfinal + (int64_t)bh * PN;
+    const int b = bh / a.nheads, h = bh % a.nheads;
     const int GN = N + 4;                   // row pitch of sG (16-byte rows, 4 mod 64 banks)
     const int grp = h / (H / G);
     const float A_h = a.A[h];
@@ -218,8 +234,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
     const int gxs = H * P, gbs = G * N;     // token strides in global memory
     const int xs = STAGE ? XPe : gxs, bs = STAGE ? BPe : gbs;   // ... where operands are read
 
-    for (int e = tid; e < PN; e += kBwdThreads)
-        sG[(e / N) * GN + e % N] = a.dfinal ? a.dfinal[(int64_t)bh * PN + e] : 0.f;
+    for (int e = tid; e < PN; e += kBwdThreads) sG[(e / N) * GN + e % N] = g0 ? g0[e] : 0.f;
     if (tid == 0) {
         sDD = 0.f;
         sDA = 0.f;
@@ -231,7 +246,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
     float dt_next = 0.f;
     int flag_next = 0;
     if (tid < Q) {
-        const int cl0 = a.nchunks - 1;
+        const int cl0 = c_hi - 1;
         seg_fetch_token(tid, cl0 * Q, min(Q, L - cl0 * Q), dt_row, H, seq_row, dt_next, flag_next);
     }
     // H_{c-1}: from the forward's scan, or (a single chunk) the initial state or 0
@@ -254,7 +269,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
             for (int e = 0; e < 4; ++e)
                 hv[4 * u + e] = Hc ? *at_off(Hc, (16 * u + 4 * g_ + e) * N + n) : 0.f;
     };
-    load_hv(a.nchunks - 1, tid & 15, (tid & 63) >> 4);
+    load_hv(c_hi - 1, tid & 15, (tid & 63) >> 4);
     // Staging payload of a chunk, 16 bytes a piece, loaded a chunk ahead into
     // registers (rows past the end of the row hold the last valid token): one
     // piece of x and of dy (Q * P / 8 <= 512 pieces at headdim <= 64) and two
@@ -302,8 +317,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
             *(uint4 *)&sCs[r * BPe + q8 * 8] = stc1;
         }
     };
-    if constexpr (STAGE) stage_load(a.nchunks - 1);
-    for (int c = a.nchunks - 1; c >= 0; --c) {
+    if constexpr (STAGE) stage_load(c_hi - 1);
+    for (int c = c_hi - 1; c >= c_lo; --c) {
         const int t0 = c * Q;
         const int nvalid = min(Q, L - t0);
         const float *Hs = hs_of(c);
@@ -344,7 +359,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
         if (tid < Q) {
             seg_store_token<Q>(sg, tid, dt_next, A_h, flag_next);
             flag_any = flag_next;
-            if (c > 0) seg_fetch_token(tid, t0 - Q, Q, dt_row, H, seq_row, dt_next, flag_next);
+            if (c > c_lo) seg_fetch_token(tid, t0 - Q, Q, dt_row, H, seq_row, dt_next, flag_next);
         }
         flag_any = __syncthreads_or(flag_any);
         if (tid == 0) {
@@ -739,7 +754,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
                 }
             }
         }
-        if (c > 0) load_hv(c - 1, l16, g);
+        if (c > c_lo) load_hv(c - 1, l16, g);
         ddsum = wave_sum(ddsum);
         if (lane == 0) atomicAdd(&sDD, ddsum);
         __syncthreads();
@@ -788,7 +803,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
         // global store: vmcnt also counts stores, and the wait for these loads
         // at the next chunk's start then finds nothing younger to drain.
         if constexpr (STAGE)
-            if (c > 0) stage_load(c - 1);
+            if (c > c_lo) stage_load(c - 1);
         // ---- G_{c-1} = T G_c + sum_i u_i dy_i C_i^T: tiles over (p, n)
         // A wave keeps one block of 16 headdim rows p (the block count divides
         // the wave count) over its tiles, so u o dy for those rows is read once.
@@ -856,11 +871,15 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
         }
     }
     __syncthreads();
-    if (a.dinit)
+    if (a.dinit && c_lo == 0)
         for (int e = tid; e < PN; e += kBwdThreads) a.dinit[(int64_t)bh * PN + e] = sG[(e / N) * GN + e % N];
     if (tid == 0) {
-        a.dA_part[bh] = sDA;
-        a.dD_part[bh] = sDD;
+        a.dA_part[2 * bh + slot] = sDA;
+        a.dD_part[2 * bh + slot] = sDD;
+        if (c_lo == 0 && c_hi == a.nchunks) {   // a whole walk fills both slots
+            a.dA_part[2 * bh + 1] = 0.f;
+            a.dD_part[2 * bh + 1] = 0.f;
+        }
     }
 }
 
@@ -887,8 +906,11 @@ __global__ __launch_bounds__(256) void ssd_bwd_reduce_kernel(BwdArgs a) {
         const int h = (int)(e - nbg);
         float sa = 0.f, sd = 0.f;
         for (int bb = 0; bb < a.batch; ++bb) {
-            sa += a.dA_part[(int64_t)bb * H + h];
-            sd += a.dD_part[(int64_t)bb * H + h];
+            const int64_t o = 2 * ((int64_t)bb * H + h);
+            sa += a.dA_part[o];
+            sa += a.dA_part[o + 1];
+            sd += a.dD_part[o];
+            sd += a.dD_part[o + 1];
         }
         a.dA[h] = sa;
         if (a.dD) a.dD[h] = sd;
@@ -934,6 +956,13 @@ __device__ inline void states_fence(f32x4 (&v)[K]) {
 // state is stored right after its update, so the accumulators are next
 // overwritten a whole chunk later: they are the stores' data registers, and
 // rewriting them waits for those stores.
+//
+// Workgroups past batch * nheads walk the adjoint of a tail walk instead (see
+// BwdArgs): G_{c-1} = T_c G_c + sum_t u_t dy_t C_t^T from dfinal over chunks
+// nchunks - 1 down to split_chunk, u_t the decay from the chunk start through
+// t (0 from a document boundary on, and past the end of the row), the form
+// of the state walk with dy, C and u for x, B and w, in reverse.  Only the
+// last G is stored, to g_tail.
 template <typename IO, int P, int N>
 __global__ __launch_bounds__(kStThreads, (P <= 32 || (P == 64 && std::is_same<IO, bf16>::value)) ? 3 : P == 64 ? 2 : 1)
 void ssd_bwd_states_kernel(BwdArgs a, float *out) {
@@ -951,14 +980,21 @@ void ssd_bwd_states_kernel(BwdArgs a, float *out) {
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
     const int H = a.nheads, L = a.seqlen, G = a.ngroups;
-    const int bh = blockIdx.x, b = bh / H, h = bh % H, grp = h / (H / G);
     const int nch = a.nchunks;
+    const bool adj = (int)blockIdx.x >= a.batch * H;   // uniform: the workgroup's role
+    const int tk = (int)blockIdx.x - a.batch * H;      // adjoint: tail walk tk
+    const int bh = adj ? a.whole_units + tk : (int)blockIdx.x;
+    const int b = bh / H, h = bh % H, grp = h / (H / G);
     constexpr int PN = P * N;
     const float A_h = a.A[h];
     const float *dt_row = a.dt + (int64_t)b * L * H + h;
     const int32_t *seq_row = a.seq_idx ? a.seq_idx + (int64_t)b * L : nullptr;
-    float *outh = out + (int64_t)bh * nch * PN;
-    const IO *xg = (const IO *)a.x, *bg = (const IO *)a.B;
+    float *outh = adj ? a.g_tail + (int64_t)tk * PN : out + (int64_t)bh * nch * PN;
+    const IO *xg = (const IO *)(adj ? a.dy : a.x), *bg = (const IO *)(adj ? a.C : a.B);
+    // the chunks walked: state 0 .. nch - 2 (every state stored), adjoint
+    // nch - 1 down to split_chunk (the last G stored)
+    const int nsteps = adj ? nch - a.split_chunk : nch - 1;
+    auto chunk_of = [&](int s) { return adj ? nch - 1 - s : s; };
 
     // this wave's tiles: i = wave + 4 j, rows of p block i % PBn, columns of
     // n block i / PBn; lane holds rows 4 g + r, column l16
@@ -968,7 +1004,8 @@ void ssd_bwd_states_kernel(BwdArgs a, float *out) {
         return ((i % PBn) * 16 + 4 * g + r) * N + (i / PBn) * 16 + l16;
     };
     f32x4 acc[MAXT];
-    const float *h0 = a.init_states ? a.init_states + (int64_t)bh * PN : nullptr;
+    const float *h0 = adj ? (a.dfinal ? a.dfinal + (int64_t)bh * PN : nullptr)
+                          : (a.init_states ? a.init_states + (int64_t)bh * PN : nullptr);
 #pragma unroll
     for (int j = 0; j < MAXT; ++j)
 #pragma unroll
@@ -982,16 +1019,18 @@ void ssd_bwd_states_kernel(BwdArgs a, float *out) {
                 for (int r = 0; r < 4; ++r) oc[tile_off(j, r)] = acc[j][r];
     };
 
-    // chunk operands in 16-byte pieces, loaded a chunk ahead; every chunk
-    // but the last is whole, and the last is never staged
+    // chunk operands in 16-byte pieces, loaded a chunk ahead; rows past the
+    // end of the row (only the adjoint walk stages the last chunk) are read
+    // at the last valid token, and their weight is 0
     uint4 rx[XPC], rb[BPC];
     auto load_chunk = [&](int c) {
         const int64_t r0 = (int64_t)b * L + c * Q;
+        const int tmax = min(Q, L - c * Q) - 1;
 #pragma unroll
         for (int k = 0; k < XPC; ++k) {
             const int piece = tid + k * kStThreads;
             if (XP % kStThreads == 0 || piece < XP) {
-                const int t = piece / (P / EPV), q = piece % (P / EPV);
+                const int t = min(piece / (P / EPV), tmax), q = piece % (P / EPV);
                 rx[k] = *(const uint4 *)(xg + ((r0 + t) * H + h) * P + q * EPV);
             }
         }
@@ -999,7 +1038,7 @@ void ssd_bwd_states_kernel(BwdArgs a, float *out) {
         for (int k = 0; k < BPC; ++k) {
             const int piece = tid + k * kStThreads;
             if (BP % kStThreads == 0 || piece < BP) {
-                const int t = piece / (N / EPV), q = piece % (N / EPV);
+                const int t = min(piece / (N / EPV), tmax), q = piece % (N / EPV);
                 rb[k] = *(const uint4 *)(bg + ((r0 + t) * G + grp) * N + q * EPV);
             }
         }
@@ -1009,36 +1048,59 @@ void ssd_bwd_states_kernel(BwdArgs a, float *out) {
     // not complete before the chunk's stores are issued
     float dtv = 0.f;
     int sq_cur = 0, sq_prev = 0;
+    int tok_valid = 0;
     auto fetch_tokens = [&](int c) {
         const int t = c * Q + tid;
-        dtv = dt_row[(int64_t)t * H];
-        if (seq_row) {
-            sq_cur = seq_row[t];
-            sq_prev = t > 0 ? seq_row[t - 1] : sq_cur;
+        tok_valid = t < L;
+        dtv = 0.f;
+        sq_cur = sq_prev = 0;
+        if (tok_valid) {
+            dtv = dt_row[(int64_t)t * H];
+            if (seq_row) {
+                sq_cur = seq_row[t];
+                sq_prev = t > 0 ? seq_row[t - 1] : sq_cur;
+            }
         }
     };
-    if (nch > 1) {
-        load_chunk(0);
-        if (tid < Q) fetch_tokens(0);
+    if (nsteps > 0) {
+        load_chunk(chunk_of(0));
+        if (tid < Q) fetch_tokens(chunk_of(0));
     }
-    store_state(0);
-    for (int c = 0; c + 1 < nch; ++c) {
-        // w_t and T of chunk c: wave 0, lane = token; log2 decays summed over
-        // the lanes after each one; a reset after t (or anywhere) zeroes w_t (T)
+    if (!adj) store_state(0);
+    for (int s = 0; s < nsteps; ++s) {
+        const int c = chunk_of(s);
+        // the token weights and T of chunk c: wave 0, lane = token, log2
+        // decays summed over lanes.  State walk: w_t = dt_t 2^(sum after t),
+        // 0 if a document starts after t.  Adjoint walk: u_t = 2^(sum through
+        // t), 0 from a document start on.  T = 2^(sum), 0 if any starts.
         if (wave == 0) {
-            const int flag = sq_cur != sq_prev;   // token t starts a document
-            const float d = flag ? 0.f : __fmul_rn(__fmul_rn(dtv, A_h), kLog2e);
-            float sfx = d;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float o = __shfl_down(sfx, off, 64);
-                if (lane + off < 64) sfx += o;
-            }
-            const float after = __shfl_down(sfx, 1, 64);   // sum over (t, 63]
+            const int flag = tok_valid && sq_cur != sq_prev;   // token t starts a document
+            const float d = (flag || !tok_valid) ? 0.f : __fmul_rn(__fmul_rn(dtv, A_h), kLog2e);
             const unsigned long long m = __ballot(flag);
-            const bool cut = lane < 63 && (m >> (lane + 1)) != 0ull;
-            sw[lane] = cut ? 0.f : dtv * __builtin_amdgcn_exp2f(lane < 63 ? after : 0.f);
-            if (lane == 0) sT = m ? 0.f : __builtin_amdgcn_exp2f(sfx);
+            float tot;
+            if (!adj) {
+                float sfx = d;
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const float o = __shfl_down(sfx, off, 64);
+                    if (lane + off < 64) sfx += o;
+                }
+                const float after = __shfl_down(sfx, 1, 64);   // sum over (t, 63]
+                const bool cut = lane < 63 && (m >> (lane + 1)) != 0ull;
+                sw[lane] = cut ? 0.f : dtv * __builtin_amdgcn_exp2f(lane < 63 ? after : 0.f);
+                tot = sfx;                                     // lane 0: the whole sum
+            } else {
+                float pre = d;
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const float o = __shfl_up(pre, off, 64);
+                    if (lane >= off) pre += o;
+                }
+                const bool cut = (m & ((2ull << lane) - 1ull)) != 0ull;   // a start at or before t
+                sw[lane] = (cut || !tok_valid) ? 0.f : __builtin_amdgcn_exp2f(pre);
+                tot = __shfl(pre, 63, 64);                     // the whole sum
+            }
+            if (lane == 0) sT = m ? 0.f : __builtin_amdgcn_exp2f(tot);
         }
         __syncthreads();   // the last chunk's MFMAs are done with the tiles; w and T visible
         const float T = sT;
@@ -1084,9 +1146,9 @@ void ssd_bwd_states_kernel(BwdArgs a, float *out) {
                 }
             }
         }
-        if (c + 2 < nch) {   // chunk c + 1 is staged in the next pass
-            load_chunk(c + 1);
-            if (tid < Q) fetch_tokens(c + 1);
+        if (s + 1 < nsteps) {   // the next chunk is staged in the next pass
+            load_chunk(chunk_of(s + 1));
+            if (tid < Q) fetch_tokens(chunk_of(s + 1));
         }
         __syncthreads();   // staged tiles visible
 #pragma unroll
@@ -1118,12 +1180,13 @@ void ssd_bwd_states_kernel(BwdArgs a, float *out) {
             acc[j] = v;
         }
         states_fence<!kBf>(acc);
-        store_state(c + 1);
+        if (!adj) store_state(c + 1);
     }
+    if (adj) store_state(0);   // g_tail[tk]: G at the end of chunk split_chunk - 1
 }
 
 void launch_bwd_states(bool bf16_io, const BwdArgs &a, float *out, hipStream_t stream) {
-    const dim3 grid(a.batch * a.nheads), block(kStThreads);
+    const dim3 grid(a.batch * a.nheads + a.tail_units), block(kStThreads);
     auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, block, 0, stream, a, out); };
     auto by_n = [&](auto pc) {   // the API admits dstate 16, 32, 64 and 128
         constexpr int P = decltype(pc)::value;
@@ -1143,7 +1206,7 @@ void launch_bwd_states(bool bf16_io, const BwdArgs &a, float *out, hipStream_t s
 }
 
 void launch_bwd(bool bf16_io, const BwdArgs &a, hipStream_t stream) {
-    const dim3 grid(a.batch * a.nheads), block(kBwdThreads);
+    const dim3 grid(a.whole_units + 2 * a.tail_units), block(kBwdThreads);
     auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, block, 0, stream, a); };
     switch (a.headdim) {   // the API admits 16, 32, 64 and 128
     case 16: bf16_io ? go(ssd_bwd_kernel<bf16, 16>) : go(ssd_bwd_kernel<float, 16>); break;

@@ -173,9 +173,17 @@ struct BwdArgs {
     const float *dfinal;              // nullable
     float *dx, *ddt;                  // [b][L][H][P], [b][L][H]
     float *dB_head, *dC_head;         // [b][L][H][N] workspace
-    float *dA_part, *dD_part;         // [b][H] workspace
+    float *dA_part, *dD_part;         // [b][H][2] workspace (two slots per walk)
     float *dB, *dC, *dA, *dD, *dinit; // dD, dinit nullable
     int batch, seqlen, nheads, headdim, dstate, ngroups, nchunks;
+    // The (batch row, head) walks whole_units .. whole_units + tail_units - 1
+    // (the last, partial round of workgroups) run as two workgroups each:
+    // chunks [split_chunk, nchunks) from dfinal, and chunks [0, split_chunk)
+    // from g_tail[k] [headdim][dstate] fp32, the adjoint of the state at the
+    // end of chunk split_chunk - 1, which the states kernel's extra workgroups
+    // compute.  tail_units = 0: every walk whole.
+    int whole_units, tail_units, split_chunk;
+    float *g_tail;
 };
 
 struct Unit {

@@ -229,6 +229,7 @@ int main(void) {
     for (size_t k = 0; k < sizeof(cases) / sizeof(cases[0]); ++k) run_fwd(&cases[k]);
     run_bwd(1, 300, 4, 64, 64, 2, SSD_BF16, 1);
     run_bwd(2, 130, 2, 128, 32, 1, SSD_F32, 0);
+    run_bwd(1, 300, 272, 16, 16, 1, SSD_BF16, 1);   /* 272 walks: the last 16 split in two */
     run_decode(4, 8, 64, 128, 2, SSD_BF16, 0);
     run_decode(2, 4, 32, 16, 1, SSD_F32, 1);
     run_errors();

@@ -179,6 +179,14 @@ void launch_bwd_states(bool bf16_io, const BwdArgs &a, float *out, hipStream_t) 
     rd(a.A, H * 4);
     rd(a.init_states, a.init_states ? b * H * P * N * 4 : 0);
     wr(out, b * H * a.nchunks * P * N * 4);
+    if (a.tail_units > 0) {   // the tail walks' adjoints: dy, C, dt, seq_idx, dfinal of their rows
+        rd(a.dy, b * L * H * P * esz);
+        rd(a.C, b * L * G * N * esz);
+        rd(a.dt, b * L * H * 4);
+        rd(a.seq_idx, a.seq_idx ? b * L * 4 : 0);
+        rd(a.dfinal, a.dfinal ? b * H * P * N * 4 : 0);
+        wr(a.g_tail, (size_t)a.tail_units * P * N * 4);
+    }
 }
 
 void launch_bwd(bool bf16_io, const BwdArgs &a, hipStream_t) {
@@ -200,8 +208,9 @@ void launch_bwd(bool bf16_io, const BwdArgs &a, hipStream_t) {
     wr(a.ddt, b * L * H * 4);
     wr(a.dB_head, b * L * H * N * 4);
     wr(a.dC_head, b * L * H * N * 4);
-    wr(a.dA_part, b * H * 4);
-    wr(a.dD_part, b * H * 4);
+    rd(a.g_tail, a.tail_units > 0 ? (size_t)a.tail_units * P * N * 4 : 0);
+    wr(a.dA_part, b * H * 2 * 4);
+    wr(a.dD_part, b * H * 2 * 4);
     wr(a.dB, b * L * G * N * 4);
     wr(a.dC, b * L * G * N * 4);
     wr(a.dA, H * 4);

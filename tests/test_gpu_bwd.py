@@ -173,3 +173,30 @@ def test_bwd_full_layer_dA_dD_of_sampled_heads():
         e_d = abs(dD[h] - ref["dD"][0]) / abs(ref["dD"][0])
         print(f"layer27b bwd head {h}: dA {e_a:.1e} dD {e_d:.1e}")
         assert e_a <= TOL["bf16"] and e_d <= TOL["bf16"], (h, e_a, e_d)
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_bwd_split_tail_walks(io):
+    """More (batch row, head) walks than compute units, the last round holding
+    at most half of them: those walks run as two workgroups each (chunks
+    [split, end) from the final-state gradient, chunks [0, split) from the
+    adjoint the states kernel computes for them).  1 x 300 tokens (5 chunks,
+    split after 2), 272 heads of two groups, document resets in both halves,
+    an initial state and a final-state gradient; every gradient against the
+    oracle."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    H = cus + 16
+    wl = workloads.custom_workload(name=f"bwd_tail_{io}", batch=1, seqlen=300, nheads=H, headdim=16,
+                                   dstate=16, ngroups=2, chunk_size=64, io=io)
+    inp = workloads.make_inputs(wl, seed=31)
+    r = np.random.default_rng(37)
+    seq = np.zeros((1, 300), dtype=np.int32)
+    seq[0, 50:] = 1      # in the first half (chunks 0-1)
+    seq[0, 200:] = 2     # in the second half (chunks 2-4)
+    seq[0, 256:] = 3     # at a chunk start
+    h0 = r.standard_normal((1, H, 16, 16))
+    dfinal = r.standard_normal((1, H, 16, 16))
+    g, ref = _run(inp, seq, h0, dfinal, seed=31)
+    errs = _check(g, ref, TOL[io], wl.name)
+    print(wl.name, {k: f"{e:.1e}" for k, e in errs.items()})
