@@ -183,12 +183,12 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
     // bf16, two steps, about 16 bits: they give the terms of dl, where sums of
     // both signs magnify rounding.  fp32 inputs keep fp32 MFMA throughout.
     constexpr bool kBf = std::is_same<IO, bf16>::value;
-    __shared__ __attribute__((aligned(16))) SegLds<Q> sg;
+    __shared__ __attribute__((aligned(16))) SegLds<Q> sgb[2];   // segsum values of the chunk (c & 1)
     __shared__ __attribute__((aligned(16))) float sG[kMaxGN];  // adjoint of the state at the chunk end, [P][N + 4]
     __shared__ float sL[Q * LQ];            // decay mask L[i][j], then V[i][j] = dy_i . x_j
     __shared__ float sS[Q * LQ];            // (L o C B^T)[i][j]
     __shared__ float sV[Q * LQ];            // (L o V)[i][j], then row prefix sums of R
-    __shared__ float sw[Q];                 // decay from token j to the chunk end
+    __shared__ float swb[2][Q];             // decay from token j to the chunk end (c & 1)
     __shared__ float sq[Q], sp[Q], sxdX[Q], sdl[Q];
     __shared__ float sK, sDD, sDA;
     // bf16 inputs with headdim <= 64: the chunk's x, dy, B and C rows are
@@ -241,13 +241,41 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
     }
     __syncthreads();
 
-    // token values (dt, reset flag) of the next chunk in the walk are fetched
-    // one chunk ahead, so their memory latency overlaps a chunk's work
-    float dt_next = 0.f;
-    int flag_next = 0;
-    if (tid < Q) {
+    // The segsum values of a chunk (the forward kernels' helpers) are formed
+    // one chunk ahead by the last wave, during the mask phase of the chunk
+    // before it in the walk (the mask's row tiles leave that wave idle), into
+    // the other of two buffers; the chunk's token values are fetched a chunk
+    // before that.  Lane = token: the helpers' steps read values other lanes
+    // of the same wave wrote, which needs no workgroup barrier.
+    static_assert(Q == 64 && NB <= kBwdThreads / 64 - 1, "one token a lane; the segsum wave has no mask tile");
+    constexpr int SW = kBwdThreads / 64 - 1;   // the segsum wave
+    float dt_tok = 0.f;                        // wave SW: token (lane) values fetched ahead
+    int flag_tok = 0;
+    auto wave_sync = [] {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+    auto seg_make = [&](int cc) {   // wave SW only
+        const int t = tid & 63;
+        SegLds<Q> &s = sgb[cc & 1];
+        seg_store_token<Q>(s, t, dt_tok, A_h, flag_tok);
+        const int any = __ballot(flag_tok) != 0ull;
+        if (t == 0) s.any_reset = any;
+        wave_sync();
+        seg_block_sums<Q>(s, t);
+        wave_sync();
+        seg_chunk_products<Q>(s, t);
+        const int K = t >> 4;
+        float Z = 1.f;
+        for (int k = NB - 1; k > K; --k) Z = __fmul_rn(Z, s.Tb[k]);
+        swb[cc & 1][t] = __fmul_rn(s.W[t], Z);
+    };
+    if (wave == SW) {
         const int cl0 = c_hi - 1;
-        seg_fetch_token(tid, cl0 * Q, min(Q, L - cl0 * Q), dt_row, H, seq_row, dt_next, flag_next);
+        seg_fetch_token(tid & 63, cl0 * Q, min(Q, L - cl0 * Q), dt_row, H, seq_row, dt_tok, flag_tok);
+        seg_make(cl0);
+        if (cl0 > c_lo) seg_fetch_token(tid & 63, (cl0 - 1) * Q, Q, dt_row, H, seq_row, dt_tok, flag_tok);
     }
     // H_{c-1}: from the forward's scan, or (a single chunk) the initial state or 0
     auto hs_of = [&](int cc) -> const float * {
@@ -319,6 +347,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
     };
     if constexpr (STAGE) stage_load(c_hi - 1);
     for (int c = c_hi - 1; c >= c_lo; --c) {
+        SegLds<Q> &sg = sgb[c & 1];
+        float *const sw = swb[c & 1];
         const int t0 = c * Q;
         const int nvalid = min(Q, L - t0);
         const float *Hs = hs_of(c);
@@ -354,30 +384,15 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
             Cc = (const IO *)a.C + bo(t0);
         }
 
-        // ---- segsum values of the chunk (the forward kernels' helpers)
-        int flag_any = 0;
+        // the chunk's segsum values are in sgb[c & 1] (formed during the
+        // previous chunk, or before the walk); this barrier also publishes
+        // the staged rows and the cleared per-chunk sums
         if (tid < Q) {
-            seg_store_token<Q>(sg, tid, dt_next, A_h, flag_next);
-            flag_any = flag_next;
-            if (c > c_lo) seg_fetch_token(tid, t0 - Q, Q, dt_row, H, seq_row, dt_next, flag_next);
-        }
-        flag_any = __syncthreads_or(flag_any);
-        if (tid == 0) {
-            sg.any_reset = flag_any;
-            sK = 0.f;
-        }
-        if (tid < Q) seg_block_sums<Q>(sg, tid);
-        __syncthreads();
-        if (tid < Q) {
-            seg_chunk_products<Q>(sg, tid);
-            const int K = tid >> 4;
-            float Z = 1.f;
-            for (int k = NB - 1; k > K; --k) Z = __fmul_rn(Z, sg.Tb[k]);
-            sw[tid] = __fmul_rn(sg.W[tid], Z);
             sq[tid] = 0.f;
             sp[tid] = 0.f;
             sxdX[tid] = 0.f;
         }
+        if (tid == 0) sK = 0.f;
         __syncthreads();
 
         // ---- mask, built as the forward kernels build it: nested sums inside
@@ -402,6 +417,13 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) sL[i * LQ + jt * 16 + 4 * g + r] = (i < nvalid) ? v[r] : 0.f;
             }
+        }
+        // the segsum wave: the next chunk's values (chunk c - 1, whole), then
+        // the fetch of the chunk after it; its buffer was the previous chunk's,
+        // whose readers are behind the barriers since
+        if (wave == SW && c > c_lo) {
+            seg_make(c - 1);
+            if (c - 1 > c_lo) seg_fetch_token(tid & 63, (c - 2) * Q, Q, dt_row, H, seq_row, dt_tok, flag_tok);
         }
         __syncthreads();
 
