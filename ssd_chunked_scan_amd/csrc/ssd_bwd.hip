@@ -245,31 +245,85 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
     // one chunk ahead by the last wave, during the mask phase of the chunk
     // before it in the walk (the mask's row tiles leave that wave idle), into
     // the other of two buffers; the chunk's token values are fetched a chunk
-    // before that.  Lane = token: the helpers' steps read values other lanes
-    // of the same wave wrote, which needs no workgroup barrier.
+    // before that.
     static_assert(Q == 64 && NB <= kBwdThreads / 64 - 1, "one token a lane; the segsum wave has no mask tile");
     constexpr int SW = kBwdThreads / 64 - 1;   // the segsum wave
     float dt_tok = 0.f;                        // wave SW: token (lane) values fetched ahead
     int flag_tok = 0;
-    auto wave_sync = [] {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    };
+    // The helpers' steps 1-3 in registers (lane = token; a 16-lane DPP row
+    // is one sub-block): nested sums by row shifts, in the association order
+    // of seg_block_sums' loops (suffix (t, end] from the right, prefix
+    // [B0, t] from the left), so every value is the helpers' bit for bit;
+    // the sub-block totals and last resets are read out of lanes 16 k and
+    // 16 k + 15.  One write of each field.
     auto seg_make = [&](int cc) {   // wave SW only
-        const int t = tid & 63;
+        const int t = tid & 63, K = t >> 4;
         SegLds<Q> &s = sgb[cc & 1];
-        seg_store_token<Q>(s, t, dt_tok, A_h, flag_tok);
-        const int any = __ballot(flag_tok) != 0ull;
-        if (t == 0) s.any_reset = any;
-        wave_sync();
-        seg_block_sums<Q>(s, t);
-        wave_sync();
-        seg_chunk_products<Q>(s, t);
-        const int K = t >> 4;
-        float Z = 1.f;
-        for (int k = NB - 1; k > K; --k) Z = __fmul_rn(Z, s.Tb[k]);
-        swb[cc & 1][t] = __fmul_rn(s.W[t], Z);
+        const int flag = flag_tok;
+        const float d = __fmul_rn(__fmul_rn(dt_tok, A_h), kLog2e);
+        float e = d, pre = d;
+#pragma unroll
+        for (int k = 0; k < 15; ++k) {
+            e = __fadd_rn(dpp_f<kDppRowShl1>(e), d);    // d_t + sum over (t, t + k + 1]
+            pre = __fadd_rn(dpp_f<kDppRowShr1>(pre), d);  // sum over [t - k - 1, t]
+        }
+        const float suf = dpp_f<kDppRowShl1>(e);          // sum over (t, end of sub-block]
+        int lastin = -1, fsuf = 0;
+        if (seq_row) {
+            int v = flag ? t + 1 : 0;                      // 1 + last reset <= t in the sub-block
+            v = max(v, dpp_row<kDppRowShr1>(v));
+            v = max(v, dpp_row<kDppRowShr1 + 1>(v));
+            v = max(v, dpp_row<kDppRowShr1 + 3>(v));
+            v = max(v, dpp_row<kDppRowShr1 + 7>(v));
+            lastin = v - 1;
+            int f = dpp_row<kDppRowShl1>(flag);            // a reset in (t, end of sub-block]
+            f |= dpp_row<kDppRowShl1>(f);
+            f |= dpp_row<kDppRowShl1 + 1>(f);
+            f |= dpp_row<kDppRowShl1 + 3>(f);
+            f |= dpp_row<kDppRowShl1 + 7>(f);
+            fsuf = f;
+        }
+        const float W = fsuf ? 0.f : __builtin_amdgcn_exp2f(suf);
+        const float u0 = (lastin >= 0) ? 0.f : __builtin_amdgcn_exp2f(pre);
+        const float tb = (fsuf | flag) ? 0.f : __builtin_amdgcn_exp2f(e);   // lane 16 k: Tb[k]
+        float Tb[NB];
+        int blast[NB];
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+            Tb[k] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, tb), 16 * k));
+            blast[k] = __builtin_amdgcn_readlane(lastin, 16 * k + 15);
+        }
+        const int any = __ballot(flag) != 0ull;
+        float V = 1.f, Z = 1.f, T = 1.f;
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+            if (k < K) V = __fmul_rn(V, Tb[k]);
+            T = __fmul_rn(T, Tb[k]);
+        }
+#pragma unroll
+        for (int k = NB - 1; k >= 0; --k)
+            if (k > K) Z = __fmul_rn(Z, Tb[k]);
+        int rs = lastin;
+        if (any && rs < 0)
+#pragma unroll
+            for (int k = 0; k < NB; ++k)
+                if (k < K && blast[k] >= 0) rs = blast[k];
+        s.d[t] = d;
+        s.dt[t] = dt_tok;
+        s.flag[t] = flag;
+        s.W[t] = W;
+        s.u[t] = __fmul_rn(u0, V);
+        s.wcd[t] = __fmul_rn(__fmul_rn(W, Z), dt_tok);
+        s.rs[t] = rs;
+        if (t < NB) {
+            s.Tb[t] = Tb[t];
+            s.blast[t] = blast[t];
+        }
+        if (t == 0) {
+            s.T = T;
+            s.any_reset = any;
+        }
+        swb[cc & 1][t] = __fmul_rn(W, Z);
     };
     if (wave == SW) {
         const int cl0 = c_hi - 1;
