@@ -187,7 +187,15 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) float sG[kMaxGN];  // adjoint of the state at the chunk end, [P][N + 4]
     __shared__ float sL[Q * LQ];            // decay mask L[i][j], then V[i][j] = dy_i . x_j
     __shared__ float sS[Q * LQ];            // (L o C B^T)[i][j]
-    __shared__ float sV[Q * LQ];            // (L o V)[i][j], then row prefix sums of R
+    // fp32 inputs: (L o V)[i][j], the masked operand of dB and dC
+    __shared__ float sV[kBf ? 1 : Q * LQ];
+    // bf16 inputs: the masked operands of dB and dC as bf16 in MFMA k-slot
+    // order, one 16-byte read per step: row t holds at slot (4 q + s) 8 + e
+    // the value at token 32 q + 4 e + s of (L o V)[.][t] (dB) or of
+    // dt o (L o V)[t][.] (dC); rows of 64 + 8 elements.  Upper tiles are
+    // never written and stay 0 from the clear at the start.
+    constexpr int LPB = Q + 8;
+    __shared__ __attribute__((aligned(16))) bf16 sLVt[kBf ? Q * LPB : 8], sLdVt[kBf ? Q * LPB : 8];
     __shared__ float swb[2][Q];             // decay from token j to the chunk end (c & 1)
     __shared__ float sq[Q], sp[Q], sxdX[Q], sdl[Q];
     __shared__ float sK, sDD, sDA;
@@ -235,6 +243,11 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
     const int xs = STAGE ? XPe : gxs, bs = STAGE ? BPe : gbs;   // ... where operands are read
 
     for (int e = tid; e < PN; e += kBwdThreads) sG[(e / N) * GN + e % N] = g0 ? g0[e] : 0.f;
+    if constexpr (kBf)
+        for (int e = tid; e < Q * LPB / 8; e += kBwdThreads) {
+            ((uint4 *)sLVt)[e] = uint4{0u, 0u, 0u, 0u};
+            ((uint4 *)sLdVt)[e] = uint4{0u, 0u, 0u, 0u};
+        }
     if (tid == 0) {
         sDD = 0.f;
         sDA = 0.f;
@@ -542,10 +555,19 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
                 const f32x4 vv = product(dyc, xc, cl(i) * xs, cl(j) * xs, P);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int e = (I * 16 + 4 * g + r) * LQ + J * 16 + l16;
+                    const int ii = I * 16 + 4 * g + r;
+                    const int e = ii * LQ + J * 16 + l16;
                     const float l = sL[e];
+                    const float lv = l * vv[r];
                     sS[e] = l * sv[r];
-                    sV[e] = l * vv[r];
+                    if constexpr (kBf) {
+                        // (L o V)[ii][j] into row j of the dB operand at token ii,
+                        // dt_j (L o V)[ii][j] into row ii of the dC operand at token j
+                        sLVt[j * LPB + ((ii >> 5) * 4 + (ii & 3)) * 8 + ((ii >> 2) & 7)] = (bf16)lv;
+                        sLdVt[ii * LPB + ((j >> 5) * 4 + (j & 3)) * 8 + ((j >> 2) & 7)] = (bf16)(sg.dt[j] * lv);
+                    } else {
+                        sV[e] = lv;
+                    }
                     sL[e] = vv[r];
                 }
             }
@@ -728,16 +750,13 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
                     if constexpr (kBf) {
 #pragma unroll
-                        for (int q = 0; q < NB / 2; ++q) {   // pairs of blocks, blocks I < T zeroed
+                        for (int q = 0; q < NB / 2; ++q) {   // pairs of blocks; blocks I < T read as 0
                             if (2 * q + 1 < T) continue;
-                            float av[8], bw[8];
+                            float bw[8];
 #pragma unroll
-                            for (int e = 0; e < 8; ++e) {
-                                const int st = 8 * q + e;
-                                av[e] = (2 * q + (e >> 2) < T) ? 0.f : sV[(4 * st + g) * LQ + tr];   // (L o V)[i][t]
-                                bw[e] = cvs[st];
-                            }
-                            acc = mfma_bf16(bf16x8_of(av), bf16x8_of(bw), acc);
+                            for (int e = 0; e < 8; ++e) bw[e] = cvs[8 * q + e];
+                            const bf16x8 av = *(const bf16x8 *)&sLVt[tr * LPB + (4 * q + g) * 8];   // (L o V)[i][t]
+                            acc = mfma_bf16(av, bf16x8_of(bw), acc);
                         }
 #pragma unroll
                         for (int v = 0; v < PV; ++v) {
@@ -775,16 +794,13 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
                     acc2 = f32x4{0.f, 0.f, 0.f, 0.f};
                     if constexpr (kBf) {
 #pragma unroll
-                        for (int q = 0; q < NB / 2; ++q) {   // pairs of blocks, blocks J > T zeroed
+                        for (int q = 0; q < NB / 2; ++q) {   // pairs of blocks; blocks J > T read as 0
                             if (2 * q > T) break;
-                            float av[8], bw[8];
+                            float bw[8];
 #pragma unroll
-                            for (int e = 0; e < 8; ++e) {
-                                const int j = 4 * (8 * q + e) + g;
-                                av[e] = (2 * q + (e >> 2) > T) ? 0.f : sg.dt[j] * sV[tr * LQ + j];   // (L o dt o V)[t][j]
-                                bw[e] = bvs[8 * q + e];
-                            }
-                            acc = mfma_bf16(bf16x8_of(av), bf16x8_of(bw), acc);
+                            for (int e = 0; e < 8; ++e) bw[e] = bvs[8 * q + e];
+                            const bf16x8 av = *(const bf16x8 *)&sLdVt[tr * LPB + (4 * q + g) * 8];   // (L o dt o V)[t][j]
+                            acc = mfma_bf16(av, bf16x8_of(bw), acc);
                         }
                     } else {
 #pragma unroll
@@ -851,7 +867,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
             float run = group8_scan(loc, q) - loc;
 #pragma unroll
             for (int c8 = 0; c8 < CPL; ++c8) {
-                sV[s * LQ + CPL * q + c8] = run;   // sum_{r' < r} R_{s r'}
+                sL[s * LQ + CPL * q + c8] = run;   // sum_{r' < r} R_{s r'}, over V (read above)
                 run += Rv[c8];
             }
         }
@@ -862,7 +878,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
 #pragma unroll
             for (int k8 = 0; k8 < CPL; ++k8) {
                 const int s = q + LPR * k8;
-                if (s >= t) dl += sV[s * LQ + t] + sq[s];
+                if (s >= t) dl += sL[s * LQ + t] + sq[s];
                 else dl += sp[s];
             }
             dl = group8_sum(dl);
