@@ -185,7 +185,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
     constexpr bool kBf = std::is_same<IO, bf16>::value;
     __shared__ __attribute__((aligned(16))) SegLds<Q> sgb[2];   // segsum values of the chunk (c & 1)
     __shared__ __attribute__((aligned(16))) float sG[kMaxGN];  // adjoint of the state at the chunk end, [P][N + 4]
-    __shared__ float sL[Q * LQ];            // decay mask L[i][j], then V[i][j] = dy_i . x_j
+    // fp32 inputs: the decay mask L[i][j], then V[i][j] = dy_i . x_j, then R's
+    // row prefix sums (bf16 inputs form L inside the S/V job instead)
+    __shared__ float sL[kBf ? 1 : Q * LQ];
     __shared__ float sS[Q * LQ];            // (L o C B^T)[i][j]
     // fp32 inputs: (L o V)[i][j], the masked operand of dB and dC
     __shared__ float sV[kBf ? 1 : Q * LQ];
@@ -196,6 +198,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
     // never written and stay 0 from the clear at the start.
     constexpr int LPB = Q + 8;
     __shared__ __attribute__((aligned(16))) bf16 sLVt[kBf ? Q * LPB : 8], sLdVt[kBf ? Q * LPB : 8];
+    // bf16 inputs: the masked operand of dX, (L o S)[.][j] in row j, same layout
+    __shared__ __attribute__((aligned(16))) bf16 sLSt[kBf ? Q * LPB : 8];
     __shared__ float swb[2][Q];             // decay from token j to the chunk end (c & 1)
     __shared__ float sq[Q], sp[Q], sxdX[Q], sdl[Q];
     __shared__ float sK, sDD, sDA;
@@ -247,6 +251,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
         for (int e = tid; e < Q * LPB / 8; e += kBwdThreads) {
             ((uint4 *)sLVt)[e] = uint4{0u, 0u, 0u, 0u};
             ((uint4 *)sLdVt)[e] = uint4{0u, 0u, 0u, 0u};
+            ((uint4 *)sLSt)[e] = uint4{0u, 0u, 0u, 0u};
         }
     if (tid == 0) {
         sDD = 0.f;
@@ -462,9 +467,22 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
         if (tid == 0) sK = 0.f;
         __syncthreads();
 
-        // ---- mask, built as the forward kernels build it: nested sums inside
-        // 16-token sub-blocks, rank-one factors across them.  A wave takes a
-        // 16-row tile, a lane row i and columns 16 jt + 4 g + r.
+        // the segsum wave: the next chunk's values (chunk c - 1, whole), then
+        // the fetch of the chunk after it; its buffer was the previous chunk's,
+        // whose readers are behind the barriers since.  It runs in the first
+        // phase that leaves it idle: the mask (fp32 inputs), or the S/V jobs
+        // (bf16 inputs: ten jobs over eight waves).
+        auto seg_ahead = [&] {
+            if (wave == SW && c > c_lo) {
+                seg_make(c - 1);
+                if (c - 1 > c_lo) seg_fetch_token(tid & 63, (c - 2) * Q, Q, dt_row, H, seq_row, dt_tok, flag_tok);
+            }
+        };
+
+        // ---- mask (fp32 inputs), built as the forward kernels build it:
+        // nested sums inside 16-token sub-blocks, rank-one factors across them.
+        // A wave takes a 16-row tile, a lane row i and columns 16 jt + 4 g + r.
+        if constexpr (!kBf) {
         for (int I = wave; I < NB; I += kBwdThreads / 64) {
             const int i = I * 16 + l16;
             const int rs_i = sg.rs[i];
@@ -485,14 +503,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
                 for (int r = 0; r < 4; ++r) sL[i * LQ + jt * 16 + 4 * g + r] = (i < nvalid) ? v[r] : 0.f;
             }
         }
-        // the segsum wave: the next chunk's values (chunk c - 1, whole), then
-        // the fetch of the chunk after it; its buffer was the previous chunk's,
-        // whose readers are behind the barriers since
-        if (wave == SW && c > c_lo) {
-            seg_make(c - 1);
-            if (c - 1 > c_lo) seg_fetch_token(tid & 63, (c - 2) * Q, Q, dt_row, H, seq_row, dt_tok, flag_tok);
-        }
+        seg_ahead();
         __syncthreads();
+        }
 
         // ---- S = C B^T and V = dY X^T on the lower 16 x 16 tiles (upper tiles
         // are never read), one job per tile computing both.  Stored: L o S in
@@ -553,25 +566,63 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
                 const int i = I * 16 + l16, j = J * 16 + l16;
                 const f32x4 sv = product(Cc, Bc, cl(i) * bs, cl(j) * bs, N);
                 const f32x4 vv = product(dyc, xc, cl(i) * xs, cl(j) * xs, P);
+                if constexpr (kBf) {
+                    // the mask entries of this lane, L[ii][j] for rows
+                    // ii = 16 I + 4 g + r, with the mask loop's arithmetic:
+                    // diagonal tile, the nested sum over (j, ii] added from ii
+                    // down; off the diagonal, the chain start (the sum over
+                    // [16 I, ii]) times the sub-block decays Tb[I-1] .. Tb[J+1]
+                    // in that order, times W_j
+                    const int I0 = I * 16;
+                    float dd[16];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int ii = I * 16 + 4 * g + r;
-                    const int e = ii * LQ + J * 16 + l16;
-                    const float l = sL[e];
-                    const float lv = l * vv[r];
-                    sS[e] = l * sv[r];
-                    if constexpr (kBf) {
-                        // (L o V)[ii][j] into row j of the dB operand at token ii,
-                        // dt_j (L o V)[ii][j] into row ii of the dC operand at token j
-                        sLVt[j * LPB + ((ii >> 5) * 4 + (ii & 3)) * 8 + ((ii >> 2) & 7)] = (bf16)lv;
-                        sLdVt[ii * LPB + ((j >> 5) * 4 + (j & 3)) * 8 + ((j >> 2) & 7)] = (bf16)(sg.dt[j] * lv);
-                    } else {
-                        sV[e] = lv;
+                    for (int kk = 0; kk < 16; ++kk) dd[kk] = sg.d[I0 + kk];
+                    const float dtj = sg.dt[j], Wj = sg.W[j];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int ii = I0 + 4 * g + r;
+                        const int rs_i = sg.rs[ii];
+                        float lm;
+                        if (I == J) {
+                            float es = 0.f;
+#pragma unroll
+                            for (int kk = 15; kk >= 0; --kk)
+                                if (I0 + kk <= ii && I0 + kk > j) es = __fadd_rn(es, dd[kk]);
+                            lm = seg_diag_value(es, ii, j, rs_i);
+                        } else {
+                            float sum0 = 0.f;
+#pragma unroll
+                            for (int kk = 15; kk >= 0; --kk)
+                                if (I0 + kk <= ii) sum0 = __fadd_rn(sum0, dd[kk]);
+                            float F = seg_chain_start(sum0, I0, rs_i);
+                            for (int jt = I - 2; jt >= J; --jt) F = seg_chain_step(F, sg.Tb[jt + 1]);
+                            lm = seg_offdiag(F, Wj);
+                        }
+                        if (ii >= nvalid) lm = 0.f;
+                        const float ls = lm * sv[r], lv = lm * vv[r];
+                        const int si = ((ii >> 5) * 4 + (ii & 3)) * 8 + ((ii >> 2) & 7);   // ii's slot
+                        // (L o S)[ii][j] and (L o V)[ii][j] into row j of the dX
+                        // and dB operands at token ii; dt_j (L o V)[ii][j] into
+                        // row ii of the dC operand at token j; R[ii][j] =
+                        // (L o S) dt V (the order of the fp32 path's R walk)
+                        sLSt[j * LPB + si] = (bf16)ls;
+                        sLVt[j * LPB + si] = (bf16)lv;
+                        sLdVt[ii * LPB + ((j >> 5) * 4 + (j & 3)) * 8 + ((j >> 2) & 7)] = (bf16)(dtj * lv);
+                        sS[ii * LQ + j] = ls * dtj * vv[r];
                     }
-                    sL[e] = vv[r];
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int e = (I * 16 + 4 * g + r) * LQ + J * 16 + l16;
+                        const float l = sL[e];
+                        sS[e] = l * sv[r];
+                        sV[e] = l * vv[r];
+                        sL[e] = vv[r];
+                    }
                 }
             }
         }
+        if constexpr (kBf) seg_ahead();
         __syncthreads();
 
         float ddsum = 0.f;
@@ -620,14 +671,11 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
 #pragma unroll
                         for (int q = 0; q < NB / 2; ++q) {
                             if (2 * q + 1 < J) continue;
-                            float av[8], bw[8];
+                            float bw[8];
 #pragma unroll
-                            for (int e = 0; e < 8; ++e) {
-                                const int st = 8 * q + e;
-                                av[e] = (2 * q + (e >> 2) < J) ? 0.f : sS[(4 * st + g) * LQ + jr];
-                                bw[e] = dyv[st];
-                            }
-                            acc = mfma_bf16(bf16x8_of(av), bf16x8_of(bw), acc);
+                            for (int e = 0; e < 8; ++e) bw[e] = dyv[8 * q + e];
+                            const bf16x8 av = *(const bf16x8 *)&sLSt[jr * LPB + (4 * q + g) * 8];   // (L o S)[i][j]
+                            acc = mfma_bf16(av, bf16x8_of(bw), acc);
                         }
                     } else {
 #pragma unroll
@@ -861,13 +909,16 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
 #pragma unroll
             for (int c8 = 0; c8 < CPL; ++c8) {
                 const int r = CPL * q + c8;
-                Rv[c8] = (r <= s) ? sS[s * LQ + r] * sg.dt[r] * sL[s * LQ + r] : 0.f;   // (L o S) dt V
+                if constexpr (kBf)
+                    Rv[c8] = (r <= s) ? sS[s * LQ + r] : 0.f;   // R, formed by the S/V job
+                else
+                    Rv[c8] = (r <= s) ? sS[s * LQ + r] * sg.dt[r] * sL[s * LQ + r] : 0.f;   // (L o S) dt V
                 loc += Rv[c8];
             }
             float run = group8_scan(loc, q) - loc;
 #pragma unroll
             for (int c8 = 0; c8 < CPL; ++c8) {
-                sL[s * LQ + CPL * q + c8] = run;   // sum_{r' < r} R_{s r'}, over V (read above)
+                (kBf ? sS : sL)[s * LQ + CPL * q + c8] = run;   // sum_{r' < r} R_{s r'}, over what was read above
                 run += Rv[c8];
             }
         }
@@ -878,7 +929,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
 #pragma unroll
             for (int k8 = 0; k8 < CPL; ++k8) {
                 const int s = q + LPR * k8;
-                if (s >= t) dl += sL[s * LQ + t] + sq[s];
+                if (s >= t) dl += (kBf ? sS : sL)[s * LQ + t] + sq[s];
                 else dl += sp[s];
             }
             dl = group8_sum(dl);
