@@ -955,6 +955,46 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
             static_assert(kWaves % 8 == 0, "headdim blocks divide the wave count");
             const int Pb = wave % PU;
             const int p = Pb * 16 + l16;
+            if constexpr (STAGE) {
+                // staged bf16 rows: lane group g takes tokens 32 q + 8 g + e
+                // (e = 0..7) of the u o dy and C columns, each operand two
+                // 16-bit transpose reads of four consecutive rows (rows past
+                // the end hold the last valid token and meet u = 0)
+                auto tr8 = [&](const bf16 *base, int pitch, int q, int col0) {
+                    const int rr = 32 * q + 8 * g + (l16 >> 2), cc = col0 + 4 * (l16 & 3);
+                    return join_bf16x8(lds_read_tr16(base + rr * pitch + cc),
+                                       lds_read_tr16(base + (rr + 4) * pitch + cc));
+                };
+                bf16x8 dvhi[NB / 2], dvlo[NB / 2];
+#pragma unroll
+                for (int q = 0; q < NB / 2; ++q) {
+                    const bf16x8 d8 = tr8(sDYs, XPe, q, Pb * 16);
+                    const float4 u0 = *(const float4 *)&sg.u[32 * q + 8 * g];
+                    const float4 u1 = *(const float4 *)&sg.u[32 * q + 8 * g + 4];
+                    const float uu[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+                    float w[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) w[e] = ok(32 * q + 8 * g + e) ? uu[e] * (float)d8[e] : 0.f;
+                    bf16x8_split(w, dvhi[q], dvlo[q]);
+                }
+                for (int Nb = wave / PU; Nb < N / 16; Nb += kWaves / PU) {
+                    const int n = Nb * 16 + l16;
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int q = 0; q < NB / 2; ++q) {
+                        if (32 * q >= nvalid) break;
+                        const bf16x8 cc = tr8(sCs, BPe, q, Nb * 16);
+                        acc = mfma_bf16(dvhi[q], cc, acc);
+                        acc2 = mfma_bf16(dvlo[q], cc, acc2);
+                    }
+                    mfma_f32_fence(acc, acc2);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        float *gp = &sG[(Pb * 16 + 4 * g + r) * GN + n];
+                        *gp = fmaf(sg.T, *gp, acc[r] + acc2[r]);
+                    }
+                }
+            } else {
             float dv[4 * NB];
 #pragma unroll
             for (int st = 0; st < 4 * NB; ++st) {
@@ -1004,6 +1044,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
                     float *gp = &sG[(Pb * 16 + 4 * g + r) * GN + n];
                     *gp = fmaf(sg.T, *gp, acc[r] + acc2[r]);
                 }
+            }
             }
         }
         __syncthreads();
