@@ -191,11 +191,11 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
     __shared__ float sS[Q * LQ];            // (L o C B^T)[i][j]
     // fp32 inputs: (L o V)[i][j], the masked operand of dB and dC
     __shared__ float sV[kBf ? 1 : Q * LQ];
-    // bf16 inputs: the masked operands of dB and dC as bf16 in MFMA k-slot
-    // order, one 16-byte read per step: row t holds at slot (4 q + s) 8 + e
-    // the value at token 32 q + 4 e + s of (L o V)[.][t] (dB) or of
-    // dt o (L o V)[t][.] (dC); rows of 64 + 8 elements.  Upper tiles are
-    // never written and stay 0 from the clear at the start.
+    // bf16 inputs: the masked operands of dB and dC as bf16, row t holding
+    // (L o V)[i][t] at i (dB) or dt_j (L o V)[t][j] at j (dC), so that a
+    // lane group's 8 consecutive tokens (its contraction slots) are one
+    // 16-byte read; rows of 64 + 8 elements.  Upper tiles are never written
+    // and stay 0 from the clear at the start.
     constexpr int LPB = Q + 8;
     __shared__ __attribute__((aligned(16))) bf16 sLVt[kBf ? Q * LPB : 8], sLdVt[kBf ? Q * LPB : 8];
     // bf16 inputs: the masked operand of dX, (L o S)[.][j] in row j, same layout
@@ -437,6 +437,17 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
         // dt = 0, or by the output row's own guard (the state update zeroes
         // them explicitly).
         auto cl = [&](int t) { return min(t, nvalid - 1); };
+        // Contraction slots of the masked products and the adjoint update
+        // with bf16 inputs: lane group g takes the 8 consecutive tokens
+        // 32 q + 8 g + e of slab q (fp32 inputs: token 4 st + g of step st).
+        // With staged rows a column's 8 tokens are two 16-bit transpose reads
+        // of four consecutive rows (rows past the end hold the last valid
+        // token; every product meets a 0 there).
+        auto ktok = [&](int st) { return kBf ? 32 * (st >> 3) + 8 * g + (st & 7) : 4 * st + g; };
+        auto tr8 = [&](const bf16 *base, int pitch, int q, int col0) {
+            const int rr = 32 * q + 8 * g + (l16 >> 2), cc = col0 + 4 * (l16 & 3);
+            return join_bf16x8(lds_read_tr16(base + rr * pitch + cc), lds_read_tr16(base + (rr + 4) * pitch + cc));
+        };
         // the chunk's first token rows; tokens step by xs (x, dy) or bs (B, C)
         // elements, so in-chunk offsets fit 32 bits and the loads take a
         // scalar base
@@ -600,14 +611,13 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
                         }
                         if (ii >= nvalid) lm = 0.f;
                         const float ls = lm * sv[r], lv = lm * vv[r];
-                        const int si = ((ii >> 5) * 4 + (ii & 3)) * 8 + ((ii >> 2) & 7);   // ii's slot
                         // (L o S)[ii][j] and (L o V)[ii][j] into row j of the dX
                         // and dB operands at token ii; dt_j (L o V)[ii][j] into
                         // row ii of the dC operand at token j; R[ii][j] =
                         // (L o S) dt V (the order of the fp32 path's R walk)
-                        sLSt[j * LPB + si] = (bf16)ls;
-                        sLVt[j * LPB + si] = (bf16)lv;
-                        sLdVt[ii * LPB + ((j >> 5) * 4 + (j & 3)) * 8 + ((j >> 2) & 7)] = (bf16)(dtj * lv);
+                        sLSt[j * LPB + ii] = (bf16)ls;
+                        sLVt[j * LPB + ii] = (bf16)lv;
+                        sLdVt[ii * LPB + j] = (bf16)(dtj * lv);
                         sS[ii * LQ + j] = ls * dtj * vv[r];
                     }
                 } else {
@@ -641,7 +651,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
                 float dyv[4 * NB];
                 float4 gv[kMaxK / 16];
 #pragma unroll
-                for (int st = 0; st < 4 * NB; ++st) dyv[st] = ld1(dyc, cl(4 * st + g) * xs + p);
+                for (int st = 0; st < 4 * NB; ++st)
+                    dyv[st] = STAGE ? 0.f : ld1(dyc, cl(ktok(st)) * xs + p);   // staged: transpose reads below
 #pragma unroll
                 for (int u = 0; u < kMaxK / 16; ++u)   // blocks past N: B is 0 there, G read at a valid column
                     gv[u] = *(const float4 *)&sG[p * GN + min(16 * u, N - 16) + 4 * g];
@@ -671,11 +682,17 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
 #pragma unroll
                         for (int q = 0; q < NB / 2; ++q) {
                             if (2 * q + 1 < J) continue;
-                            float bw[8];
+                            bf16x8 bb;
+                            if constexpr (STAGE) {
+                                bb = tr8(sDYs, XPe, q, Pb * 16);
+                            } else {
+                                float bw[8];
 #pragma unroll
-                            for (int e = 0; e < 8; ++e) bw[e] = dyv[8 * q + e];
-                            const bf16x8 av = *(const bf16x8 *)&sLSt[jr * LPB + (4 * q + g) * 8];   // (L o S)[i][j]
-                            acc = mfma_bf16(av, bf16x8_of(bw), acc);
+                                for (int e = 0; e < 8; ++e) bw[e] = dyv[8 * q + e];
+                                bb = bf16x8_of(bw);
+                            }
+                            const bf16x8 av = *(const bf16x8 *)&sLSt[jr * LPB + 32 * q + 8 * g];   // (L o S)[i][j]
+                            acc = mfma_bf16(av, bb, acc);
                         }
                     } else {
 #pragma unroll
@@ -749,10 +766,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
             if (T0 < NB) {
                 float cvs[4 * NB], bvs[4 * NB], gq[4 * PU];
 #pragma unroll
-                for (int st = 0; st < 4 * NB; ++st) {
-                    const int i = 4 * st + g;
-                    cvs[st] = ld1(Cc, cl(i) * bs + n);
-                    bvs[st] = ld1(Bc, cl(i) * bs + n);
+                for (int st = 0; st < 4 * NB; ++st) {   // staged: transpose reads below
+                    const int i = ktok(st);
+                    cvs[st] = STAGE ? 0.f : ld1(Cc, cl(i) * bs + n);
+                    bvs[st] = STAGE ? 0.f : ld1(Bc, cl(i) * bs + n);
                 }
 #pragma unroll
                 for (int u = 0; u < PU; ++u)
@@ -800,11 +817,17 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
 #pragma unroll
                         for (int q = 0; q < NB / 2; ++q) {   // pairs of blocks; blocks I < T read as 0
                             if (2 * q + 1 < T) continue;
-                            float bw[8];
+                            bf16x8 bb;
+                            if constexpr (STAGE) {
+                                bb = tr8(sCs, BPe, q, Nb * 16);
+                            } else {
+                                float bw[8];
 #pragma unroll
-                            for (int e = 0; e < 8; ++e) bw[e] = cvs[8 * q + e];
-                            const bf16x8 av = *(const bf16x8 *)&sLVt[tr * LPB + (4 * q + g) * 8];   // (L o V)[i][t]
-                            acc = mfma_bf16(av, bf16x8_of(bw), acc);
+                                for (int e = 0; e < 8; ++e) bw[e] = cvs[8 * q + e];
+                                bb = bf16x8_of(bw);
+                            }
+                            const bf16x8 av = *(const bf16x8 *)&sLVt[tr * LPB + 32 * q + 8 * g];   // (L o V)[i][t]
+                            acc = mfma_bf16(av, bb, acc);
                         }
 #pragma unroll
                         for (int v = 0; v < PV; ++v) {
@@ -844,11 +867,17 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
 #pragma unroll
                         for (int q = 0; q < NB / 2; ++q) {   // pairs of blocks; blocks J > T read as 0
                             if (2 * q > T) break;
-                            float bw[8];
+                            bf16x8 bb;
+                            if constexpr (STAGE) {
+                                bb = tr8(sBs, BPe, q, Nb * 16);
+                            } else {
+                                float bw[8];
 #pragma unroll
-                            for (int e = 0; e < 8; ++e) bw[e] = bvs[8 * q + e];
-                            const bf16x8 av = *(const bf16x8 *)&sLdVt[tr * LPB + (4 * q + g) * 8];   // (L o dt o V)[t][j]
-                            acc = mfma_bf16(av, bf16x8_of(bw), acc);
+                                for (int e = 0; e < 8; ++e) bw[e] = bvs[8 * q + e];
+                                bb = bf16x8_of(bw);
+                            }
+                            const bf16x8 av = *(const bf16x8 *)&sLdVt[tr * LPB + 32 * q + 8 * g];   // (L o dt o V)[t][j]
+                            acc = mfma_bf16(av, bb, acc);
                         }
                     } else {
 #pragma unroll
@@ -956,15 +985,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
             const int Pb = wave % PU;
             const int p = Pb * 16 + l16;
             if constexpr (STAGE) {
-                // staged bf16 rows: lane group g takes tokens 32 q + 8 g + e
-                // (e = 0..7) of the u o dy and C columns, each operand two
-                // 16-bit transpose reads of four consecutive rows (rows past
-                // the end hold the last valid token and meet u = 0)
-                auto tr8 = [&](const bf16 *base, int pitch, int q, int col0) {
-                    const int rr = 32 * q + 8 * g + (l16 >> 2), cc = col0 + 4 * (l16 & 3);
-                    return join_bf16x8(lds_read_tr16(base + rr * pitch + cc),
-                                       lds_read_tr16(base + (rr + 4) * pitch + cc));
-                };
+                // staged bf16 rows: the u o dy and C columns by transpose
+                // reads, tokens 32 q + 8 g + e (u = 0 past the end)
                 bf16x8 dvhi[NB / 2], dvlo[NB / 2];
 #pragma unroll
                 for (int q = 0; q < NB / 2; ++q) {
