@@ -457,12 +457,16 @@ def ssd_decode_step(x, dt, A, B, C, D, state, y=None, stream=None, dt_bias=None,
     return y
 
 
-def ssd_bwd(x, dt, A, B, C, D, dy, seq_idx=None, init_states=None, dfinal=None, stream=None):
+def ssd_bwd(x, dt, A, B, C, D, dy, seq_idx=None, init_states=None, dfinal=None, stream=None,
+            workspace=None, out=None):
     """Gradients of J = <dy, y> + <dfinal, final_states> for y, final_states =
     ssd_fwd(x, dt, A, B, C, D, seq_idx, init_states=init_states): returns a
     dict of fp32 tensors dx, ddt, dA, dB, dC, dD (None if D is None) and
     dinit (None if init_states is None).  dy has x's dtype; dfinal is fp32
-    [b, H, P, N] or None."""
+    [b, H, P, N] or None.  workspace: a uint8 device tensor of at least
+    ssd_bwd_workspace_bytes (allocated per call when None); out: a dict of
+    the output tensors to write (every gradient the call returns, each of the
+    shape and fp32 dtype above), allocated per call when None."""
     import torch
     lib = load_library()
     dev = x.device
@@ -486,15 +490,30 @@ def ssd_bwd(x, dt, A, B, C, D, dy, seq_idx=None, init_states=None, dfinal=None, 
     if dfinal is not None:
         _need(dfinal, "dfinal", (b, H, P, N), torch.float32, dev)
     f32 = dict(dtype=torch.float32, device=dev)
-    out = {"dx": torch.empty((b, L, H, P), **f32), "ddt": torch.empty((b, L, H), **f32),
-           "dA": torch.empty((H,), **f32), "dB": torch.empty((b, L, G, N), **f32),
-           "dC": torch.empty((b, L, G, N), **f32),
-           "dD": None if D is None else torch.empty((H,), **f32),
-           "dinit": None if init_states is None else torch.empty((b, H, P, N), **f32)}
+    shapes = {"dx": (b, L, H, P), "ddt": (b, L, H), "dA": (H,), "dB": (b, L, G, N),
+              "dC": (b, L, G, N), "dD": None if D is None else (H,),
+              "dinit": None if init_states is None else (b, H, P, N)}
+    if out is None:
+        out = {k: None if v is None else torch.empty(v, **f32) for k, v in shapes.items()}
+    else:
+        out = dict(out)
+        for k, v in shapes.items():
+            if v is None:
+                out[k] = None
+            else:
+                _need(out[k], k, v, torch.float32, dev)
     shape = Shape(b, L, H, P, N, G)
     with torch.cuda.device(dev):
         ws_bytes = int(lib.ssd_bwd_workspace_bytes(ctypes.byref(shape), io))
-        ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+        if workspace is None:
+            ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+        else:
+            if workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous():
+                raise ValueError("workspace: a contiguous uint8 tensor on %s" % dev)
+            if workspace.numel() < ws_bytes:
+                raise ValueError(f"workspace: {workspace.numel()} bytes, {ws_bytes} needed")
+            ws = workspace
+            ws_bytes = workspace.numel()
         if stream is None:
             stream = torch.cuda.current_stream(dev).cuda_stream
         st = lib.ssd_bwd(ctypes.byref(shape), io, _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
