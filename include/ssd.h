@@ -305,10 +305,9 @@ ssd_status_t ssd_decode_step_fused(const ssd_shape_t *shape, ssd_dtype_t io,
  * last round are split in two, 4 P N bytes for each of them (at most half the
  * compute units), each part rounded up to 256 bytes; nothing in it survives
  * the call, and nothing is read from it before the call writes it.
- * Repeatability: dx, dB and dC are the same bit for bit on every call
- * with the same inputs; ddt, dA and dD take sums over the waves of a
- * workgroup in the order the waves arrive, so their last bits may vary from
- * call to call (measured: within 2.2e-7 of each tensor's largest value). */
+ * Repeatability: every gradient is the same bit for bit on every call with
+ * the same inputs (each sum, over the waves of a workgroup, the chunks, the
+ * heads of a group and the batch rows, is taken in a fixed order). */
 size_t ssd_bwd_workspace_bytes(const ssd_shape_t *shape, ssd_dtype_t io);
 ssd_status_t ssd_bwd(const ssd_shape_t *shape, ssd_dtype_t io,
                      const void *x, const float *dt, const float *A,

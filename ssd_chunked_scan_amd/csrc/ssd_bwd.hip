@@ -203,6 +203,13 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
     __shared__ float swb[2][Q];             // decay from token j to the chunk end (c & 1)
     __shared__ float sq[Q], sp[Q], sxdX[Q], sdl[Q];
     __shared__ float sK, sDD, sDA;
+    // Per-wave parts of q, K (one per 16-column block of dstate), p, x . dX
+    // (one per 16-column block of headdim) and dy . x (one per wave): each
+    // written by one lane, then added in a fixed order, so that every
+    // gradient is the same bit for bit from call to call (LDS atomics add in
+    // the order the waves arrive).
+    __shared__ float sqp[kMaxK / 16][Q], spp[PU][Q], sxdXp[PU][Q];
+    __shared__ float sKp[kMaxK / 16], sDDw[kBwdThreads / 64];
     // bf16 inputs with headdim <= 64: the chunk's x, dy, B and C rows are
     // staged in LDS (56 KB), read there by every job.  Row pitches of 40 and
     // 72 dwords (8 mod 32 banks) keep four rows of 16 consecutive columns on
@@ -257,6 +264,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
         sDD = 0.f;
         sDA = 0.f;
     }
+    if (tid < kBwdThreads / 64) sDDw[tid] = 0.f;
     __syncthreads();
 
     // The segsum values of a chunk (the forward kernels' helpers) are formed
@@ -470,12 +478,12 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
         // the chunk's segsum values are in sgb[c & 1] (formed during the
         // previous chunk, or before the walk); this barrier also publishes
         // the staged rows and the cleared per-chunk sums
-        if (tid < Q) {
-            sq[tid] = 0.f;
-            sp[tid] = 0.f;
-            sxdX[tid] = 0.f;
+        for (int e = tid; e < (kMaxK / 16) * Q; e += kBwdThreads) (&sqp[0][0])[e] = 0.f;
+        for (int e = tid; e < PU * Q; e += kBwdThreads) {
+            (&spp[0][0])[e] = 0.f;
+            (&sxdXp[0][0])[e] = 0.f;
         }
-        if (tid == 0) sK = 0.f;
+        if (tid < kMaxK / 16) sKp[tid] = 0.f;
         __syncthreads();
 
         // the segsum wave: the next chunk's values (chunk c - 1, whole), then
@@ -742,8 +750,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
                         xd = row_sum16(xd);
                         pr = row_sum16(pr);
                         if (l16 == 0 && ok(j)) {
-                            atomicAdd(&sxdX[j], xd);
-                            atomicAdd(&sp[j], pr);
+                            sxdXp[Pb][j] = xd;
+                            spp[Pb][j] = pr;
                         }
                     }
                 }
@@ -780,7 +788,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
 #pragma unroll
                     for (int e = 0; e < 4 * PU; ++e) k = fmaf(gq[e], hv[e], k);
                     k = wave_sum(k);
-                    if (lane == 0) atomicAdd(&sK, k);
+                    if (lane == 0) sKp[Nb] = k;   // T0 == 0: one wave per Nb
                 }
                 // bf16: G and H columns as hi + lo bf16 (see dX)
                 constexpr int PV = (PU + 1) / 2;
@@ -918,14 +926,14 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
                             qv = sg.u[t] * acc2[r] * cq[r];
                         }
                         qv = row_sum16(qv);
-                        if (l16 == 0 && ok(t)) atomicAdd(&sq[t], qv);
+                        if (l16 == 0 && ok(t)) sqp[Nb][t] = qv;
                     }
                 }
             }
         }
         if (c > c_lo) load_hv(c - 1, l16, g);
         ddsum = wave_sum(ddsum);
-        if (lane == 0) atomicAdd(&sDD, ddsum);
+        if (lane == 0) sDDw[wave] += ddsum;
         __syncthreads();
 
         // ---- R = L o dt o S o V, then prefix sums of each row over r < t
@@ -949,6 +957,20 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
             for (int c8 = 0; c8 < CPL; ++c8) {
                 (kBf ? sS : sL)[s * LQ + CPL * q + c8] = run;   // sum_{r' < r} R_{s r'}, over what was read above
                 run += Rv[c8];
+            }
+            // the per-wave parts of q_s, p_s, x_s . dX_s and K: lane q of the
+            // row takes part q (parts past dstate or headdim hold 0), then
+            // the row's eight lanes are summed in a fixed order
+            static_assert(kMaxK / 16 == LPR && PU <= LPR, "one part per lane of a row");
+            const float vq = group8_sum(sqp[q][s]);
+            const float vp = group8_sum(q < PU ? spp[q][s] : 0.f);
+            const float vx = group8_sum(q < PU ? sxdXp[q][s] : 0.f);
+            const float vk = group8_sum(sKp[q]);
+            if (q == 0) {
+                sq[s] = vq;
+                sp[s] = vp;
+                sxdX[s] = vx;
+                if (s == 0) sK = vk;
             }
         }
         __syncthreads();
@@ -1080,6 +1102,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void ssd_bwd_kernel(BwdArgs a) {
     if (a.dinit && c_lo == 0)
         for (int e = tid; e < PN; e += kBwdThreads) a.dinit[(int64_t)bh * PN + e] = sG[(e / N) * GN + e % N];
     if (tid == 0) {
+#pragma unroll
+        for (int w = 0; w < kBwdThreads / 64; ++w) sDD += sDDw[w];
         a.dA_part[2 * bh + slot] = sDA;
         a.dD_part[2 * bh + slot] = sDD;
         if (c_lo == 0 && c_hi == a.nchunks) {   // a whole walk fills both slots
